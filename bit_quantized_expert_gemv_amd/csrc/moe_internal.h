@@ -1,0 +1,66 @@
+// Internal interface between the host entry points (moe_host.cpp) and the kernels (moe_kernels.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "moe.h"
+
+namespace bqmoe {
+
+// Shape and blob layout of one layer, validated on the host.
+struct Geometry {
+  int H, I, E, K, NE;  // NE = K + has_shared: expert slots per token
+  int bits, G, has_shared;
+  uint64_t off_codes[3];  // byte offsets of gate / up / down codes inside a blob
+  uint64_t off_sb[3];     // byte offsets of gate / up / down (scale, bias) words
+  uint64_t blob_bytes;
+};
+
+struct LayerPtrs {
+  const uint8_t* experts;
+  uint64_t stride;
+  const uint8_t* shared;
+  const uint16_t* router;
+  const uint16_t* sgate;
+};
+
+// Device workspace carved from the caller's buffer (per token t).
+struct Workspace {
+  double* logits;  // [T][E + 1]: router logits, then the shared-gate logit
+  int32_t* idx;    // [T][K]
+  float* w;        // [T][K]
+  float* g;        // [T]
+  float* h;        // [T][NE][I]: SwiGLU outputs
+  float* u;        // [T][H]: normalised layer input (stack only)
+};
+
+bool geometry_from(const moe_layer_t* L, Geometry* g, const char** why);
+size_t workspace_layer_bytes(const Geometry& g, int T);
+Workspace carve_workspace(const Geometry& g, int T, void* base);
+
+// ---- launchers (moe_kernels.hip); all return hipSuccess or the launch error ----
+
+// Phase 1: router logits (+ shared-gate logit) and, if with_shared_ffn, the shared expert's gate/up
+// SwiGLU into h[t][K]. If norm_src is non-null the layer input is RMSNorm(norm_src) (written to ws.u),
+// otherwise it is x.
+hipError_t launch_router_phase(const Geometry& g, const LayerPtrs& p, const float* x, const float* norm_src, float eps,
+                               int T, const Workspace& ws, bool with_shared_ffn, hipStream_t s);
+// Phase 2: gate/up SwiGLU of the routed experts (slots 0..K-1), plus slot K (shared) if with_shared.
+// If idx_in is null the top-K is computed from ws.logits and written to ws.idx/w/g (and idx_out).
+hipError_t launch_gateup(const Geometry& g, const LayerPtrs& p, const float* x, int T, const Workspace& ws,
+                         const int32_t* idx_in, int32_t* idx_out, bool with_shared, hipStream_t s);
+// Phase 3: down projections. combine: out = residual + sum_k w_k y_k + g y_s; otherwise y[t][k][:] = y_k.
+hipError_t launch_down(const Geometry& g, const LayerPtrs& p, int T, const Workspace& ws, const int32_t* idx,
+                       const float* residual, float* out, float* y, hipStream_t s);
+// Top-K + weights from ws.logits (router-only path).
+hipError_t launch_topk(const Geometry& g, int T, const Workspace& ws, int32_t* idx, float* w, float* sg,
+                       double* logits_out, hipStream_t s);
+hipError_t launch_combine(const Geometry& g, int T, const float* residual, const float* y, const float* w,
+                          const float* sg, float* out, hipStream_t s);
+hipError_t launch_dequant(const Geometry& g, const uint8_t* blob, int matrix, int out_dtype, void* out, hipStream_t s);
+hipError_t launch_pack(int H, int I, int bits, int G, const moe_expert_arrays_t* a, uint8_t* blob, hipStream_t s);
+
+}  // namespace bqmoe

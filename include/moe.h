@@ -1,0 +1,178 @@
+/* moe.h — C ABI of the quantised Mixture-of-Experts expert-layer library for AMD MI355X (gfx950).
+ *
+ * The library computes one MoE layer per token, for the 397B, 512-expert, hidden-4096 model
+ * described on the Flash-MoE pages:
+ *   router GEMV -> softmax top-K -> group-affine 4-bit or 2-bit dequantised GEMVs for each
+ *   selected expert's gate/up/down -> SwiGLU -> weighted combine with the sigmoid-gated
+ *   shared expert and the residual.
+ * Sources: GN+ summary "Flash-MoE - Ejecutar un modelo de 397 mil millones de parámetros en una
+ * laptop" (es) and its (id) twin, sections "Arquitectura del modelo" and "Tecnologías clave"
+ * (subsections "Kernel de dequantización optimizado con FMA", "Metal Compute Shaders" and
+ * "Deferred GPU Expert Compute"); HN thread "Flash-MoE: Running a 397B Parameter Model on a
+ * Laptop" (the router's result gates which experts are read).
+ *
+ * Conventions
+ *  - Pointers named *_dev are device (HBM) pointers. The caller allocates and owns every buffer;
+ *    the library never allocates or frees memory and keeps no mutable global state.
+ *  - Calls that take a stream enqueue work on it (a hipStream_t; NULL means the default stream)
+ *    and return at once. Results are valid once the stream has reached that point. No call
+ *    synchronises the host, so calls can be captured into a HIP graph.
+ *  - Return value: MOE_OK (0) or a negative MOE_E* code. Arguments are validated on the host
+ *    before any HIP call, so a rejected call enqueues nothing. moe_last_error() gives a one-line
+ *    reason (thread-local).
+ *  - Dtypes: activations, residuals and outputs are fp32. Router and shared-gate weights are bf16
+ *    (uint16 bit patterns). Expert weights live in packed blobs (format below).
+ *  - Thread safety: concurrent calls on distinct streams are safe.
+ *
+ * Packed expert blob (one expert = gate I x H, up I x H, down H x I; bits b in {2, 4}; group G):
+ *   [gate codes][up codes][down codes][gate sb][up sb][down sb]
+ *   - codes: row-major. Element c of a row is stored at byte c*b/8, at bit offset
+ *     b*(c mod (8/b)), lowest bits first.
+ *   - sb: one uint32 per (row, group) with row-major [rows][cols/G] order. The low half is the
+ *     bf16 scale and the high half the bf16 bias.
+ *   - A dequantised weight is W[r][c] = scale[r][c/G] * q[r][c] + bias[r][c/G]: the pages' form
+ *     nibble*scale + bias ("Kernel de dequantización optimizado con FMA").
+ *   - Size: 3*I*H*b/8 + 3*I*(H/G)*4 bytes, which is 7,077,888 B (6.75 MiB) at 4-bit and
+ *     3,932,160 B at 2-bit for H = 4096, I = 1024.
+ */
+#ifndef BQ_MOE_H
+#define BQ_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_OK 0
+#define MOE_EINVAL (-1)       /* null or misaligned pointer, bad sizes, expert index out of range */
+#define MOE_EUNSUPPORTED (-2) /* a shape or format this build does not implement (see moe_layer_t) */
+#define MOE_ENOSPC (-3)       /* workspace smaller than moe_workspace_bytes() */
+#define MOE_EHIP (-4)         /* a HIP call or kernel launch failed */
+
+#define MOE_MAX_TOP_K 8
+#define MOE_MAX_EXPERTS 1024
+/* Token counts at or above this run the prefill path in moe_layer_forward (grouped by expert). */
+#define MOE_PREFILL_MIN_TOKENS 64
+
+/* One MoE layer.
+ *   hidden H, inter I: powers of two with 64 <= I and 256 <= H <= 8192. group must be 64, bits 2 or 4.
+ *   n_experts E: 1..MOE_MAX_EXPERTS. top_k K: 1..min(E, MOE_MAX_TOP_K).
+ *   experts_dev: E packed blobs, expert e at experts_dev + e*expert_stride. expert_stride is at
+ *   least moe_blob_bytes(H, I, bits, group) and a multiple of 256.
+ *   shared_blob_dev and shared_gate_dev: the shared expert's blob and its gate vector (bf16 [H]).
+ *   Required when has_shared is 1, ignored when it is 0.
+ *   router_dev: bf16 [E][H] row-major; logit e = row e . x, with no bias. */
+typedef struct moe_layer_t {
+  int32_t hidden;
+  int32_t inter;
+  int32_t n_experts;
+  int32_t top_k;
+  int32_t has_shared;
+  int32_t bits;
+  int32_t group;
+  int32_t reserved;
+  const void* experts_dev;
+  uint64_t expert_stride;
+  const void* shared_blob_dev;
+  const uint16_t* router_dev;
+  const uint16_t* shared_gate_dev;
+} moe_layer_t;
+
+/* Canonical (unpacked) arrays of one expert, as host or device pointers. Matrix m = 0 gate, 1 up,
+ * 2 down. q[m] holds one code per byte, row-major [rows][cols]. scale[m] and bias[m] are bf16
+ * [rows][cols/G]. */
+typedef struct moe_expert_arrays_t {
+  const uint8_t* q[3];
+  const uint16_t* scale[3];
+  const uint16_t* bias[3];
+} moe_expert_arrays_t;
+
+/* ---- sizes -------------------------------------------------------------------------------------- */
+
+/* Bytes of one packed expert blob, or 0 if the shape or format is unsupported. */
+size_t moe_blob_bytes(int hidden, int inter, int bits, int group);
+
+/* Workspace bytes that moe_router / moe_expert_ffn / moe_layer_forward need for T tokens
+ * (and moe_stack_forward, which needs the same plus two [T][H] fp32 buffers). Returns 0 for an
+ * invalid layer. */
+size_t moe_workspace_bytes(const moe_layer_t* layer, int T);
+size_t moe_stack_workspace_bytes(const moe_layer_t* layer, int T);
+
+/* ---- packing -------------------------------------------------------------------------------------- */
+
+/* Pack one expert from canonical host arrays into a host blob of moe_blob_bytes() bytes.
+ * Codes must be < 2^bits (MOE_EINVAL otherwise). Pure host code; usable without a GPU. */
+int moe_pack_expert(int hidden, int inter, int bits, int group, const moe_expert_arrays_t* arrays_host,
+                    void* blob_host);
+
+/* As moe_pack_expert, but every array pointer and blob_dev are device pointers. The pack runs on
+ * `stream`. arrays_dev itself (the struct) lives in host memory. */
+int moe_pack_expert_device(int hidden, int inter, int bits, int group, const moe_expert_arrays_t* arrays_dev,
+                           void* blob_dev, void* stream);
+
+/* Dense dequantisation of one matrix (test export). expert -1 selects the shared expert, matrix is
+ * 0 gate, 1 up, 2 down. out_dtype 0 writes fp32 [rows][cols]. out_dtype 1 writes the bf16
+ * (round-to-nearest-even) of each weight. Every 2-bit and 4-bit weight in the supported ranges is
+ * exact in fp32. The pages' form: nibble*scale + bias ("Kernel de dequantización optimizado con
+ * FMA"). */
+int moe_dequant(const moe_layer_t* layer, int expert, int matrix, int out_dtype, void* w_out_dev, void* stream);
+
+/* ---- the layer, step by step --------------------------------------------------------------------- */
+
+/* Router (HN thread: the router result decides which experts are read; GN+ "Arquitectura del modelo":
+ * K routed experts per token plus the shared one).
+ *   x_dev fp32 [T][H] -> idx_dev int32 [T][K] (descending logit, ties to the lower index),
+ *   w_dev fp32 [T][K] (softmax over all E logits renormalised over the K chosen),
+ *   shared_g_dev fp32 [T] (sigmoid(shared_gate . x); may be NULL; ignored if !has_shared),
+ *   logits_dev fp64 [T][E] (may be NULL).
+ * Logits are accumulated in fp64, so the top-K decision is exact up to fp64 rounding. */
+int moe_router(const moe_layer_t* layer, const float* x_dev, int T, int32_t* idx_dev, float* w_dev,
+               float* shared_g_dev, double* logits_dev, void* ws_dev, size_t ws_bytes, void* stream);
+
+/* Expert FFNs ("Metal Compute Shaders": dequant mat-vec, SwiGLU; "Kernel de dequantización optimizado
+ * con FMA"). For each token t and slot k < K, expert idx[t][k] computes
+ *   y = W_down (silu(W_gate x) * (W_up x)),
+ * and slot K is the shared expert when has_shared is 1.
+ *   idx_dev int32 [T][K] (device). Entries outside [0, E) make the call write NaN to that slot's
+ *   output and set MOE_EINVAL in the error word, if one is given.
+ *   y_dev fp32 [T][K + has_shared][H]. */
+int moe_expert_ffn(const moe_layer_t* layer, const float* x_dev, int T, const int32_t* idx_dev, float* y_dev,
+                   void* ws_dev, size_t ws_bytes, void* stream);
+
+/* Combine ("Metal Compute Shaders": MoE combine + residual + gate):
+ *   out[t] = residual[t] + sum_k w[t][k] * y[t][k] + g[t] * y[t][K]   (shared term if has_shared)
+ * y_dev fp32 [T][K + has_shared][H]; w_dev fp32 [T][K]; shared_g_dev fp32 [T] (NULL iff !has_shared). */
+int moe_combine(const moe_layer_t* layer, const float* residual_dev, const float* y_dev, const float* w_dev,
+                const float* shared_g_dev, int T, float* out_dev, void* stream);
+
+/* ---- fused ------------------------------------------------------------------------------------- */
+
+/* The whole layer: router -> top-K -> experts -> combine + residual, with out = residual + MoE(x).
+ * T < MOE_PREFILL_MIN_TOKENS runs the decode path, in which each token streams its experts'
+ * weights with GEMV kernels. Larger T runs the prefill path, which groups tokens by expert
+ * ("Deferred GPU Expert Compute" is the one-stream, no-host-sync submission model both follow).
+ * idx_out_dev int32 [T][K] may be NULL. x_dev and out_dev may not alias; residual_dev may alias x_dev. */
+int moe_layer_forward(const moe_layer_t* layer, const float* x_dev, const float* residual_dev, int T, float* out_dev,
+                      int32_t* idx_out_dev, void* ws_dev, size_t ws_bytes, void* stream);
+
+/* A stack of L layers, decode only ("Deferred GPU Expert Compute": combine + norm + residual on the
+ * GPU hand off to the next layer). With h_0 = x:
+ *   u_l = h_l for l = 0, u_l = h_l / sqrt(mean(h_l^2) + eps) for l >= 1 (unit-weight RMS norm);
+ *   h_{l+1} = h_l + MoE_l(u_l), where the router, experts and shared gate of layer l all read u_l.
+ * out_dev = h_L, fp32 [T][H]. layers is a host array of L descriptors. All layers must share
+ * H, I, E, K, bits, group and has_shared. idx_out_dev int32 [L][T][K] may be NULL. */
+int moe_stack_forward(const moe_layer_t* layers, int L, float eps, const float* x_dev, int T, float* out_dev,
+                      int32_t* idx_out_dev, void* ws_dev, size_t ws_bytes, void* stream);
+
+/* ---- errors ------------------------------------------------------------------------------------- */
+
+const char* moe_strerror(int code);
+/* Reason for the last failing call on this thread ("" if none). */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BQ_MOE_H */

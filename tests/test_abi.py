@@ -1,0 +1,177 @@
+"""The C-ABI library without a GPU: it loads, exports every declared symbol, sizes and packs blobs,
+and rejects bad arguments on the host before any HIP call (CPU only)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import bit_quantized_expert_gemv_amd as bq
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    syms = declared_symbols()
+    assert len(syms) >= 12
+    L = bq.lib()
+    for s in syms:
+        assert hasattr(L, s), f"{s} declared in moe.h but not exported"
+    assert set(syms) == set(bq.SIGNATURES), "binding and header disagree"
+
+
+def test_no_oracle_in_product():
+    """The product package and library never reference the oracle."""
+    pkg = os.path.join(ROOT, "bit_quantized_expert_gemv_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".h")):
+                txt = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in txt and "oracle/" not in txt and "liboracle" not in txt, f
+
+
+def test_blob_bytes_closed_form():
+    for H, I in ((256, 128), (4096, 1024), (1024, 4096), (512, 64)):
+        for bits in (2, 4):
+            n = 3 * H * I
+            assert bq.moe_blob_bytes(H, I, bits) == n * bits // 8 + (n // 64) * 4
+    assert bq.moe_blob_bytes(4096, 1024, 4) == 7_077_888
+    assert bq.moe_blob_bytes(4096, 1024, 2) == 3_932_160
+    assert bq.moe_blob_bytes(256, 128, 4) == 55_296
+    assert bq.moe_blob_bytes(4096, 1024, 3) == 0
+    assert bq.moe_blob_bytes(4096, 1024, 4, 32) == 0
+    assert bq.moe_blob_bytes(100, 1024, 4) == 0
+
+
+def _unpack_codes(raw: np.ndarray, bits: int, n: int) -> np.ndarray:
+    """Independent unpacking of the blob's code bytes: element c sits at byte c*bits/8, lowest bits first."""
+    per = 8 // bits
+    fields = [(raw >> (bits * j)) & ((1 << bits) - 1) for j in range(per)]
+    return np.stack(fields, axis=1).reshape(-1)[:n]
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode2"])
+def test_host_pack_roundtrip(name):
+    w = synth.WORKLOADS[name]
+    if name == "decode2":  # keep the CPU test small: a reduced-width layer with the 2-bit recipe
+        w = synth.Workload("small2", 512, 4, 128, 2, bits=2, scale_range=w.scale_range, bias_range=w.bias_range)
+    ex = synth.expert_arrays(w, 0, 1)
+    H, I = w.hidden, w.inter
+    blob = np.zeros(bq.moe_blob_bytes(H, I, w.bits), dtype=np.uint8)
+    bq.moe_pack_expert(H, I, w.bits, 64, [m.q for m in ex.mats], [m.scale for m in ex.mats],
+                       [m.bias for m in ex.mats], blob)
+    cb = I * H * w.bits // 8
+    ng = I * H // 64
+    for m, mat in enumerate(ex.mats):
+        codes = _unpack_codes(blob[m * cb:(m + 1) * cb], w.bits, I * H)
+        assert np.array_equal(codes, mat.q.reshape(-1))
+        sb = blob[3 * cb + m * ng * 4: 3 * cb + (m + 1) * ng * 4].view(np.uint32)
+        assert np.array_equal((sb & 0xFFFF).astype(np.uint16), mat.scale.reshape(-1))
+        assert np.array_equal((sb >> 16).astype(np.uint16), mat.bias.reshape(-1))
+
+
+def test_host_pack_rejects_wide_codes():
+    H, I = 256, 64
+    q = [np.zeros(H * I, np.uint8) for _ in range(3)]
+    s = [np.zeros(H * I // 64, np.uint16) for _ in range(3)]
+    q[2][17] = 4
+    blob = np.zeros(bq.moe_blob_bytes(H, I, 2), np.uint8)
+    with pytest.raises(bq.MoeError) as e:
+        bq.moe_pack_expert(H, I, 2, 64, q, s, s, blob)
+    assert e.value.code == bq.MOE_EINVAL
+
+
+FAKE = 1 << 40  # a 256-aligned address that validation never dereferences
+
+
+def _layer(**kw):
+    base = dict(hidden=4096, inter=1024, n_experts=512, top_k=3, bits=4, experts=FAKE,
+                expert_stride=7_077_888, router=FAKE, shared_blob=FAKE, shared_gate=FAKE)
+    base.update(kw)
+    return bq.make_layer(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(bits=3), bq.MOE_EUNSUPPORTED),
+    (dict(group=32), bq.MOE_EUNSUPPORTED),
+    (dict(hidden=3000), bq.MOE_EUNSUPPORTED),
+    (dict(hidden=128), bq.MOE_EUNSUPPORTED),
+    (dict(inter=96), bq.MOE_EUNSUPPORTED),
+    (dict(n_experts=2048), bq.MOE_EUNSUPPORTED),
+    (dict(top_k=9), bq.MOE_EUNSUPPORTED),
+    (dict(top_k=0), bq.MOE_EUNSUPPORTED),
+    (dict(n_experts=2, top_k=3), bq.MOE_EUNSUPPORTED),
+    (dict(experts=0), bq.MOE_EINVAL),
+    (dict(experts=FAKE + 16), bq.MOE_EINVAL),
+    (dict(expert_stride=7_077_888 - 256), bq.MOE_EINVAL),
+    (dict(expert_stride=7_077_888 + 8), bq.MOE_EINVAL),
+    (dict(router=0), bq.MOE_EINVAL),
+    (dict(shared_gate=FAKE + 2), bq.MOE_EINVAL),
+])
+def test_layer_validation(kw, code):
+    layer = _layer(**kw)
+    if "shared_gate" in kw and kw["shared_gate"] == FAKE + 2:
+        pass
+    rc = bq.lib().moe_layer_forward(ctypes.byref(layer), FAKE, FAKE, 1, FAKE + 4096, None, FAKE, 1 << 30, None)
+    assert rc == code, bq.moe_last_error()
+    assert bq.moe_last_error() != ""
+
+
+def test_call_validation():
+    L = bq.lib()
+    layer = _layer()
+    ref = ctypes.byref(layer)
+    need = bq.moe_workspace_bytes(layer, 1)
+    assert need > 0
+    # workspace too small
+    assert L.moe_layer_forward(ref, FAKE, FAKE, 1, FAKE + 4096, None, FAKE, need - 1, None) == bq.MOE_ENOSPC
+    # misaligned activations / workspace, aliasing, negative T
+    assert L.moe_layer_forward(ref, FAKE + 4, FAKE, 1, FAKE + 4096, None, FAKE, need, None) == bq.MOE_EINVAL
+    assert L.moe_layer_forward(ref, FAKE, FAKE, 1, FAKE + 4096, None, FAKE + 64, need, None) == bq.MOE_EINVAL
+    assert L.moe_layer_forward(ref, FAKE, FAKE, 1, FAKE, None, FAKE, need, None) == bq.MOE_EINVAL
+    assert L.moe_layer_forward(ref, FAKE, FAKE, -1, FAKE + 4096, None, FAKE, need, None) == bq.MOE_EINVAL
+    # T == 0 is a no-op that touches nothing
+    assert L.moe_layer_forward(ref, None, None, 0, None, None, None, 0, None) == bq.MOE_OK
+    assert L.moe_router(ref, FAKE, 1, None, FAKE, None, None, FAKE, need, None) == bq.MOE_EINVAL
+    assert L.moe_expert_ffn(ref, FAKE, 1, None, FAKE, FAKE, need, None) == bq.MOE_EINVAL
+    assert L.moe_combine(ref, FAKE, FAKE, FAKE, None, 1, FAKE, None) == bq.MOE_EINVAL
+    assert L.moe_dequant(ref, 512, 0, 0, FAKE, None) == bq.MOE_EINVAL
+    assert L.moe_dequant(ref, 0, 3, 0, FAKE, None) == bq.MOE_EINVAL
+    assert L.moe_dequant(ref, 0, 0, 2, FAKE, None) == bq.MOE_EINVAL
+    no_shared = _layer(shared_blob=None, shared_gate=None)
+    assert L.moe_dequant(ctypes.byref(no_shared), -1, 0, 0, FAKE, None) == bq.MOE_EINVAL
+    # the stack: mismatched layers, bad eps, small workspace
+    other = _layer(top_k=2)
+    arr = (bq.moe_layer_t * 2)(layer, other)
+    assert L.moe_stack_forward(arr, 2, 1e-6, FAKE, 1, FAKE + 4096, None, FAKE, 1 << 30, None) == bq.MOE_EINVAL
+    arr = (bq.moe_layer_t * 2)(layer, layer)
+    assert L.moe_stack_forward(arr, 2, -1.0, FAKE, 1, FAKE + 4096, None, FAKE, 1 << 30, None) == bq.MOE_EINVAL
+    sneed = bq.moe_stack_workspace_bytes(layer, 1)
+    assert sneed > need
+    assert L.moe_stack_forward(arr, 2, 1e-6, FAKE, 1, FAKE + 4096, None, FAKE, sneed - 1, None) == bq.MOE_ENOSPC
+    assert L.moe_stack_forward(arr, 0, 1e-6, FAKE, 1, FAKE + 4096, None, FAKE, sneed, None) == bq.MOE_EINVAL
+
+
+def test_workspace_monotone():
+    layer = _layer()
+    sizes = [bq.moe_workspace_bytes(layer, t) for t in (1, 2, 64, 2048)]
+    assert sizes == sorted(sizes) and sizes[0] % 256 == 0
+    bad = _layer(bits=3)
+    assert bq.moe_workspace_bytes(bad, 1) == 0
+
+
+def test_strerror():
+    for c in (0, -1, -2, -3, -4):
+        assert bq.moe_strerror(c) != "unknown error"
+    assert bq.moe_strerror(-99) == "unknown error"
