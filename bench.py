@@ -1,0 +1,239 @@
+#!/usr/bin/env python3
+"""Benchmark: single-token MoE-layer decode on one MI355X.
+
+Workload "decode4": one MoE layer at the 397B model's shape (hidden 4096, 512 experts,
+intermediate 1024, top-3 routed + 1 shared, 4-bit group-64 experts). It runs 1000 seeded
+tokens, each as its own single-token moe_layer_forward call, stream-ordered and captured in
+one HIP graph. A step is one pass over those 1000 tokens. The inputs are synthetic (the
+trained weights are not available) and resident in HBM before timing starts.
+
+Printed as one JSON line:
+- value: tokens/s over the K timed steps.
+- roofline: achieved algorithmic GB/s of the dominant kernel, timed live with HIP events
+  around each of its launches, against the 8 TB/s HBM peak.
+- cold: the same decode with the router and shared expert rotated over 64 replicas, so that
+  no weight byte is reused from the 256 MB Infinity Cache between tokens.
+- cpu_baseline: the fp64 oracle on a bounded sample of the same tokens, on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+KERNEL_NAMES = ["router phase (router + shared gate/up)", "routed gate/up + SwiGLU", "down + combine"]
+
+
+def _hip():
+    h = ctypes.CDLL("libamdhip64.so")
+    h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    h.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+    h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return h
+
+
+def algorithmic_bytes(w, bq):
+    """Bytes each kernel must read once per token (weights only; activations excluded)."""
+    H, I, E, K = w.hidden, w.inter, w.n_experts, w.top_k
+    blob = bq.moe_blob_bytes(H, I, w.bits, w.group)
+    gate_up = 2 * blob // 3  # gate + up codes and (scale, bias) words
+    down = blob // 3
+    router = E * H * 2 + H * 2
+    return [router + gate_up, K * gate_up, (K + 1) * down], K * blob + blob, router
+
+
+def kernel_hash():
+    src = os.path.join(ROOT, "bit_quantized_expert_gemv_amd", "csrc", "moe_kernels.hip")
+    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic(kernel_label):
+    """HBM traffic per launch from committed rocprofv3 --pmc summaries, if taken on this kernel source."""
+    path = os.path.join(ROOT, "profiles", "decode4_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+    except ValueError:
+        return None
+    if d.get("kernel_source_sha256_16") != kernel_hash():
+        return None
+    return d.get("per_launch_bytes", {}).get(kernel_label)
+
+
+def cpu_baseline(w, budget_s):
+    """The oracle as it stands, on the host cores, over the first tokens until ~budget_s of oracle time."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    router = synth.router_weights(w)
+    gate = synth.shared_gate_weights(w)
+    shared = synth.expert_arrays(w, 0, synth.SHARED)
+    spent, n = 0.0, 0
+    while spent < budget_s and n < w.tokens:
+        x = synth.tokens_x(w, n, 1)[0].astype(np.float64)
+        idx = oracle.topk(oracle.router_logits(router, x), w.top_k)  # untimed: which experts to generate
+        arrays = {int(e): synth.expert_arrays(w, 0, int(e)) for e in idx}
+        t0 = time.perf_counter()
+        oracle.layer(x, x, router, gate, arrays.__getitem__, w.top_k, w.group, shared_expert=shared)
+        spent += time.perf_counter() - t0
+        n += 1
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count()
+    return {"value": n / spent, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} of the {w.tokens} decode4 tokens, one at a time (router, top-K, 4 experts "
+                      f"dense-dequantised in fp64, combine); expert generation untimed; {spent:.1f} s of oracle time"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="decode4", choices=["decode4", "decode2"])
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cold", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the multi-GPU sharding is design-only, "
+              "see the sharding section of the design notes", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import bit_quantized_expert_gemv_amd as bq
+    import synth
+    from synth.gpu_layers import DeviceLayer
+
+    w = synth.WORKLOADS[args.workload]
+    N = w.tokens
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] building {w.name} layer", file=sys.stderr, flush=True)
+    L = DeviceLayer(w, device=dev)
+    X = torch.from_numpy(synth.tokens_x(w, 0, N)).to(dev)
+    out = torch.empty_like(X)
+    idx = torch.empty(N, w.top_k, dtype=torch.int32, device=dev)
+    nws = bq.moe_workspace_bytes(L.desc, 1)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.Stream(device=dev)
+    torch.cuda.synchronize()
+
+    def capture(desc_for_token):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for t in range(N):
+                bq.moe_layer_forward(desc_for_token(t), X[t], X[t], 1, out[t], idx[t], ws, nws, stream=stream)
+        return g
+
+    def timed(g, steps, warmup):
+        with torch.cuda.stream(stream):
+            for _ in range(warmup):
+                g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            for _ in range(steps):
+                g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1000.0
+
+    print("[bench] capturing graph", file=sys.stderr, flush=True)
+    g = capture(lambda t: L.desc)
+    secs = timed(g, args.steps, args.warmup)
+    tok_s = args.steps * N / secs
+    ms_per_step = secs * 1000.0 / args.steps
+    print(f"[bench] warm: {tok_s:,.0f} tokens/s ({secs * 1e6 / (args.steps * N):.2f} us/token)", file=sys.stderr,
+          flush=True)
+
+    # ---- per-kernel durations, live, with HIP events around each launch (eager, same stream)
+    hip = _hip()
+    per_kernel_bytes, expert_bytes, router_bytes = algorithmic_bytes(w, bq)
+    events = []
+    for _ in range(6 * N):
+        e = ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(e)) == 0
+        events.append(e.value)
+    with torch.cuda.stream(stream):
+        for t in range(N):
+            bq.moe_layer_forward_timed(L.desc, X[t], X[t], 1, out[t], idx[t], ws, nws, events[6 * t: 6 * t + 6],
+                                       stream=stream)
+    torch.cuda.synchronize()
+    dur = np.zeros((N, 3))
+    f = ctypes.c_float()
+    for t in range(N):
+        for k in range(3):
+            assert hip.hipEventElapsedTime(ctypes.byref(f), events[6 * t + 2 * k], events[6 * t + 2 * k + 1]) == 0
+            dur[t, k] = f.value * 1e-3
+    for e in events:
+        hip.hipEventDestroy(e)
+    avg = dur[10:].mean(axis=0)  # skip the first tokens (cold instruction caches)
+    dom = int(np.argmax(per_kernel_bytes))
+    achieved = per_kernel_bytes[dom] / avg[dom] / 1e9
+    kernels = {KERNEL_NAMES[k]: {"avg_us": round(avg[k] * 1e6, 3), "bytes": per_kernel_bytes[k],
+                                 "GB/s": round(per_kernel_bytes[k] / avg[k] / 1e9, 1)} for k in range(3)}
+    print(f"[bench] kernels: {json.dumps(kernels)}", file=sys.stderr, flush=True)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(KERNEL_NAMES[dom]),
+                "kernel": KERNEL_NAMES[dom], "algorithmic_bytes_per_launch": per_kernel_bytes[dom],
+                "avg_launch_us": round(avg[dom] * 1e6, 3), "timing": "HIP events around each launch, eager, "
+                f"{N - 10} launches", "kernels": kernels}
+
+    # ---- cache-cold variant: rotate 64 replicas of router + shared expert + gate
+    cold = None
+    if not args.no_cold:
+        R = 64
+        rep_router = L.router.repeat(R, 1) if L.router.dim() == 1 else L.router.reshape(1, -1).repeat(R, 1)
+        rep_gate = L.shared_gate.reshape(1, -1).repeat(R, 1)
+        rep_shared = torch.empty(R, L.stride, dtype=torch.uint8, device=dev)
+        rep_shared[:] = L.shared.reshape(1, -1)
+        descs = [bq.make_layer(w.hidden, w.inter, w.n_experts, w.top_k, w.bits, L.experts, L.stride, rep_router[r],
+                               rep_shared[r], rep_gate[r], w.group) for r in range(R)]
+        gc = capture(lambda t: descs[t % R])
+        csecs = timed(gc, args.steps, args.warmup)
+        ctok = args.steps * N / csecs
+        us = csecs * 1e6 / (args.steps * N)
+        cold = {"tokens_per_s": round(ctok, 1), "us_per_token": round(us, 3),
+                "expert_GB/s": round(expert_bytes / (us * 1e-6) / 1e9, 1),
+                "all_weights_GB/s": round((expert_bytes + router_bytes) / (us * 1e-6) / 1e9, 1),
+                "replicas": R, "replica_bytes": int((L.stride + L.router.numel() * 2 + L.shared_gate.numel() * 2) * R)}
+        print(f"[bench] cold: {json.dumps(cold)}", file=sys.stderr, flush=True)
+        del gc
+
+    us_tok = secs * 1e6 / (args.steps * N)
+    result = {
+        "metric": "MoE-layer decode tokens/s + achieved HBM GB/s on expert weights (frac of peak)",
+        "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp32", "data": "synthetic (seeded; trained weights unavailable)",
+        "config": {"workload": f"{w.name}: one MoE layer, hidden {w.hidden}, {w.n_experts} experts, inter {w.inter}, "
+                               f"top-{w.top_k} + shared, {w.bits}-bit group-{w.group} experts; a step is {N} "
+                               f"sequential single-token calls in one HIP graph",
+                   "tokens_per_step": N, "hidden": w.hidden, "n_experts": w.n_experts, "inter": w.inter,
+                   "top_k": w.top_k, "bits": w.bits, "group": w.group, "parallelism": "single GPU"},
+        "us_per_token": round(us_tok, 3),
+        "expert_GB/s": round(expert_bytes / (us_tok * 1e-6) / 1e9, 1),
+        "expert_frac_of_peak": round(expert_bytes / (us_tok * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "roofline": roofline,
+        "cold": cold,
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_budget),
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -26,6 +26,7 @@ from ._binding import (  # noqa: F401
     moe_expert_ffn,
     moe_last_error,
     moe_layer_forward,
+    moe_layer_forward_timed,
     moe_layer_t,
     moe_pack_expert,
     moe_pack_expert_device,

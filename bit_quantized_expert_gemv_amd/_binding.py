@@ -44,6 +44,8 @@ SIGNATURES = {
     "moe_combine": (ctypes.c_int, [ctypes.POINTER(moe_layer_t), c_vp, c_vp, c_vp, c_vp, ctypes.c_int, c_vp, c_vp]),
     "moe_layer_forward": (ctypes.c_int, [ctypes.POINTER(moe_layer_t), c_vp, c_vp, ctypes.c_int, c_vp, c_vp, c_vp,
                                          c_size, c_vp]),
+    "moe_layer_forward_timed": (ctypes.c_int, [ctypes.POINTER(moe_layer_t), c_vp, c_vp, ctypes.c_int, c_vp, c_vp, c_vp,
+                                               c_size, c_vp, ctypes.POINTER(c_vp)]),
     "moe_stack_forward": (ctypes.c_int, [ctypes.POINTER(moe_layer_t), ctypes.c_int, c_f32, c_vp, ctypes.c_int, c_vp,
                                          c_vp, c_vp, c_size, c_vp]),
     "moe_strerror": (ctypes.c_char_p, [ctypes.c_int]),
@@ -165,6 +167,13 @@ def moe_combine(layer, residual, y, w, shared_g, T, out, stream=None) -> None:
 def moe_layer_forward(layer, x, residual, T, out, idx_out, ws, ws_bytes, stream=None) -> None:
     _check(lib().moe_layer_forward(_ref(layer), ptr(x), ptr(residual), T, ptr(out), ptr(idx_out), ptr(ws), ws_bytes,
                                    stream_handle(stream)), "moe_layer_forward")
+
+
+def moe_layer_forward_timed(layer, x, residual, T, out, idx_out, ws, ws_bytes, events, stream=None) -> None:
+    """events: 6 raw hipEvent_t handles (ints) or None entries."""
+    ev = (c_vp * 6)(*[(e if e else None) for e in events])
+    _check(lib().moe_layer_forward_timed(_ref(layer), ptr(x), ptr(residual), T, ptr(out), ptr(idx_out), ptr(ws),
+                                         ws_bytes, stream_handle(stream), ev), "moe_layer_forward_timed")
 
 
 def moe_stack_forward(layers, eps, x, T, out, idx_out, ws, ws_bytes, stream=None) -> None:

@@ -81,7 +81,7 @@ bool geometry_from(const moe_layer_t* L, Geometry* g, const char** why) {
   if (L->bits != 2 && L->bits != 4) { *why = "bits must be 2 or 4"; return false; }
   if (L->group != 64) { *why = "group must be 64"; return false; }
   if (!pow2_in(L->hidden, 256, 8192)) { *why = "hidden must be a power of two in [256, 8192]"; return false; }
-  if (!pow2_in(L->inter, 64, 8192)) { *why = "inter must be a power of two in [64, 8192]"; return false; }
+  if (!pow2_in(L->inter, 64, 2048)) { *why = "inter must be a power of two in [64, 2048]"; return false; }
   if (L->n_experts < 1 || L->n_experts > MOE_MAX_EXPERTS) { *why = "n_experts must be in [1, 1024]"; return false; }
   if (L->top_k < 1 || L->top_k > MOE_MAX_TOP_K || L->top_k > L->n_experts) {
     *why = "top_k must be in [1, min(n_experts, 8)]";
@@ -259,6 +259,11 @@ int moe_combine(const moe_layer_t* layer, const float* residual, const float* y,
 
 int moe_layer_forward(const moe_layer_t* layer, const float* x, const float* residual, int T, float* out,
                       int32_t* idx_out, void* ws, size_t ws_bytes, void* stream) {
+  return moe_layer_forward_timed(layer, x, residual, T, out, idx_out, ws, ws_bytes, stream, nullptr);
+}
+
+int moe_layer_forward_timed(const moe_layer_t* layer, const float* x, const float* residual, int T, float* out,
+                            int32_t* idx_out, void* ws, size_t ws_bytes, void* stream, void* const* events) {
   Geometry g;
   int rc = check_layer(layer, &g);
   if (rc) return rc;
@@ -273,9 +278,19 @@ int moe_layer_forward(const moe_layer_t* layer, const float* x, const float* res
   const Workspace W = carve_workspace(g, T, ws);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const LayerPtrs p = ptrs_of(layer);
-  hipError_t e = launch_router_phase(g, p, x, nullptr, 0.0f, T, W, true, s);
+  auto mark = [&](int i) {
+    if (events != nullptr && events[i] != nullptr) return hipEventRecord(static_cast<hipEvent_t>(events[i]), s);
+    return hipSuccess;
+  };
+  hipError_t e = mark(0);
+  if (e == hipSuccess) e = launch_router_phase(g, p, x, nullptr, 0.0f, T, W, true, s);
+  if (e == hipSuccess) e = mark(1);
+  if (e == hipSuccess) e = mark(2);
   if (e == hipSuccess) e = launch_gateup(g, p, x, T, W, nullptr, idx_out, false, s);
+  if (e == hipSuccess) e = mark(3);
+  if (e == hipSuccess) e = mark(4);
   if (e == hipSuccess) e = launch_down(g, p, T, W, W.idx, residual, out, nullptr, s);
+  if (e == hipSuccess) e = mark(5);
   return hip_status(e);
 }
 

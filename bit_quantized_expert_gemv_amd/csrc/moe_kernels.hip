@@ -38,7 +38,6 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kBlock = 64 * kWaves;
-constexpr int kMaxPerLane = MOE_MAX_EXPERTS / 64;
 
 // Lane layout of a row of COLS codes at BITS bits (16-byte chunks).
 template <int BITS, int COLS>
@@ -139,28 +138,6 @@ __device__ __forceinline__ float row_partial(const uint4 (&cw)[C::CPL], const ui
   return a;
 }
 
-// Load this lane's activations (scaled) and their per-chunk sums.
-template <class C>
-__device__ __forceinline__ void load_act(const float* __restrict__ v, int lir, float scale, float (&xr)[C::XPL],
-                                         float (&S)[C::CPL]) {
-#pragma unroll
-  for (int j = 0; j < C::CPL; ++j) {
-    const float4* p = reinterpret_cast<const float4*>(v + (lir + j * C::LPR) * C::CH);
-#pragma unroll
-    for (int q = 0; q < C::CH / 4; ++q) {
-      const float4 t = p[q];
-      xr[j * C::CH + 4 * q + 0] = t.x * scale;
-      xr[j * C::CH + 4 * q + 1] = t.y * scale;
-      xr[j * C::CH + 4 * q + 2] = t.z * scale;
-      xr[j * C::CH + 4 * q + 3] = t.w * scale;
-    }
-    float s = 0.0f;
-#pragma unroll
-    for (int i = 0; i < C::CH; ++i) s += xr[j * C::CH + i];
-    S[j] = s;
-  }
-}
-
 template <class C>
 __device__ __forceinline__ void load_row(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ sbp, int r,
                                          int lir, uint4 (&cw)[C::CPL], uint32_t (&sb)[C::CPL]) {
@@ -173,10 +150,109 @@ __device__ __forceinline__ void load_row(const uint8_t* __restrict__ codes, cons
   }
 }
 
+// ---- activation staging through LDS -------------------------------------------------------------
+// A lane needs CH consecutive activations per chunk, and neighbouring lanes own neighbouring
+// chunks. Loading that straight into registers makes each load instruction touch 64 cache
+// lines. Instead the vector is read with coalesced 16-byte loads and parked in LDS, with the
+// 16-byte slots of each chunk XOR-swizzled so that consecutive lanes hit distinct banks. Each
+// lane then reads its slice back. The coalesced loads are issued before the expert weights
+// and written to LDS only after the weight loads are in flight, so in-order completion
+// counting never makes the weight loads wait for them.
+template <class C>
+__device__ __forceinline__ int xslot(int chunk, int q) {
+  if constexpr (C::CH == 32) return chunk * 8 + (q ^ ((chunk >> 1) & 7));
+  else return chunk * 16 + (q ^ (chunk & 15));
+}
+
+// COLS floats loaded by NT cooperating lanes: lane i takes float4 i, i + NT, ...
+template <int COLS, int NT>
+struct Stage {
+  static constexpr int N4 = COLS / 4;
+  static constexpr int PER = (N4 + NT - 1) / NT;
+  float4 v[PER];
+  __device__ __forceinline__ void load(const float* __restrict__ src, int tid) {
+    const float4* s4 = reinterpret_cast<const float4*>(src);
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int i = tid + k * NT;
+      v[k] = (N4 % NT == 0 || i < N4) ? s4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+  template <class C>
+  __device__ __forceinline__ void store(float4* __restrict__ xs, int tid, float scale) const {
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int i = tid + k * NT;
+      if (N4 % NT == 0 || i < N4) {
+        float4 t = v[k];
+        t.x *= scale; t.y *= scale; t.z *= scale; t.w *= scale;
+        xs[xslot<C>(i / (C::CH / 4), i % (C::CH / 4))] = t;
+      }
+    }
+  }
+};
+
+// This lane's activations (from LDS) and their per-chunk sums.
+template <class C>
+__device__ __forceinline__ void read_act(const float4* __restrict__ xs, int lir, float (&xr)[C::XPL],
+                                         float (&S)[C::CPL]) {
+#pragma unroll
+  for (int j = 0; j < C::CPL; ++j) {
+    const int chunk = lir + j * C::LPR;
+#pragma unroll
+    for (int q = 0; q < C::CH / 4; ++q) {
+      const float4 t = xs[xslot<C>(chunk, q)];
+      xr[j * C::CH + 4 * q + 0] = t.x;
+      xr[j * C::CH + 4 * q + 1] = t.y;
+      xr[j * C::CH + 4 * q + 2] = t.z;
+      xr[j * C::CH + 4 * q + 3] = t.w;
+    }
+    float sum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < C::CH; ++i) sum += xr[j * C::CH + i];
+    S[j] = sum;
+  }
+}
+
+// ---- cross-lane reductions on the VALU with DPP (gfx9 controls) -----------------------------------
+constexpr int kDppQuadXor1 = 0xB1;    // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;    // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <- lane 7-i within each 8
+constexpr int kDppRowMirror = 0x140;  // lane i <- lane 15-i within each 16
+constexpr int kDppBcast15 = 0x142;    // lane 15 of row r -> row r+1 (row mask 0xA)
+constexpr int kDppBcast31 = 0x143;    // lane 31 -> rows 2 and 3 (row mask 0xC)
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_i(int old, int v) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, ROWS, 0xF, false);
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_f(float old, float v) {
+  return __int_as_float(dpp_i<CTRL, ROWS>(__float_as_int(old), __float_as_int(v)));
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_d(double old, double v) {
+  const long long o = __double_as_longlong(old), x = __double_as_longlong(v);
+  const int lo = dpp_i<CTRL, ROWS>((int)(o & 0xFFFFFFFF), (int)(x & 0xFFFFFFFF));
+  const int hi = dpp_i<CTRL, ROWS>((int)(o >> 32), (int)(x >> 32));
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float pick_dpp(float old, float v) { return dpp_f<CTRL, ROWS>(old, v); }
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double pick_dpp(double old, double v) { return dpp_d<CTRL, ROWS>(old, v); }
+
+// Sum over aligned segments of LPR lanes. The full sum is valid in the LAST lane of each segment
+// (lanes of a segment never read another segment). Same order on every call: deterministic.
 template <int LPR, class T>
 __device__ __forceinline__ T seg_sum(T v) {
-#pragma unroll
-  for (int m = LPR / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  if constexpr (LPR >= 2) v += pick_dpp<kDppQuadXor1, 0xF>(T(0), v);
+  if constexpr (LPR >= 4) v += pick_dpp<kDppQuadXor2, 0xF>(T(0), v);
+  if constexpr (LPR >= 8) v += pick_dpp<kDppHalfMirror, 0xF>(T(0), v);
+  if constexpr (LPR >= 16) v += pick_dpp<kDppRowMirror, 0xF>(T(0), v);
+  if constexpr (LPR >= 32) v += pick_dpp<kDppBcast15, 0xA>(T(0), v);
+  if constexpr (LPR >= 64) v += pick_dpp<kDppBcast31, 0xC>(T(0), v);
   return v;
 }
 
@@ -202,74 +278,82 @@ LayerArgs make_args(const Geometry& g, const LayerPtrs& p, const Workspace& ws) 
   return a;
 }
 
-// gate/up/SwiGLU for P row steps of one expert; writes h rows (lane 0 of each row).
-template <int BITS, int COLS, int P>
-__device__ __forceinline__ void gateup_rows(const LayerArgs& a, const uint8_t* __restrict__ blob,
-                                            const float (&xr)[RowCfg<BITS, COLS>::XPL],
-                                            const float (&S)[RowCfg<BITS, COLS>::CPL], int lir, int rig, int step0,
-                                            float* __restrict__ h) {
-  using C = RowCfg<BITS, COLS>;
-  const uint8_t* gc = blob + a.off_codes[0];
-  const uint8_t* uc = blob + a.off_codes[1];
-  const uint32_t* gs = reinterpret_cast<const uint32_t*>(blob + a.off_sb[0]);
-  const uint32_t* us = reinterpret_cast<const uint32_t*>(blob + a.off_sb[1]);
-  uint4 cg[P][C::CPL], cu[P][C::CPL];
-  uint32_t sg[P][C::CPL], su[P][C::CPL];
-#pragma unroll
-  for (int p = 0; p < P; ++p) {
-    const int r = (step0 + p) * C::RPW + rig;
-    if (r < a.I) {
-      load_row<C>(gc, gs, r, lir, cg[p], sg[p]);
-      load_row<C>(uc, us, r, lir, cu[p], su[p]);
-    }
-  }
-#pragma unroll
-  for (int p = 0; p < P; ++p) {
-    const int r = (step0 + p) * C::RPW + rig;
-    if (r < a.I) {
-      const float ga = seg_sum<C::LPR>(row_partial<BITS, C>(cg[p], sg[p], xr, S));
-      const float ua = seg_sum<C::LPR>(row_partial<BITS, C>(cu[p], su[p], xr, S));
-      if (lir == 0) h[r] = silu_mul(ga, ua);
-    }
-  }
+// ---- top-K ---------------------------------------------------------------------------------------
+// (value, index) order of the top-K: larger value first, then lower index.
+__device__ __forceinline__ bool better(double v, int i, double bv, int bi) { return v > bv || (v == bv && i < bi); }
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ void argmax_step(double& v, int& i) {
+  const double ov = dpp_d<CTRL, ROWS>(-INFINITY, v);
+  const int oi = dpp_i<CTRL, ROWS>(0x7FFFFFFF, i);
+  if (better(ov, oi, v, i)) { v = ov; i = oi; }
 }
 
-// Wave-wide top-K over logits[0..E): descending value, ties to the lower index. Result is wave-uniform.
-__device__ __forceinline__ void wave_topk(const double* __restrict__ logits, int E, int K, int lane, int32_t* sel,
-                                          double* val) {
-  double v[kMaxPerLane];
+// Wave-wide top-K of logits[0..E): descending value, ties to the lower index. Lane l holds logits
+// l, l+64, ... (PL per lane, E <= 64*PL). The loads are unconditional (indexes are clamped), so they
+// leave back to back. Each round takes every lane's best remaining value and carries the best pair
+// to lane 63 with DPP steps, with no LDS round trips. It is read back wave-uniform and retired.
+// Lane 0 records the choices in sel/val (LDS) when `record` is set. Returns the expert at
+// position `want`, clamped into [0, E) so that NaN logits can never address memory outside the pool.
+template <int PL>
+__device__ __forceinline__ void load_topk_values(const double* __restrict__ lg, int E, int lane, double (&v)[PL]) {
 #pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i) {
+  for (int i = 0; i < PL; ++i) {
     const int e = lane + 64 * i;
-    v[i] = (e < E) ? logits[e] : -INFINITY;
-  }
-  for (int k = 0; k < K; ++k) {
-    double bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
-#pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) {
-      const int e = lane + 64 * i;
-      if (e < E && (v[i] > bv || (v[i] == bv && e < bi))) { bv = v[i]; bi = e; }
-    }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      const double ov = __shfl_xor(bv, m, 64);
-      const int oi = __shfl_xor(bi, m, 64);
-      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-    }
-    sel[k] = bi;
-    val[k] = bv;
-#pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i)
-      if (lane + 64 * i == bi) v[i] = -INFINITY;
+    const double t = lg[min(e, E - 1)];
+    v[i] = e < E ? t : -INFINITY;
   }
 }
 
-// Softmax of the K chosen logits (the full softmax over E renormalised over the chosen set reduces to this).
-__device__ __forceinline__ void route_weights(const double* val, int K, float* w) {
+template <int PL>
+__device__ __forceinline__ int wave_topk(double (&v)[PL], int E, int K, int lane, int want, bool record,
+                                         int32_t* __restrict__ sel, double* __restrict__ val) {
+  int chosen = 0;
+  for (int k = 0; k < K; ++k) {
+    double bv = v[0];
+    int bi = lane;
+#pragma unroll
+    for (int i = 1; i < PL; ++i) {
+      const bool c = v[i] > bv;  // strict: the earlier (lower) index keeps a tie
+      bv = c ? v[i] : bv;
+      bi = c ? lane + 64 * i : bi;
+    }
+    argmax_step<kDppQuadXor1, 0xF>(bv, bi);
+    argmax_step<kDppQuadXor2, 0xF>(bv, bi);
+    argmax_step<kDppHalfMirror, 0xF>(bv, bi);
+    argmax_step<kDppRowMirror, 0xF>(bv, bi);
+    argmax_step<kDppBcast15, 0xA>(bv, bi);
+    argmax_step<kDppBcast31, 0xC>(bv, bi);
+    // read back with every lane active (values computed under a partial exec mask would be stale)
+    const long long bits = __double_as_longlong(bv);
+    const int lo = __builtin_amdgcn_readlane((int)(bits & 0xFFFFFFFF), 63);
+    const int hi = __builtin_amdgcn_readlane((int)(bits >> 32), 63);
+    const int win = min(max(__builtin_amdgcn_readlane(bi, 63), 0), E - 1);
+    if (k == want) chosen = win;
+    if (record && lane == 0) {
+      sel[k] = win;
+      val[k] = __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+    }
+#pragma unroll
+    for (int i = 0; i < PL; ++i) v[i] = (lane + 64 * i == win) ? -INFINITY : v[i];
+  }
+  return chosen;
+}
+
+// Softmax of the K chosen logits (the full softmax over E renormalised over the chosen set reduces to
+// this), written with the choices and the shared gate for token t. One lane calls this.
+__device__ __forceinline__ void write_routing(const LayerArgs& a, int t, const int32_t* __restrict__ sel,
+                                              const double* __restrict__ val, const double* __restrict__ lg,
+                                              int32_t* __restrict__ idx_a, float* __restrict__ w_a,
+                                              int32_t* __restrict__ idx_b, float* __restrict__ g_out) {
   double z = 0.0;
-  for (int k = 0; k < K; ++k) z += exp(val[k] - val[0]);
-  for (int k = 0; k < K; ++k) w[k] = (float)(exp(val[k] - val[0]) / z);
+  for (int k = 0; k < a.K; ++k) z += exp(val[k] - val[0]);
+  for (int k = 0; k < a.K; ++k) {
+    idx_a[(size_t)t * a.K + k] = sel[k];
+    w_a[(size_t)t * a.K + k] = (float)(exp(val[k] - val[0]) / z);
+    if (idx_b) idx_b[(size_t)t * a.K + k] = sel[k];
+  }
+  if (g_out && a.has_shared) g_out[t] = (float)(1.0 / (1.0 + exp(-lg[a.E])));
 }
 
 // RMS norm scale of h (fp64 accumulation, one fixed order for every block).
@@ -287,6 +371,39 @@ __device__ float block_rms_inv(const float* __restrict__ h, int H, float eps, do
   return (float)(1.0 / sqrt(tot / (double)H + (double)eps));
 }
 
+// gate/up/SwiGLU for P row steps of one expert, for a whole block: weight loads go out first,
+// then the staged activations are parked in LDS (one barrier) and read back per lane.
+template <int BITS, int H, int P>
+__device__ __forceinline__ void gateup_block(const LayerArgs& a, const uint8_t* __restrict__ blob,
+                                             const Stage<H, kBlock>& st, float scale, float4* __restrict__ xs,
+                                             int step0, int lir, int rig, float* __restrict__ h) {
+  using C = RowCfg<BITS, H>;
+  const uint8_t* gc = blob + a.off_codes[0];
+  const uint8_t* uc = blob + a.off_codes[1];
+  const uint32_t* gs = reinterpret_cast<const uint32_t*>(blob + a.off_sb[0]);
+  const uint32_t* us = reinterpret_cast<const uint32_t*>(blob + a.off_sb[1]);
+  uint4 cg[P][C::CPL], cu[P][C::CPL];
+  uint32_t sg[P][C::CPL], su[P][C::CPL];
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const int r = min((step0 + p) * C::RPW + rig, a.I - 1);  // rows past the end re-read the last row
+    load_row<C>(gc, gs, r, lir, cg[p], sg[p]);
+    load_row<C>(uc, us, r, lir, cu[p], su[p]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  st.template store<C>(xs, threadIdx.x, scale);
+  __syncthreads();
+  float xr[C::XPL], S[C::CPL];
+  read_act<C>(xs, lir, xr, S);
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const int r = (step0 + p) * C::RPW + rig;
+    const float ga = seg_sum<C::LPR>(row_partial<BITS, C>(cg[p], sg[p], xr, S));
+    const float ua = seg_sum<C::LPR>(row_partial<BITS, C>(cu[p], su[p], xr, S));
+    if (lir == C::LPR - 1 && r < a.I) h[r] = silu_mul(ga, ua);
+  }
+}
+
 // ---------------------------------------------------------------------------------------------
 // Kernel 1: router logits (+ shared-gate logit) and the shared expert's gate/up.
 // Blocks [0, n_router_blocks) do router rows (row E is the shared-gate vector); the rest do the
@@ -298,6 +415,7 @@ __global__ __launch_bounds__(kBlock) void k_router_phase(LayerArgs a, const floa
   using C = RowCfg<BITS, H>;
   using R = RouterCfg<H>;
   __shared__ double red[kBlock];
+  __shared__ float4 xs[H / 4];
   const int t = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   float scale = 1.0f;
@@ -310,100 +428,95 @@ __global__ __launch_bounds__(kBlock) void k_router_phase(LayerArgs a, const floa
   }
   if ((int)blockIdx.x < n_router_blocks) {
     const int lir = lane % R::LPR, rig = lane / R::LPR;
-    float xr[R::XPL];
-#pragma unroll
-    for (int j = 0; j < R::CPL; ++j) {
-      const float4* p = reinterpret_cast<const float4*>(src + (lir + j * R::LPR) * 8);
-      const float4 u0 = p[0], u1 = p[1];
-      xr[j * 8 + 0] = u0.x * scale; xr[j * 8 + 1] = u0.y * scale; xr[j * 8 + 2] = u0.z * scale;
-      xr[j * 8 + 3] = u0.w * scale; xr[j * 8 + 4] = u1.x * scale; xr[j * 8 + 5] = u1.y * scale;
-      xr[j * 8 + 6] = u1.z * scale; xr[j * 8 + 7] = u1.w * scale;
-    }
     const int nrows = a.E + a.has_shared;
     for (int s = 0; s < router_steps; ++s) {
-      const int r = ((blockIdx.x * kWaves + wave) * router_steps + s) * R::RPW + rig;
-      if (r >= nrows) break;  // uniform across the LPR lanes of a row
-      const uint16_t* row = (r < a.E) ? a.router + (size_t)r * H : a.sgate;
+      const int base = ((blockIdx.x * kWaves + wave) * router_steps + s) * R::RPW;
+      if (base >= nrows) break;  // wave-uniform
+      const int r = base + rig;
+      const int rr = min(r, nrows - 1);
+      const uint16_t* row = (rr < a.E) ? a.router + (size_t)rr * H : a.sgate;
       uint4 w[R::CPL];
 #pragma unroll
       for (int j = 0; j < R::CPL; ++j) w[j] = *reinterpret_cast<const uint4*>(row + (lir + j * R::LPR) * 8);
-      double acc = 0.0;
+      double acc[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
       for (int j = 0; j < R::CPL; ++j) {
+        const float4* p = reinterpret_cast<const float4*>(src + (lir + j * R::LPR) * 8);
+        const float4 u0 = p[0], u1 = p[1];
+        const float xv[8] = {u0.x * scale, u0.y * scale, u0.z * scale, u0.w * scale,
+                             u1.x * scale, u1.y * scale, u1.z * scale, u1.w * scale};
         const uint32_t ww[4] = {w[j].x, w[j].y, w[j].z, w[j].w};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          acc = fma((double)bf16_lo(ww[q]), (double)xr[j * 8 + 2 * q], acc);
-          acc = fma((double)bf16_hi(ww[q]), (double)xr[j * 8 + 2 * q + 1], acc);
+          acc[q] = fma((double)bf16_lo(ww[q]), (double)xv[2 * q], acc[q]);
+          acc[q] = fma((double)bf16_hi(ww[q]), (double)xv[2 * q + 1], acc[q]);
         }
       }
-      acc = seg_sum<R::LPR>(acc);
-      if (lir == 0) a.ws.logits[(size_t)t * (a.E + 1) + r] = acc;
+      const double tot = seg_sum<R::LPR>((acc[0] + acc[1]) + (acc[2] + acc[3]));
+      if (lir == R::LPR - 1 && r < nrows) a.ws.logits[(size_t)t * (a.E + 1) + r] = tot;
     }
     return;
   }
   // shared expert gate/up
   const int lir = lane % C::LPR, rig = lane / C::LPR;
-  float xr[C::XPL], S[C::CPL];
-  load_act<C>(src, lir, scale, xr, S);
+  Stage<H, kBlock> st;
+  st.load(src, threadIdx.x);
   const int step0 = ((blockIdx.x - n_router_blocks) * kWaves + wave) * P;
-  gateup_rows<BITS, H, P>(a, a.shared, xr, S, lir, rig, step0, a.ws.h + ((size_t)t * a.NE + a.K) * a.I);
+  gateup_block<BITS, H, P>(a, a.shared, st, scale, xs, step0, lir, rig, a.ws.h + ((size_t)t * a.NE + a.K) * a.I);
 }
 
 // Kernel 2: gate/up/SwiGLU of routed experts (blockIdx.y = slot; slot K = shared when included).
-template <int BITS, int H, int P>
+template <int BITS, int H, int P, int PL>
 __global__ __launch_bounds__(kBlock) void k_gateup(LayerArgs a, const float* __restrict__ x,
                                                    const int32_t* __restrict__ idx_in, int32_t* __restrict__ idx_out) {
   using C = RowCfg<BITS, H>;
+  __shared__ float4 xs[H / 4];
+  __shared__ int32_t sel[MOE_MAX_TOP_K];
+  __shared__ double val[MOE_MAX_TOP_K];
   const int t = blockIdx.z, slot = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int lir = lane % C::LPR, rig = lane / C::LPR;
-  const uint8_t* blob;
+  const int step0 = (blockIdx.x * kWaves + wave) * P;
+  const uint8_t* blob = a.shared;
+  Stage<H, kBlock> st;
   if (slot < a.K) {
     int e;
     if (idx_in != nullptr) {
       e = idx_in[(size_t)t * a.K + slot];
+      st.load(x + (size_t)t * H, threadIdx.x);
     } else {
-      int32_t sel[MOE_MAX_TOP_K];
-      double val[MOE_MAX_TOP_K];
-      wave_topk(a.ws.logits + (size_t)t * (a.E + 1), a.E, a.K, lane, sel, val);
-      e = sel[slot];
-      if (blockIdx.x == 0 && blockIdx.y == 0 && wave == 0 && lane == 0) {
-        float w[MOE_MAX_TOP_K];
-        route_weights(val, a.K, w);
-        for (int k = 0; k < a.K; ++k) {
-          a.ws.idx[(size_t)t * a.K + k] = sel[k];
-          a.ws.w[(size_t)t * a.K + k] = w[k];
-          if (idx_out) idx_out[(size_t)t * a.K + k] = sel[k];
-        }
-        if (a.has_shared) a.ws.g[t] = (float)(1.0 / (1.0 + exp(-a.ws.logits[(size_t)t * (a.E + 1) + a.E])));
-      }
+      const double* lg = a.ws.logits + (size_t)t * (a.E + 1);
+      // the logits are requested first, so waiting for them never waits for the activations
+      double v[PL];
+      load_topk_values<PL>(lg, a.E, lane, v);
+      st.load(x + (size_t)t * H, threadIdx.x);
+      const bool writer = blockIdx.x == 0 && blockIdx.y == 0 && wave == 0;
+      e = wave_topk<PL>(v, a.E, a.K, lane, slot, writer, sel, val);
+      if (writer && lane == 0) write_routing(a, t, sel, val, lg, a.ws.idx, a.ws.w, idx_out, a.ws.g);
     }
     if (e < 0 || e >= a.E) {  // never read outside the pool: mark the slot's output as invalid
-      const int step0 = (blockIdx.x * kWaves + wave) * P;
       for (int p = 0; p < P; ++p) {
         const int r = (step0 + p) * C::RPW + rig;
-        if (r < a.I && lir == 0) a.ws.h[((size_t)t * a.NE + slot) * a.I + r] = NAN;
+        if (r < a.I && lir == C::LPR - 1) a.ws.h[((size_t)t * a.NE + slot) * a.I + r] = NAN;
       }
-      return;
+      return;  // the whole block takes this branch (slot is per block)
     }
     blob = a.experts + (size_t)e * a.stride;
   } else {
-    blob = a.shared;
+    st.load(x + (size_t)t * H, threadIdx.x);
   }
-  float xr[C::XPL], S[C::CPL];
-  load_act<C>(x + (size_t)t * H, lir, 1.0f, xr, S);
-  const int step0 = (blockIdx.x * kWaves + wave) * P;
-  gateup_rows<BITS, H, P>(a, blob, xr, S, lir, rig, step0, a.ws.h + ((size_t)t * a.NE + slot) * a.I);
+  gateup_block<BITS, H, P>(a, blob, st, 1.0f, xs, step0, lir, rig, a.ws.h + ((size_t)t * a.NE + slot) * a.I);
 }
 
 // Kernel 3: down projections of all expert slots for a block of output rows; combine or store.
+// Wave w handles slots w, w+4, ...; each stages its slot's SwiGLU vector through its own LDS region.
 template <int BITS, int I, int P>
 __global__ __launch_bounds__(kBlock) void k_down(LayerArgs a, const int32_t* __restrict__ idx,
                                                  const float* __restrict__ residual, float* __restrict__ out,
                                                  float* __restrict__ y) {
   using C = RowCfg<BITS, I>;
   constexpr int RB = C::RPW * P;
+  __shared__ float4 hs[kWaves][I / 4];
   __shared__ float part[kWaves][RB];
   const int t = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -412,41 +525,41 @@ __global__ __launch_bounds__(kBlock) void k_down(LayerArgs a, const int32_t* __r
   const bool combine = out != nullptr;
   bool first = true;
   for (int k = wave; k < a.NE; k += kWaves) {
-    const uint8_t* blob;
-    float coef = 1.0f;
+    const uint8_t* blob = a.shared;
     bool valid = true;
+    float coef = 1.0f;
     if (k < a.K) {
       const int e = idx[(size_t)t * a.K + k];
       valid = (e >= 0 && e < a.E);
       blob = a.experts + (size_t)(valid ? e : 0) * a.stride;
       if (combine) coef = a.ws.w[(size_t)t * a.K + k];
-    } else {
-      blob = a.shared;
-      if (combine) coef = a.ws.g[t];
+    } else if (combine) {
+      coef = a.ws.g[t];
     }
+    Stage<I, 64> st;
+    st.load(a.ws.h + ((size_t)t * a.NE + k) * I, lane);
     float yv[P];
     if (valid) {
-      float xr[C::XPL], S[C::CPL];
-      load_act<C>(a.ws.h + ((size_t)t * a.NE + k) * I, lir, 1.0f, xr, S);
       const uint8_t* dc = blob + a.off_codes[2];
       const uint32_t* ds = reinterpret_cast<const uint32_t*>(blob + a.off_sb[2]);
       uint4 cw[P][C::CPL];
       uint32_t sb[P][C::CPL];
 #pragma unroll
-      for (int p = 0; p < P; ++p) {
-        const int r = row0 + p * C::RPW + rig;
-        if (r < a.H) load_row<C>(dc, ds, r, lir, cw[p], sb[p]);
-      }
+      for (int p = 0; p < P; ++p) load_row<C>(dc, ds, min(row0 + p * C::RPW + rig, a.H - 1), lir, cw[p], sb[p]);
+      __builtin_amdgcn_sched_barrier(0);
+      st.template store<C>(hs[wave], lane, 1.0f);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      float xr[C::XPL], S[C::CPL];
+      read_act<C>(hs[wave], lir, xr, S);
 #pragma unroll
-      for (int p = 0; p < P; ++p) {
-        const int r = row0 + p * C::RPW + rig;
-        yv[p] = (r < a.H) ? seg_sum<C::LPR>(row_partial<BITS, C>(cw[p], sb[p], xr, S)) : 0.0f;
-      }
+      for (int p = 0; p < P; ++p) yv[p] = seg_sum<C::LPR>(row_partial<BITS, C>(cw[p], sb[p], xr, S));
     } else {
 #pragma unroll
       for (int p = 0; p < P; ++p) yv[p] = NAN;
     }
-    if (lir == 0) {
+    if (lir == C::LPR - 1) {
 #pragma unroll
       for (int p = 0; p < P; ++p) {
         const int r = row0 + p * C::RPW + rig;
@@ -460,6 +573,7 @@ __global__ __launch_bounds__(kBlock) void k_down(LayerArgs a, const int32_t* __r
       }
     }
     first = false;
+    __builtin_amdgcn_wave_barrier();  // the next slot reuses this wave's LDS region
   }
   if (!combine) return;
   __syncthreads();
@@ -473,24 +587,19 @@ __global__ __launch_bounds__(kBlock) void k_down(LayerArgs a, const int32_t* __r
 }
 
 // Router-only top-K: one wave per token.
+template <int PL>
 __global__ __launch_bounds__(64) void k_topk(LayerArgs a, int32_t* __restrict__ idx, float* __restrict__ w,
                                              float* __restrict__ sg, double* __restrict__ logits_out) {
+  __shared__ int32_t sel[MOE_MAX_TOP_K];
+  __shared__ double val[MOE_MAX_TOP_K];
   const int t = blockIdx.x, lane = threadIdx.x;
   const double* lg = a.ws.logits + (size_t)t * (a.E + 1);
-  int32_t sel[MOE_MAX_TOP_K];
-  double val[MOE_MAX_TOP_K];
-  wave_topk(lg, a.E, a.K, lane, sel, val);
+  double v[PL];
+  load_topk_values<PL>(lg, a.E, lane, v);
+  wave_topk<PL>(v, a.E, a.K, lane, -1, true, sel, val);
   if (logits_out)
     for (int e = lane; e < a.E; e += 64) logits_out[(size_t)t * a.E + e] = lg[e];
-  if (lane == 0) {
-    float ww[MOE_MAX_TOP_K];
-    route_weights(val, a.K, ww);
-    for (int k = 0; k < a.K; ++k) {
-      idx[(size_t)t * a.K + k] = sel[k];
-      w[(size_t)t * a.K + k] = ww[k];
-    }
-    if (sg && a.has_shared) sg[t] = (float)(1.0 / (1.0 + exp(-lg[a.E])));
-  }
+  if (lane == 0) write_routing(a, t, sel, val, lg, idx, w, nullptr, sg);
 }
 
 __global__ void k_combine(int T, int H, int K, int has_shared, const float* __restrict__ res,
@@ -546,18 +655,31 @@ unsigned blocks_for(int64_t n, int bs) { return (unsigned)((n + bs - 1) / bs); }
 // ---- dispatch over the supported (bits, row length) pairs ----------------------------------------
 
 #define BQ_FOR_H(X) X(256) X(512) X(1024) X(2048) X(4096) X(8192)
-#define BQ_FOR_I(X) X(64) X(128) X(256) X(512) X(1024) X(2048) X(4096) X(8192)
+#define BQ_FOR_I(X) X(64) X(128) X(256) X(512) X(1024) X(2048)
 
-constexpr int kP1 = 1;  // row steps per wave: shared gate/up in kernel 1
-constexpr int kP2 = 2;  // routed gate/up
-constexpr int kP3 = 4;  // down
+// Row steps per wave (the bytes each wave has in flight), tuned on MI355X for the 4096/1024 shape.
+#ifndef BQ_P1
+#define BQ_P1 2
+#endif
+#ifndef BQ_P2
+#define BQ_P2 1
+#endif
+#ifndef BQ_P3
+#define BQ_P3 8
+#endif
+#ifndef BQ_ROUTER_STEPS
+#define BQ_ROUTER_STEPS 1
+#endif
+constexpr int kP1 = BQ_P1;  // shared gate/up in kernel 1
+constexpr int kP2 = BQ_P2;  // routed gate/up
+constexpr int kP3 = BQ_P3;  // down
 
 template <int BITS, int H>
 hipError_t router_phase_impl(const LayerArgs& a, const float* x, const float* norm_src, float eps, int T,
                              bool with_shared_ffn, hipStream_t s) {
   using R = RouterCfg<H>;
   using C = RowCfg<BITS, H>;
-  const int router_steps = 1;
+  const int router_steps = BQ_ROUTER_STEPS;
   const int nrows = a.E + a.has_shared;
   const int rows_per_block = kWaves * router_steps * R::RPW;
   const int nrb = (nrows + rows_per_block - 1) / rows_per_block;
@@ -578,7 +700,10 @@ hipError_t gateup_impl(const LayerArgs& a, const float* x, int T, const int32_t*
   const int rows_per_block = kWaves * kP2 * C::RPW;
   const int nb = (a.I + rows_per_block - 1) / rows_per_block;
   const int slots = a.K + ((with_shared && a.has_shared) ? 1 : 0);
-  hipLaunchKernelGGL((k_gateup<BITS, H, kP2>), dim3(nb, slots, T), dim3(kBlock), 0, s, a, x, idx_in, idx_out);
+  if (a.E <= 512)
+    hipLaunchKernelGGL((k_gateup<BITS, H, kP2, 8>), dim3(nb, slots, T), dim3(kBlock), 0, s, a, x, idx_in, idx_out);
+  else
+    hipLaunchKernelGGL((k_gateup<BITS, H, kP2, 16>), dim3(nb, slots, T), dim3(kBlock), 0, s, a, x, idx_in, idx_out);
   return hipGetLastError();
 }
 
@@ -634,7 +759,10 @@ hipError_t launch_topk(const Geometry& g, int T, const Workspace& ws, int32_t* i
                        double* logits_out, hipStream_t s) {
   LayerPtrs p{};
   const LayerArgs a = make_args(g, p, ws);
-  hipLaunchKernelGGL(k_topk, dim3(T), dim3(64), 0, s, a, idx, w, sg, logits_out);
+  if (g.E <= 512)
+    hipLaunchKernelGGL(k_topk<8>, dim3(T), dim3(64), 0, s, a, idx, w, sg, logits_out);
+  else
+    hipLaunchKernelGGL(k_topk<16>, dim3(T), dim3(64), 0, s, a, idx, w, sg, logits_out);
   return hipGetLastError();
 }
 

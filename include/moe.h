@@ -57,7 +57,7 @@ extern "C" {
 #define MOE_PREFILL_MIN_TOKENS 64
 
 /* One MoE layer.
- *   hidden H, inter I: powers of two with 64 <= I and 256 <= H <= 8192. group must be 64, bits 2 or 4.
+ *   hidden H, inter I: powers of two with 256 <= H <= 8192 and 64 <= I <= 2048. group must be 64, bits 2 or 4.
  *   n_experts E: 1..MOE_MAX_EXPERTS. top_k K: 1..min(E, MOE_MAX_TOP_K).
  *   experts_dev: E packed blobs, expert e at experts_dev + e*expert_stride. expert_stride is at
  *   least moe_blob_bytes(H, I, bits, group) and a multiple of 256.
@@ -156,6 +156,14 @@ int moe_combine(const moe_layer_t* layer, const float* residual_dev, const float
  * idx_out_dev int32 [T][K] may be NULL. x_dev and out_dev may not alias; residual_dev may alias x_dev. */
 int moe_layer_forward(const moe_layer_t* layer, const float* x_dev, const float* residual_dev, int T, float* out_dev,
                       int32_t* idx_out_dev, void* ws_dev, size_t ws_bytes, void* stream);
+
+/* Instrumented moe_layer_forward, for timing kernels in place: the same kernels on `stream`, with
+ * hipEventRecord(events[2p]) before and hipEventRecord(events[2p+1]) after phase p (decode path:
+ * p = 0 router phase, 1 routed gate/up, 2 down + combine). events is a host array of 6 hipEvent_t
+ * created by the caller. A NULL entry is skipped. Returns as moe_layer_forward. */
+int moe_layer_forward_timed(const moe_layer_t* layer, const float* x_dev, const float* residual_dev, int T,
+                            float* out_dev, int32_t* idx_out_dev, void* ws_dev, size_t ws_bytes, void* stream,
+                            void* const* events);
 
 /* A stack of L layers, decode only ("Deferred GPU Expert Compute": combine + norm + residual on the
  * GPU hand off to the next layer). With h_0 = x:
