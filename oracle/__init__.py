@@ -164,3 +164,37 @@ def layer(x, res, router, gate_vec, get_expert, K: int, group: int, shared_exper
         g = float("nan")
         out = combine(res, np.stack(ys), w, 0.0, None)
     return LayerResult(out, idx, w, g, logits, np.stack(ys), margin)
+
+
+@dataclass
+class StackResult:
+    out: np.ndarray  # h_L [H]
+    idx: np.ndarray  # [L][K] choices the oracle followed
+    near_ties: list  # (layer, oracle idx, followed idx, max logit gap) where a near-tie choice was followed
+
+
+def stack(x, layers, K: int, group: int, eps: float, follow=None, tie_bound: float = 0.0) -> StackResult:
+    """A stack of MoE layers for one token (GN+ summary, "Deferred GPU Expert Compute": combine, norm
+    and residual feed the next layer). h_0 = x; layer l reads u_l = h_l for l = 0 and
+    u_l = rmsnorm(h_l) for l >= 1, and h_{l+1} = h_l + MoE_l(u_l).
+
+    layers[l] = (router, gate_vec, get_expert, shared_expert). When follow[l] (another
+    implementation's top-K at layer l) differs from the oracle's choice, the oracle adopts it only
+    if every rank's logit differs from the oracle's by at most tie_bound (a near-tie under that
+    implementation's rounding). Otherwise it keeps its own choice and the caller sees the
+    mismatch in .idx.
+    """
+    h = np.asarray(x, dtype=np.float64)
+    idx_all, ties = [], []
+    for l, (router, gate_vec, get_expert, shared) in enumerate(layers):
+        u = h if l == 0 else rmsnorm(h, eps)
+        r = layer(u, h, router, gate_vec, get_expert, K, group, shared_expert=shared)
+        if follow is not None and list(follow[l]) != list(r.idx):
+            f = np.asarray(follow[l], dtype=np.int32)
+            gap = float(np.max(np.abs(r.logits[f] - r.logits[r.idx])))
+            if len(set(f.tolist())) == K and gap <= tie_bound:
+                ties.append((l, list(r.idx), list(f), gap))
+                r = layer(u, h, router, gate_vec, get_expert, K, group, shared_expert=shared, force_idx=f)
+        idx_all.append(r.idx)
+        h = r.out
+    return StackResult(h, np.stack(idx_all), ties)

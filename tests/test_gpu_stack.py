@@ -1,0 +1,116 @@
+"""GPU parity of the decode stack (moe_stack_forward) against the fp64 oracle's stack.
+
+Between layers the stack applies a unit-weight RMS norm (eps 1e-6); layer 0 reads the raw input.
+The top-K must match the oracle bit for bit. The one exception is a genuine near-tie: there the
+oracle's fp64 logits of the two choices differ by less than the GPU's fp32 activation rounding can
+move them (1e-4, derived in the design notes). The oracle then follows the GPU's branch, and the
+test counts these events.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import bit_quantized_expert_gemv_amd as bq
+import oracle
+import synth
+from synth.gpu_layers import DeviceLayer
+from tests._ref import Reference, assert_close
+
+pytestmark = pytest.mark.gpu
+
+EPS = 1e-6
+TIE_BOUND = 1e-4
+TINYSTACK = synth.Workload("tinystack", 256, 8, 128, 2, bits=4, tokens=8, layers=4, weight_family=5, x_family=5)
+
+
+def _log(msg):
+    print(f"[gpu-test] {msg}", flush=True)
+
+
+def _oracle_layers(refs):
+    return [(r.router, r.gate, r.expert, r.shared) for r in refs]
+
+
+def _run_stack(layers, x, T):
+    w = layers[0].w
+    n = bq.moe_stack_workspace_bytes(layers[0].desc, T)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(x)
+    idx = torch.empty(len(layers), T, w.top_k, dtype=torch.int32, device="cuda")
+    bq.moe_stack_forward([L.desc for L in layers], EPS, x, T, out, idx, ws, n)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), idx.cpu().numpy()
+
+
+def test_stack_tiny(gpu_device):
+    w = TINYSTACK
+    layers = [DeviceLayer(w, l) for l in range(w.layers)]
+    refs = [Reference(w, l) for l in range(w.layers)]
+    x = torch.from_numpy(synth.tokens_x(w, 0, w.tokens)).cuda()
+    out, idx = _run_stack(layers, x, w.tokens)
+    xs = x.cpu().numpy()
+    for t in range(w.tokens):
+        r = oracle.stack(xs[t], _oracle_layers(refs), w.top_k, w.group, EPS)
+        assert np.array_equal(idx[:, t, :], r.idx), f"token {t}: {idx[:, t, :]} vs {r.idx}"
+        assert_close(out[t], r.out, f"stack out[{t}]")
+
+
+def test_stack_single_layer_equals_layer_forward(gpu_device):
+    """Layer 0 of the stack reads the raw input, so a one-layer stack is exactly moe_layer_forward."""
+    w = synth.WORKLOADS["decode4"]
+    L = DeviceLayer(w)
+    x = torch.from_numpy(synth.tokens_x(w, 0, 3)).cuda()
+    out_s, idx_s = _run_stack([L], x, 3)
+    n = bq.moe_workspace_bytes(L.desc, 3)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(x)
+    idx = torch.empty(3, w.top_k, dtype=torch.int32, device="cuda")
+    bq.moe_layer_forward(L.desc, x, x, 3, out, idx, ws, n)
+    torch.cuda.synchronize()
+    assert np.array_equal(out_s, out.cpu().numpy()) and np.array_equal(idx_s[0], idx.cpu().numpy())
+
+
+def test_stack60_sequence(gpu_device):
+    """The full 60-layer stack with every expert resident (about 218 GB), as 128 sequential
+    single-token calls in one graph; sampled tokens are checked against the oracle's stack."""
+    w = synth.WORKLOADS["stack60"]
+    free, _ = torch.cuda.mem_get_info()
+    need = w.layers * (w.n_experts + 1) * bq.moe_blob_bytes(w.hidden, w.inter, w.bits) + (8 << 30)
+    if free < need:
+        pytest.skip(f"needs {need / 2**30:.0f} GiB free, have {free / 2**30:.0f} GiB")
+    layers = []
+    for l in range(w.layers):
+        layers.append(DeviceLayer(w, l))
+        if l % 10 == 9:
+            torch.cuda.synchronize()
+            _log(f"stack60: built {l + 1} layers")
+    N = w.tokens
+    X = torch.from_numpy(synth.tokens_x(w, 0, N)).cuda()
+    out = torch.empty_like(X)
+    idx = torch.empty(N, w.layers, w.top_k, dtype=torch.int32, device="cuda")
+    n = bq.moe_stack_workspace_bytes(layers[0].desc, 1)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    descs = [L.desc for L in layers]
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for t in range(N):
+            bq.moe_stack_forward(descs, EPS, X[t], 1, out[t], idx[t], ws, n, stream=s)
+    g.replay()
+    torch.cuda.synchronize()
+    _log("stack60: graph replayed")
+    on, ix, xs = out.cpu().numpy(), idx.cpu().numpy(), X.cpu().numpy()
+    refs = [Reference(w, l, cache=4) for l in range(w.layers)]
+    ties = 0
+    for t in (0, N - 1):
+        r = oracle.stack(xs[t], _oracle_layers(refs), w.top_k, w.group, EPS, follow=ix[t], tie_bound=TIE_BOUND)
+        ties += len(r.near_ties)
+        for (l, oi, fi, gap) in r.near_ties:
+            _log(f"token {t} layer {l}: near-tie followed, oracle {oi} gpu {fi}, logit gap {gap:.2e}")
+        assert np.array_equal(ix[t], r.idx), f"token {t}: top-K differs beyond a near-tie"
+        assert_close(on[t], r.out, f"stack60 out[{t}]")
+        _log(f"stack60: token {t} matches")
+    assert ties <= 2

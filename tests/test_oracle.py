@@ -384,3 +384,31 @@ def test_mutants_are_caught(name, tmp_path):
     finally:
         oracle._lib = good
     assert caught, f"mutant '{name}' passed every pin"
+
+
+# ---- the stack composition ----------------------------------------------------------------------
+
+def test_stack_two_layers_bruteforce():
+    """Two tiny layers: h1 = x + MoE0(x), u1 = h1 / rms(h1), out = h1 + MoE1(u1), by numpy brute force."""
+    w = synth.Workload("tinystack", 256, 8, 128, 2, bits=4, weight_family=5, x_family=5)
+    per = []
+    for l in range(2):
+        R = synth.router_weights(w, l)
+        gs = synth.shared_gate_weights(w, l)
+        ex = [synth.expert_arrays(w, l, e) for e in range(w.n_experts)]
+        sh = synth.expert_arrays(w, l, synth.SHARED)
+        per.append((R, gs, ex, sh))
+    x = synth.tokens_x(w, 0, 1)[0].astype(np.float64)
+    h1, top0, _, _ = _np_layer(x, x, per[0][0], per[0][1], per[0][2], per[0][3], w.top_k)
+    u1 = h1 / np.sqrt(np.mean(h1 * h1) + 1e-6)
+    out, top1, _, _ = _np_layer(u1, h1, per[1][0], per[1][1], per[1][2], per[1][3], w.top_k)
+    layers = [(R, gs, (lambda ex: (lambda e: ex[e]))(ex), sh) for (R, gs, ex, sh) in per]
+    r = oracle.stack(x, layers, w.top_k, w.group, 1e-6)
+    assert np.array_equal(r.idx, np.stack([top0, top1]))
+    assert np.allclose(r.out, out, rtol=1e-12, atol=1e-12)
+    # a followed choice is adopted only within the tie bound
+    alt = [list(r.idx[0]), list(r.idx[1][::-1])]
+    r2 = oracle.stack(x, layers, w.top_k, w.group, 1e-6, follow=alt, tie_bound=0.0)
+    assert np.array_equal(r2.idx, r.idx) and not r2.near_ties
+    r3 = oracle.stack(x, layers, w.top_k, w.group, 1e-6, follow=alt, tie_bound=1e9)
+    assert list(r3.idx[1]) == alt[1] and len(r3.near_ties) == 1
