@@ -11,7 +11,7 @@ LIB = os.path.join(HERE, "libbqmoe.so")
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-shared", "-std=c++17", "-Wall",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-I", os.path.join(ROOT, "include"), "-I", CSRC]
-SOURCES = ["moe_host.cpp", "moe_kernels.hip"]
+SOURCES = ["moe_host.cpp", "moe_kernels.hip", "moe_prefill.hip"]
 
 
 def build(verbose: bool = False) -> str:

@@ -107,6 +107,59 @@ size_t workspace_layer_bytes(const Geometry& g, int T) {
          align256(t * g.NE * g.I * 4) + align256(t * g.H * 4);
 }
 
+namespace {
+struct Carver {
+  uint8_t* p;
+  size_t used = 0;
+  template <class T>
+  T* take(size_t count) {
+    T* r = reinterpret_cast<T*>(p == nullptr ? nullptr : p + used);
+    used += align256(count * sizeof(T));
+    return r;
+  }
+};
+
+PrefillWorkspace carve_prefill_impl(const Geometry& g, int T, void* base, size_t* total) {
+  Carver c{static_cast<uint8_t*>(base)};
+  const size_t t = (size_t)T, N = t * g.K, R = N + t * g.has_shared;
+  PrefillWorkspace w;
+  w.layer.logits = c.take<double>(t * (g.E + 1));
+  w.layer.idx = c.take<int32_t>(N);
+  w.layer.w = c.take<float>(N);
+  w.layer.g = c.take<float>(t);
+  w.layer.h = nullptr;
+  w.layer.u = nullptr;
+  w.xh = c.take<uint16_t>(t * g.H);
+  w.xl = c.take<uint16_t>(t * g.H);
+  w.xs = c.take<float>(t * (g.H / 64));
+  w.hist = c.take<int32_t>(((N + 255) / 256) * g.E);
+  w.counts = c.take<int32_t>(g.E);
+  w.offsets = c.take<int32_t>(g.E + 1);
+  w.tile_e = c.take<int32_t>(g.E + (N + 31) / 32);
+  w.tile_first = c.take<int32_t>(g.E + (N + 31) / 32);
+  w.ntiles = c.take<int32_t>(1);
+  w.pos = c.take<int32_t>(N);
+  w.perm = c.take<int32_t>(N);
+  w.hh = c.take<uint16_t>(R * g.I);
+  w.hl = c.take<uint16_t>(R * g.I);
+  w.hs = c.take<float>(R * (g.I / 64));
+  w.y = c.take<float>(R * g.H);
+  *total = c.used;
+  return w;
+}
+}  // namespace
+
+size_t workspace_prefill_bytes(const Geometry& g, int T) {
+  size_t total = 0;
+  carve_prefill_impl(g, T, nullptr, &total);
+  return total;
+}
+
+PrefillWorkspace carve_prefill(const Geometry& g, int T, void* base) {
+  size_t total = 0;
+  return carve_prefill_impl(g, T, base, &total);
+}
+
 Workspace carve_workspace(const Geometry& g, int T, void* base) {
   const size_t t = (size_t)T;
   uint8_t* p = static_cast<uint8_t*>(base);
@@ -137,7 +190,13 @@ size_t moe_workspace_bytes(const moe_layer_t* layer, int T) {
   Geometry g;
   const char* why = nullptr;
   if (layer == nullptr || T < 0 || !geometry_from(layer, &g, &why)) return 0;
-  return workspace_layer_bytes(g, T < 1 ? 1 : T);
+  const int t = T < 1 ? 1 : T;
+  size_t n = workspace_layer_bytes(g, t);
+  if (t >= MOE_PREFILL_MIN_TOKENS) {
+    const size_t pf = workspace_prefill_bytes(g, t);
+    if (pf > n) n = pf;
+  }
+  return n;
 }
 
 size_t moe_stack_workspace_bytes(const moe_layer_t* layer, int T) {
@@ -205,6 +264,17 @@ int moe_dequant(const moe_layer_t* layer, int expert, int matrix, int out_dtype,
   return hip_status(launch_dequant(g, blob, matrix, out_dtype, w_out, static_cast<hipStream_t>(stream)));
 }
 
+namespace {
+size_t needed_ws(const Geometry& g, int T) {
+  size_t n = workspace_layer_bytes(g, T);
+  if (T >= MOE_PREFILL_MIN_TOKENS) {
+    const size_t pf = workspace_prefill_bytes(g, T);
+    if (pf > n) n = pf;
+  }
+  return n;
+}
+}  // namespace
+
 int moe_router(const moe_layer_t* layer, const float* x, int T, int32_t* idx, float* w, float* shared_g,
                double* logits, void* ws, size_t ws_bytes, void* stream) {
   Geometry g;
@@ -215,10 +285,11 @@ int moe_router(const moe_layer_t* layer, const float* x, int T, int32_t* idx, fl
   if ((rc = check_act(x, "x"))) return rc;
   if (idx == nullptr || w == nullptr) return fail(MOE_EINVAL, "idx and w must be non-NULL");
   if (ws == nullptr || !aligned(ws, 256)) return fail(MOE_EINVAL, "workspace must be non-NULL and 256-byte aligned");
-  if (ws_bytes < workspace_layer_bytes(g, T)) return fail(MOE_ENOSPC, "workspace smaller than moe_workspace_bytes()");
+  if (ws_bytes < needed_ws(g, T)) return fail(MOE_ENOSPC, "workspace smaller than moe_workspace_bytes()");
   const Workspace W = carve_workspace(g, T, ws);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = launch_router_phase(g, ptrs_of(layer), x, nullptr, 0.0f, T, W, false, s);
+  hipError_t e = (T >= MOE_PREFILL_MIN_TOKENS) ? launch_router_gemm(g, ptrs_of(layer), x, T, W, s)
+                                                : launch_router_phase(g, ptrs_of(layer), x, nullptr, 0.0f, T, W, false, s);
   if (e == hipSuccess) e = launch_topk(g, T, W, idx, w, shared_g, logits, s);
   return hip_status(e);
 }
@@ -234,10 +305,12 @@ int moe_expert_ffn(const moe_layer_t* layer, const float* x, int T, const int32_
   if ((rc = check_act(y, "y"))) return rc;
   if (idx == nullptr) return fail(MOE_EINVAL, "idx is NULL");
   if (ws == nullptr || !aligned(ws, 256)) return fail(MOE_EINVAL, "workspace must be non-NULL and 256-byte aligned");
-  if (ws_bytes < workspace_layer_bytes(g, T)) return fail(MOE_ENOSPC, "workspace smaller than moe_workspace_bytes()");
-  const Workspace W = carve_workspace(g, T, ws);
+  if (ws_bytes < needed_ws(g, T)) return fail(MOE_ENOSPC, "workspace smaller than moe_workspace_bytes()");
   hipStream_t s = static_cast<hipStream_t>(stream);
   const LayerPtrs p = ptrs_of(layer);
+  if (T >= MOE_PREFILL_MIN_TOKENS)
+    return hip_status(launch_prefill(g, p, x, nullptr, T, carve_prefill(g, T, ws), idx, nullptr, nullptr, y, s));
+  const Workspace W = carve_workspace(g, T, ws);
   hipError_t e = launch_gateup(g, p, x, T, W, idx, nullptr, true, s);
   if (e == hipSuccess) e = launch_down(g, p, T, W, idx, nullptr, nullptr, y, s);
   return hip_status(e);
@@ -274,14 +347,21 @@ int moe_layer_forward_timed(const moe_layer_t* layer, const float* x, const floa
   if (residual == nullptr) return fail(MOE_EINVAL, "residual is NULL");
   if (x == out) return fail(MOE_EINVAL, "x and out may not alias");
   if (ws == nullptr || !aligned(ws, 256)) return fail(MOE_EINVAL, "workspace must be non-NULL and 256-byte aligned");
-  if (ws_bytes < workspace_layer_bytes(g, T)) return fail(MOE_ENOSPC, "workspace smaller than moe_workspace_bytes()");
-  const Workspace W = carve_workspace(g, T, ws);
+  if (ws_bytes < needed_ws(g, T)) return fail(MOE_ENOSPC, "workspace smaller than moe_workspace_bytes()");
   hipStream_t s = static_cast<hipStream_t>(stream);
   const LayerPtrs p = ptrs_of(layer);
   auto mark = [&](int i) {
     if (events != nullptr && events[i] != nullptr) return hipEventRecord(static_cast<hipEvent_t>(events[i]), s);
     return hipSuccess;
   };
+  if (T >= MOE_PREFILL_MIN_TOKENS) {
+    hipError_t e = mark(0);
+    if (e == hipSuccess)
+      e = launch_prefill(g, p, x, residual, T, carve_prefill(g, T, ws), nullptr, idx_out, out, nullptr, s);
+    if (e == hipSuccess) e = mark(5);
+    return hip_status(e);
+  }
+  const Workspace W = carve_workspace(g, T, ws);
   hipError_t e = mark(0);
   if (e == hipSuccess) e = launch_router_phase(g, p, x, nullptr, 0.0f, T, W, true, s);
   if (e == hipSuccess) e = mark(1);

@@ -37,7 +37,29 @@ struct Workspace {
   float* u;        // [T][H]: normalised layer input (stack only)
 };
 
+// Prefill (grouped) workspace for T tokens; N = T*K routed entries, R = N + T*has_shared rows.
+struct PrefillWorkspace {
+  Workspace layer;  // logits [T][E+1], idx [T][K], w [T][K], g [T]; h and u unused
+  uint16_t* xh;     // [T][H] bf16 hi of the activations
+  uint16_t* xl;     // [T][H] bf16 lo
+  float* xs;        // [T][H/64] group sums of hi + lo
+  int32_t* hist;    // [ceil(N/256)][E]
+  int32_t* counts;  // [E]
+  int32_t* offsets; // [E+1]
+  int32_t* tile_e;  // [E + ceil(N/32)]
+  int32_t* tile_first;
+  int32_t* ntiles;  // [1]
+  int32_t* pos;     // [N] entry -> position
+  int32_t* perm;    // [N] position -> entry
+  uint16_t* hh;     // [R][I] SwiGLU outputs, bf16 hi
+  uint16_t* hl;     // [R][I] bf16 lo
+  float* hs;        // [R][I/64] group sums of hi + lo
+  float* y;         // [R][H] down outputs
+};
+
 bool geometry_from(const moe_layer_t* L, Geometry* g, const char** why);
+size_t workspace_prefill_bytes(const Geometry& g, int T);
+PrefillWorkspace carve_prefill(const Geometry& g, int T, void* base);
 size_t workspace_layer_bytes(const Geometry& g, int T);
 Workspace carve_workspace(const Geometry& g, int T, void* base);
 
@@ -62,5 +84,15 @@ hipError_t launch_combine(const Geometry& g, int T, const float* residual, const
                           const float* sg, float* out, hipStream_t s);
 hipError_t launch_dequant(const Geometry& g, const uint8_t* blob, int matrix, int out_dtype, void* out, hipStream_t s);
 hipError_t launch_pack(int H, int I, int bits, int G, const moe_expert_arrays_t* a, uint8_t* blob, hipStream_t s);
+
+// Prefill (moe_prefill.hip). With idx_in null the router runs first (fp64 GEMM + top-K). Then come
+// grouping, the grouped gate/up and down GEMMs, and either out = residual + combine (out non-null) or
+// y_out[t][k][:] = expert outputs (y_out non-null).
+hipError_t launch_prefill(const Geometry& g, const LayerPtrs& p, const float* x, const float* residual, int T,
+                          const PrefillWorkspace& w, const int32_t* idx_in, int32_t* idx_out, float* out,
+                          float* y_out, hipStream_t s);
+// Router logits of T tokens as one fp64 GEMM into ws.logits.
+hipError_t launch_router_gemm(const Geometry& g, const LayerPtrs& p, const float* x, int T, const Workspace& ws,
+                              hipStream_t s);
 
 }  // namespace bqmoe

@@ -1,0 +1,143 @@
+"""GPU parity of the prefill (grouped, MFMA) path against the fp64 oracle.
+
+Prefill runs when T >= MOE_PREFILL_MIN_TOKENS. Its bar is the decode path's bar:
+- bit-exact top-K for every token;
+- outputs within 2e-3*max|oracle| + 1e-5 per token;
+- a prefill row equals the decode of the same token within the same tolerance.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import bit_quantized_expert_gemv_amd as bq
+import oracle
+import synth
+from synth.gpu_layers import DeviceLayer
+from tests._ref import Reference, assert_close
+
+pytestmark = pytest.mark.gpu
+
+TINY, DEC2, PRE4 = synth.WORKLOADS["tiny"], synth.WORKLOADS["decode2"], synth.WORKLOADS["prefill4"]
+
+
+def _log(msg):
+    print(f"[gpu-test] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def tiny(gpu_device):
+    return DeviceLayer(TINY), Reference(TINY)
+
+
+@pytest.fixture(scope="module")
+def pre4(gpu_device):
+    _log("build the 4-bit layer (512 experts) for prefill")
+    L = DeviceLayer(PRE4)
+    torch.cuda.synchronize()
+    return L, Reference(PRE4)
+
+
+def _forward(L, x, res=None):
+    T = x.shape[0]
+    n = bq.moe_workspace_bytes(L.desc, T)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(x)
+    idx = torch.empty(T, L.w.top_k, dtype=torch.int32, device="cuda")
+    bq.moe_layer_forward(L.desc, x, x if res is None else res, T, out, idx, ws, n)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), idx.cpu().numpy()
+
+
+@pytest.mark.parametrize("T", [64, 100, 300])
+def test_prefill_tiny_all_tokens(tiny, T):
+    L, ref = tiny
+    x = torch.from_numpy(synth.tokens_x(TINY, 7, T)).cuda()
+    out, idx = _forward(L, x)
+    xs = x.cpu().numpy()
+    for t in range(T):
+        r = ref.token(xs[t])
+        assert list(idx[t]) == list(r.idx), f"token {t}"
+        assert_close(out[t], r.out, f"out[{t}]")
+    counts = np.bincount(idx.reshape(-1), minlength=TINY.n_experts)
+    assert counts.sum() == T * TINY.top_k
+
+
+def test_prefill_tiny_residual_and_determinism(tiny):
+    L, ref = tiny
+    x = torch.from_numpy(synth.tokens_x(TINY, 0, 80)).cuda()
+    res = torch.randn_like(x)
+    a, ia = _forward(L, x, res)
+    b, ib = _forward(L, x, res)
+    assert np.array_equal(a, b) and np.array_equal(ia, ib)
+    for t in (0, 41, 79):
+        r = ref.token(x[t].cpu().numpy(), res[t].cpu().numpy())
+        assert_close(a[t], r.out)
+
+
+def test_prefill4_full(pre4):
+    """2048 tokens through the 4-bit layer: every token's top-K against the oracle's fp64 routing,
+    sampled outputs against the oracle, and prefill rows against the decode path's rows."""
+    L, ref = pre4
+    T = PRE4.tokens
+    x = torch.from_numpy(synth.tokens_x(PRE4, 0, T)).cuda()
+    _log("prefill4: 2048-token forward")
+    out, idx = _forward(L, x)
+    xs = x.cpu().numpy().astype(np.float64)
+    _log("prefill4: oracle routing for every token")
+    for t in range(T):
+        lg = oracle.router_logits(ref.router, xs[t])
+        assert list(idx[t]) == list(oracle.topk(lg, PRE4.top_k)), f"token {t}"
+    counts = np.bincount(idx.reshape(-1), minlength=PRE4.n_experts)
+    _log(f"prefill4: tokens per expert min {counts.min()} mean {counts.mean():.1f} max {counts.max()}, "
+         f"untouched {(counts == 0).sum()}")
+    assert counts.sum() == T * PRE4.top_k
+    sample = [0, 1, 17, 500, 1023, 1024, 2046, 2047]
+    for t in sample:
+        r = ref.token(xs[t])
+        assert_close(out[t], r.out, f"prefill out[{t}]")
+    # the same tokens through the decode path (T=1 calls)
+    n = bq.moe_workspace_bytes(L.desc, 1)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    for t in sample:
+        o1 = torch.empty(1, PRE4.hidden, device="cuda")
+        bq.moe_layer_forward(L.desc, x[t:t + 1], x[t:t + 1], 1, o1, None, ws, n)
+        torch.cuda.synchronize()
+        assert_close(out[t], o1[0].cpu().numpy(), f"prefill vs decode [{t}]")
+
+
+def test_prefill_expert_ffn_and_router(pre4):
+    L, ref = pre4
+    T = 96
+    x = torch.from_numpy(synth.tokens_x(PRE4, 3000, T)).cuda()
+    n = bq.moe_workspace_bytes(L.desc, T)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    idx = torch.empty(T, PRE4.top_k, dtype=torch.int32, device="cuda")
+    wt = torch.empty(T, PRE4.top_k, device="cuda")
+    g = torch.empty(T, device="cuda")
+    bq.moe_router(L.desc, x, T, idx, wt, g, None, ws, n)
+    y = torch.empty(T, PRE4.top_k + 1, PRE4.hidden, device="cuda")
+    bq.moe_expert_ffn(L.desc, x, T, idx, y, ws, n)
+    torch.cuda.synchronize()
+    xs = x.cpu().numpy().astype(np.float64)
+    ix, yn = idx.cpu().numpy(), y.cpu().numpy()
+    for t in range(T):
+        lg = oracle.router_logits(ref.router, xs[t])
+        assert list(ix[t]) == list(oracle.topk(lg, PRE4.top_k)), f"token {t}"
+    for t in (0, 50, 95):
+        for k, e in enumerate(list(ix[t]) + [synth.SHARED]):
+            assert_close(yn[t, k], ref.expert_out(xs[t], int(e)), f"y[{t}][{k}]")
+
+
+def test_prefill_2bit(gpu_device):
+    L = DeviceLayer(DEC2)
+    ref = Reference(DEC2)
+    T = 128
+    x = torch.from_numpy(synth.tokens_x(DEC2, 0, T)).cuda()
+    out, idx = _forward(L, x)
+    xs = x.cpu().numpy()
+    for t in (0, 63, 127):
+        r = ref.token(xs[t])
+        assert list(idx[t]) == list(r.idx)
+        assert_close(out[t], r.out, f"2-bit prefill out[{t}]")
