@@ -289,7 +289,7 @@ int moe_router(const moe_layer_t* layer, const float* x, int T, int32_t* idx, fl
   const Workspace W = carve_workspace(g, T, ws);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = (T >= MOE_PREFILL_MIN_TOKENS) ? launch_router_gemm(g, ptrs_of(layer), x, T, W, s)
-                                                : launch_router_phase(g, ptrs_of(layer), x, nullptr, 0.0f, T, W, false, s);
+                                                : launch_router_phase(g, ptrs_of(layer), x, nullptr, 0.0f, T, W, s);
   if (e == hipSuccess) e = launch_topk(g, T, W, idx, w, shared_g, logits, s);
   return hip_status(e);
 }
@@ -350,27 +350,28 @@ int moe_layer_forward_timed(const moe_layer_t* layer, const float* x, const floa
   if (ws_bytes < needed_ws(g, T)) return fail(MOE_ENOSPC, "workspace smaller than moe_workspace_bytes()");
   hipStream_t s = static_cast<hipStream_t>(stream);
   const LayerPtrs p = ptrs_of(layer);
-  auto mark = [&](int i) {
-    if (events != nullptr && events[i] != nullptr) return hipEventRecord(static_cast<hipEvent_t>(events[i]), s);
-    return hipSuccess;
+  auto ev = [&](int k) {
+    KernelEvents e;
+    if (events != nullptr) {
+      e.start = static_cast<hipEvent_t>(events[2 * k]);
+      e.stop = static_cast<hipEvent_t>(events[2 * k + 1]);
+    }
+    return e;
   };
   if (T >= MOE_PREFILL_MIN_TOKENS) {
-    hipError_t e = mark(0);
+    // many kernels: events[0] and events[5] are recorded around all of them
+    hipError_t e = hipSuccess;
+    if (events != nullptr && events[0] != nullptr) e = hipEventRecord(static_cast<hipEvent_t>(events[0]), s);
     if (e == hipSuccess)
       e = launch_prefill(g, p, x, residual, T, carve_prefill(g, T, ws), nullptr, idx_out, out, nullptr, s);
-    if (e == hipSuccess) e = mark(5);
+    if (e == hipSuccess && events != nullptr && events[5] != nullptr)
+      e = hipEventRecord(static_cast<hipEvent_t>(events[5]), s);
     return hip_status(e);
   }
   const Workspace W = carve_workspace(g, T, ws);
-  hipError_t e = mark(0);
-  if (e == hipSuccess) e = launch_router_phase(g, p, x, nullptr, 0.0f, T, W, true, s);
-  if (e == hipSuccess) e = mark(1);
-  if (e == hipSuccess) e = mark(2);
-  if (e == hipSuccess) e = launch_gateup(g, p, x, T, W, nullptr, idx_out, false, s);
-  if (e == hipSuccess) e = mark(3);
-  if (e == hipSuccess) e = mark(4);
-  if (e == hipSuccess) e = launch_down(g, p, T, W, W.idx, residual, out, nullptr, s);
-  if (e == hipSuccess) e = mark(5);
+  hipError_t e = launch_router_phase(g, p, x, nullptr, 0.0f, T, W, s, ev(0));
+  if (e == hipSuccess) e = launch_gateup(g, p, x, T, W, nullptr, idx_out, true, s, ev(1));
+  if (e == hipSuccess) e = launch_down(g, p, T, W, W.idx, residual, out, nullptr, s, ev(2));
   return hip_status(e);
 }
 
@@ -407,8 +408,8 @@ int moe_stack_forward(const moe_layer_t* layers, int L, float eps, const float* 
     const float* norm_src = (l == 0) ? nullptr : h;
     const float* xin = (l == 0) ? x : W.u;
     int32_t* io = idx_out ? idx_out + (size_t)l * T * g.K : nullptr;
-    e = launch_router_phase(g, p, x, norm_src, eps, T, W, true, s);
-    if (e == hipSuccess) e = launch_gateup(g, p, xin, T, W, nullptr, io, false, s);
+    e = launch_router_phase(g, p, x, norm_src, eps, T, W, s);
+    if (e == hipSuccess) e = launch_gateup(g, p, xin, T, W, nullptr, io, true, s);
     if (e == hipSuccess) e = launch_down(g, p, T, W, W.idx, h, h_next, nullptr, s);
     h = h_next;
   }

@@ -65,18 +65,25 @@ Workspace carve_workspace(const Geometry& g, int T, void* base);
 
 // ---- launchers (moe_kernels.hip); all return hipSuccess or the launch error ----
 
-// Phase 1: router logits (+ shared-gate logit) and, if with_shared_ffn, the shared expert's gate/up
-// SwiGLU into h[t][K]. If norm_src is non-null the layer input is RMSNorm(norm_src) (written to ws.u),
-// otherwise it is x.
+// Optional start/stop events that a launch hands to the dispatch itself (hipExtLaunchKernel), so
+// that they carry the kernel's own begin and end timestamps.
+struct KernelEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
+// Phase 1: router logits and the shared-gate logit into ws.logits. If norm_src is non-null the layer
+// input is RMSNorm(norm_src) (also written to ws.u), otherwise it is x.
 hipError_t launch_router_phase(const Geometry& g, const LayerPtrs& p, const float* x, const float* norm_src, float eps,
-                               int T, const Workspace& ws, bool with_shared_ffn, hipStream_t s);
+                               int T, const Workspace& ws, hipStream_t s, const KernelEvents& ev = {});
 // Phase 2: gate/up SwiGLU of the routed experts (slots 0..K-1), plus slot K (shared) if with_shared.
 // If idx_in is null the top-K is computed from ws.logits and written to ws.idx/w/g (and idx_out).
 hipError_t launch_gateup(const Geometry& g, const LayerPtrs& p, const float* x, int T, const Workspace& ws,
-                         const int32_t* idx_in, int32_t* idx_out, bool with_shared, hipStream_t s);
+                         const int32_t* idx_in, int32_t* idx_out, bool with_shared, hipStream_t s,
+                         const KernelEvents& ev = {});
 // Phase 3: down projections. combine: out = residual + sum_k w_k y_k + g y_s; otherwise y[t][k][:] = y_k.
 hipError_t launch_down(const Geometry& g, const LayerPtrs& p, int T, const Workspace& ws, const int32_t* idx,
-                       const float* residual, float* out, float* y, hipStream_t s);
+                       const float* residual, float* out, float* y, hipStream_t s, const KernelEvents& ev = {});
 // Top-K + weights from ws.logits (router-only path).
 hipError_t launch_topk(const Geometry& g, int T, const Workspace& ws, int32_t* idx, float* w, float* sg,
                        double* logits_out, hipStream_t s);

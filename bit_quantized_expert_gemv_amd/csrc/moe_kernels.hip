@@ -26,6 +26,7 @@
 // owns chunks i, i+LPR, ..., so each wave-wide load is contiguous. A lane keeps the activations
 // of its own columns in registers for every row it processes. Rows are reduced across their LPR
 // lanes with butterfly shuffles, which give every lane the bitwise-same sum.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -329,10 +330,11 @@ __device__ __forceinline__ int wave_topk(double (&v)[PL], int E, int K, int lane
     const int lo = __builtin_amdgcn_readlane((int)(bits & 0xFFFFFFFF), 63);
     const int hi = __builtin_amdgcn_readlane((int)(bits >> 32), 63);
     const int win = min(max(__builtin_amdgcn_readlane(bi, 63), 0), E - 1);
+    const double wv = __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
     if (k == want) chosen = win;
     if (record && lane == 0) {
       sel[k] = win;
-      val[k] = __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+      val[k] = wv;
     }
 #pragma unroll
     for (int i = 0; i < PL; ++i) v[i] = (lane + 64 * i == win) ? -INFINITY : v[i];
@@ -405,17 +407,20 @@ __device__ __forceinline__ void gateup_block(const LayerArgs& a, const uint8_t* 
 }
 
 // ---------------------------------------------------------------------------------------------
-// Kernel 1: router logits (+ shared-gate logit) and the shared expert's gate/up.
-// Blocks [0, n_router_blocks) do router rows (row E is the shared-gate vector); the rest do the
-// shared expert's gate/up rows.
-template <int BITS, int H, int P>
+// Kernel 1: router logits and the shared-gate logit (row E), accumulated in fp64. In a stack the
+// input is RMS-normalised first; block 0 stores the normalised vector for kernel 2.
+#ifndef BQ_ROUTER_SPLIT
+#define BQ_ROUTER_SPLIT 4
+#endif
+template <int H>
 __global__ __launch_bounds__(kBlock) void k_router_phase(LayerArgs a, const float* __restrict__ x,
                                                          const float* __restrict__ norm_src, float eps,
-                                                         int n_router_blocks, int router_steps) {
-  using C = RowCfg<BITS, H>;
+                                                         int router_steps) {
   using R = RouterCfg<H>;
+  constexpr int SPLIT = (R::CPL % BQ_ROUTER_SPLIT == 0) ? BQ_ROUTER_SPLIT : 1;  // waves per row
+  constexpr int CPW = R::CPL / SPLIT;                                            // chunks per lane
   __shared__ double red[kBlock];
-  __shared__ float4 xs[H / 4];
+  __shared__ double part[kWaves];
   const int t = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   float scale = 1.0f;
@@ -426,46 +431,50 @@ __global__ __launch_bounds__(kBlock) void k_router_phase(LayerArgs a, const floa
     if (blockIdx.x == 0)
       for (int i = threadIdx.x; i < H; i += kBlock) a.ws.u[(size_t)t * H + i] = src[i] * scale;
   }
-  if ((int)blockIdx.x < n_router_blocks) {
-    const int lir = lane % R::LPR, rig = lane / R::LPR;
-    const int nrows = a.E + a.has_shared;
-    for (int s = 0; s < router_steps; ++s) {
-      const int base = ((blockIdx.x * kWaves + wave) * router_steps + s) * R::RPW;
-      if (base >= nrows) break;  // wave-uniform
-      const int r = base + rig;
-      const int rr = min(r, nrows - 1);
-      const uint16_t* row = (rr < a.E) ? a.router + (size_t)rr * H : a.sgate;
-      uint4 w[R::CPL];
+  const int lir = lane % R::LPR, rig = lane / R::LPR;
+  const int nrows = a.E + a.has_shared;
+  const int piece = wave % SPLIT;
+  for (int s = 0; s < router_steps; ++s) {
+    const int base = ((blockIdx.x * (kWaves / SPLIT) + wave / SPLIT) * router_steps + s) * R::RPW;
+    const int r = base + rig;
+    const int rr = min(r, nrows - 1);
+    const uint16_t* row = (rr < a.E) ? a.router + (size_t)rr * H : a.sgate;
+    uint4 w[CPW];
 #pragma unroll
-      for (int j = 0; j < R::CPL; ++j) w[j] = *reinterpret_cast<const uint4*>(row + (lir + j * R::LPR) * 8);
-      double acc[4] = {0.0, 0.0, 0.0, 0.0};
+    for (int j = 0; j < CPW; ++j) w[j] = *reinterpret_cast<const uint4*>(row + (lir + (j * SPLIT + piece) * R::LPR) * 8);
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-      for (int j = 0; j < R::CPL; ++j) {
-        const float4* p = reinterpret_cast<const float4*>(src + (lir + j * R::LPR) * 8);
-        const float4 u0 = p[0], u1 = p[1];
-        const float xv[8] = {u0.x * scale, u0.y * scale, u0.z * scale, u0.w * scale,
-                             u1.x * scale, u1.y * scale, u1.z * scale, u1.w * scale};
-        const uint32_t ww[4] = {w[j].x, w[j].y, w[j].z, w[j].w};
+    for (int j = 0; j < CPW; ++j) {
+      const float4* p = reinterpret_cast<const float4*>(src + (lir + (j * SPLIT + piece) * R::LPR) * 8);
+      const float4 u0 = p[0], u1 = p[1];
+      const float xv[8] = {u0.x * scale, u0.y * scale, u0.z * scale, u0.w * scale,
+                           u1.x * scale, u1.y * scale, u1.z * scale, u1.w * scale};
+      const uint32_t ww[4] = {w[j].x, w[j].y, w[j].z, w[j].w};
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          acc[q] = fma((double)bf16_lo(ww[q]), (double)xv[2 * q], acc[q]);
-          acc[q] = fma((double)bf16_hi(ww[q]), (double)xv[2 * q + 1], acc[q]);
-        }
+      for (int q = 0; q < 4; ++q) {
+        acc[q] = fma((double)bf16_lo(ww[q]), (double)xv[2 * q], acc[q]);
+        acc[q] = fma((double)bf16_hi(ww[q]), (double)xv[2 * q + 1], acc[q]);
       }
-      const double tot = seg_sum<R::LPR>((acc[0] + acc[1]) + (acc[2] + acc[3]));
-      if (lir == R::LPR - 1 && r < nrows) a.ws.logits[(size_t)t * (a.E + 1) + r] = tot;
     }
-    return;
+    const double tot = seg_sum<R::LPR>((acc[0] + acc[1]) + (acc[2] + acc[3]));
+    if constexpr (SPLIT == 1) {
+      if (lir == R::LPR - 1 && r < nrows) a.ws.logits[(size_t)t * (a.E + 1) + r] = tot;
+    } else {
+      if (lane == 63) part[wave] = tot;
+      __syncthreads();
+      if (piece == 0 && lane == 63 && r < nrows) {
+        double v = part[wave];
+        for (int q = 1; q < SPLIT; ++q) v += part[wave + q];
+        a.ws.logits[(size_t)t * (a.E + 1) + r] = v;
+      }
+      __syncthreads();
+    }
   }
-  // shared expert gate/up
-  const int lir = lane % C::LPR, rig = lane / C::LPR;
-  Stage<H, kBlock> st;
-  st.load(src, threadIdx.x);
-  const int step0 = ((blockIdx.x - n_router_blocks) * kWaves + wave) * P;
-  gateup_block<BITS, H, P>(a, a.shared, st, scale, xs, step0, lir, rig, a.ws.h + ((size_t)t * a.NE + a.K) * a.I);
 }
 
-// Kernel 2: gate/up/SwiGLU of routed experts (blockIdx.y = slot; slot K = shared when included).
+// Kernel 2: gate/up/SwiGLU of the routed experts (blockIdx.y = slot) and, as slot K, of the shared
+// expert. The shared slot needs no routing, so its blocks stream weights while the routed blocks are
+// still picking their experts.
 template <int BITS, int H, int P, int PL>
 __global__ __launch_bounds__(kBlock) void k_gateup(LayerArgs a, const float* __restrict__ x,
                                                    const int32_t* __restrict__ idx_in, int32_t* __restrict__ idx_out) {
@@ -658,9 +667,6 @@ unsigned blocks_for(int64_t n, int bs) { return (unsigned)((n + bs - 1) / bs); }
 #define BQ_FOR_I(X) X(64) X(128) X(256) X(512) X(1024) X(2048)
 
 // Row steps per wave (the bytes each wave has in flight), tuned on MI355X for the 4096/1024 shape.
-#ifndef BQ_P1
-#define BQ_P1 2
-#endif
 #ifndef BQ_P2
 #define BQ_P2 1
 #endif
@@ -670,86 +676,87 @@ unsigned blocks_for(int64_t n, int bs) { return (unsigned)((n + bs - 1) / bs); }
 #ifndef BQ_ROUTER_STEPS
 #define BQ_ROUTER_STEPS 1
 #endif
-constexpr int kP1 = BQ_P1;  // shared gate/up in kernel 1
-constexpr int kP2 = BQ_P2;  // routed gate/up
+constexpr int kP2 = BQ_P2;  // gate/up
 constexpr int kP3 = BQ_P3;  // down
 
-template <int BITS, int H>
-hipError_t router_phase_impl(const LayerArgs& a, const float* x, const float* norm_src, float eps, int T,
-                             bool with_shared_ffn, hipStream_t s) {
-  using R = RouterCfg<H>;
-  using C = RowCfg<BITS, H>;
-  const int router_steps = BQ_ROUTER_STEPS;
-  const int nrows = a.E + a.has_shared;
-  const int rows_per_block = kWaves * router_steps * R::RPW;
-  const int nrb = (nrows + rows_per_block - 1) / rows_per_block;
-  int nsb = 0;
-  if (with_shared_ffn && a.has_shared) {
-    const int rows_per_sblock = kWaves * kP1 * C::RPW;
-    nsb = (a.I + rows_per_sblock - 1) / rows_per_sblock;
-  }
-  hipLaunchKernelGGL((k_router_phase<BITS, H, kP1>), dim3(nrb + nsb, T), dim3(kBlock), 0, s, a, x, norm_src, eps, nrb,
-                     router_steps);
+// A launch that, when events are given, has the dispatch itself record its start and end time
+// (the same timestamps a kernel-trace profiler reports), not separate event packets around it.
+template <typename F, typename... Args>
+hipError_t launch_timed(F kernel, dim3 grid, dim3 block, hipStream_t s, const KernelEvents& ev, Args... args) {
+  if (ev.start != nullptr || ev.stop != nullptr)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ev.start, ev.stop, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
   return hipGetLastError();
 }
 
 template <int BITS, int H>
+hipError_t router_phase_impl(const LayerArgs& a, const float* x, const float* norm_src, float eps, int T,
+                             hipStream_t s, const KernelEvents& ev) {
+  using R = RouterCfg<H>;
+  const int router_steps = BQ_ROUTER_STEPS;
+  const int nrows = a.E + a.has_shared;
+  constexpr int SPLIT = (R::CPL % BQ_ROUTER_SPLIT == 0) ? BQ_ROUTER_SPLIT : 1;
+  const int rows_per_block = kWaves / SPLIT * router_steps * R::RPW;
+  const int nrb = (nrows + rows_per_block - 1) / rows_per_block;
+  return launch_timed(k_router_phase<H>, dim3(nrb, T), dim3(kBlock), s, ev, a, x, norm_src, eps, router_steps);
+}
+
+template <int BITS, int H>
 hipError_t gateup_impl(const LayerArgs& a, const float* x, int T, const int32_t* idx_in, int32_t* idx_out,
-                       bool with_shared, hipStream_t s) {
+                       bool with_shared, hipStream_t s, const KernelEvents& ev) {
   using C = RowCfg<BITS, H>;
   const int rows_per_block = kWaves * kP2 * C::RPW;
   const int nb = (a.I + rows_per_block - 1) / rows_per_block;
   const int slots = a.K + ((with_shared && a.has_shared) ? 1 : 0);
   if (a.E <= 512)
-    hipLaunchKernelGGL((k_gateup<BITS, H, kP2, 8>), dim3(nb, slots, T), dim3(kBlock), 0, s, a, x, idx_in, idx_out);
-  else
-    hipLaunchKernelGGL((k_gateup<BITS, H, kP2, 16>), dim3(nb, slots, T), dim3(kBlock), 0, s, a, x, idx_in, idx_out);
-  return hipGetLastError();
+    return launch_timed(k_gateup<BITS, H, kP2, 8>, dim3(nb, slots, T), dim3(kBlock), s, ev, a, x, idx_in, idx_out);
+  return launch_timed(k_gateup<BITS, H, kP2, 16>, dim3(nb, slots, T), dim3(kBlock), s, ev, a, x, idx_in, idx_out);
 }
 
 template <int BITS, int I>
 hipError_t down_impl(const LayerArgs& a, int T, const int32_t* idx, const float* residual, float* out, float* y,
-                     hipStream_t s) {
+                     hipStream_t s, const KernelEvents& ev) {
   using C = RowCfg<BITS, I>;
   constexpr int RB = C::RPW * kP3;
   const int nb = (a.H + RB - 1) / RB;
-  hipLaunchKernelGGL((k_down<BITS, I, kP3>), dim3(nb, T), dim3(kBlock), 0, s, a, idx, residual, out, y);
-  return hipGetLastError();
+  return launch_timed(k_down<BITS, I, kP3>, dim3(nb, T), dim3(kBlock), s, ev, a, idx, residual, out, y);
 }
 
 }  // namespace
 
 hipError_t launch_router_phase(const Geometry& g, const LayerPtrs& p, const float* x, const float* norm_src, float eps,
-                               int T, const Workspace& ws, bool with_shared_ffn, hipStream_t s) {
+                               int T, const Workspace& ws, hipStream_t s, const KernelEvents& ev) {
   const LayerArgs a = make_args(g, p, ws);
-#define BQ_CASE(HV)                                                                                 \
-  case HV:                                                                                          \
-    return g.bits == 4 ? router_phase_impl<4, HV>(a, x, norm_src, eps, T, with_shared_ffn, s)       \
-                       : router_phase_impl<2, HV>(a, x, norm_src, eps, T, with_shared_ffn, s);
+#define BQ_CASE(HV)                                                                 \
+  case HV:                                                                          \
+    return g.bits == 4 ? router_phase_impl<4, HV>(a, x, norm_src, eps, T, s, ev)    \
+                       : router_phase_impl<2, HV>(a, x, norm_src, eps, T, s, ev);
   switch (g.H) { BQ_FOR_H(BQ_CASE) }
 #undef BQ_CASE
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_gateup(const Geometry& g, const LayerPtrs& p, const float* x, int T, const Workspace& ws,
-                         const int32_t* idx_in, int32_t* idx_out, bool with_shared, hipStream_t s) {
+                         const int32_t* idx_in, int32_t* idx_out, bool with_shared, hipStream_t s,
+                         const KernelEvents& ev) {
   const LayerArgs a = make_args(g, p, ws);
-#define BQ_CASE(HV)                                                                          \
-  case HV:                                                                                   \
-    return g.bits == 4 ? gateup_impl<4, HV>(a, x, T, idx_in, idx_out, with_shared, s)        \
-                       : gateup_impl<2, HV>(a, x, T, idx_in, idx_out, with_shared, s);
+#define BQ_CASE(HV)                                                                              \
+  case HV:                                                                                       \
+    return g.bits == 4 ? gateup_impl<4, HV>(a, x, T, idx_in, idx_out, with_shared, s, ev)        \
+                       : gateup_impl<2, HV>(a, x, T, idx_in, idx_out, with_shared, s, ev);
   switch (g.H) { BQ_FOR_H(BQ_CASE) }
 #undef BQ_CASE
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_down(const Geometry& g, const LayerPtrs& p, int T, const Workspace& ws, const int32_t* idx,
-                       const float* residual, float* out, float* y, hipStream_t s) {
+                       const float* residual, float* out, float* y, hipStream_t s, const KernelEvents& ev) {
   const LayerArgs a = make_args(g, p, ws);
-#define BQ_CASE(IV)                                                               \
-  case IV:                                                                        \
-    return g.bits == 4 ? down_impl<4, IV>(a, T, idx, residual, out, y, s)         \
-                       : down_impl<2, IV>(a, T, idx, residual, out, y, s);
+#define BQ_CASE(IV)                                                                   \
+  case IV:                                                                            \
+    return g.bits == 4 ? down_impl<4, IV>(a, T, idx, residual, out, y, s, ev)         \
+                       : down_impl<2, IV>(a, T, idx, residual, out, y, s, ev);
   switch (g.I) { BQ_FOR_I(BQ_CASE) }
 #undef BQ_CASE
   return hipErrorInvalidValue;

@@ -157,10 +157,13 @@ int moe_combine(const moe_layer_t* layer, const float* residual_dev, const float
 int moe_layer_forward(const moe_layer_t* layer, const float* x_dev, const float* residual_dev, int T, float* out_dev,
                       int32_t* idx_out_dev, void* ws_dev, size_t ws_bytes, void* stream);
 
-/* Instrumented moe_layer_forward, for timing kernels in place: the same kernels on `stream`, with
- * hipEventRecord(events[2p]) before and hipEventRecord(events[2p+1]) after phase p (decode path:
- * p = 0 router phase, 1 routed gate/up, 2 down + combine). events is a host array of 6 hipEvent_t
- * created by the caller. A NULL entry is skipped. Returns as moe_layer_forward. */
+/* Instrumented moe_layer_forward, for timing kernels in place: the same kernels on `stream`. In
+ * the decode path kernel p (0 router, 1 gate/up + SwiGLU of the routed and shared experts,
+ * 2 down + combine) is launched with events[2p] and events[2p+1] as its start and stop events
+ * (hipExtLaunchKernel). They then carry the dispatch's own begin and end timestamps, with no
+ * extra packets in between. In the prefill path, events[0] and events[5] are recorded
+ * (hipEventRecord) before and after all of its kernels. events is a host array of 6 hipEvent_t
+ * created by the caller, and a NULL entry is skipped. Returns as moe_layer_forward. */
 int moe_layer_forward_timed(const moe_layer_t* layer, const float* x_dev, const float* residual_dev, int T,
                             float* out_dev, int32_t* idx_out_dev, void* ws_dev, size_t ws_bytes, void* stream,
                             void* const* events);
