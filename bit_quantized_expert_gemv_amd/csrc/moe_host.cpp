@@ -129,8 +129,7 @@ PrefillWorkspace carve_prefill_impl(const Geometry& g, int T, void* base, size_t
   w.layer.g = c.take<float>(t);
   w.layer.h = nullptr;
   w.layer.u = nullptr;
-  w.xh = c.take<uint16_t>(t * g.H);
-  w.xl = c.take<uint16_t>(t * g.H);
+  w.xq = c.take<uint16_t>(t * g.H);
   w.xs = c.take<float>(t * (g.H / 64));
   w.hist = c.take<int32_t>(((N + 255) / 256) * g.E);
   w.counts = c.take<int32_t>(g.E);
@@ -140,8 +139,7 @@ PrefillWorkspace carve_prefill_impl(const Geometry& g, int T, void* base, size_t
   w.ntiles = c.take<int32_t>(1);
   w.pos = c.take<int32_t>(N);
   w.perm = c.take<int32_t>(N);
-  w.hh = c.take<uint16_t>(R * g.I);
-  w.hl = c.take<uint16_t>(R * g.I);
+  w.hq = c.take<uint16_t>(R * g.I);
   w.hs = c.take<float>(R * (g.I / 64));
   w.y = c.take<float>(R * g.H);
   *total = c.used;

@@ -40,9 +40,8 @@ struct Workspace {
 // Prefill (grouped) workspace for T tokens; N = T*K routed entries, R = N + T*has_shared rows.
 struct PrefillWorkspace {
   Workspace layer;  // logits [T][E+1], idx [T][K], w [T][K], g [T]; h and u unused
-  uint16_t* xh;     // [T][H] bf16 hi of the activations
-  uint16_t* xl;     // [T][H] bf16 lo
-  float* xs;        // [T][H/64] group sums of hi + lo
+  uint16_t* xq;     // [T][H] fp16 activations (each 8-block stored in the order 0,2,4,6,1,3,5,7)
+  float* xs;        // [T][H/64] group sums of the fp16 activations
   int32_t* hist;    // [ceil(N/256)][E]
   int32_t* counts;  // [E]
   int32_t* offsets; // [E+1]
@@ -51,9 +50,8 @@ struct PrefillWorkspace {
   int32_t* ntiles;  // [1]
   int32_t* pos;     // [N] entry -> position
   int32_t* perm;    // [N] position -> entry
-  uint16_t* hh;     // [R][I] SwiGLU outputs, bf16 hi
-  uint16_t* hl;     // [R][I] bf16 lo
-  float* hs;        // [R][I/64] group sums of hi + lo
+  uint16_t* hq;     // [R][I] SwiGLU outputs in fp16 (same 8-block order as xq)
+  float* hs;        // [R][I/64] group sums of the fp16 SwiGLU outputs
   float* y;         // [R][H] down outputs
 };
 

@@ -1,8 +1,8 @@
 // Prefill path of the quantised MoE layer for MI355X (gfx950): many tokens through one layer,
 // grouped by expert so that each expert's weights are streamed once per tile of tokens.
 //
-//   1. prep: every activation is split into bf16 hi + lo (x ~ hi + lo to ~2^-18 relative), and
-//      per-64-group sums of hi + lo are taken;
+//   1. prep: activations to fp16 (each 8-block stored in the order 0,2,4,6,1,3,5,7, the order in
+//      which the code widening below produces weights) and per-64-group sums of the fp16 values;
 //   2. router: logits = X . [R; gate]^T as an fp64 tiled GEMM, so the top-K decision is exact
 //      up to fp64 rounding; then the top-K and weights per token (the decode top-K kernel);
 //   3. grouping: per-expert counts, exclusive scan and a stable permutation by token index,
@@ -15,16 +15,22 @@
 // which experts are read. p4 "300b on 32gb MoE-streaming findings": even short prompts touch most
 // experts, which is why prefill streams the whole pool once.
 //
-// Exactness of the weights. A dequantised weight is s*q + b ("Kernel de dequantización optimizado
-// con FMA"), which needs up to 15 significant bits, so rounding weights to bf16 would lose
-// accuracy. The MFMA operands are instead the raw codes, which are exact in bf16 as 128 + q (the
-// bit pattern 0x4300 | q, made with byte permutes), times the hi and lo activation parts. Per
-// 64-wide group the fp32 result D = sum (128 + q) x is scaled in the epilogue:
-//   s * D + (b - 128 s) * S,   S = sum x   (hi + lo).
-// The 128 offset cancels exactly against the bias term.
+// Exact weights. A dequantised weight is s*q + b ("Kernel de dequantización optimizado con FMA").
+// It needs up to 15 significant bits, so rounding the weights to a 16-bit type would lose
+// accuracy. Instead the MFMA's weight operand is the raw code q itself, exact in fp16: a 4-bit code
+// in a byte is the e4m3 value q * 2^-9, and a 2-bit code in a nibble is the e2m1 value q / 2.
+// v_cvt_scalef32_pk_f16_fp8 / _fp4 widen them two at a time, with the scale folded in, to exactly q.
+// Per 64-wide group the fp32 MFMA result D = sum q x is finished in the epilogue as
+//   s * D + b * S,   S = sum x over the group (of the fp16 activations the MFMA sees).
+// The activations are rounded to fp16 once (relative 2^-11), which keeps the layer output well
+// inside its error bound.
 //
-// MFMA: v_mfma_f32_16x16x32_bf16. A[i][k] sits in lane i + 16*(k/8), element k%8; B[k][j] in lane
-// j + 16*(k/8), element k%8; D[i][j] in lane j + 16*(i/4), element i%4 (checked on the device).
+// MFMA: v_mfma_f32_32x32x16_f16 with A = activations (32 token rows) and B = codes (32 weight
+// rows). A[i][k] sits in lane i + 32*(k/8), element k%8; B[k][j] in lane j + 32*(k/8), element k%8;
+// D[i][j] in lane j + 32*((i/4)%2), element (i/8)*4 + i%4 (checked on the device). The sum over k is
+// order-free, so a lane's 16-byte code load (32 codes of one row, half a 4-bit group) supplies
+// MFMAs m = 0..3 with codes 8m..8m+7. Lanes 32..63 hold the other half of the same group, so every
+// MFMA stays inside one scale group, and the activation operand is read in the same k order.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -35,95 +41,93 @@
 namespace bqmoe {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
 
-__device__ __forceinline__ uint16_t bf16_rne_bits(float v) {
-  uint32_t b = __float_as_uint(v);
-  b += 0x7FFFu + ((b >> 16) & 1u);
-  return (uint16_t)(b >> 16);
-}
 __device__ __forceinline__ float bf16_val(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
-// Split v into bf16 hi + lo; returns hi + lo as float (what the MFMA sees).
-__device__ __forceinline__ float split_bf16(float v, uint16_t& hi, uint16_t& lo) {
-  hi = bf16_rne_bits(v);
-  const float r = v - bf16_val(hi);
-  lo = bf16_rne_bits(r);
-  return bf16_val(hi) + bf16_val(lo);
-}
+// Stored position of element e (0..7) of an 8-block: the order 0,2,4,6,1,3,5,7.
+__device__ __forceinline__ int perm8(int e) { return (e >> 1) + 4 * (e & 1); }
 
 // ---- 1. activation prep -------------------------------------------------------------------------
-// One block per token: hi/lo bf16 copies and per-64-group sums of hi + lo.
-__global__ __launch_bounds__(kThreads) void k_prep(int H, const float* __restrict__ x, uint16_t* __restrict__ xh,
-                                                   uint16_t* __restrict__ xl, float* __restrict__ xs) {
+// One block per token: fp16 copy (8-blocks permuted) and per-64-group sums of the fp16 values.
+__global__ __launch_bounds__(kThreads) void k_prep(int H, const float* __restrict__ x, _Float16* __restrict__ xq,
+                                                   float* __restrict__ xs) {
   const int t = blockIdx.x;
   const float* xr = x + (size_t)t * H;
-  // each wave takes whole groups: lane l of a group sums with its neighbours by shuffles
   const int ng = H / 64;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   for (int gi = wave; gi < ng; gi += kThreads / 64) {
     const int j = gi * 64 + lane;
-    uint16_t hi, lo;
-    float v = split_bf16(xr[j], hi, lo);
-    xh[(size_t)t * H + j] = hi;
-    xl[(size_t)t * H + j] = lo;
+    const _Float16 q = (_Float16)xr[j];
+    xq[(size_t)t * H + (j & ~7) + perm8(j & 7)] = q;
+    float v = (float)q;
     for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
     if (lane == 0) xs[(size_t)t * ng + gi] = v;
   }
 }
 
-// ---- 2. router GEMM (fp64) ------------------------------------------------------------------------
-// logits[t][e] = sum_j R[e][j] x[t][j] for e < E, and the shared-gate vector as row E.
-// Block tile 64 tokens x 64 rows, k step 32; each thread owns 4 x 4 outputs. Tiles sit in LDS as
-// fp64, transposed, so every read is a broadcast or a conflict-free 32-byte run.
-constexpr int kRT = 64, kRK = 32;
+// ---- 2. router GEMM (fp64 MFMA) ---------------------------------------------------------------------
+// logits[t][e] = sum_j R[e][j] x[t][j] for e < E, and the shared-gate vector as row E, on
+// v_mfma_f64_16x16x4_f64: every bf16 x fp32 product is exact in fp64 and the sums are fp64, so the
+// top-K decision is exact up to fp64 rounding. Lane layout (checked on the device): A[i][k] in lane
+// i + 16k, B[k][j] in lane j + 16k, D[i][j] in lane j + 16*(i%4), element i/4.
+// Block: 4 waves, 32 tokens x 32 rows; wave w owns the 16 x 16 output tile (w/2, w%2). Tiles this
+// small keep the fp64 MFMA pipes of all SIMDs evenly loaded. Operands are staged in LDS as fp64,
+// [k][token or row], rows padded to 48 doubles so that two 16-lane halves never share banks.
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
+constexpr int kRT = 32, kRK = 32, kRP = 48;
 __global__ __launch_bounds__(kThreads) void k_router_gemm(int T, int H, int E, int has_shared,
                                                           const float* __restrict__ x,
                                                           const uint16_t* __restrict__ router,
                                                           const uint16_t* __restrict__ sgate,
                                                           double* __restrict__ logits) {
-  __shared__ double xs[kRK][kRT];
-  __shared__ double rs[kRK][kRT];
+  __shared__ double xs[kRK][kRP];
+  __shared__ double rs[kRK][kRP];
   const int t0 = blockIdx.y * kRT, e0 = blockIdx.x * kRT;
   const int nrows = E + has_shared;
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-  double acc[4][4] = {};
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int c = lane & 15, kk = lane >> 4;
+  const int ti = wave >> 1, ej = wave & 1;
+  // staging: thread -> (row tid/8, k 4*(tid%8) .. +3) of the 32 x 32 tiles
+  const int sr = tid >> 3, sk = (tid & 7) * 4;
+  const float* xp = x + (size_t)min(t0 + sr, T - 1) * H + sk;
+  const int er = min(e0 + sr, nrows - 1);
+  const uint16_t* rp = ((er < E) ? router + (size_t)er * H : sgate) + sk;
+  float4 xv = *reinterpret_cast<const float4*>(xp);
+  uint2 rv = *reinterpret_cast<const uint2*>(rp);
+  f64x4_t acc = {0.0, 0.0, 0.0, 0.0};
   for (int k0 = 0; k0 < H; k0 += kRK) {
-    // cooperative loads: 64 x 32 of each (2048 elements, 8 per thread)
-    for (int i = threadIdx.x; i < kRT * kRK; i += kThreads) {
-      const int r = i / kRK, c = i % kRK;
-      const int t = min(t0 + r, T - 1);
-      xs[c][r] = (double)x[(size_t)t * H + k0 + c];
-      const int e = min(e0 + r, nrows - 1);
-      const uint16_t* row = (e < E) ? router + (size_t)e * H : sgate;
-      rs[c][r] = (double)bf16_val(row[k0 + c]);
-    }
+    xs[sk + 0][sr] = (double)xv.x; xs[sk + 1][sr] = (double)xv.y;
+    xs[sk + 2][sr] = (double)xv.z; xs[sk + 3][sr] = (double)xv.w;
+    rs[sk + 0][sr] = (double)bf16_val((uint16_t)(rv.x & 0xFFFFu));
+    rs[sk + 1][sr] = (double)bf16_val((uint16_t)(rv.x >> 16));
+    rs[sk + 2][sr] = (double)bf16_val((uint16_t)(rv.y & 0xFFFFu));
+    rs[sk + 3][sr] = (double)bf16_val((uint16_t)(rv.y >> 16));
     __syncthreads();
-#pragma unroll 8
-    for (int c = 0; c < kRK; ++c) {
-      double a[4], b[4];
+    if (k0 + kRK < H) {  // next tile in flight during the MFMAs
+      xv = *reinterpret_cast<const float4*>(xp + k0 + kRK);
+      rv = *reinterpret_cast<const uint2*>(rp + k0 + kRK);
+    }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) { a[i] = xs[c][ty * 4 + i]; b[i] = rs[c][tx * 4 + i]; }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
+    for (int s4 = 0; s4 < kRK / 4; ++s4) {
+      const double av = xs[4 * s4 + kk][ti * 16 + c];
+      const double bv = rs[4 * s4 + kk][ej * 16 + c];
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc, 0, 0, 0);
     }
     __syncthreads();
   }
+  const int e = e0 + ej * 16 + c;
+  if (e >= nrows) return;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = t0 + ty * 4 + i;
-    if (t >= T) continue;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = e0 + tx * 4 + j;
-      if (e < nrows) logits[(size_t)t * (E + 1) + e] = acc[i][j];
-    }
+  for (int q = 0; q < 4; ++q) {
+    const int t = t0 + ti * 16 + kk + 4 * q;
+    if (t < T) logits[(size_t)t * (E + 1) + e] = acc[q];
   }
 }
 
@@ -210,9 +214,8 @@ struct GroupArgs {
   uint64_t stride;
   const uint8_t* shared;
   uint64_t off_codes[2], off_sb[2];  // (gate, up) or (down, unused)
-  const uint16_t* ah;                // activations, bf16 hi [rows][KDIM]
-  const uint16_t* al;                // bf16 lo
-  const float* as;                   // group sums of hi + lo [rows][KDIM/64]
+  const _Float16* a;                 // activations [rows][KDIM], fp16, 8-blocks permuted
+  const float* as;                   // their group sums [rows][KDIM/64]
   const int32_t* perm;               // routed: position -> entry (t*K + k)
   int K;
   const int32_t* tile_e;
@@ -221,158 +224,271 @@ struct GroupArgs {
   const int32_t* offsets;
   int shared_base;  // output row of the shared expert's token 0 (= T*K)
   int T;
-  uint16_t* oh;  // gate/up: SwiGLU output hi/lo [rows][nout], group sums [rows][nout/64]
-  uint16_t* ol;
+  _Float16* oh;  // gate/up: SwiGLU outputs [rows][nout] (fp16, 8-blocks permuted), group sums os [rows][nout/64]
   float* os;
   float* oy;  // down: [rows][nout]
   int nout;
 };
 
-// 8 codes -> 8 bf16 values (128 + q) for one MFMA operand.
+constexpr int kTileM = 32;  // token rows per tile
+
+// One MFMA's B operand: 8 codes (one dword at 4-bit, one 16-bit half at 2-bit) widened to fp16 q,
+// in the element order 0,2,4,6,1,3,5,7.
 template <int BITS>
-__device__ __forceinline__ bf16x8_t codes_to_bf16(const uint8_t* __restrict__ p) {
-  u32x4_t d;
+__device__ __forceinline__ f16x8_t codes_f16(uint32_t w, int half) {
+  f16x2_t p0, p1, p2, p3;
   if constexpr (BITS == 4) {
-    const uint32_t w = *reinterpret_cast<const uint32_t*>(p);   // element e at bits 4e..4e+3
-    const uint32_t u = w & 0x0F0F0F0Fu;                          // bytes: elements 0, 2, 4, 6
-    const uint32_t v = (w >> 4) & 0x0F0F0F0Fu;                   // bytes: elements 1, 3, 5, 7
-    // dword j = [u.byte j, 0, v.byte j, 0] | 0x43004300 (v_perm_b32: selectors 0-3 pick u, 4-7 pick v, 12 = 0)
-    d[0] = __builtin_amdgcn_perm(v, u, 0x0C040C00u) | 0x43004300u;
-    d[1] = __builtin_amdgcn_perm(v, u, 0x0C050C01u) | 0x43004300u;
-    d[2] = __builtin_amdgcn_perm(v, u, 0x0C060C02u) | 0x43004300u;
-    d[3] = __builtin_amdgcn_perm(v, u, 0x0C070C03u) | 0x43004300u;
+    const uint32_t u = w & 0x0F0F0F0Fu;         // bytes: codes 0, 2, 4, 6
+    const uint32_t v = (w >> 4) & 0x0F0F0F0Fu;  // bytes: codes 1, 3, 5, 7
+    p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(u, 512.0f, false);
+    p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(u, 512.0f, true);
+    p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v, 512.0f, false);
+    p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v, 512.0f, true);
   } else {
-    const uint32_t w = *reinterpret_cast<const uint16_t*>(p);   // element e at bits 2e..2e+1
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t nib = (w >> (4 * j)) & 0xFu;
-      d[j] = 0x43004300u | (nib & 3u) | ((nib >> 2) << 16);
+    const uint32_t u = w & 0x33333333u;         // nibble n: code 2n
+    const uint32_t v = (w >> 2) & 0x33333333u;  // nibble n: code 2n + 1
+    if (half == 0) {
+      p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(u, 2.0f, 0);
+      p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(u, 2.0f, 1);
+      p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 2.0f, 0);
+      p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 2.0f, 1);
+    } else {
+      p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(u, 2.0f, 2);
+      p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(u, 2.0f, 3);
+      p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 2.0f, 2);
+      p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 2.0f, 3);
     }
   }
-  return __builtin_bit_cast(bf16x8_t, d);
+  return f16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
-__device__ __forceinline__ bf16x8_t load_bf16x8(const uint16_t* __restrict__ p) {
-  return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(p));
-}
+// Per-lane registers of U groups of weights: codes and (scale, bias) words.
+template <int BITS, int NTILE, int U>
+struct GStage {
+  static constexpr int CW = BITS == 4 ? 4 : 2;  // code dwords per lane per group
+  uint32_t c[U][NTILE][CW];
+  uint32_t sb[U][NTILE];
+};
 
-// Block: 4 waves x 16 weight rows (per matrix) = 64 rows, BM = 16*MT token rows.
-template <int BITS, int KDIM, int MT, bool GATEUP, bool SHARED>
+// Block: 4 waves. Wave w owns NT 32-row tiles of each of its NM matrices (NM = 2 for gate/up);
+// a block covers 4*NT*32 rows of each matrix for one tile of up to 32 token rows. The tile and
+// the row slab come from blockIdx.x so that all slabs of a tile run on one XCD (blocks are dealt
+// to the 8 XCDs round robin), where they share the tile's activations in L2.
+//
+// Pipeline, per step of U groups: the block's activations for the next step are loaded (16 bytes
+// per thread and group), then each wave's weights for the next step; then this step is computed
+// from registers (weights) and an LDS ring (activations); the next step's activations are parked
+// in the ring and one barrier closes the step. Loads retire in order, so the activations are
+// requested before the weights: waiting for them never waits for the weights in flight.
+template <int BITS, int KDIM, int NT, int UMAX, bool GATEUP, bool SHARED>
 __global__ __launch_bounds__(kThreads) void k_grouped(GroupArgs g) {
-  constexpr int BM = 16 * MT;
   constexpr int NM = GATEUP ? 2 : 1;
+  constexpr int NTILE = NM * NT;
   constexpr int NG = KDIM / 64;
+  constexpr int U = NG >= UMAX ? UMAX : NG;  // groups per pipeline step
+  constexpr int NSTEP = NG / U;
   constexpr int ROWB = KDIM * BITS / 8;
-  __shared__ float ssum[4][BM];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int lm = lane & 15, lq = lane >> 4;
+  constexpr int GB = 64 * BITS / 8;  // code bytes per row and group
+  constexpr int LB = GB / 2;         // per lane half
+  constexpr int ROWS_W = NT * 32;
+  constexpr int ROWS_B = 4 * ROWS_W;
+  constexpr int AS = U * 8;          // 16-byte activation slots per row and step
+  constexpr int ASW = AS >= 16 ? 15 : AS - 1;  // slot swizzle: 16 consecutive rows hit distinct banks
+  using Stage = GStage<BITS, NTILE, U>;
+  static_assert(!GATEUP || 64 % ROWS_W == 0, "a 64-row group of the SwiGLU output spans whole waves");
+  __shared__ float s_lds[NG * kTileM];                  // group sums of the tile's activations, [group][row]
+  __shared__ float h_lds[GATEUP ? 4 : 1][kTileM];        // gate/up: per-wave sums of the fp16 SwiGLU outputs
+  __shared__ u32x4_t a_lds[2][kTileM * AS];             // activation ring: [step parity][row][slot ^ swizzle]
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int j = lane & 31, hk = lane >> 5;
+  const int nslab = (g.nout + ROWS_B - 1) / ROWS_B;
+  const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
+  const int tau = xcd + 8 * (q / nslab), slab = q % nslab;
   int first, count;
   const uint8_t* blob;
   if constexpr (SHARED) {
-    first = blockIdx.y * BM;
-    count = min(BM, g.T - first);
+    first = tau * kTileM;
+    if (first >= g.T) return;  // uniform per block
+    count = min(kTileM, g.T - first);
     blob = g.shared;
   } else {
-    const int tau = blockIdx.y;
     if (tau >= *g.ntiles) return;  // uniform per block
     const int e = g.tile_e[tau];
     first = g.tile_first[tau];
-    count = min(BM, g.offsets[e + 1] - first);
+    count = min(kTileM, g.offsets[e + 1] - first);
     blob = g.experts + (size_t)e * g.stride;
   }
-  // activation row of token slot m (clamped into the tile)
+  // activation row of token slot m (clamped into the tile) and output row
   auto arow = [&](int m) -> int {
     const int mm = first + min(m, count - 1);
     if constexpr (SHARED) return GATEUP ? mm : g.shared_base + mm;
     else return GATEUP ? g.perm[mm] / g.K : mm;
   };
-  auto orow = [&](int m) -> int {
-    const int mm = first + m;
-    if constexpr (SHARED) return g.shared_base + mm;
-    else return mm;
+  auto orow = [&](int m) -> int { return SHARED ? g.shared_base + first + m : first + m; };
+
+  for (int i = tid; i < NG * kTileM; i += kThreads) {
+    const int m = i % kTileM, gi = i / kTileM;
+    s_lds[i] = g.as[(size_t)arow(m) * NG + gi];
+  }
+  // this thread's 16-byte activation slot: row tid/8, slot tid%8 of every group
+  const int a_row = tid >> 3, a_slot = tid & 7;
+  const u32x4_t* a_src = reinterpret_cast<const u32x4_t*>(g.a + (size_t)arow(a_row) * KDIM) + a_slot;
+  u32x4_t a_reg[U];
+  auto load_act = [&](int step) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) a_reg[u] = a_src[(step * U + u) * 8];
   };
-  int ar[MT], sr[MT][4];
+  auto park_act = [&](int /*loaded step*/, int slot_step) {
 #pragma unroll
-  for (int st = 0; st < MT; ++st) {
-    ar[st] = arow(st * 16 + lm);
+    for (int u = 0; u < U; ++u) a_lds[slot_step & 1][a_row * AS + ((u * 8 + a_slot) ^ (a_row & ASW))] = a_reg[u];
+  };
+
+  const int r0w = slab * ROWS_B + wave * ROWS_W;  // first row (per matrix) of this wave
+  const bool active = r0w < g.nout;               // wave-uniform; idle waves still join the barriers
+  const uint8_t* cp[NTILE];
+  const uint32_t* sp[NTILE];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sr[st][e] = arow(st * 16 + 4 * lq + e);
+  for (int t = 0; t < NTILE; ++t) {
+    const int mi = t / NT, nt = t % NT;
+    const int row = min(r0w + nt * 32 + j, g.nout - 1);
+    cp[t] = blob + g.off_codes[mi] + (size_t)row * ROWB + hk * LB;
+    sp[t] = reinterpret_cast<const uint32_t*>(blob + g.off_sb[mi]) + (size_t)row * NG;
   }
-  const int n = blockIdx.x * 64 + wave * 16 + lm;  // weight row of this lane's B column (and D column)
-  f32x4_t acc[MT][NM];
+  // unconditional (idle waves read a clamped row): a load skipped on some path would make the
+  // compiler's wait counts conservative and drain the prefetch at every barrier
+  auto load_w = [&](Stage& st, int step) {
 #pragma unroll
-  for (int st = 0; st < MT; ++st)
+    for (int u = 0; u < U; ++u) {
+      const int gi = step * U + u;
 #pragma unroll
-    for (int mi = 0; mi < NM; ++mi) acc[st][mi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 1
-  for (int gi = 0; gi < NG; ++gi) {
-    bf16x8_t bq[NM][2];
-    float sc[NM], bb[NM];
-#pragma unroll
-    for (int mi = 0; mi < NM; ++mi) {
-      const uint8_t* row = blob + g.off_codes[mi] + (size_t)n * ROWB;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) bq[mi][h] = codes_to_bf16<BITS>(row + ((gi * 64 + 32 * h + 8 * lq) * BITS) / 8);
-      const uint32_t p = *reinterpret_cast<const uint32_t*>(blob + g.off_sb[mi] + ((size_t)n * NG + gi) * 4);
-      sc[mi] = __uint_as_float(p << 16);
-      bb[mi] = __uint_as_float(p & 0xFFFF0000u) - 128.0f * sc[mi];
-    }
-#pragma unroll
-    for (int st = 0; st < MT; ++st) {
-      const uint16_t* ph = g.ah + (size_t)ar[st] * KDIM + gi * 64 + 8 * lq;
-      const uint16_t* pl = g.al + (size_t)ar[st] * KDIM + gi * 64 + 8 * lq;
-      const bf16x8_t xh0 = load_bf16x8(ph), xh1 = load_bf16x8(ph + 32);
-      const bf16x8_t xl0 = load_bf16x8(pl), xl1 = load_bf16x8(pl + 32);
-      float S[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) S[e] = g.as[(size_t)sr[st][e] * NG + gi];
-#pragma unroll
-      for (int mi = 0; mi < NM; ++mi) {
-        f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh0, bq[mi][0], zero, 0, 0, 0);
-        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xl0, bq[mi][0], d, 0, 0, 0);
-        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh1, bq[mi][1], d, 0, 0, 0);
-        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xl1, bq[mi][1], d, 0, 0, 0);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[st][mi][e] = fmaf(sc[mi], d[e], fmaf(bb[mi], S[e], acc[st][mi][e]));
-      }
-    }
-  }
-  if constexpr (GATEUP) {
-    // SwiGLU, split to bf16 hi/lo for the down GEMM, and per-row sums over this block's 64 columns
-    // (one input group of the down projection).
-#pragma unroll
-    for (int st = 0; st < MT; ++st) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int m = st * 16 + 4 * lq + e;
-        const float a = acc[st][0][e], c = acc[st][1][e];
-        const float hv = a / (1.0f + expf(-a)) * c;
-        uint16_t hi, lo;
-        float seen = split_bf16(hv, hi, lo);
-        if (m < count) {
-          const size_t o = (size_t)orow(m) * g.nout + n;
-          g.oh[o] = hi;
-          g.ol[o] = lo;
+      for (int t = 0; t < NTILE; ++t) {
+        if constexpr (BITS == 4) {
+          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(cp[t] + gi * GB);
+          st.c[u][t][0] = v[0]; st.c[u][t][1] = v[1]; st.c[u][t][2] = v[2]; st.c[u][t][3] = v[3];
         } else {
-          seen = 0.0f;
+          const u32x2_t v = *reinterpret_cast<const u32x2_t*>(cp[t] + gi * GB);
+          st.c[u][t][0] = v[0]; st.c[u][t][1] = v[1];
         }
-        // sum over the 16 columns of this wave: lanes 16*lq .. 16*lq+15 (one DPP row)
-        for (int msk = 8; msk >= 1; msk >>= 1) seen += __shfl_xor(seen, msk, 16);
-        if (lm == 0) ssum[wave][m] = seen;
+        st.sb[u][t] = sp[t][gi];
       }
+    }
+  };
+
+  f32x16_t acc[NTILE];
+#pragma unroll
+  for (int t = 0; t < NTILE; ++t)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[t][v] = 0.0f;
+
+  auto compute = [&](const Stage& st, int step) {
+    if (!active) return;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int gi = step * U + u;
+      // group sums of this lane's 16 token rows: rows 8a + 4*hk + b for element 4a + b
+      float S[16];
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const float4 v = *reinterpret_cast<const float4*>(&s_lds[gi * kTileM + 8 * a4 + 4 * hk]);
+        S[4 * a4 + 0] = v.x; S[4 * a4 + 1] = v.y; S[4 * a4 + 2] = v.z; S[4 * a4 + 3] = v.w;
+      }
+      f16x8_t af[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        af[m] = __builtin_bit_cast(f16x8_t, a_lds[step & 1][j * AS + ((u * 8 + 4 * hk + m) ^ (j & ASW))]);
+#pragma unroll
+      for (int t = 0; t < NTILE; ++t) {
+        f32x16_t d;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) d[v] = 0.0f;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const uint32_t w = BITS == 4 ? st.c[u][t][m] : st.c[u][t][m >> 1];
+          d = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[m], codes_f16<BITS>(w, m & 1), d, 0, 0, 0);
+        }
+        const uint32_t p = st.sb[u][t];
+        const float sc = bf16_val((uint16_t)(p & 0xFFFFu)), bi = bf16_val((uint16_t)(p >> 16));
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[t][v] = fmaf(sc, d[v], fmaf(bi, S[v], acc[t][v]));
+      }
+    }
+  };
+
+  // Two weight stages in ping-pong: one is in flight while the other is computed. Every load is
+  // issued on every path (past the end it re-reads the last step, from cache), so that the
+  // compiler's wait counts stay exact and never drain the loads in flight. (A third stage costs
+  // the second wave per SIMD and measured slower.)
+  Stage s0, s1;
+  load_act(0);
+  load_w(s0, 0);
+  park_act(0, 0);
+  __syncthreads();
+#pragma unroll 1
+  for (int step = 0; step < NSTEP; step += 2) {
+    const int n1 = min(step + 1, NSTEP - 1), n2 = min(step + 2, NSTEP - 1);
+    load_act(n1);
+    load_w(s1, n1);
+    compute(s0, step);
+    park_act(n1, step + 1);
+    __syncthreads();
+    load_act(n2);
+    load_w(s0, n2);
+    if (step + 1 < NSTEP) compute(s1, step + 1);
+    park_act(n2, step + 2);
+    __syncthreads();
+  }
+
+  // element v of a tile holds token row 8*(v/4) + 4*hk + v%4 and weight row r0w + 32*nt + j
+  if constexpr (GATEUP) {
+    float part[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int m = 8 * (v >> 2) + 4 * hk + (v & 3);
+      float sum = 0.0f;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const float a = acc[nt][v], c = acc[NT + nt][v];
+        const _Float16 h = (_Float16)(a / (1.0f + expf(-a)) * c);
+        sum += (float)h;
+        const int col = r0w + 32 * nt + j;
+        if (active && m < count) g.oh[(size_t)orow(m) * g.nout + (col & ~7) + perm8(col & 7)] = h;
+      }
+      part[v] = active ? sum : 0.0f;
+    }
+    // sum over the 32 lanes of each half, then over the waves that share a 64-column group (the
+    // group sums of the down projection's input)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+#pragma unroll
+      for (int msk = 16; msk >= 1; msk >>= 1) part[v] += __shfl_xor(part[v], msk, 32);
+    }
+    if (j == 0) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) h_lds[wave][8 * (v >> 2) + 4 * hk + (v & 3)] = part[v];
     }
     __syncthreads();
-    for (int m = threadIdx.x; m < count; m += kThreads)
-      g.os[(size_t)orow(m) * (g.nout / 64) + blockIdx.x] = (ssum[0][m] + ssum[1][m]) + (ssum[2][m] + ssum[3][m]);
+    constexpr int WPG = 64 / ROWS_W;  // waves per group
+    for (int i = tid; i < (4 / WPG) * kTileM; i += kThreads) {
+      const int m = i % kTileM, gl = i / kTileM;
+      const int col0 = slab * ROWS_B + gl * 64;
+      if (m >= count || col0 >= g.nout) continue;
+      float v = 0.0f;
+      for (int w = 0; w < WPG; ++w) v += h_lds[gl * WPG + w][m];
+      g.os[(size_t)orow(m) * (g.nout / 64) + col0 / 64] = v;
+    }
   } else {
+    if (!active) return;
 #pragma unroll
-    for (int st = 0; st < MT; ++st)
+    for (int nt = 0; nt < NT; ++nt) {
+      const int col = r0w + 32 * nt + j;
+      if (col >= g.nout) continue;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int m = st * 16 + 4 * lq + e;
-        if (m < count) g.oy[(size_t)orow(m) * g.nout + n] = acc[st][0][e];
+      for (int v = 0; v < 16; ++v) {
+        const int m = 8 * (v >> 2) + 4 * hk + (v & 3);
+        if (m < count) g.oy[(size_t)orow(m) * g.nout + col] = acc[nt][v];
       }
+    }
   }
 }
 
@@ -405,20 +521,41 @@ __global__ void k_copy_i32(int n, const int32_t* __restrict__ src, int32_t* __re
   if (i < n) dst[i] = src[i];
 }
 
-constexpr int kMTRouted = 2;  // 32 tokens per routed tile (an expert sees about 12 on average)
-constexpr int kMTShared = 4;  // 64 tokens per shared-expert tile
-
 unsigned cdiv(long long a, long long b) { return (unsigned)((a + b - 1) / b); }
+
+#ifndef BQ_NT_GU
+#define BQ_NT_GU 1
+#endif
+#ifndef BQ_NT_DOWN
+#define BQ_NT_DOWN 1
+#endif
+#ifndef BQ_U_LINE
+#define BQ_U_LINE 1
+#endif
+// 32-row tiles per matrix per wave, and groups per pipeline step: by default a step takes one
+// 128-byte line of every row (4 groups at 4-bit, 8 at 2-bit), so that no line is fetched twice.
+constexpr int kNTGateUp = BQ_NT_GU;
+constexpr int kNTDown = BQ_NT_DOWN;
+template <int BITS>
+constexpr int kULine = BQ_U_LINE * (BITS == 4 ? 4 : 8);
+
+// Blocks for `tiles` tiles of `nout` rows: slabs of 4*NT*32 rows, tiles padded to a multiple of 8.
+unsigned grouped_blocks(int tiles, int nout, int nt) {
+  const int nslab = (int)cdiv(nout, 4 * nt * 32);
+  return (unsigned)(8 * nslab) * cdiv(tiles, 8);
+}
 
 template <int BITS, int KDIM, bool GATEUP>
 hipError_t launch_grouped(const GroupArgs& ga, int nout, int T, int N, int E, bool has_shared, hipStream_t s) {
+  constexpr int NT = GATEUP ? kNTGateUp : kNTDown;
+  constexpr int UM = kULine<BITS>;
   const dim3 block(kThreads);
-  const unsigned nx = (unsigned)(nout / 64);
-  const int max_tiles = E + (int)cdiv(N, 16 * kMTRouted);
-  hipLaunchKernelGGL((k_grouped<BITS, KDIM, kMTRouted, GATEUP, false>), dim3(nx, max_tiles), block, 0, s, ga);
+  const int max_tiles = E + (int)cdiv(N, kTileM);
+  hipLaunchKernelGGL((k_grouped<BITS, KDIM, NT, UM, GATEUP, false>), dim3(grouped_blocks(max_tiles, nout, NT)), block,
+                     0, s, ga);
   if (has_shared)
-    hipLaunchKernelGGL((k_grouped<BITS, KDIM, kMTShared, GATEUP, true>), dim3(nx, cdiv(T, 16 * kMTShared)), block, 0,
-                       s, ga);
+    hipLaunchKernelGGL((k_grouped<BITS, KDIM, NT, UM, GATEUP, true>),
+                       dim3(grouped_blocks((int)cdiv(T, kTileM), nout, NT)), block, 0, s, ga);
   return hipGetLastError();
 }
 
@@ -460,7 +597,7 @@ hipError_t launch_prefill(const Geometry& g, const LayerPtrs& p, const float* x,
   const int H = g.H, I = g.I, E = g.E, K = g.K;
   const int N = T * K;
   const int nchunks = (int)cdiv(N, kChunk);
-  hipLaunchKernelGGL(k_prep, dim3(T), dim3(kThreads), 0, s, H, x, w.xh, w.xl, w.xs);
+  hipLaunchKernelGGL(k_prep, dim3(T), dim3(kThreads), 0, s, H, x, reinterpret_cast<_Float16*>(w.xq), w.xs);
   const int32_t* idx = idx_in;
   if (idx_in == nullptr) {
     hipError_t e = launch_router_gemm(g, p, x, T, w.layer, s);
@@ -469,7 +606,7 @@ hipError_t launch_prefill(const Geometry& g, const LayerPtrs& p, const float* x,
     idx = w.layer.idx;
   }
   hipLaunchKernelGGL(k_group_hist, dim3(nchunks), dim3(kChunk), E * sizeof(int32_t), s, N, E, idx, w.hist);
-  hipLaunchKernelGGL(k_group_scan, dim3(1), dim3(1024), 0, s, nchunks, E, 16 * kMTRouted, w.hist, w.counts,
+  hipLaunchKernelGGL(k_group_scan, dim3(1), dim3(1024), 0, s, nchunks, E, kTileM, w.hist, w.counts,
                      w.offsets, w.tile_e, w.tile_first, w.ntiles);
   hipLaunchKernelGGL(k_group_place, dim3(nchunks), dim3(kChunk), 0, s, N, E, idx, w.hist, w.offsets, w.pos, w.perm);
   GroupArgs ga{};
@@ -479,13 +616,13 @@ hipError_t launch_prefill(const Geometry& g, const LayerPtrs& p, const float* x,
   // gate/up + SwiGLU
   ga.off_codes[0] = g.off_codes[0]; ga.off_codes[1] = g.off_codes[1];
   ga.off_sb[0] = g.off_sb[0]; ga.off_sb[1] = g.off_sb[1];
-  ga.ah = w.xh; ga.al = w.xl; ga.as = w.xs;
-  ga.oh = w.hh; ga.ol = w.hl; ga.os = w.hs; ga.nout = I;
+  ga.a = reinterpret_cast<const _Float16*>(w.xq); ga.as = w.xs;
+  ga.oh = reinterpret_cast<_Float16*>(w.hq); ga.os = w.hs; ga.nout = I;
   hipError_t e = dispatch_gateup(g.bits, H, ga, I, T, N, E, g.has_shared != 0, s);
   if (e != hipSuccess) return e;
   // down
   ga.off_codes[0] = g.off_codes[2]; ga.off_sb[0] = g.off_sb[2];
-  ga.ah = w.hh; ga.al = w.hl; ga.as = w.hs;
+  ga.a = reinterpret_cast<const _Float16*>(w.hq); ga.as = w.hs;
   ga.oy = w.y; ga.nout = H;
   e = dispatch_down(g.bits, I, ga, H, T, N, E, g.has_shared != 0, s);
   if (e != hipSuccess) return e;

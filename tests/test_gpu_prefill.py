@@ -141,3 +141,28 @@ def test_prefill_2bit(gpu_device):
         r = ref.token(xs[t])
         assert list(idx[t]) == list(r.idx)
         assert_close(out[t], r.out, f"2-bit prefill out[{t}]")
+
+
+def test_prefill_duplicate_router_rows_tie_to_lower_index(gpu_device):
+    """Equal router rows give bitwise-equal fp64 logits in the router GEMM, and the top-K keeps the
+    lower expert index, as the oracle's sort does, for every token of a prefill batch."""
+    L = DeviceLayer(TINY)
+    ref = Reference(TINY)
+    T = 64
+    x = torch.from_numpy(synth.tokens_x(TINY, 11, T)).cuda()
+    xs = x.cpu().numpy().astype(np.float64)
+    best = int(np.argmax(oracle.router_logits(ref.router, xs[0])))
+    R = ref.router.copy()
+    for r in (2, 5):
+        R[r] = R[best]
+    ref.router = R
+    L.router.copy_(torch.from_numpy(R.view(np.int16)))
+    out, idx = _forward(L, x)
+    tied_tokens = 0
+    for t in range(T):
+        want = oracle.topk(oracle.router_logits(R, xs[t]), TINY.top_k)
+        assert list(idx[t]) == list(want), f"token {t}"
+        tied_tokens += len({best, 2, 5} & set(want)) >= 2
+    assert tied_tokens >= 1  # the tie decides at least token 0's choice
+    for t in (0, 31, 63):
+        assert_close(out[t], ref.token(xs[t]).out, f"out[{t}]")
