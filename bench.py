@@ -71,6 +71,24 @@ def load_traffic(kernel_label):
     return d.get("per_launch_bytes", {}).get(kernel_label)
 
 
+def stream_read_gbs(torch, gib=4, reps=5):
+    """Measured streaming-read rate of this GPU: a plain reduction (torch.sum) over a `gib` GiB
+    fp32 buffer, best of `reps` runs. The reachable read bandwidth, next to the 8 TB/s spec peak."""
+    buf = torch.ones((gib << 30) // 4, dtype=torch.float32, device="cuda:0")
+    torch.cuda.synchronize()
+    best = float("inf")
+    for _ in range(reps + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        buf.sum()
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1) / 1000.0)
+    del buf
+    torch.cuda.empty_cache()
+    return (gib << 30) / best / 1e9
+
+
 def cpu_baseline(w, budget_s):
     """The oracle as it stands, on the host cores, over the first tokens until ~budget_s of oracle time."""
     import numpy as np
@@ -233,6 +251,8 @@ def main():
         del gc
 
     us_tok = secs * 1e6 / (args.steps * N)
+    read_peak = stream_read_gbs(torch)
+    print(f"[bench] measured streaming read: {read_peak:,.0f} GB/s", file=sys.stderr, flush=True)
     result = {
         "metric": "MoE-layer decode tokens/s + achieved HBM GB/s on expert weights (frac of peak)",
         "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -247,6 +267,8 @@ def main():
         "expert_GB/s": round(expert_bytes / (us_tok * 1e-6) / 1e9, 1),
         "expert_frac_of_peak": round(expert_bytes / (us_tok * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
         "roofline": roofline,
+        "stream_read_GB/s": round(read_peak, 1),
+        "expert_frac_of_measured_read": round(expert_bytes / (us_tok * 1e-6) / 1e9 / read_peak, 4),
         "cold": cold,
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_budget),
     }
@@ -301,12 +323,14 @@ def bench_prefill(args, w):
     weight_bytes = touched * blob + blob + w.n_experts * w.hidden * 2 + w.hidden * 2
     flops = 2.0 * (T * w.top_k + T) * 3 * w.hidden * w.inter + 2.0 * T * (w.n_experts + 1) * w.hidden
     gbs = weight_bytes / per / 1e9
+    read_peak = stream_read_gbs(torch)
     _common(args, w, T / per, "tokens/s", per * 1000.0,
             {"workload": f"{w.name}: {T}-token prefill through one MoE layer (hidden {w.hidden}, {w.n_experts} experts, "
                          f"inter {w.inter}, top-{w.top_k} + shared, {w.bits}-bit), grouped by expert on MFMA",
              "tokens_per_step": T, "parallelism": "single GPU"},
             {"weight_bytes_per_step": weight_bytes, "weight_GB/s": round(gbs, 1),
-             "hbm_frac_of_peak": round(gbs / HBM_PEAK_GBS, 4), "useful_TFLOP/s": round(flops / per / 1e12, 2),
+             "hbm_frac_of_peak": round(gbs / HBM_PEAK_GBS, 4), "stream_read_GB/s": round(read_peak, 1),
+             "frac_of_measured_read": round(gbs / read_peak, 4), "useful_TFLOP/s": round(flops / per / 1e12, 2),
              "tokens_per_expert": {"min": int(counts.min()), "mean": round(float(counts.mean()), 2),
                                    "max": int(counts.max()), "untouched": int((counts == 0).sum()),
                                    "histogram": np.bincount(counts).tolist()}})

@@ -33,6 +33,7 @@
 // MFMA stays inside one scale group, and the activation operand is read in the same k order.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -231,6 +232,8 @@ struct GroupArgs {
 };
 
 constexpr int kTileM = 32;  // token rows per tile
+// Word 3 of a raw buffer descriptor on gfx9 (32-bit data format, no swizzle).
+constexpr int kRsrcWord3 = 0x00020000;
 
 // One MFMA's B operand: 8 codes (one dword at 4-bit, one 16-bit half at 2-bit) widened to fp16 q,
 // in the element order 0,2,4,6,1,3,5,7.
@@ -270,41 +273,61 @@ struct GStage {
   uint32_t sb[U][NTILE];
 };
 
-// Block: 4 waves. Wave w owns NT 32-row tiles of each of its NM matrices (NM = 2 for gate/up);
-// a block covers 4*NT*32 rows of each matrix for one tile of up to 32 token rows. The tile and
-// the row slab come from blockIdx.x so that all slabs of a tile run on one XCD (blocks are dealt
-// to the 8 XCDs round robin), where they share the tile's activations in L2.
+#ifndef BQ_LB_GU
+#define BQ_LB_GU 3
+#endif
+#ifndef BQ_LB_DOWN
+#define BQ_LB_DOWN 3
+#endif
+#ifndef BQ_GROUP_SCHED_BARRIER
+#define BQ_GROUP_SCHED_BARRIER 1
+#endif
+#ifndef BQ_U_LINE
+#define BQ_U_LINE 1
+#endif
+#ifndef BQ_ST_GU
+#define BQ_ST_GU 2
+#endif
+#ifndef BQ_ST_DOWN
+#define BQ_ST_DOWN 2
+#endif
+// Groups per pipeline step (by default one 128-byte line of every row: 4 groups at 4-bit, 8 at
+// 2-bit, so that no line is fetched twice) and weight stages in flight + 1.
+// Block: 4 waves, one tile of up to 32 token rows, all rows of the weight matrices. Each wave owns
+// one 32-row tile of one matrix in every slab: for down, waves 0..3 take rows 32w..32w+31 of a
+// 128-row slab; for gate/up, waves 0, 1 take 32-row tiles of gate and waves 2, 3 the same rows of
+// up, in a 64-row slab, and the SwiGLU pairs meet through LDS at the end of the slab. One tile
+// per wave keeps a wave's registers low enough for three waves per SIMD. The block walks the
+// slabs one after the other, and the pipeline runs over the flattened (slab, step) sequence, so
+// it fills once per block rather than once per slab; there are about as many blocks as tiles.
 //
-// Pipeline, per step of U groups: the block's activations for the next step are loaded (16 bytes
-// per thread and group), then each wave's weights for the next step; then this step is computed
-// from registers (weights) and an LDS ring (activations); the next step's activations are parked
-// in the ring and one barrier closes the step. Loads retire in order, so the activations are
+// Pipeline, per step of U groups: the tile's activations for the next step are loaded (16 bytes
+// per thread and group), then each wave's weights for the step STAGES-1 ahead; this step is
+// computed from registers (weights) and an LDS ring (activations); the next step's activations are
+// parked in the ring and one barrier closes the step. Loads retire in order, so the activations are
 // requested before the weights: waiting for them never waits for the weights in flight.
-template <int BITS, int KDIM, int NT, int UMAX, bool GATEUP, bool SHARED>
-__global__ __launch_bounds__(kThreads) void k_grouped(GroupArgs g) {
-  constexpr int NM = GATEUP ? 2 : 1;
-  constexpr int NTILE = NM * NT;
+template <int BITS, int KDIM, int UMAX, int STAGES, bool GATEUP, bool SHARED>
+__global__ __launch_bounds__(kThreads, GATEUP ? BQ_LB_GU : BQ_LB_DOWN) void k_grouped(GroupArgs g) {
   constexpr int NG = KDIM / 64;
   constexpr int U = NG >= UMAX ? UMAX : NG;  // groups per pipeline step
-  constexpr int NSTEP = NG / U;
+  constexpr int NSTEP = NG / U;               // steps per slab
   constexpr int ROWB = KDIM * BITS / 8;
   constexpr int GB = 64 * BITS / 8;  // code bytes per row and group
   constexpr int LB = GB / 2;         // per lane half
-  constexpr int ROWS_W = NT * 32;
-  constexpr int ROWS_B = 4 * ROWS_W;
+  constexpr int ROWS_B = GATEUP ? 64 : 128;  // rows per matrix per slab
   constexpr int AS = U * 8;          // 16-byte activation slots per row and step
   constexpr int ASW = AS >= 16 ? 15 : AS - 1;  // slot swizzle: 16 consecutive rows hit distinct banks
-  using Stage = GStage<BITS, NTILE, U>;
-  static_assert(!GATEUP || 64 % ROWS_W == 0, "a 64-row group of the SwiGLU output spans whole waves");
-  __shared__ float s_lds[NG * kTileM];                  // group sums of the tile's activations, [group][row]
-  __shared__ float h_lds[GATEUP ? 4 : 1][kTileM];        // gate/up: per-wave sums of the fp16 SwiGLU outputs
-  __shared__ u32x4_t a_lds[2][kTileM * AS];             // activation ring: [step parity][row][slot ^ swizzle]
+  using Stage = GStage<BITS, 1, U>;
+  __shared__ float s_lds[NG * kTileM];             // group sums of the tile's activations, [group][row]
+  __shared__ u32x4_t a_lds[2][kTileM * AS];        // activation ring: [step parity][row][slot ^ swizzle]
+  __shared__ float x_lds[GATEUP ? 2 : 1][16][64];  // gate/up: gate results handed to the up waves
+  __shared__ float h_lds[GATEUP ? 2 : 1][kTileM];  // gate/up: per-wave sums of the fp16 SwiGLU outputs
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int j = lane & 31, hk = lane >> 5;
-  const int nslab = (g.nout + ROWS_B - 1) / ROWS_B;
-  const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
-  const int tau = xcd + 8 * (q / nslab), slab = q % nslab;
+  const int mi = GATEUP ? (wave >> 1) : 0;         // matrix of this wave (gate 0, up 1)
+  const int wrow = (GATEUP ? (wave & 1) : wave) * 32;  // first row of this wave in a slab
+  const int tau = blockIdx.x;
   int first, count;
   const uint8_t* blob;
   if constexpr (SHARED) {
@@ -335,159 +358,176 @@ __global__ __launch_bounds__(kThreads) void k_grouped(GroupArgs g) {
   const int a_row = tid >> 3, a_slot = tid & 7;
   const u32x4_t* a_src = reinterpret_cast<const u32x4_t*>(g.a + (size_t)arow(a_row) * KDIM) + a_slot;
   u32x4_t a_reg[U];
-  auto load_act = [&](int step) {
+  auto load_act = [&](int s) {  // s: flattened step; the activations depend on its step in the slab only
+    const int k = s % NSTEP;
 #pragma unroll
-    for (int u = 0; u < U; ++u) a_reg[u] = a_src[(step * U + u) * 8];
+    for (int u = 0; u < U; ++u) a_reg[u] = a_src[(k * U + u) * 8];
   };
-  auto park_act = [&](int /*loaded step*/, int slot_step) {
+  auto park_act = [&](int s) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) a_lds[slot_step & 1][a_row * AS + ((u * 8 + a_slot) ^ (a_row & ASW))] = a_reg[u];
+    for (int u = 0; u < U; ++u) a_lds[s & 1][a_row * AS + ((u * 8 + a_slot) ^ (a_row & ASW))] = a_reg[u];
   };
 
-  const int r0w = slab * ROWS_B + wave * ROWS_W;  // first row (per matrix) of this wave
-  const bool active = r0w < g.nout;               // wave-uniform; idle waves still join the barriers
-  const uint8_t* cp[NTILE];
-  const uint32_t* sp[NTILE];
-#pragma unroll
-  for (int t = 0; t < NTILE; ++t) {
-    const int mi = t / NT, nt = t % NT;
-    const int row = min(r0w + nt * 32 + j, g.nout - 1);
-    cp[t] = blob + g.off_codes[mi] + (size_t)row * ROWB + hk * LB;
-    sp[t] = reinterpret_cast<const uint32_t*>(blob + g.off_sb[mi]) + (size_t)row * NG;
-  }
-  // unconditional (idle waves read a clamped row): a load skipped on some path would make the
-  // compiler's wait counts conservative and drain the prefetch at every barrier
-  auto load_w = [&](Stage& st, int step) {
+  // this block's slabs: blockIdx.y of gridDim.y equal ranges (more blocks when there are few tiles)
+  const int nslab = (g.nout + ROWS_B - 1) / ROWS_B;
+  const int spb = (nslab + gridDim.y - 1) / gridDim.y;
+  const int slab0 = blockIdx.y * spb;
+  const int ntot = (min(nslab, slab0 + spb) - slab0) * NSTEP;  // flattened steps
+  if (ntot <= 0) return;  // uniform per block
+  // Weights through buffer loads: a descriptor per section (scalar registers), a 32-bit lane
+  // offset, and the step's group offset as a scalar. Rows past nout are clamped.
+  const __amdgpu_buffer_rsrc_t crs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(blob + g.off_codes[mi]), (short)0, g.nout * ROWB, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t srs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(blob + g.off_sb[mi]), (short)0, g.nout * NG * 4, kRsrcWord3);
+  // unconditional (past the end, a clamped step is re-read): a load skipped on some path would
+  // make the compiler's wait counts conservative and drain the prefetch
+  auto load_w = [&](Stage& st, int s) {
+    const int slab = slab0 + s / NSTEP, k = s % NSTEP;
+    const int row = min(slab * ROWS_B + wrow + j, g.nout - 1);
+    const int voff = row * ROWB + hk * LB;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int gi = step * U + u;
-#pragma unroll
-      for (int t = 0; t < NTILE; ++t) {
-        if constexpr (BITS == 4) {
-          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(cp[t] + gi * GB);
-          st.c[u][t][0] = v[0]; st.c[u][t][1] = v[1]; st.c[u][t][2] = v[2]; st.c[u][t][3] = v[3];
-        } else {
-          const u32x2_t v = *reinterpret_cast<const u32x2_t*>(cp[t] + gi * GB);
-          st.c[u][t][0] = v[0]; st.c[u][t][1] = v[1];
-        }
-        st.sb[u][t] = sp[t][gi];
+      if constexpr (BITS == 4) {
+        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(crs, voff, (k * U + u) * GB, 0);
+        st.c[u][0][0] = v[0]; st.c[u][0][1] = v[1]; st.c[u][0][2] = v[2]; st.c[u][0][3] = v[3];
+      } else {
+        const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(crs, voff, (k * U + u) * GB, 0);
+        st.c[u][0][0] = v[0]; st.c[u][0][1] = v[1];
       }
+    }
+    const int soff = row * (NG * 4);
+#pragma unroll
+    for (int u4 = 0; u4 < U; u4 += 4) {
+      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(srs, soff, (k * U + u4) * 4, 0);
+#pragma unroll
+      for (int q = 0; q < 4 && u4 + q < U; ++q) st.sb[u4 + q][0] = v[q];
     }
   };
 
-  f32x16_t acc[NTILE];
+  f32x16_t acc;
 #pragma unroll
-  for (int t = 0; t < NTILE; ++t)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) acc[t][v] = 0.0f;
+  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
 
-  auto compute = [&](const Stage& st, int step) {
-    if (!active) return;
+  auto compute = [&](const Stage& st, int s) {
+    const int k = s % NSTEP;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int gi = step * U + u;
+      const int gi = k * U + u;
+      f32x16_t d;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) d[v] = 0.0f;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const f16x8_t af = __builtin_bit_cast(f16x8_t, a_lds[s & 1][j * AS + ((u * 8 + 4 * hk + m) ^ (j & ASW))]);
+        const uint32_t w = BITS == 4 ? st.c[u][0][m] : st.c[u][0][m >> 1];
+        d = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, codes_f16<BITS>(w, m & 1), d, 0, 0, 0);
+      }
+      const uint32_t p = st.sb[u][0];
+      const float sc = bf16_val((uint16_t)(p & 0xFFFFu)), bi = bf16_val((uint16_t)(p >> 16));
       // group sums of this lane's 16 token rows: rows 8a + 4*hk + b for element 4a + b
-      float S[16];
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
-        const float4 v = *reinterpret_cast<const float4*>(&s_lds[gi * kTileM + 8 * a4 + 4 * hk]);
-        S[4 * a4 + 0] = v.x; S[4 * a4 + 1] = v.y; S[4 * a4 + 2] = v.z; S[4 * a4 + 3] = v.w;
+        const float4 S = *reinterpret_cast<const float4*>(&s_lds[gi * kTileM + 8 * a4 + 4 * hk]);
+        acc[4 * a4 + 0] = fmaf(sc, d[4 * a4 + 0], fmaf(bi, S.x, acc[4 * a4 + 0]));
+        acc[4 * a4 + 1] = fmaf(sc, d[4 * a4 + 1], fmaf(bi, S.y, acc[4 * a4 + 1]));
+        acc[4 * a4 + 2] = fmaf(sc, d[4 * a4 + 2], fmaf(bi, S.z, acc[4 * a4 + 2]));
+        acc[4 * a4 + 3] = fmaf(sc, d[4 * a4 + 3], fmaf(bi, S.w, acc[4 * a4 + 3]));
       }
-      f16x8_t af[4];
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-        af[m] = __builtin_bit_cast(f16x8_t, a_lds[step & 1][j * AS + ((u * 8 + 4 * hk + m) ^ (j & ASW))]);
-#pragma unroll
-      for (int t = 0; t < NTILE; ++t) {
-        f32x16_t d;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) d[v] = 0.0f;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const uint32_t w = BITS == 4 ? st.c[u][t][m] : st.c[u][t][m >> 1];
-          d = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[m], codes_f16<BITS>(w, m & 1), d, 0, 0, 0);
-        }
-        const uint32_t p = st.sb[u][t];
-        const float sc = bf16_val((uint16_t)(p & 0xFFFFu)), bi = bf16_val((uint16_t)(p >> 16));
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[t][v] = fmaf(sc, d[v], fmaf(bi, S[v], acc[t][v]));
-      }
+#if BQ_GROUP_SCHED_BARRIER
+      // one group at a time: stops the scheduler from widening every group of the step up front,
+      // which would cost the registers of a third wave per SIMD
+      __builtin_amdgcn_sched_barrier(0);
+#endif
     }
   };
 
-  // Two weight stages in ping-pong: one is in flight while the other is computed. Every load is
-  // issued on every path (past the end it re-reads the last step, from cache), so that the
-  // compiler's wait counts stay exact and never drain the loads in flight. (A third stage costs
-  // the second wave per SIMD and measured slower.)
+  // End of a slab: write its outputs and clear the accumulators. Element v of acc holds token row
+  // 8*(v/4) + 4*hk + v%4 and weight row slab*ROWS_B + wrow + j. (Block-uniform; holds barriers.)
+  auto finish_slab = [&](int slab) {
+    const int row = slab * ROWS_B + wrow + j;
+    if constexpr (GATEUP) {
+      // the gate waves hand their results to the up waves that hold the same rows
+      if (mi == 0) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) x_lds[wave][v][lane] = acc[v];
+      }
+      __syncthreads();
+      if (mi == 1) {
+        const bool active = slab * ROWS_B + wrow < g.nout;  // wave-uniform
+        float part[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int m = 8 * (v >> 2) + 4 * hk + (v & 3);
+          const float a = x_lds[wave - 2][v][lane], c = acc[v];
+          const _Float16 h = (_Float16)(a / (1.0f + expf(-a)) * c);
+          if (active && m < count) g.oh[(size_t)orow(m) * g.nout + (row & ~7) + perm8(row & 7)] = h;
+          part[v] = active ? (float)h : 0.0f;
+        }
+        // sum over the 32 rows of this wave (the 32 lanes of each half), then over the two up waves:
+        // the slab's 64 rows are one group of the down projection's input
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+#pragma unroll
+          for (int msk = 16; msk >= 1; msk >>= 1) part[v] += __shfl_xor(part[v], msk, 32);
+        }
+        if (j == 0) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) h_lds[wave - 2][8 * (v >> 2) + 4 * hk + (v & 3)] = part[v];
+        }
+      }
+      __syncthreads();
+      const int col0 = slab * ROWS_B;
+      if (tid < kTileM && tid < count && col0 < g.nout)
+        g.os[(size_t)orow(tid) * (g.nout / 64) + col0 / 64] = h_lds[0][tid] + h_lds[1][tid];
+    } else {
+      if (row < g.nout) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int m = 8 * (v >> 2) + 4 * hk + (v & 3);
+          if (m < count) g.oy[(size_t)orow(m) * g.nout + row] = acc[v];
+        }
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+  };
+
+  // STAGES weight stages in a ring: step s computes stage s % STAGES while the next STAGES - 1
+  // steps' loads are in flight. The activations of step s+1 are requested before the weights of
+  // step s + STAGES - 1, so parking them at the end of step s waits only for loads that step s+1
+  // needs anyway. Every load is issued on every path (past the end it re-reads the last step, from
+  // cache), so that the compiler's wait counts stay exact and never drain the loads in flight.
+  auto body = [&](const Stage& cur, Stage& ahead, int s) {
+    load_act(min(s + 1, ntot - 1));
+    load_w(ahead, min(s + STAGES - 1, ntot - 1));
+    if (s < ntot) {
+      compute(cur, s);
+      if (s % NSTEP == NSTEP - 1) finish_slab(slab0 + s / NSTEP);
+    }
+    park_act(s + 1);
+    __syncthreads();
+  };
   Stage s0, s1;
   load_act(0);
   load_w(s0, 0);
-  park_act(0, 0);
-  __syncthreads();
+  park_act(0);
+  if constexpr (STAGES == 2) {
+    __syncthreads();
 #pragma unroll 1
-  for (int step = 0; step < NSTEP; step += 2) {
-    const int n1 = min(step + 1, NSTEP - 1), n2 = min(step + 2, NSTEP - 1);
-    load_act(n1);
-    load_w(s1, n1);
-    compute(s0, step);
-    park_act(n1, step + 1);
-    __syncthreads();
-    load_act(n2);
-    load_w(s0, n2);
-    if (step + 1 < NSTEP) compute(s1, step + 1);
-    park_act(n2, step + 2);
-    __syncthreads();
-  }
-
-  // element v of a tile holds token row 8*(v/4) + 4*hk + v%4 and weight row r0w + 32*nt + j
-  if constexpr (GATEUP) {
-    float part[16];
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int m = 8 * (v >> 2) + 4 * hk + (v & 3);
-      float sum = 0.0f;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const float a = acc[nt][v], c = acc[NT + nt][v];
-        const _Float16 h = (_Float16)(a / (1.0f + expf(-a)) * c);
-        sum += (float)h;
-        const int col = r0w + 32 * nt + j;
-        if (active && m < count) g.oh[(size_t)orow(m) * g.nout + (col & ~7) + perm8(col & 7)] = h;
-      }
-      part[v] = active ? sum : 0.0f;
-    }
-    // sum over the 32 lanes of each half, then over the waves that share a 64-column group (the
-    // group sums of the down projection's input)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-#pragma unroll
-      for (int msk = 16; msk >= 1; msk >>= 1) part[v] += __shfl_xor(part[v], msk, 32);
-    }
-    if (j == 0) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) h_lds[wave][8 * (v >> 2) + 4 * hk + (v & 3)] = part[v];
-    }
-    __syncthreads();
-    constexpr int WPG = 64 / ROWS_W;  // waves per group
-    for (int i = tid; i < (4 / WPG) * kTileM; i += kThreads) {
-      const int m = i % kTileM, gl = i / kTileM;
-      const int col0 = slab * ROWS_B + gl * 64;
-      if (m >= count || col0 >= g.nout) continue;
-      float v = 0.0f;
-      for (int w = 0; w < WPG; ++w) v += h_lds[gl * WPG + w][m];
-      g.os[(size_t)orow(m) * (g.nout / 64) + col0 / 64] = v;
+    for (int s = 0; s < ntot; s += 2) {
+      body(s0, s1, s);
+      body(s1, s0, s + 1);
     }
   } else {
-    if (!active) return;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int col = r0w + 32 * nt + j;
-      if (col >= g.nout) continue;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int m = 8 * (v >> 2) + 4 * hk + (v & 3);
-        if (m < count) g.oy[(size_t)orow(m) * g.nout + col] = acc[nt][v];
-      }
+    Stage s2;
+    load_w(s1, min(1, ntot - 1));
+    __syncthreads();
+#pragma unroll 1
+    for (int s = 0; s < ntot; s += 3) {
+      body(s0, s2, s);
+      body(s1, s0, s + 1);
+      body(s2, s1, s + 2);
     }
   }
 }
@@ -523,39 +563,32 @@ __global__ void k_copy_i32(int n, const int32_t* __restrict__ src, int32_t* __re
 
 unsigned cdiv(long long a, long long b) { return (unsigned)((a + b - 1) / b); }
 
-#ifndef BQ_NT_GU
-#define BQ_NT_GU 1
-#endif
-#ifndef BQ_NT_DOWN
-#define BQ_NT_DOWN 1
-#endif
-#ifndef BQ_U_LINE
-#define BQ_U_LINE 1
-#endif
-// 32-row tiles per matrix per wave, and groups per pipeline step: by default a step takes one
-// 128-byte line of every row (4 groups at 4-bit, 8 at 2-bit), so that no line is fetched twice.
-constexpr int kNTGateUp = BQ_NT_GU;
-constexpr int kNTDown = BQ_NT_DOWN;
+constexpr int kStGateUp = BQ_ST_GU;
+constexpr int kStDown = BQ_ST_DOWN;
 template <int BITS>
 constexpr int kULine = BQ_U_LINE * (BITS == 4 ? 4 : 8);
 
-// Blocks for `tiles` tiles of `nout` rows: slabs of 4*NT*32 rows, tiles padded to a multiple of 8.
-unsigned grouped_blocks(int tiles, int nout, int nt) {
-  const int nslab = (int)cdiv(nout, 4 * nt * 32);
-  return (unsigned)(8 * nslab) * cdiv(tiles, 8);
+// Blocks: one per tile, times enough slab groups that a launch has about 1024 blocks when tiles
+// are few (the shared expert's 64 tiles at 2048 tokens; small batches).
+unsigned slab_groups(int tiles, int nout, int rows_per_slab) {
+  const int nslab = (nout + rows_per_slab - 1) / rows_per_slab;
+  return (unsigned)std::max(1, std::min(nslab, 1024 / std::max(1, tiles)));
 }
 
 template <int BITS, int KDIM, bool GATEUP>
 hipError_t launch_grouped(const GroupArgs& ga, int nout, int T, int N, int E, bool has_shared, hipStream_t s) {
-  constexpr int NT = GATEUP ? kNTGateUp : kNTDown;
   constexpr int UM = kULine<BITS>;
+  constexpr int ST = GATEUP ? kStGateUp : kStDown;
+  constexpr int RS = GATEUP ? 64 : 128;  // rows per matrix per slab
   const dim3 block(kThreads);
   const int max_tiles = E + (int)cdiv(N, kTileM);
-  hipLaunchKernelGGL((k_grouped<BITS, KDIM, NT, UM, GATEUP, false>), dim3(grouped_blocks(max_tiles, nout, NT)), block,
-                     0, s, ga);
-  if (has_shared)
-    hipLaunchKernelGGL((k_grouped<BITS, KDIM, NT, UM, GATEUP, true>),
-                       dim3(grouped_blocks((int)cdiv(T, kTileM), nout, NT)), block, 0, s, ga);
+  hipLaunchKernelGGL((k_grouped<BITS, KDIM, UM, ST, GATEUP, false>),
+                     dim3(max_tiles, slab_groups(max_tiles, nout, RS)), block, 0, s, ga);
+  if (has_shared) {
+    const int st = (int)cdiv(T, kTileM);
+    hipLaunchKernelGGL((k_grouped<BITS, KDIM, UM, ST, GATEUP, true>), dim3(st, slab_groups(st, nout, RS)), block, 0,
+                       s, ga);
+  }
   return hipGetLastError();
 }
 
