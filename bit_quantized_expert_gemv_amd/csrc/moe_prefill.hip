@@ -78,57 +78,72 @@ __global__ __launch_bounds__(kThreads) void k_prep(int H, const float* __restric
 // v_mfma_f64_16x16x4_f64: every bf16 x fp32 product is exact in fp64 and the sums are fp64, so the
 // top-K decision is exact up to fp64 rounding. Lane layout (checked on the device): A[i][k] in lane
 // i + 16k, B[k][j] in lane j + 16k, D[i][j] in lane j + 16*(i%4), element i/4.
-// Block: 4 waves, 32 tokens x 32 rows; wave w owns the 16 x 16 output tile (w/2, w%2). Tiles this
-// small keep the fp64 MFMA pipes of all SIMDs evenly loaded. Operands are staged in LDS as fp64,
-// [k][token or row], rows padded to 48 doubles so that two 16-lane halves never share banks.
+// Block: 4 waves, 64 tokens x 32 rows; wave (wt, wr) owns tokens 32wt..32wt+31 x rows 16wr..16wr+15
+// as two 16 x 16 tiles that share the row operand. Operands are staged in LDS as fp64, token- or
+// row-major with a 34-double stride: a fragment read (16 rows x 4 consecutive k per 32-lane pass)
+// and the 16-byte staging writes both touch distinct banks. The next k-slice is in flight during
+// the MFMAs.
 typedef double f64x4_t __attribute__((ext_vector_type(4)));
-constexpr int kRT = 32, kRK = 32, kRP = 48;
+typedef double f64x2_t __attribute__((ext_vector_type(2)));
+constexpr int kRTok = 64, kRRow = 32, kRK = 32, kRS = kRK + 2;
 __global__ __launch_bounds__(kThreads) void k_router_gemm(int T, int H, int E, int has_shared,
                                                           const float* __restrict__ x,
                                                           const uint16_t* __restrict__ router,
                                                           const uint16_t* __restrict__ sgate,
                                                           double* __restrict__ logits) {
-  __shared__ double xs[kRK][kRP];
-  __shared__ double rs[kRK][kRP];
-  const int t0 = blockIdx.y * kRT, e0 = blockIdx.x * kRT;
+  __shared__ double xs[kRTok][kRS];
+  __shared__ double rs[kRRow][kRS];
+  const int t0 = blockIdx.y * kRTok, e0 = blockIdx.x * kRRow;
   const int nrows = E + has_shared;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int c = lane & 15, kk = lane >> 4;
-  const int ti = wave >> 1, ej = wave & 1;
-  // staging: thread -> (row tid/8, k 4*(tid%8) .. +3) of the 32 x 32 tiles
-  const int sr = tid >> 3, sk = (tid & 7) * 4;
-  const float* xp = x + (size_t)min(t0 + sr, T - 1) * H + sk;
-  const int er = min(e0 + sr, nrows - 1);
-  const uint16_t* rp = ((er < E) ? router + (size_t)er * H : sgate) + sk;
-  float4 xv = *reinterpret_cast<const float4*>(xp);
+  const int wt = wave >> 1, wr = wave & 1;
+  // staging: x as (token tid/4, k 8*(tid%4) .. +7); R as (row tid/8, k 4*(tid%8) .. +3)
+  const int xt = tid >> 2, xk = (tid & 3) * 8;
+  const int rr = tid >> 3, rk = (tid & 7) * 4;
+  const float* xp = x + (size_t)min(t0 + xt, T - 1) * H + xk;
+  const int er = min(e0 + rr, nrows - 1);
+  const uint16_t* rp = ((er < E) ? router + (size_t)er * H : sgate) + rk;
+  float4 xv[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) xv[q] = *reinterpret_cast<const float4*>(xp + 4 * q);
   uint2 rv = *reinterpret_cast<const uint2*>(rp);
-  f64x4_t acc = {0.0, 0.0, 0.0, 0.0};
+  f64x4_t acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = {0.0, 0.0, 0.0, 0.0};
   for (int k0 = 0; k0 < H; k0 += kRK) {
-    xs[sk + 0][sr] = (double)xv.x; xs[sk + 1][sr] = (double)xv.y;
-    xs[sk + 2][sr] = (double)xv.z; xs[sk + 3][sr] = (double)xv.w;
-    rs[sk + 0][sr] = (double)bf16_val((uint16_t)(rv.x & 0xFFFFu));
-    rs[sk + 1][sr] = (double)bf16_val((uint16_t)(rv.x >> 16));
-    rs[sk + 2][sr] = (double)bf16_val((uint16_t)(rv.y & 0xFFFFu));
-    rs[sk + 3][sr] = (double)bf16_val((uint16_t)(rv.y >> 16));
+    f64x2_t* xw = reinterpret_cast<f64x2_t*>(&xs[xt][xk]);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      xw[2 * q] = f64x2_t{(double)xv[q].x, (double)xv[q].y};
+      xw[2 * q + 1] = f64x2_t{(double)xv[q].z, (double)xv[q].w};
+    }
+    f64x2_t* rw = reinterpret_cast<f64x2_t*>(&rs[rr][rk]);
+    const uint32_t rw32[2] = {rv.x, rv.y};
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      rw[q] = f64x2_t{(double)bf16_val((uint16_t)(rw32[q] & 0xFFFFu)), (double)bf16_val((uint16_t)(rw32[q] >> 16))};
     __syncthreads();
-    if (k0 + kRK < H) {  // next tile in flight during the MFMAs
-      xv = *reinterpret_cast<const float4*>(xp + k0 + kRK);
+    if (k0 + kRK < H) {  // next slice in flight during the MFMAs
+#pragma unroll
+      for (int q = 0; q < 2; ++q) xv[q] = *reinterpret_cast<const float4*>(xp + k0 + kRK + 4 * q);
       rv = *reinterpret_cast<const uint2*>(rp + k0 + kRK);
     }
 #pragma unroll
     for (int s4 = 0; s4 < kRK / 4; ++s4) {
-      const double av = xs[4 * s4 + kk][ti * 16 + c];
-      const double bv = rs[4 * s4 + kk][ej * 16 + c];
-      acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc, 0, 0, 0);
+      const double bv = rs[wr * 16 + c][4 * s4 + kk];
+      const double a0 = xs[wt * 32 + c][4 * s4 + kk];
+      const double a1 = xs[wt * 32 + 16 + c][4 * s4 + kk];
+      acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, bv, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, bv, acc1, 0, 0, 0);
     }
     __syncthreads();
   }
-  const int e = e0 + ej * 16 + c;
+  const int e = e0 + wr * 16 + c;
   if (e >= nrows) return;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const int t = t0 + ti * 16 + kk + 4 * q;
-    if (t < T) logits[(size_t)t * (E + 1) + e] = acc[q];
+    const int ta = t0 + wt * 32 + kk + 4 * q;
+    if (ta < T) logits[(size_t)ta * (E + 1) + e] = acc0[q];
+    if (ta + 16 < T) logits[(size_t)(ta + 16) * (E + 1) + e] = acc1[q];
   }
 }
 
@@ -619,7 +634,7 @@ hipError_t dispatch_down(int bits, int I, const GroupArgs& ga, int H, int T, int
 
 hipError_t launch_router_gemm(const Geometry& g, const LayerPtrs& p, const float* x, int T, const Workspace& ws,
                               hipStream_t s) {
-  hipLaunchKernelGGL(k_router_gemm, dim3(cdiv(g.E + g.has_shared, kRT), cdiv(T, kRT)), dim3(kThreads), 0, s, T, g.H,
+  hipLaunchKernelGGL(k_router_gemm, dim3(cdiv(g.E + g.has_shared, kRRow), cdiv(T, kRTok)), dim3(kThreads), 0, s, T, g.H,
                      g.E, g.has_shared, x, p.router, p.sgate, ws.logits);
   return hipGetLastError();
 }
