@@ -583,8 +583,9 @@ constexpr int kStDown = BQ_ST_DOWN;
 template <int BITS>
 constexpr int kULine = BQ_U_LINE * (BITS == 4 ? 4 : 8);
 
-// Blocks: one per tile, times enough slab groups that a launch has about 1024 blocks when tiles
-// are few (the shared expert's 64 tiles at 2048 tokens; small batches).
+// Blocks: one per tile, times enough slab groups that a launch has about 1024 working blocks when
+// tiles are few (the shared expert's 64 tiles at 2048 tokens; small batches). `tiles` is the number
+// expected to hold tokens: for the routed experts at most one per routed entry.
 unsigned slab_groups(int tiles, int nout, int rows_per_slab) {
   const int nslab = (nout + rows_per_slab - 1) / rows_per_slab;
   return (unsigned)std::max(1, std::min(nslab, 1024 / std::max(1, tiles)));
@@ -598,7 +599,7 @@ hipError_t launch_grouped(const GroupArgs& ga, int nout, int T, int N, int E, bo
   const dim3 block(kThreads);
   const int max_tiles = E + (int)cdiv(N, kTileM);
   hipLaunchKernelGGL((k_grouped<BITS, KDIM, UM, ST, GATEUP, false>),
-                     dim3(max_tiles, slab_groups(max_tiles, nout, RS)), block, 0, s, ga);
+                     dim3(max_tiles, slab_groups(std::min(max_tiles, N), nout, RS)), block, 0, s, ga);
   if (has_shared) {
     const int st = (int)cdiv(T, kTileM);
     hipLaunchKernelGGL((k_grouped<BITS, KDIM, UM, ST, GATEUP, true>), dim3(st, slab_groups(st, nout, RS)), block, 0,

@@ -53,8 +53,9 @@ extern "C" {
 
 #define MOE_MAX_TOP_K 8
 #define MOE_MAX_EXPERTS 1024
-/* Token counts at or above this run the prefill path in moe_layer_forward (grouped by expert). */
-#define MOE_PREFILL_MIN_TOKENS 64
+/* Token counts at or above this run the prefill path in moe_layer_forward (grouped by expert). Below
+ * it, per-token streaming is faster on MI355X for a 512-expert, top-3 layer (measured crossover). */
+#define MOE_PREFILL_MIN_TOKENS 96
 
 /* One MoE layer.
  *   hidden H, inter I: powers of two with 256 <= H <= 8192 and 64 <= I <= 2048. group must be 64, bits 2 or 4.

@@ -175,3 +175,14 @@ def test_strerror():
     for c in (0, -1, -2, -3, -4):
         assert bq.moe_strerror(c) != "unknown error"
     assert bq.moe_strerror(-99) == "unknown error"
+
+
+def test_binding_constants_match_header():
+    """The binding's copies of the header's numeric #defines (limits, status codes) agree with it."""
+    import re
+    text = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "moe.h")).read()
+    found = dict(re.findall(r"^#define\s+(MOE_[A-Z0-9_]+)\s+\(?(-?\d+)\)?\s*$", text, flags=re.M))
+    assert {"MOE_MAX_TOP_K", "MOE_MAX_EXPERTS", "MOE_PREFILL_MIN_TOKENS", "MOE_OK"} <= set(found)
+    for name, value in found.items():
+        assert hasattr(bq, name), name
+        assert getattr(bq, name) == int(value), name

@@ -50,7 +50,7 @@ def _forward(L, x, res=None):
     return out.cpu().numpy(), idx.cpu().numpy()
 
 
-@pytest.mark.parametrize("T", [64, 100, 300])
+@pytest.mark.parametrize("T", [bq.MOE_PREFILL_MIN_TOKENS, 100, 300])
 def test_prefill_tiny_all_tokens(tiny, T):
     L, ref = tiny
     x = torch.from_numpy(synth.tokens_x(TINY, 7, T)).cuda()
@@ -66,12 +66,12 @@ def test_prefill_tiny_all_tokens(tiny, T):
 
 def test_prefill_tiny_residual_and_determinism(tiny):
     L, ref = tiny
-    x = torch.from_numpy(synth.tokens_x(TINY, 0, 80)).cuda()
+    x = torch.from_numpy(synth.tokens_x(TINY, 0, 128)).cuda()
     res = torch.randn_like(x)
     a, ia = _forward(L, x, res)
     b, ib = _forward(L, x, res)
     assert np.array_equal(a, b) and np.array_equal(ia, ib)
-    for t in (0, 41, 79):
+    for t in (0, 41, 127):
         r = ref.token(x[t].cpu().numpy(), res[t].cpu().numpy())
         assert_close(a[t], r.out)
 
@@ -148,7 +148,7 @@ def test_prefill_duplicate_router_rows_tie_to_lower_index(gpu_device):
     lower expert index, as the oracle's sort does, for every token of a prefill batch."""
     L = DeviceLayer(TINY)
     ref = Reference(TINY)
-    T = 64
+    T = bq.MOE_PREFILL_MIN_TOKENS
     x = torch.from_numpy(synth.tokens_x(TINY, 11, T)).cuda()
     xs = x.cpu().numpy().astype(np.float64)
     best = int(np.argmax(oracle.router_logits(ref.router, xs[0])))
@@ -164,5 +164,5 @@ def test_prefill_duplicate_router_rows_tie_to_lower_index(gpu_device):
         assert list(idx[t]) == list(want), f"token {t}"
         tied_tokens += len({best, 2, 5} & set(want)) >= 2
     assert tied_tokens >= 1  # the tie decides at least token 0's choice
-    for t in (0, 31, 63):
+    for t in (0, 31, T - 1):
         assert_close(out[t], ref.token(xs[t]).out, f"out[{t}]")
