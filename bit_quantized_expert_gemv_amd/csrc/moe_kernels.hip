@@ -358,18 +358,16 @@ __device__ __forceinline__ void write_routing(const LayerArgs& a, int t, const i
   if (g_out && a.has_shared) g_out[t] = (float)(1.0 / (1.0 + exp(-lg[a.E])));
 }
 
-// RMS norm scale of h (fp64 accumulation, one fixed order for every block).
-__device__ float block_rms_inv(const float* __restrict__ h, int H, float eps, double* red) {
-  double ss = 0.0;
-  for (int i = threadIdx.x; i < H; i += kBlock) ss += (double)h[i] * (double)h[i];
-  red[threadIdx.x] = ss;
-  __syncthreads();
-  for (int s = kBlock / 2; s >= 1; s >>= 1) {
-    if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
-    __syncthreads();
-  }
-  const double tot = red[0];
-  __syncthreads();
+// RMS norm scale 1/sqrt(mean(h^2) + eps) from the previous layer's per-block partial sums of h^2
+// (fp64). Lane l holds partials l, l + 64, ...; every wave adds them in the same fixed order, so
+// every wave of every block gets the same value without a barrier.
+constexpr int kNormSqPerLane = 16;  // partial sums per lane: up to 1024 phase-3 blocks (H 8192, I 2048)
+__device__ __forceinline__ float wave_rms_inv(double ss, int H, float eps) {
+  ss = seg_sum<64>(ss);
+  const long long b = __double_as_longlong(ss);
+  const int lo = __builtin_amdgcn_readlane((int)(b & 0xFFFFFFFF), 63);
+  const int hi = __builtin_amdgcn_readlane((int)(b >> 32), 63);
+  const double tot = __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
   return (float)(1.0 / sqrt(tot / (double)H + (double)eps));
 }
 
@@ -414,34 +412,56 @@ __device__ __forceinline__ void gateup_block(const LayerArgs& a, const uint8_t* 
 #endif
 template <int H>
 __global__ __launch_bounds__(kBlock) void k_router_phase(LayerArgs a, const float* __restrict__ x,
-                                                         const float* __restrict__ norm_src, float eps,
+                                                         const float* __restrict__ norm_src,
+                                                         const double* __restrict__ norm_sq, int nsq, float eps,
                                                          int router_steps) {
   using R = RouterCfg<H>;
   constexpr int SPLIT = (R::CPL % BQ_ROUTER_SPLIT == 0) ? BQ_ROUTER_SPLIT : 1;  // waves per row
   constexpr int CPW = R::CPL / SPLIT;                                            // chunks per lane
-  __shared__ double red[kBlock];
   __shared__ double part[kWaves];
   const int t = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  float scale = 1.0f;
-  const float* src = x + (size_t)t * H;
-  if (norm_src != nullptr) {
-    src = norm_src + (size_t)t * H;
-    scale = block_rms_inv(src, H, eps, red);
-    if (blockIdx.x == 0)
-      for (int i = threadIdx.x; i < H; i += kBlock) a.ws.u[(size_t)t * H + i] = src[i] * scale;
-  }
   const int lir = lane % R::LPR, rig = lane / R::LPR;
   const int nrows = a.E + a.has_shared;
   const int piece = wave % SPLIT;
-  for (int s = 0; s < router_steps; ++s) {
+  auto row_of = [&](int s) {
     const int base = ((blockIdx.x * (kWaves / SPLIT) + wave / SPLIT) * router_steps + s) * R::RPW;
-    const int r = base + rig;
-    const int rr = min(r, nrows - 1);
+    return base + rig;
+  };
+  auto load_w = [&](int s, uint4 (&w)[CPW]) {
+    const int rr = min(row_of(s), nrows - 1);
     const uint16_t* row = (rr < a.E) ? a.router + (size_t)rr * H : a.sgate;
-    uint4 w[CPW];
 #pragma unroll
     for (int j = 0; j < CPW; ++j) w[j] = *reinterpret_cast<const uint4*>(row + (lir + (j * SPLIT + piece) * R::LPR) * 8);
+  };
+  // Order of requests: the norm's partial sums, then the first router rows, then (after the scale
+  // is known) the activations. Loads retire in order, so reducing the partial sums never waits for
+  // the router rows.
+  const bool norm = norm_src != nullptr;
+  double sqv[kNormSqPerLane];
+  if (norm) {
+    const double* sq = norm_sq + (size_t)t * nsq;
+#pragma unroll
+    for (int i = 0; i < kNormSqPerLane; ++i) {
+      const int k = lane + 64 * i;
+      const double v = sq[min(k, nsq - 1)];
+      sqv[i] = k < nsq ? v : 0.0;
+    }
+  }
+  uint4 w[CPW];
+  load_w(0, w);
+  float scale = 1.0f;
+  const float* src = x + (size_t)t * H;
+  if (norm) {
+    src = norm_src + (size_t)t * H;
+    double ss = 0.0;
+#pragma unroll
+    for (int i = 0; i < kNormSqPerLane; ++i) ss += sqv[i];
+    scale = wave_rms_inv(ss, H, eps);
+  }
+  for (int s = 0; s < router_steps; ++s) {
+    if (s > 0) load_w(s, w);
+    const int r = row_of(s);
     double acc[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int j = 0; j < CPW; ++j) {
@@ -470,6 +490,9 @@ __global__ __launch_bounds__(kBlock) void k_router_phase(LayerArgs a, const floa
       __syncthreads();
     }
   }
+  // the normalised input for phase 2 (block 0 only, off the router's critical path)
+  if (norm && blockIdx.x == 0)
+    for (int i = threadIdx.x; i < H; i += kBlock) a.ws.u[(size_t)t * H + i] = src[i] * scale;
 }
 
 // Kernel 2: gate/up/SwiGLU of the routed experts (blockIdx.y = slot) and, as slot K, of the shared
@@ -522,7 +545,7 @@ __global__ __launch_bounds__(kBlock) void k_gateup(LayerArgs a, const float* __r
 template <int BITS, int I, int P>
 __global__ __launch_bounds__(kBlock) void k_down(LayerArgs a, const int32_t* __restrict__ idx,
                                                  const float* __restrict__ residual, float* __restrict__ out,
-                                                 float* __restrict__ y) {
+                                                 float* __restrict__ y, double* __restrict__ sq_out) {
   using C = RowCfg<BITS, I>;
   constexpr int RB = C::RPW * P;
   __shared__ float4 hs[kWaves][I / 4];
@@ -586,13 +609,23 @@ __global__ __launch_bounds__(kBlock) void k_down(LayerArgs a, const int32_t* __r
   }
   if (!combine) return;
   __syncthreads();
+  double ss = 0.0;
   for (int i = threadIdx.x; i < RB; i += kBlock) {
     const int r = row0 + i;
     if (r >= a.H) continue;
     float acc = residual[(size_t)t * a.H + r];
     for (int w = 0; w < kWaves && w < a.NE; ++w) acc += part[w][i];
     out[(size_t)t * a.H + r] = acc;
+    ss += (double)acc * (double)acc;
   }
+  if (sq_out == nullptr) return;
+  // this block's sum of out^2 for the next layer's RMS norm (fixed order: DPP within each wave,
+  // then the waves in index order)
+  __shared__ double wsq[kWaves];
+  ss = seg_sum<64>(ss);
+  if (lane == 63) wsq[wave] = ss;
+  __syncthreads();
+  if (threadIdx.x == 0) sq_out[(size_t)t * gridDim.x + blockIdx.x] = (wsq[0] + wsq[1]) + (wsq[2] + wsq[3]);
 }
 
 // Router-only top-K: one wave per token.
@@ -691,15 +724,16 @@ hipError_t launch_timed(F kernel, dim3 grid, dim3 block, hipStream_t s, const Ke
 }
 
 template <int BITS, int H>
-hipError_t router_phase_impl(const LayerArgs& a, const float* x, const float* norm_src, float eps, int T,
-                             hipStream_t s, const KernelEvents& ev) {
+hipError_t router_phase_impl(const LayerArgs& a, const float* x, const float* norm_src, const double* norm_sq,
+                             int nsq, float eps, int T, hipStream_t s, const KernelEvents& ev) {
   using R = RouterCfg<H>;
   const int router_steps = BQ_ROUTER_STEPS;
   const int nrows = a.E + a.has_shared;
   constexpr int SPLIT = (R::CPL % BQ_ROUTER_SPLIT == 0) ? BQ_ROUTER_SPLIT : 1;
   const int rows_per_block = kWaves / SPLIT * router_steps * R::RPW;
   const int nrb = (nrows + rows_per_block - 1) / rows_per_block;
-  return launch_timed(k_router_phase<H>, dim3(nrb, T), dim3(kBlock), s, ev, a, x, norm_src, eps, router_steps);
+  return launch_timed(k_router_phase<H>, dim3(nrb, T), dim3(kBlock), s, ev, a, x, norm_src, norm_sq, nsq, eps,
+                      router_steps);
 }
 
 template <int BITS, int H>
@@ -716,22 +750,30 @@ hipError_t gateup_impl(const LayerArgs& a, const float* x, int T, const int32_t*
 
 template <int BITS, int I>
 hipError_t down_impl(const LayerArgs& a, int T, const int32_t* idx, const float* residual, float* out, float* y,
-                     hipStream_t s, const KernelEvents& ev) {
+                     double* sq_out, hipStream_t s, const KernelEvents& ev) {
   using C = RowCfg<BITS, I>;
   constexpr int RB = C::RPW * kP3;
   const int nb = (a.H + RB - 1) / RB;
-  return launch_timed(k_down<BITS, I, kP3>, dim3(nb, T), dim3(kBlock), s, ev, a, idx, residual, out, y);
+  return launch_timed(k_down<BITS, I, kP3>, dim3(nb, T), dim3(kBlock), s, ev, a, idx, residual, out, y, sq_out);
+}
+
+template <int BITS, int I>
+int down_blocks_impl(int H) {
+  using C = RowCfg<BITS, I>;
+  constexpr int RB = C::RPW * kP3;
+  return (H + RB - 1) / RB;
 }
 
 }  // namespace
 
-hipError_t launch_router_phase(const Geometry& g, const LayerPtrs& p, const float* x, const float* norm_src, float eps,
-                               int T, const Workspace& ws, hipStream_t s, const KernelEvents& ev) {
+hipError_t launch_router_phase(const Geometry& g, const LayerPtrs& p, const float* x, const float* norm_src,
+                               const double* norm_sq, int nsq, float eps, int T, const Workspace& ws, hipStream_t s,
+                               const KernelEvents& ev) {
   const LayerArgs a = make_args(g, p, ws);
-#define BQ_CASE(HV)                                                                 \
-  case HV:                                                                          \
-    return g.bits == 4 ? router_phase_impl<4, HV>(a, x, norm_src, eps, T, s, ev)    \
-                       : router_phase_impl<2, HV>(a, x, norm_src, eps, T, s, ev);
+#define BQ_CASE(HV)                                                                                  \
+  case HV:                                                                                           \
+    return g.bits == 4 ? router_phase_impl<4, HV>(a, x, norm_src, norm_sq, nsq, eps, T, s, ev)       \
+                       : router_phase_impl<2, HV>(a, x, norm_src, norm_sq, nsq, eps, T, s, ev);
   switch (g.H) { BQ_FOR_H(BQ_CASE) }
 #undef BQ_CASE
   return hipErrorInvalidValue;
@@ -751,15 +793,27 @@ hipError_t launch_gateup(const Geometry& g, const LayerPtrs& p, const float* x, 
 }
 
 hipError_t launch_down(const Geometry& g, const LayerPtrs& p, int T, const Workspace& ws, const int32_t* idx,
-                       const float* residual, float* out, float* y, hipStream_t s, const KernelEvents& ev) {
+                       const float* residual, float* out, float* y, double* sq_out, hipStream_t s,
+                       const KernelEvents& ev) {
   const LayerArgs a = make_args(g, p, ws);
-#define BQ_CASE(IV)                                                                   \
-  case IV:                                                                            \
-    return g.bits == 4 ? down_impl<4, IV>(a, T, idx, residual, out, y, s, ev)         \
-                       : down_impl<2, IV>(a, T, idx, residual, out, y, s, ev);
+#define BQ_CASE(IV)                                                                        \
+  case IV:                                                                                 \
+    return g.bits == 4 ? down_impl<4, IV>(a, T, idx, residual, out, y, sq_out, s, ev)      \
+                       : down_impl<2, IV>(a, T, idx, residual, out, y, sq_out, s, ev);
   switch (g.I) { BQ_FOR_I(BQ_CASE) }
 #undef BQ_CASE
   return hipErrorInvalidValue;
+}
+
+int max_norm_partials() { return 64 * kNormSqPerLane; }
+
+int down_blocks(const Geometry& g) {
+#define BQ_CASE(IV) \
+  case IV:          \
+    return g.bits == 4 ? down_blocks_impl<4, IV>(g.H) : down_blocks_impl<2, IV>(g.H);
+  switch (g.I) { BQ_FOR_I(BQ_CASE) }
+#undef BQ_CASE
+  return 0;
 }
 
 hipError_t launch_topk(const Geometry& g, int T, const Workspace& ws, int32_t* idx, float* w, float* sg,
