@@ -123,6 +123,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cold", action="store_true")
+    ap.add_argument("--dequant", default="xsum", choices=["xsum", "literal", "naive"],
+                    help="decode GEMV arithmetic: per-chunk x-sum form (default), the pages' per-element "
+                         "fma(q, s*x, b*x) form, or the naive (q*s + b)*x form; an A/B ablation")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="first run a plain device copy of this many MiB (a known-size reference for HBM counters)")
     args = ap.parse_args()
@@ -157,6 +160,8 @@ def main():
     torch.cuda.set_device(dev)
     print(f"[bench] building {w.name} layer", file=sys.stderr, flush=True)
     L = DeviceLayer(w, device=dev)
+    flags = {"xsum": 0, "literal": bq.MOE_FLAG_DEQUANT_LITERAL, "naive": bq.MOE_FLAG_DEQUANT_NAIVE}[args.dequant]
+    L.desc.flags = flags
     X = torch.from_numpy(synth.tokens_x(w, 0, N)).to(dev)
     out = torch.empty_like(X)
     idx = torch.empty(N, w.top_k, dtype=torch.int32, device=dev)
@@ -238,7 +243,7 @@ def main():
         rep_shared = torch.empty(R, L.stride, dtype=torch.uint8, device=dev)
         rep_shared[:] = L.shared.reshape(1, -1)
         descs = [bq.make_layer(w.hidden, w.inter, w.n_experts, w.top_k, w.bits, L.experts, L.stride, rep_router[r],
-                               rep_shared[r], rep_gate[r], w.group) for r in range(R)]
+                               rep_shared[r], rep_gate[r], w.group, flags) for r in range(R)]
         gc = capture(lambda t: descs[t % R])
         csecs = timed(gc, args.steps, args.warmup)
         ctok = args.steps * N / csecs
@@ -262,7 +267,8 @@ def main():
                                f"top-{w.top_k} + shared, {w.bits}-bit group-{w.group} experts; a step is {N} "
                                f"sequential single-token calls in one HIP graph",
                    "tokens_per_step": N, "hidden": w.hidden, "n_experts": w.n_experts, "inter": w.inter,
-                   "top_k": w.top_k, "bits": w.bits, "group": w.group, "parallelism": "single GPU"},
+                   "top_k": w.top_k, "bits": w.bits, "group": w.group, "dequant_form": args.dequant,
+                   "parallelism": "single GPU"},
         "us_per_token": round(us_tok, 3),
         "expert_GB/s": round(expert_bytes / (us_tok * 1e-6) / 1e9, 1),
         "expert_frac_of_peak": round(expert_bytes / (us_tok * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),

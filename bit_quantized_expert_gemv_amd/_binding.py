@@ -15,13 +15,14 @@ LIB_PATH = os.path.join(_HERE, "libbqmoe.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ENOSPC, MOE_EHIP = 0, -1, -2, -3, -4
 MOE_MAX_TOP_K, MOE_MAX_EXPERTS, MOE_PREFILL_MIN_TOKENS = 8, 1024, 96
+MOE_FLAG_DEQUANT_LITERAL, MOE_FLAG_DEQUANT_NAIVE = 1, 2
 
 c_i32, c_u64, c_size, c_vp, c_f32 = ctypes.c_int32, ctypes.c_uint64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
 
 
 class moe_layer_t(ctypes.Structure):
     _fields_ = [("hidden", c_i32), ("inter", c_i32), ("n_experts", c_i32), ("top_k", c_i32),
-                ("has_shared", c_i32), ("bits", c_i32), ("group", c_i32), ("reserved", c_i32),
+                ("has_shared", c_i32), ("bits", c_i32), ("group", c_i32), ("flags", c_i32),
                 ("experts_dev", c_vp), ("expert_stride", c_u64), ("shared_blob_dev", c_vp),
                 ("router_dev", c_vp), ("shared_gate_dev", c_vp)]
 
@@ -104,8 +105,8 @@ def stream_handle(stream) -> int | None:
 
 
 def make_layer(hidden, inter, n_experts, top_k, bits, experts, expert_stride, router, shared_blob=None,
-               shared_gate=None, group=64) -> moe_layer_t:
-    return moe_layer_t(hidden, inter, n_experts, top_k, 1 if shared_blob is not None else 0, bits, group, 0,
+               shared_gate=None, group=64, flags=0) -> moe_layer_t:
+    return moe_layer_t(hidden, inter, n_experts, top_k, 1 if shared_blob is not None else 0, bits, group, flags,
                        ptr(experts), expert_stride, ptr(shared_blob), ptr(router), ptr(shared_gate))
 
 

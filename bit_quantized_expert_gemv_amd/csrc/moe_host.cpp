@@ -88,6 +88,11 @@ bool geometry_from(const moe_layer_t* L, Geometry* g, const char** why) {
     return false;
   }
   if (L->has_shared != 0 && L->has_shared != 1) { *why = "has_shared must be 0 or 1"; return false; }
+  if (L->flags != 0 && L->flags != MOE_FLAG_DEQUANT_LITERAL && L->flags != MOE_FLAG_DEQUANT_NAIVE) {
+    *why = "flags must be 0, MOE_FLAG_DEQUANT_LITERAL or MOE_FLAG_DEQUANT_NAIVE";
+    return false;
+  }
+  g->form = L->flags == MOE_FLAG_DEQUANT_LITERAL ? 1 : L->flags == MOE_FLAG_DEQUANT_NAIVE ? 2 : 0;
   g->H = L->hidden; g->I = L->inter; g->E = L->n_experts; g->K = L->top_k;
   g->has_shared = L->has_shared; g->NE = g->K + g->has_shared;
   g->bits = L->bits; g->G = L->group;

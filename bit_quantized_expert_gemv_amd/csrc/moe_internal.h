@@ -14,6 +14,7 @@ namespace bqmoe {
 struct Geometry {
   int H, I, E, K, NE;  // NE = K + has_shared: expert slots per token
   int bits, G, has_shared;
+  int form;               // decode GEMV arithmetic: 0 per-chunk x-sums, 1 fma(q, s*x, b*x), 2 (q*s + b)*x
   uint64_t off_codes[3];  // byte offsets of gate / up / down codes inside a blob
   uint64_t off_sb[3];     // byte offsets of gate / up / down (scale, bias) words
   uint64_t blob_bytes;

@@ -125,16 +125,83 @@ __device__ __forceinline__ float chunk_dot(const uint4 w, const float* x) {
   else return chunk_dot2(w, x);
 }
 
-// This lane's share of one row: sum over its chunks of s * sum(q x) + b * S.
-template <int BITS, class C>
+// Per-element forms ("Kernel de dequantización optimizado con FMA"): every weight contributes
+// fma(q, s*x, b*x) (the pages' rewrite) or (q*s + b)*x (the form it replaced). s carries the
+// widening's scale (2^9 at 4-bit), so q here is the widened code. An A/B ablation of chunk_dot
+// with the chunk sums.
+// Per-element dequant forms of the ablation: 1 = the pages' fma(q, s*x, b*x); 2 = the naive
+// (q*s + b)*x that the pages' rewrite replaced.
+template <int FORM>
+__device__ __forceinline__ float lit_term(float q, float x, float s, float b, float acc) {
+  if constexpr (FORM == 1) return acc + fmaf(q, s * x, b * x);
+  else return fmaf(fmaf(q, s, b), x, acc);
+}
+
+template <int FORM>
+__device__ __forceinline__ float chunk_lit4(const uint4 w, const float* x, float s, float b, float acc) {
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = ws[i] & 0x0F0F0F0Fu;
+    const uint32_t hi = (ws[i] >> 4) & 0x0F0F0F0Fu;
+    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false);
+    const auto bq = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);
+    const auto c = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
+    const auto d = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
+    acc = lit_term<FORM>(a[0], x[8 * i + 0], s, b, acc);
+    acc = lit_term<FORM>(c[0], x[8 * i + 1], s, b, acc);
+    acc = lit_term<FORM>(a[1], x[8 * i + 2], s, b, acc);
+    acc = lit_term<FORM>(c[1], x[8 * i + 3], s, b, acc);
+    acc = lit_term<FORM>(bq[0], x[8 * i + 4], s, b, acc);
+    acc = lit_term<FORM>(d[0], x[8 * i + 5], s, b, acc);
+    acc = lit_term<FORM>(bq[1], x[8 * i + 6], s, b, acc);
+    acc = lit_term<FORM>(d[1], x[8 * i + 7], s, b, acc);
+  }
+  return acc;
+}
+
+template <int FORM, int N>
+__device__ __forceinline__ float lit2_byte(uint32_t lo, uint32_t hi, const float* x, float s, float b, float acc) {
+  const auto a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(lo, 2.0f, N);
+  const auto c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(hi, 2.0f, N);
+  acc = lit_term<FORM>(a[0], x[4 * N + 0], s, b, acc);
+  acc = lit_term<FORM>(c[0], x[4 * N + 1], s, b, acc);
+  acc = lit_term<FORM>(a[1], x[4 * N + 2], s, b, acc);
+  acc = lit_term<FORM>(c[1], x[4 * N + 3], s, b, acc);
+  return acc;
+}
+
+template <int FORM>
+__device__ __forceinline__ float chunk_lit2(const uint4 w, const float* x, float s, float b, float acc) {
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = ws[i] & 0x33333333u;
+    const uint32_t hi = (ws[i] >> 2) & 0x33333333u;
+    acc = lit2_byte<FORM, 0>(lo, hi, x + 16 * i, s, b, acc);
+    acc = lit2_byte<FORM, 1>(lo, hi, x + 16 * i, s, b, acc);
+    acc = lit2_byte<FORM, 2>(lo, hi, x + 16 * i, s, b, acc);
+    acc = lit2_byte<FORM, 3>(lo, hi, x + 16 * i, s, b, acc);
+  }
+  return acc;
+}
+
+// This lane's share of one row: sum over its chunks of s * sum(q x) + b * S (FORM 0), or one of the
+// per-element forms of the ablation (FORM 1, 2).
+template <int BITS, class C, int FORM = 0>
 __device__ __forceinline__ float row_partial(const uint4 (&cw)[C::CPL], const uint32_t (&sb)[C::CPL],
                                              const float (&xr)[C::XPL], const float (&S)[C::CPL]) {
   constexpr float kCvt = BITS == 4 ? 512.0f : 1.0f;  // undo the e4m3 2^-9
   float a = 0.0f;
 #pragma unroll
   for (int j = 0; j < C::CPL; ++j) {
-    const float d = chunk_dot<BITS>(cw[j], &xr[j * C::CH]);
-    a = fmaf(bf16_lo(sb[j]) * kCvt, d, fmaf(bf16_hi(sb[j]), S[j], a));
+    if constexpr (FORM != 0) {
+      if constexpr (BITS == 4) a = chunk_lit4<FORM>(cw[j], &xr[j * C::CH], bf16_lo(sb[j]) * kCvt, bf16_hi(sb[j]), a);
+      else a = chunk_lit2<FORM>(cw[j], &xr[j * C::CH], bf16_lo(sb[j]) * kCvt, bf16_hi(sb[j]), a);
+    } else {
+      const float d = chunk_dot<BITS>(cw[j], &xr[j * C::CH]);
+      a = fmaf(bf16_lo(sb[j]) * kCvt, d, fmaf(bf16_hi(sb[j]), S[j], a));
+    }
   }
   return a;
 }
@@ -260,7 +327,7 @@ __device__ __forceinline__ T seg_sum(T v) {
 __device__ __forceinline__ float silu_mul(float a, float c) { return a / (1.0f + expf(-a)) * c; }
 
 struct LayerArgs {
-  int H, I, E, K, NE, has_shared;
+  int H, I, E, K, NE, has_shared, form;
   uint64_t off_codes[3], off_sb[3];
   const uint8_t* experts;
   uint64_t stride;
@@ -272,7 +339,7 @@ struct LayerArgs {
 
 LayerArgs make_args(const Geometry& g, const LayerPtrs& p, const Workspace& ws) {
   LayerArgs a;
-  a.H = g.H; a.I = g.I; a.E = g.E; a.K = g.K; a.NE = g.NE; a.has_shared = g.has_shared;
+  a.H = g.H; a.I = g.I; a.E = g.E; a.K = g.K; a.NE = g.NE; a.has_shared = g.has_shared; a.form = g.form;
   for (int m = 0; m < 3; ++m) { a.off_codes[m] = g.off_codes[m]; a.off_sb[m] = g.off_sb[m]; }
   a.experts = p.experts; a.stride = p.stride; a.shared = p.shared; a.router = p.router; a.sgate = p.sgate;
   a.ws = ws;
@@ -373,7 +440,7 @@ __device__ __forceinline__ float wave_rms_inv(double ss, int H, float eps) {
 
 // gate/up/SwiGLU for P row steps of one expert, for a whole block: weight loads go out first,
 // then the staged activations are parked in LDS (one barrier) and read back per lane.
-template <int BITS, int H, int P>
+template <int BITS, int H, int P, int FORM>
 __device__ __forceinline__ void gateup_block(const LayerArgs& a, const uint8_t* __restrict__ blob,
                                              const Stage<H, kBlock>& st, float scale, float4* __restrict__ xs,
                                              int step0, int lir, int rig, float* __restrict__ h) {
@@ -398,8 +465,8 @@ __device__ __forceinline__ void gateup_block(const LayerArgs& a, const uint8_t* 
 #pragma unroll
   for (int p = 0; p < P; ++p) {
     const int r = (step0 + p) * C::RPW + rig;
-    const float ga = seg_sum<C::LPR>(row_partial<BITS, C>(cg[p], sg[p], xr, S));
-    const float ua = seg_sum<C::LPR>(row_partial<BITS, C>(cu[p], su[p], xr, S));
+    const float ga = seg_sum<C::LPR>(row_partial<BITS, C, FORM>(cg[p], sg[p], xr, S));
+    const float ua = seg_sum<C::LPR>(row_partial<BITS, C, FORM>(cu[p], su[p], xr, S));
     if (lir == C::LPR - 1 && r < a.I) h[r] = silu_mul(ga, ua);
   }
 }
@@ -498,7 +565,7 @@ __global__ __launch_bounds__(kBlock) void k_router_phase(LayerArgs a, const floa
 // Kernel 2: gate/up/SwiGLU of the routed experts (blockIdx.y = slot) and, as slot K, of the shared
 // expert. The shared slot needs no routing, so its blocks stream weights while the routed blocks are
 // still picking their experts.
-template <int BITS, int H, int P, int PL>
+template <int BITS, int H, int P, int PL, int FORM>
 __global__ __launch_bounds__(kBlock) void k_gateup(LayerArgs a, const float* __restrict__ x,
                                                    const int32_t* __restrict__ idx_in, int32_t* __restrict__ idx_out) {
   using C = RowCfg<BITS, H>;
@@ -537,12 +604,12 @@ __global__ __launch_bounds__(kBlock) void k_gateup(LayerArgs a, const float* __r
   } else {
     st.load(x + (size_t)t * H, threadIdx.x);
   }
-  gateup_block<BITS, H, P>(a, blob, st, 1.0f, xs, step0, lir, rig, a.ws.h + ((size_t)t * a.NE + slot) * a.I);
+  gateup_block<BITS, H, P, FORM>(a, blob, st, 1.0f, xs, step0, lir, rig, a.ws.h + ((size_t)t * a.NE + slot) * a.I);
 }
 
 // Kernel 3: down projections of all expert slots for a block of output rows; combine or store.
 // Wave w handles slots w, w+4, ...; each stages its slot's SwiGLU vector through its own LDS region.
-template <int BITS, int I, int P>
+template <int BITS, int I, int P, int FORM>
 __global__ __launch_bounds__(kBlock) void k_down(LayerArgs a, const int32_t* __restrict__ idx,
                                                  const float* __restrict__ residual, float* __restrict__ out,
                                                  float* __restrict__ y, double* __restrict__ sq_out) {
@@ -586,7 +653,7 @@ __global__ __launch_bounds__(kBlock) void k_down(LayerArgs a, const int32_t* __r
       float xr[C::XPL], S[C::CPL];
       read_act<C>(hs[wave], lir, xr, S);
 #pragma unroll
-      for (int p = 0; p < P; ++p) yv[p] = seg_sum<C::LPR>(row_partial<BITS, C>(cw[p], sb[p], xr, S));
+      for (int p = 0; p < P; ++p) yv[p] = seg_sum<C::LPR>(row_partial<BITS, C, FORM>(cw[p], sb[p], xr, S));
     } else {
 #pragma unroll
       for (int p = 0; p < P; ++p) yv[p] = NAN;
@@ -743,9 +810,11 @@ hipError_t gateup_impl(const LayerArgs& a, const float* x, int T, const int32_t*
   const int rows_per_block = kWaves * kP2 * C::RPW;
   const int nb = (a.I + rows_per_block - 1) / rows_per_block;
   const int slots = a.K + ((with_shared && a.has_shared) ? 1 : 0);
-  if (a.E <= 512)
-    return launch_timed(k_gateup<BITS, H, kP2, 8>, dim3(nb, slots, T), dim3(kBlock), s, ev, a, x, idx_in, idx_out);
-  return launch_timed(k_gateup<BITS, H, kP2, 16>, dim3(nb, slots, T), dim3(kBlock), s, ev, a, x, idx_in, idx_out);
+  const dim3 grid(nb, slots, T);
+#define BQ_GU(PL, F) launch_timed(k_gateup<BITS, H, kP2, PL, F>, grid, dim3(kBlock), s, ev, a, x, idx_in, idx_out)
+  if (a.E <= 512) return a.form == 1 ? BQ_GU(8, 1) : a.form == 2 ? BQ_GU(8, 2) : BQ_GU(8, 0);
+  return a.form == 1 ? BQ_GU(16, 1) : a.form == 2 ? BQ_GU(16, 2) : BQ_GU(16, 0);
+#undef BQ_GU
 }
 
 template <int BITS, int I>
@@ -754,7 +823,9 @@ hipError_t down_impl(const LayerArgs& a, int T, const int32_t* idx, const float*
   using C = RowCfg<BITS, I>;
   constexpr int RB = C::RPW * kP3;
   const int nb = (a.H + RB - 1) / RB;
-  return launch_timed(k_down<BITS, I, kP3>, dim3(nb, T), dim3(kBlock), s, ev, a, idx, residual, out, y, sq_out);
+#define BQ_DN(F) launch_timed(k_down<BITS, I, kP3, F>, dim3(nb, T), dim3(kBlock), s, ev, a, idx, residual, out, y, sq_out)
+  return a.form == 1 ? BQ_DN(1) : a.form == 2 ? BQ_DN(2) : BQ_DN(0);
+#undef BQ_DN
 }
 
 template <int BITS, int I>

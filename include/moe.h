@@ -57,6 +57,14 @@ extern "C" {
  * it, per-token streaming is faster on MI355X for a 512-expert, top-3 layer (measured crossover). */
 #define MOE_PREFILL_MIN_TOKENS 96
 
+/* moe_layer_t.flags values, an A/B ablation of the one kernel claim on the pages ("Kernel de
+ * dequantización optimizado con FMA"). By default the decode GEMVs use the per-chunk form
+ * s * sum(q x) + b * sum(x). MOE_FLAG_DEQUANT_LITERAL computes every weight's term in the pages'
+ * form fma(q, s*x, b*x); MOE_FLAG_DEQUANT_NAIVE in the form it replaced, (q*s + b)*x. Results
+ * differ only by rounding. The prefill GEMMs ignore the flag. */
+#define MOE_FLAG_DEQUANT_LITERAL 1
+#define MOE_FLAG_DEQUANT_NAIVE 2
+
 /* One MoE layer.
  *   hidden H, inter I: powers of two with 256 <= H <= 8192 and 64 <= I <= 2048. group must be 64, bits 2 or 4.
  *   n_experts E: 1..MOE_MAX_EXPERTS. top_k K: 1..min(E, MOE_MAX_TOP_K).
@@ -64,7 +72,8 @@ extern "C" {
  *   least moe_blob_bytes(H, I, bits, group) and a multiple of 256.
  *   shared_blob_dev and shared_gate_dev: the shared expert's blob and its gate vector (bf16 [H]).
  *   Required when has_shared is 1, ignored when it is 0.
- *   router_dev: bf16 [E][H] row-major; logit e = row e . x, with no bias. */
+ *   router_dev: bf16 [E][H] row-major; logit e = row e . x, with no bias.
+ *   flags: 0, MOE_FLAG_DEQUANT_LITERAL or MOE_FLAG_DEQUANT_NAIVE (other values: MOE_EUNSUPPORTED). */
 typedef struct moe_layer_t {
   int32_t hidden;
   int32_t inter;
@@ -73,7 +82,7 @@ typedef struct moe_layer_t {
   int32_t has_shared;
   int32_t bits;
   int32_t group;
-  int32_t reserved;
+  int32_t flags;
   const void* experts_dev;
   uint64_t expert_stride;
   const void* shared_blob_dev;

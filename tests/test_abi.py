@@ -118,6 +118,8 @@ def _layer(**kw):
     (dict(expert_stride=7_077_888 + 8), bq.MOE_EINVAL),
     (dict(router=0), bq.MOE_EINVAL),
     (dict(shared_gate=FAKE + 2), bq.MOE_EINVAL),
+    (dict(flags=3), bq.MOE_EUNSUPPORTED),
+    (dict(flags=-1), bq.MOE_EUNSUPPORTED),
 ])
 def test_layer_validation(kw, code):
     layer = _layer(**kw)

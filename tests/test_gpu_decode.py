@@ -288,3 +288,29 @@ def test_bitwise_determinism(dec4):
     a, ia = _forward(L, x)
     b, ib = _forward(L, x)
     assert np.array_equal(a, b) and np.array_equal(ia, ib)
+
+
+# ---- per-element dequant forms (the pages' rewrite and the form it replaced), an A/B ablation ------
+
+@pytest.mark.parametrize("flag", ["MOE_FLAG_DEQUANT_LITERAL", "MOE_FLAG_DEQUANT_NAIVE"])
+@pytest.mark.parametrize("which,tokens", [("tiny", 4), ("dec4", 6), ("dec2", 6)])
+def test_per_element_dequant_forms_parity(which, tokens, flag, request):
+    """The decode GEMVs in the pages' fma(q, s*x, b*x) form, and in the naive (q*s + b)*x form, meet
+    the default form's bar: bit-exact routing, outputs within tolerance of the oracle, and within
+    rounding of the default form."""
+    L, ref = request.getfixturevalue(which)
+    w = L.w
+    x = _x(w, 40, tokens)
+    base_out, base_idx = _forward(L, x)
+    L.desc.flags = getattr(bq, flag)
+    try:
+        out, idx = _forward(L, x)
+    finally:
+        L.desc.flags = 0
+    xs = x.cpu().numpy()
+    for t in range(tokens):
+        r = ref.token(xs[t])
+        assert list(idx[t]) == list(r.idx) == list(base_idx[t]), f"{w.name} token {t}"
+        assert_close(out[t], r.out, f"{w.name} literal out[{t}]")
+        assert_close(out[t], base_out[t], f"{w.name} literal vs default out[{t}]")
+
