@@ -292,8 +292,7 @@ int moe_router(const moe_layer_t* layer, const float* x, int T, int32_t* idx, fl
   if (ws_bytes < needed_ws(g, T)) return fail(MOE_ENOSPC, "workspace smaller than moe_workspace_bytes()");
   const Workspace W = carve_workspace(g, T, ws);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = (T >= MOE_PREFILL_MIN_TOKENS) ? launch_router_gemm(g, ptrs_of(layer), x, T, W, s)
-                                                : launch_router_phase(g, ptrs_of(layer), x, nullptr, nullptr, 0, 0.0f, T, W, s);
+  hipError_t e = launch_router_tokens(g, ptrs_of(layer), x, T, W, s);
   if (e == hipSuccess) e = launch_topk(g, T, W, idx, w, shared_g, logits, s);
   return hip_status(e);
 }

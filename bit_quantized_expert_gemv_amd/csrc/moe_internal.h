@@ -106,6 +106,10 @@ hipError_t launch_pack(int H, int I, int bits, int G, const moe_expert_arrays_t*
 hipError_t launch_prefill(const Geometry& g, const LayerPtrs& p, const float* x, const float* residual, int T,
                           const PrefillWorkspace& w, const int32_t* idx_in, int32_t* idx_out, float* out,
                           float* y_out, hipStream_t s);
+// Router logits of T tokens into ws.logits: the fp64 MFMA GEMM for many tokens, per-token router
+// rows (phase 1) for few.
+hipError_t launch_router_tokens(const Geometry& g, const LayerPtrs& p, const float* x, int T, const Workspace& ws,
+                                hipStream_t s);
 // Router logits of T tokens as one fp64 GEMM into ws.logits.
 hipError_t launch_router_gemm(const Geometry& g, const LayerPtrs& p, const float* x, int T, const Workspace& ws,
                               hipStream_t s);

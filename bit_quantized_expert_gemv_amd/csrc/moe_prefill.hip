@@ -86,6 +86,10 @@ __global__ __launch_bounds__(kThreads) void k_prep(int H, const float* __restric
 typedef double f64x4_t __attribute__((ext_vector_type(4)));
 typedef double f64x2_t __attribute__((ext_vector_type(2)));
 constexpr int kRTok = 64, kRRow = 32, kRK = 32, kRS = kRK + 2;
+#ifndef BQ_ROUTER_GEMM_MIN
+#define BQ_ROUTER_GEMM_MIN 256
+#endif
+constexpr int kRouterGemmMinTokens = BQ_ROUTER_GEMM_MIN;
 __global__ __launch_bounds__(kThreads) void k_router_gemm(int T, int H, int E, int has_shared,
                                                           const float* __restrict__ x,
                                                           const uint16_t* __restrict__ router,
@@ -162,46 +166,66 @@ __global__ __launch_bounds__(kChunk) void k_group_hist(int N, int E, const int32
   for (int e = threadIdx.x; e < E; e += kChunk) hist[(size_t)blockIdx.x * E + e] = cnt[e];
 }
 
-// One block: per-expert prefix over chunks (in place), counts, offsets and the tile list
-// (tiles of BM entries per expert, in expert order).
+// Exclusive prefix sum of v over the block (1024 threads, wave64), in a fixed order; *total gets the
+// sum. wsum: 16 ints of LDS.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* __restrict__ wsum, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int inc = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(inc, d, 64);
+    if (lane >= d) inc += o;
+  }
+  if (lane == 63) wsum[wave] = inc;
+  __syncthreads();
+  int before = 0, all = 0;
+  for (int w = 0; w < 16; ++w) {  // 16 waves in a 1024-thread block
+    const int t = wsum[w];
+    if (w < wave) before += t;
+    all += t;
+  }
+  __syncthreads();
+  *total = all;
+  return before + inc - v;
+}
+
+// One block of 1024 threads, thread e for expert e: per-expert prefix over chunks (in place),
+// counts, offsets and the tile list (tiles of BM entries per expert, in expert order). The chunk
+// column is read eight loads at a time, and the expert scans are block-wide.
 __global__ __launch_bounds__(1024) void k_group_scan(int nchunks, int E, int BM, int32_t* __restrict__ hist,
                                                      int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                      int32_t* __restrict__ tile_e, int32_t* __restrict__ tile_first,
                                                      int32_t* __restrict__ ntiles) {
-  __shared__ int32_t s_cnt[MOE_MAX_EXPERTS];
-  __shared__ int32_t s_off[MOE_MAX_EXPERTS + 1];
-  __shared__ int32_t s_tiles[MOE_MAX_EXPERTS + 1];
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    int run = 0;
-    for (int c = 0; c < nchunks; ++c) {
-      const int v = hist[(size_t)c * E + e];
-      hist[(size_t)c * E + e] = run;
-      run += v;
+  __shared__ int wsum[16];
+  const int e = threadIdx.x;  // E <= MOE_MAX_EXPERTS == 1024 == blockDim.x
+  int run = 0;
+  if (e < E) {
+    for (int c0 = 0; c0 < nchunks; c0 += 8) {
+      int v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = (c0 + i < nchunks) ? hist[(size_t)(c0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (c0 + i < nchunks) hist[(size_t)(c0 + i) * E + e] = run;
+        run += v[i];
+      }
     }
-    s_cnt[e] = run;
     counts[e] = run;
   }
-  __syncthreads();
-  if (threadIdx.x == 0) {  // E <= 1024: a serial scan is a few microseconds at most
-    int off = 0, tiles = 0;
-    for (int e = 0; e < E; ++e) {
-      s_off[e] = off;
-      s_tiles[e] = tiles;
-      off += s_cnt[e];
-      tiles += (s_cnt[e] + BM - 1) / BM;
-    }
-    s_off[E] = off;
-    s_tiles[E] = tiles;
-    *ntiles = tiles;
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e <= E; e += blockDim.x) offsets[e] = s_off[e];
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    const int nt = (s_cnt[e] + BM - 1) / BM;
+  const int nt = (e < E) ? (run + BM - 1) / BM : 0;
+  int total_entries, total_tiles;
+  const int off = block_exclusive_scan(e < E ? run : 0, wsum, &total_entries);
+  const int t0 = block_exclusive_scan(nt, wsum, &total_tiles);
+  if (e < E) {
+    offsets[e] = off;
     for (int j = 0; j < nt; ++j) {
-      tile_e[s_tiles[e] + j] = e;
-      tile_first[s_tiles[e] + j] = s_off[e] + j * BM;
+      tile_e[t0 + j] = e;
+      tile_first[t0 + j] = off + j * BM;
     }
+  }
+  if (e == 0) {
+    offsets[E] = total_entries;
+    *ntiles = total_tiles;
   }
 }
 
@@ -640,6 +664,13 @@ hipError_t launch_router_gemm(const Geometry& g, const LayerPtrs& p, const float
   return hipGetLastError();
 }
 
+hipError_t launch_router_tokens(const Geometry& g, const LayerPtrs& p, const float* x, int T, const Workspace& ws,
+                                hipStream_t s) {
+  // the fp64 GEMM fills the chip only for many tokens; below that, per-token router rows win
+  if (T >= kRouterGemmMinTokens) return launch_router_gemm(g, p, x, T, ws, s);
+  return launch_router_phase(g, p, x, nullptr, nullptr, 0, 0.0f, T, ws, s);
+}
+
 hipError_t launch_prefill(const Geometry& g, const LayerPtrs& p, const float* x, const float* residual, int T,
                           const PrefillWorkspace& w, const int32_t* idx_in, int32_t* idx_out, float* out,
                           float* y_out, hipStream_t s) {
@@ -649,7 +680,8 @@ hipError_t launch_prefill(const Geometry& g, const LayerPtrs& p, const float* x,
   hipLaunchKernelGGL(k_prep, dim3(T), dim3(kThreads), 0, s, H, x, reinterpret_cast<_Float16*>(w.xq), w.xs);
   const int32_t* idx = idx_in;
   if (idx_in == nullptr) {
-    hipError_t e = launch_router_gemm(g, p, x, T, w.layer, s);
+    // the fp64 GEMM fills the chip only for many tokens; below that, per-token router rows win
+    hipError_t e = launch_router_tokens(g, p, x, T, w.layer, s);
     if (e == hipSuccess) e = launch_topk(g, T, w.layer, w.layer.idx, w.layer.w, w.layer.g, nullptr, s);
     if (e != hipSuccess) return e;
     idx = w.layer.idx;
