@@ -32,6 +32,7 @@
 // MFMAs m = 0..3 with codes 8m..8m+7. Lanes 32..63 hold the other half of the same group, so every
 // MFMA stays inside one scale group, and the activation operand is read in the same k order.
 #include <hip/hip_runtime.h>
+#include <type_traits>
 
 #include <algorithm>
 #include <cmath>
@@ -304,19 +305,28 @@ __device__ __forceinline__ f16x8_t codes_f16(uint32_t w, int half) {
   return f16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
-// Per-lane registers of U groups of weights: codes and (scale, bias) words.
-template <int BITS, int NTILE, int U>
-struct GStage {
-  static constexpr int CW = BITS == 4 ? 4 : 2;  // code dwords per lane per group
-  uint32_t c[U][NTILE][CW];
-  uint32_t sb[U][NTILE];
+// Per-lane registers of one pipeline step: NI 16-byte code loads per row block (see k_grouped), the
+// (scale, bias) words of a step pair, and the tile's activations.
+template <int NI>
+struct GCodes {
+  u32x4_t v[2][NI];  // [row block][load]
+};
+struct GWords {
+  uint32_t w[4];
+};
+struct GWordsX {
+  uint32_t w[2][2][4];  // [step of the pair][row block][group of the step]
+};
+template <int U>
+struct GAct {
+  u32x4_t v[U];
 };
 
 #ifndef BQ_LB_GU
-#define BQ_LB_GU 3
+#define BQ_LB_GU 2
 #endif
 #ifndef BQ_LB_DOWN
-#define BQ_LB_DOWN 3
+#define BQ_LB_DOWN 2
 #endif
 #ifndef BQ_GROUP_SCHED_BARRIER
 #define BQ_GROUP_SCHED_BARRIER 1
@@ -324,49 +334,66 @@ struct GStage {
 #ifndef BQ_U_LINE
 #define BQ_U_LINE 1
 #endif
-#ifndef BQ_ST_GU
-#define BQ_ST_GU 2
-#endif
-#ifndef BQ_ST_DOWN
-#define BQ_ST_DOWN 2
-#endif
-// Groups per pipeline step (by default one 128-byte line of every row: 4 groups at 4-bit, 8 at
-// 2-bit, so that no line is fetched twice) and weight stages in flight + 1.
-// Block: 4 waves, one tile of up to 32 token rows, all rows of the weight matrices. Each wave owns
-// one 32-row tile of one matrix in every slab: for down, waves 0..3 take rows 32w..32w+31 of a
-// 128-row slab; for gate/up, waves 0, 1 take 32-row tiles of gate and waves 2, 3 the same rows of
-// up, in a 64-row slab, and the SwiGLU pairs meet through LDS at the end of the slab. One tile
-// per wave keeps a wave's registers low enough for three waves per SIMD. The block walks the
-// slabs one after the other, and the pipeline runs over the flattened (slab, step) sequence, so
-// it fills once per block rather than once per slab; there are about as many blocks as tiles.
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// 8-element block of group G that K slice q of MFMA half h reads (the codes' order after the lane
+// swaps of k_grouped; the activations are read in the same order)
+template <int BITS>
+__device__ __forceinline__ int kblock(int q, int h) {
+  return BITS == 4 ? 4 * (q & 1) + 2 * (q >> 1) + h : 2 * q + h;
+}
+
+// Block: 4 waves, one tile of up to 32 tokens, all rows of the weight matrices. Each wave owns 32
+// rows (two 16-row blocks) of one matrix in every slab: for down, waves 0..3 take rows 32w..32w+31
+// of a 128-row slab; for gate/up, waves 0, 1 take 32 rows of gate and waves 2, 3 the same rows of
+// up, in a 64-row slab, and the SwiGLU pairs meet through LDS at the end of the slab. The block
+// walks the slabs one after the other, and the pipeline runs over the flattened (slab, step)
+// sequence, so it fills once per block rather than once per slab.
 //
-// Pipeline, per step of U groups: the tile's activations for the next step are loaded (16 bytes
-// per thread and group), then each wave's weights for the step STAGES-1 ahead; this step is
-// computed from registers (weights) and an LDS ring (activations); the next step's activations are
-// parked in the ring and one barrier closes the step. Loads retire in order, so the activations are
-// requested before the weights: waiting for them never waits for the weights in flight.
-template <int BITS, int KDIM, int UMAX, int STAGES, bool GATEUP, bool SHARED>
-__global__ __launch_bounds__(kThreads, GATEUP ? BQ_LB_GU : BQ_LB_DOWN) void k_grouped(GroupArgs g) {
+// Arithmetic on v_mfma_f32_16x16x32_f16 (A = 16 tokens x 32 k, B = 32 k x 16 rows; lane l holds
+// k slice l/16 of token / row l%16): the tile is one or two halves of 16 tokens, so a tile of at
+// most 16 tokens (most routed tiles) costs half the matrix work and half the epilogue. The codes
+// of one MFMA must lie in one group (one scale): a lane loads 16 contiguous bytes of its row, and
+// lane swaps regroup them (4-bit: two groups per load, the lower 32 lanes and the upper 32 lanes
+// exchange half their dwords; 2-bit: four groups per load, a 4 x 4 transpose over the four 16-lane
+// rows). The bias term sum_g bias[r][g] * S[t][g] runs as an fp32 16x16x4 MFMA per row block and
+// step (A = group sums S, B = biases), so the vector ALUs only apply the scales.
+//
+// Pipeline, per step s of U groups: the tile's activations for step s+2 are loaded into one of
+// two register sets (16 bytes per thread and group), then the wave's codes for step s+2, and on
+// even steps the (scale, bias) words of steps s+2 and s+3; step s is computed from registers
+// (weights) and an LDS ring (activations); the activations of step s+1, loaded a step earlier,
+// are parked in the ring and one barrier closes the step. Every load has two steps to land
+// before it is waited for.
+template <int BITS, int KDIM, int UMAX, bool GATEUP, bool SHARED>
+__global__ __launch_bounds__(kThreads, GATEUP ? BQ_LB_GU : BQ_LB_DOWN) void k_grouped(GroupArgs g, int sgroups) {
   constexpr int NG = KDIM / 64;
   constexpr int U = NG >= UMAX ? UMAX : NG;  // groups per pipeline step
+  static_assert(U <= 4, "a step holds at most four groups");
   constexpr int NSTEP = NG / U;               // steps per slab
   constexpr int ROWB = KDIM * BITS / 8;
-  constexpr int GB = 64 * BITS / 8;  // code bytes per row and group
-  constexpr int LB = GB / 2;         // per lane half
-  constexpr int ROWS_B = GATEUP ? 64 : 128;  // rows per matrix per slab
-  constexpr int AS = U * 8;          // 16-byte activation slots per row and step
-  constexpr int ASW = AS >= 16 ? 15 : AS - 1;  // slot swizzle: 16 consecutive rows hit distinct banks
-  using Stage = GStage<BITS, 1, U>;
+  constexpr int GB = 64 * BITS / 8;           // code bytes per row and group
+  constexpr int NI = (U * GB + 63) / 64;      // 16-byte code loads per lane, row block and step
+  constexpr int ROWS_B = GATEUP ? 64 : 128;   // rows per matrix per slab
+  constexpr int AS = U * 8;                   // 16-byte activation slots per row and step
+  constexpr int ASW = AS >= 16 ? 15 : AS - 1; // slot swizzle: 16 consecutive rows hit distinct banks
+  using Codes = GCodes<NI>;
+  using Act = GAct<U>;
   __shared__ float s_lds[NG * kTileM];             // group sums of the tile's activations, [group][row]
   __shared__ u32x4_t a_lds[2][kTileM * AS];        // activation ring: [step parity][row][slot ^ swizzle]
   __shared__ float x_lds[GATEUP ? 2 : 1][16][64];  // gate/up: gate results handed to the up waves
   __shared__ float h_lds[GATEUP ? 2 : 1][kTileM];  // gate/up: per-wave sums of the fp16 SwiGLU outputs
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int j = lane & 31, hk = lane >> 5;
+  const int c16 = lane & 15, q = lane >> 4;        // MFMA lane: token / row within 16, k slice
   const int mi = GATEUP ? (wave >> 1) : 0;         // matrix of this wave (gate 0, up 1)
   const int wrow = (GATEUP ? (wave & 1) : wave) * 32;  // first row of this wave in a slab
-  const int tau = blockIdx.x;
+  // Block b works on tile tau, slab group gy. Blocks go to the 8 XCDs round-robin, so a run of
+  // 8 * sgroups consecutive blocks holds 8 tiles, one per XCD, each with all its slab groups on that
+  // XCD: they start together and stream the same activation rows, which then come from its L2.
+  const int b8 = 8 * sgroups;
+  const int tau = (int)(blockIdx.x / b8) * 8 + (int)(blockIdx.x & 7);
+  const int gy = (int)(blockIdx.x % b8) >> 3;
   int first, count;
   const uint8_t* blob;
   if constexpr (SHARED) {
@@ -381,6 +408,7 @@ __global__ __launch_bounds__(kThreads, GATEUP ? BQ_LB_GU : BQ_LB_DOWN) void k_gr
     count = min(kTileM, g.offsets[e + 1] - first);
     blob = g.experts + (size_t)e * g.stride;
   }
+  const int nh = count > 16 ? 2 : 1;  // token halves (uniform per block)
   // activation row of token slot m (clamped into the tile) and output row
   auto arow = [&](int m) -> int {
     const int mm = first + min(m, count - 1);
@@ -396,123 +424,213 @@ __global__ __launch_bounds__(kThreads, GATEUP ? BQ_LB_GU : BQ_LB_DOWN) void k_gr
   // this thread's 16-byte activation slot: row tid/8, slot tid%8 of every group
   const int a_row = tid >> 3, a_slot = tid & 7;
   const u32x4_t* a_src = reinterpret_cast<const u32x4_t*>(g.a + (size_t)arow(a_row) * KDIM) + a_slot;
-  u32x4_t a_reg[U];
-  auto load_act = [&](int s) {  // s: flattened step; the activations depend on its step in the slab only
+  auto load_act = [&](Act& r, int s) {  // s: flattened step; the activations depend on its step in the slab only
     const int k = s % NSTEP;
 #pragma unroll
-    for (int u = 0; u < U; ++u) a_reg[u] = a_src[(k * U + u) * 8];
+    for (int u = 0; u < U; ++u) r.v[u] = a_src[(k * U + u) * 8];
   };
-  auto park_act = [&](int s) {
+  auto park_act = [&](const Act& r, int s) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) a_lds[s & 1][a_row * AS + ((u * 8 + a_slot) ^ (a_row & ASW))] = a_reg[u];
+    for (int u = 0; u < U; ++u) a_lds[s & 1][a_row * AS + ((u * 8 + a_slot) ^ (a_row & ASW))] = r.v[u];
   };
 
-  // this block's slabs: blockIdx.y of gridDim.y equal ranges (more blocks when there are few tiles)
+  // this block's slabs: range gy of sgroups equal ranges
   const int nslab = (g.nout + ROWS_B - 1) / ROWS_B;
-  const int spb = (nslab + gridDim.y - 1) / gridDim.y;
-  const int slab0 = blockIdx.y * spb;
+  const int spb = (nslab + sgroups - 1) / sgroups;
+  const int slab0 = gy * spb;
   const int ntot = (min(nslab, slab0 + spb) - slab0) * NSTEP;  // flattened steps
   if (ntot <= 0) return;  // uniform per block
   // Weights through buffer loads: a descriptor per section (scalar registers), a 32-bit lane
-  // offset, and the step's group offset as a scalar. Rows past nout are clamped.
+  // offset, and the step's offset as a scalar. Rows past nout are clamped; so are steps past the
+  // end (they re-read the last step, from cache): every load is issued on every path, because a
+  // load skipped on some path would make the compiler's wait counts conservative and drain the
+  // loads in flight. A load that runs past a row (U below 4) reads bytes that are never used, or
+  // zeros past the end of the section.
   const __amdgpu_buffer_rsrc_t crs =
       __builtin_amdgcn_make_buffer_rsrc((void*)(blob + g.off_codes[mi]), (short)0, g.nout * ROWB, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t srs =
       __builtin_amdgcn_make_buffer_rsrc((void*)(blob + g.off_sb[mi]), (short)0, g.nout * NG * 4, kRsrcWord3);
-  // unconditional (past the end, a clamped step is re-read): a load skipped on some path would
-  // make the compiler's wait counts conservative and drain the prefetch
-  auto load_w = [&](Stage& st, int s) {
+  // codes: lane (c16, q) reads 16 bytes at byte 16q of each 64-byte span of its row's step
+  auto load_codes = [&](Codes& st, int s) {
     const int slab = slab0 + s / NSTEP, k = s % NSTEP;
-    const int row = min(slab * ROWS_B + wrow + j, g.nout - 1);
-    const int voff = row * ROWB + hk * LB;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if constexpr (BITS == 4) {
-        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(crs, voff, (k * U + u) * GB, 0);
-        st.c[u][0][0] = v[0]; st.c[u][0][1] = v[1]; st.c[u][0][2] = v[2]; st.c[u][0][3] = v[3];
-      } else {
-        const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(crs, voff, (k * U + u) * GB, 0);
-        st.c[u][0][0] = v[0]; st.c[u][0][1] = v[1];
-      }
+    for (int rb = 0; rb < 2; ++rb) {
+      const int row = min(slab * ROWS_B + wrow + 16 * rb + c16, g.nout - 1);
+      const int voff = row * ROWB + 16 * q;
+#pragma unroll
+      for (int c = 0; c < NI; ++c) st.v[rb][c] = __builtin_amdgcn_raw_buffer_load_b128(crs, voff, k * U * GB + 64 * c, 0);
     }
-    const int soff = row * (NG * 4);
+  };
+  // (scale, bias) words of steps 2p and 2p+1: the 16-lane row q loads those of row block q & 1 and
+  // step 2p + q/2 (4 groups), so one instruction serves two steps; split_words then gives every
+  // lane both row blocks' words of both steps.
+  auto load_words = [&](GWords& r, int p) {
+    const int t = min(2 * p + (q >> 1), ntot - 1);
+    const int slab = slab0 + t / NSTEP, k = t % NSTEP;
+    const int row = min(slab * ROWS_B + wrow + 16 * (q & 1) + c16, g.nout - 1);
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(srs, row * (NG * 4) + k * U * 4, 0, 0);
+    r.w[0] = v[0]; r.w[1] = v[1]; r.w[2] = v[2]; r.w[3] = v[3];
+  };
+  auto split_words = [&](const GWords& r, GWordsX& x) {
 #pragma unroll
-    for (int u4 = 0; u4 < U; u4 += 4) {
-      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(srs, soff, (k * U + u4) * 4, 0);
-#pragma unroll
-      for (int q = 0; q < 4 && u4 + q < U; ++q) st.sb[u4 + q][0] = v[q];
+    for (int u = 0; u < 4; ++u) {
+      // 16-lane rows [0,0,2,2] (row block 0) and [1,1,3,3] (row block 1), then halves
+      const auto a = __builtin_amdgcn_permlane16_swap(r.w[u], r.w[u], false, false);
+      const auto b0 = __builtin_amdgcn_permlane32_swap(a[0], a[0], false, false);
+      const auto b1 = __builtin_amdgcn_permlane32_swap(a[1], a[1], false, false);
+      x.w[0][0][u] = b0[0]; x.w[1][0][u] = b0[1];
+      x.w[0][1][u] = b1[0]; x.w[1][1][u] = b1[1];
     }
   };
 
-  f32x16_t acc;
+  f32x4_t acc[2][2], accb[2][2];  // [token half][row block]: scaled code sums; bias terms
 #pragma unroll
-  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+  for (int th = 0; th < 2; ++th)
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[th][rb][e] = accb[th][rb][e] = 0.0f;
 
-  auto compute = [&](const Stage& st, int s) {
+  auto a_frag = [&](int s, int th, int G, int h) __attribute__((always_inline)) {
+    const int row = 16 * th + c16;
+    return __builtin_bit_cast(f16x8_t, a_lds[s & 1][row * AS + ((G * 8 + kblock<BITS>(q, h)) ^ (row & ASW))]);
+  };
+  // One step: regroup the codes, then per group the MFMAs of every token half and row block and the
+  // scale epilogue; the bias MFMAs first.
+  auto compute = [&](Codes& st, const uint32_t (&sw)[2][4], int s) __attribute__((always_inline)) {
     const int k = s % NSTEP;
+    // bias terms: A = S[token][group k*U + q], B = bias[row][group k*U + q] (K = the step's groups)
+    {
+      // lane row q takes word q of its row block: two 16-lane swaps give rows [w0, w1, w0, w1] and
+      // [w2, w3, w2, w3], a 32-lane swap joins their halves
+      uint32_t bw[2];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int gi = k * U + u;
-      f32x16_t d;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) d[v] = 0.0f;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const f16x8_t af = __builtin_bit_cast(f16x8_t, a_lds[s & 1][j * AS + ((u * 8 + 4 * hk + m) ^ (j & ASW))]);
-        const uint32_t w = BITS == 4 ? st.c[u][0][m] : st.c[u][0][m >> 1];
-        d = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, codes_f16<BITS>(w, m & 1), d, 0, 0, 0);
+      for (int rb = 0; rb < 2; ++rb) {
+        const auto t01 = __builtin_amdgcn_permlane16_swap(sw[rb][0], sw[rb][1], false, false);
+        const auto t23 = __builtin_amdgcn_permlane16_swap(sw[rb][2], sw[rb][3], false, false);
+        bw[rb] = __builtin_amdgcn_permlane32_swap(t01[0], t23[0], false, false)[0];
       }
-      const uint32_t p = st.sb[u][0];
-      const float sc = bf16_val((uint16_t)(p & 0xFFFFu)), bi = bf16_val((uint16_t)(p >> 16));
-      // group sums of this lane's 16 token rows: rows 8a + 4*hk + b for element 4a + b
 #pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4) {
-        const float4 S = *reinterpret_cast<const float4*>(&s_lds[gi * kTileM + 8 * a4 + 4 * hk]);
-        acc[4 * a4 + 0] = fmaf(sc, d[4 * a4 + 0], fmaf(bi, S.x, acc[4 * a4 + 0]));
-        acc[4 * a4 + 1] = fmaf(sc, d[4 * a4 + 1], fmaf(bi, S.y, acc[4 * a4 + 1]));
-        acc[4 * a4 + 2] = fmaf(sc, d[4 * a4 + 2], fmaf(bi, S.z, acc[4 * a4 + 2]));
-        acc[4 * a4 + 3] = fmaf(sc, d[4 * a4 + 3], fmaf(bi, S.w, acc[4 * a4 + 3]));
+      for (int th = 0; th < 2; ++th) {
+        if (th < nh) {
+          const float a = q < U ? s_lds[(k * U + q) * kTileM + 16 * th + c16] : 0.0f;
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) {
+            const float b = q < U ? __builtin_bit_cast(float, bw[rb] & 0xFFFF0000u) : 0.0f;
+            accb[th][rb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, accb[th][rb], 0, 0, 0);
+          }
+        }
+      }
+    }
+    // B dwords per row block, group and MFMA half
+    uint32_t bd[2][4][2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      if constexpr (BITS == 4) {
+#pragma unroll
+        for (int c = 0; c < NI; ++c) {
+          const u32x4_t v = st.v[rb][c];
+          const auto p = __builtin_amdgcn_permlane32_swap(v[0], v[2], false, false);
+          const auto r = __builtin_amdgcn_permlane32_swap(v[1], v[3], false, false);
+          bd[rb][2 * c][0] = p[0]; bd[rb][2 * c + 1][0] = p[1];
+          bd[rb][2 * c][1] = r[0]; bd[rb][2 * c + 1][1] = r[1];
+        }
+      } else {
+        const u32x4_t v = st.v[rb][0];
+        const auto x02 = __builtin_amdgcn_permlane32_swap(v[0], v[2], false, false);
+        const auto x13 = __builtin_amdgcn_permlane32_swap(v[1], v[3], false, false);
+        const auto y01 = __builtin_amdgcn_permlane16_swap(x02[0], x13[0], false, false);
+        const auto y23 = __builtin_amdgcn_permlane16_swap(x02[1], x13[1], false, false);
+        const uint32_t t4[4] = {y01[0], y01[1], y23[0], y23[1]};
+#pragma unroll
+        for (int G = 0; G < 4; ++G) bd[rb][G][0] = bd[rb][G][1] = t4[G];
+      }
+    }
+#pragma unroll
+    for (int G = 0; G < U; ++G) {
+      f16x8_t b[2][2];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) b[rb][h] = codes_f16<BITS>(bd[rb][G][h], h);
+      float sc[2];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) sc[rb] = bf16_val((uint16_t)(sw[rb][G] & 0xFFFFu));
+#pragma unroll
+      for (int th = 0; th < 2; ++th) {
+        if (th < nh) {
+          const f16x8_t a0 = a_frag(s, th, G, 0), a1 = a_frag(s, th, G, 1);
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) {
+            f32x4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
+            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b[rb][0], d, 0, 0, 0);
+            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b[rb][1], d, 0, 0, 0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[th][rb][e] = fmaf(sc[rb], d[e], acc[th][rb][e]);
+          }
+        }
       }
 #if BQ_GROUP_SCHED_BARRIER
-      // one group at a time: stops the scheduler from widening every group of the step up front,
-      // which would cost the registers of a third wave per SIMD
+      // one group at a time: keeps the scheduler from widening every group of the step up front
       __builtin_amdgcn_sched_barrier(0);
 #endif
     }
   };
 
-  // End of a slab: write its outputs and clear the accumulators. Element v of acc holds token row
-  // 8*(v/4) + 4*hk + v%4 and weight row slab*ROWS_B + wrow + j. (Block-uniform; holds barriers.)
-  auto finish_slab = [&](int slab) {
-    const int row = slab * ROWS_B + wrow + j;
+  // End of a slab: write its outputs and clear the accumulators. Element e of acc[th][rb] holds
+  // token 16*th + 4*q + e and weight row slab*ROWS_B + wrow + 16*rb + c16. (Block-uniform; holds
+  // barriers.)
+  auto finish_slab = [&](int slab) __attribute__((always_inline)) {
+#pragma unroll
+    for (int th = 0; th < 2; ++th)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[th][rb][e] += accb[th][rb][e];
+          accb[th][rb][e] = 0.0f;
+        }
     if constexpr (GATEUP) {
       // the gate waves hand their results to the up waves that hold the same rows
       if (mi == 0) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) x_lds[wave][v][lane] = acc[v];
+        for (int th = 0; th < 2; ++th)
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x_lds[wave][8 * th + 4 * rb + e][lane] = acc[th][rb][e];
       }
       __syncthreads();
       if (mi == 1) {
         const bool active = slab * ROWS_B + wrow < g.nout;  // wave-uniform
-        float part[16];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int m = 8 * (v >> 2) + 4 * hk + (v & 3);
-          const float a = x_lds[wave - 2][v][lane], c = acc[v];
-          const _Float16 h = (_Float16)(a / (1.0f + expf(-a)) * c);
-          if (active && m < count) g.oh[(size_t)orow(m) * g.nout + (row & ~7) + perm8(row & 7)] = h;
-          part[v] = active ? (float)h : 0.0f;
-        }
-        // sum over the 32 rows of this wave (the 32 lanes of each half), then over the two up waves:
-        // the slab's 64 rows are one group of the down projection's input
+        for (int th = 0; th < 2; ++th) {
+          float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+          if (th < nh) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
+            for (int rb = 0; rb < 2; ++rb) {
+              const int row = slab * ROWS_B + wrow + 16 * rb + c16;
 #pragma unroll
-          for (int msk = 16; msk >= 1; msk >>= 1) part[v] += __shfl_xor(part[v], msk, 32);
-        }
-        if (j == 0) {
+              for (int e = 0; e < 4; ++e) {
+                const int m = 16 * th + 4 * q + e;
+                const float a = x_lds[wave - 2][8 * th + 4 * rb + e][lane], c = acc[th][rb][e];
+                const _Float16 h = (_Float16)(a / (1.0f + expf(-a)) * c);
+                if (active && m < count) g.oh[(size_t)orow(m) * g.nout + (row & ~7) + perm8(row & 7)] = h;
+                part[e] += active ? (float)h : 0.0f;
+              }
+            }
+          }
+          // sum over the 32 rows of this wave (2 row blocks in-lane, 16 lanes), then over the two up
+          // waves: the slab's 64 rows are one group of the down projection's input
 #pragma unroll
-          for (int v = 0; v < 16; ++v) h_lds[wave - 2][8 * (v >> 2) + 4 * hk + (v & 3)] = part[v];
+          for (int e = 0; e < 4; ++e) {
+#pragma unroll
+            for (int msk = 8; msk >= 1; msk >>= 1) part[e] += __shfl_xor(part[e], msk, 16);
+          }
+          if (c16 == 0) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) h_lds[wave - 2][16 * th + 4 * q + e] = part[e];
+          }
         }
       }
       __syncthreads();
@@ -520,54 +638,73 @@ __global__ __launch_bounds__(kThreads, GATEUP ? BQ_LB_GU : BQ_LB_DOWN) void k_gr
       if (tid < kTileM && tid < count && col0 < g.nout)
         g.os[(size_t)orow(tid) * (g.nout / 64) + col0 / 64] = h_lds[0][tid] + h_lds[1][tid];
     } else {
-      if (row < g.nout) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int m = 8 * (v >> 2) + 4 * hk + (v & 3);
-          if (m < count) g.oy[(size_t)orow(m) * g.nout + row] = acc[v];
+      for (int rb = 0; rb < 2; ++rb) {
+        const int row = slab * ROWS_B + wrow + 16 * rb + c16;
+        if (row < g.nout) {
+#pragma unroll
+          for (int th = 0; th < 2; ++th)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int m = 16 * th + 4 * q + e;
+              if (m < count) g.oy[(size_t)orow(m) * g.nout + row] = acc[th][rb][e];
+            }
         }
       }
     }
 #pragma unroll
-    for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+    for (int th = 0; th < 2; ++th)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[th][rb][e] = 0.0f;
   };
 
-  // STAGES weight stages in a ring: step s computes stage s % STAGES while the next STAGES - 1
-  // steps' loads are in flight. The activations of step s+1 are requested before the weights of
-  // step s + STAGES - 1, so parking them at the end of step s waits only for loads that step s+1
-  // needs anyway. Every load is issued on every path (past the end it re-reads the last step, from
-  // cache), so that the compiler's wait counts stay exact and never drain the loads in flight.
-  auto body = [&](const Stage& cur, Stage& ahead, int s) {
-    load_act(min(s + 1, ntot - 1));
-    load_w(ahead, min(s + STAGES - 1, ntot - 1));
-    if (s < ntot) {
-      compute(cur, s);
+  // Three code stages (step s computes stage s % 3 while the next two are in flight), two
+  // activation register sets (step s loads set s % 2 with the activations of step s + 2 and parks
+  // the other set, which holds step s + 1), and the (scale, bias) words of a step pair: wp is
+  // loaded two steps ahead and split at the pair's first step into wx. The steps run in an
+  // unrolled period of 6 so that every register set has a fixed name. Past the end a step re-reads
+  // the last one, so every path issues the same loads.
+  Codes c0, c1, c2;
+  Act a0, a1;
+  GWords wp;
+  GWordsX wx;
+  auto body = [&](auto ci, auto ai, int s) __attribute__((always_inline)) {
+    constexpr int CI = decltype(ci)::value, AI = decltype(ai)::value;
+    Codes& cur = CI == 0 ? c0 : (CI == 1 ? c1 : c2);
+    Codes& ahead = CI == 0 ? c2 : (CI == 1 ? c0 : c1);  // stage (s + 2) % 3
+    Act& aload = AI == 0 ? a0 : a1;
+    Act& apark = AI == 0 ? a1 : a0;
+    if constexpr (AI == 0) split_words(wp, wx);
+    load_act(aload, min(s + 2, ntot - 1));
+    load_codes(ahead, min(s + 2, ntot - 1));
+    if constexpr (AI == 0) load_words(wp, s / 2 + 1);
+    if (s < ntot) {  // uniform per block
+      compute(cur, wx.w[AI], s);
       if (s % NSTEP == NSTEP - 1) finish_slab(slab0 + s / NSTEP);
     }
-    park_act(s + 1);
+    park_act(apark, s + 1);
     __syncthreads();
   };
-  Stage s0, s1;
-  load_act(0);
-  load_w(s0, 0);
-  park_act(0);
-  if constexpr (STAGES == 2) {
-    __syncthreads();
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  load_act(a0, 0);
+  load_act(a1, min(1, ntot - 1));
+  load_codes(c0, 0);
+  load_words(wp, 0);
+  load_codes(c1, min(1, ntot - 1));
+  park_act(a0, 0);
+  __syncthreads();
 #pragma unroll 1
-    for (int s = 0; s < ntot; s += 2) {
-      body(s0, s1, s);
-      body(s1, s0, s + 1);
-    }
-  } else {
-    Stage s2;
-    load_w(s1, min(1, ntot - 1));
-    __syncthreads();
-#pragma unroll 1
-    for (int s = 0; s < ntot; s += 3) {
-      body(s0, s2, s);
-      body(s1, s0, s + 1);
-      body(s2, s1, s + 2);
-    }
+  for (int s = 0; s < ntot; s += 6) {
+    body(I0{}, I0{}, s);
+    body(I1{}, I1{}, s + 1);
+    body(I2{}, I0{}, s + 2);
+    body(I0{}, I1{}, s + 3);
+    body(I1{}, I0{}, s + 4);
+    body(I2{}, I1{}, s + 5);
   }
 }
 
@@ -602,32 +739,36 @@ __global__ void k_copy_i32(int n, const int32_t* __restrict__ src, int32_t* __re
 
 unsigned cdiv(long long a, long long b) { return (unsigned)((a + b - 1) / b); }
 
-constexpr int kStGateUp = BQ_ST_GU;
-constexpr int kStDown = BQ_ST_DOWN;
 template <int BITS>
-constexpr int kULine = BQ_U_LINE * (BITS == 4 ? 4 : 8);
+constexpr int kULine = BQ_U_LINE * 4;
 
-// Blocks: one per tile, times enough slab groups that a launch has about 1024 working blocks when
-// tiles are few (the shared expert's 64 tiles at 2048 tokens; small batches). `tiles` is the number
-// expected to hold tokens: for the routed experts at most one per routed entry.
-unsigned slab_groups(int tiles, int nout, int rows_per_slab) {
+#ifndef BQ_GROUP_TARGET
+#define BQ_GROUP_TARGET 1024
+#endif
+// Blocks: one per tile, times enough slab groups that a launch has about BQ_GROUP_TARGET working
+// blocks when tiles are few (the shared expert's 64 tiles at 2048 tokens; small batches). `tiles`
+// is the number expected to hold tokens: for the routed experts at most one per routed entry.
+int slab_groups(int tiles, int nout, int rows_per_slab) {
   const int nslab = (nout + rows_per_slab - 1) / rows_per_slab;
-  return (unsigned)std::max(1, std::min(nslab, 1024 / std::max(1, tiles)));
+  return std::max(1, std::min(nslab, BQ_GROUP_TARGET / std::max(1, tiles)));
 }
+// 1-D grid for `tiles` tile slots with `sg` slab groups each, in runs of 8 tiles (see k_grouped).
+unsigned grouped_grid(int tiles, int sg) { return cdiv(tiles, 8) * 8u * (unsigned)sg; }
 
 template <int BITS, int KDIM, bool GATEUP>
 hipError_t launch_grouped(const GroupArgs& ga, int nout, int T, int N, int E, bool has_shared, hipStream_t s) {
   constexpr int UM = kULine<BITS>;
-  constexpr int ST = GATEUP ? kStGateUp : kStDown;
   constexpr int RS = GATEUP ? 64 : 128;  // rows per matrix per slab
   const dim3 block(kThreads);
   const int max_tiles = E + (int)cdiv(N, kTileM);
-  hipLaunchKernelGGL((k_grouped<BITS, KDIM, UM, ST, GATEUP, false>),
-                     dim3(max_tiles, slab_groups(std::min(max_tiles, N), nout, RS)), block, 0, s, ga);
+  const int rg = slab_groups(std::min(max_tiles, N), nout, RS);
+  hipLaunchKernelGGL((k_grouped<BITS, KDIM, UM, GATEUP, false>), dim3(grouped_grid(max_tiles, rg)), block, 0, s,
+                     ga, rg);
   if (has_shared) {
     const int st = (int)cdiv(T, kTileM);
-    hipLaunchKernelGGL((k_grouped<BITS, KDIM, UM, ST, GATEUP, true>), dim3(st, slab_groups(st, nout, RS)), block, 0,
-                       s, ga);
+    const int sg = slab_groups(st, nout, RS);
+    hipLaunchKernelGGL((k_grouped<BITS, KDIM, UM, GATEUP, true>), dim3(grouped_grid(st, sg)), block, 0, s, ga,
+                       sg);
   }
   return hipGetLastError();
 }
