@@ -5,6 +5,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "moe.h"
@@ -88,11 +89,12 @@ bool geometry_from(const moe_layer_t* L, Geometry* g, const char** why) {
     return false;
   }
   if (L->has_shared != 0 && L->has_shared != 1) { *why = "has_shared must be 0 or 1"; return false; }
-  if (L->flags != 0 && L->flags != MOE_FLAG_DEQUANT_LITERAL && L->flags != MOE_FLAG_DEQUANT_NAIVE) {
-    *why = "flags must be 0, MOE_FLAG_DEQUANT_LITERAL or MOE_FLAG_DEQUANT_NAIVE";
+  const int form = L->flags & ~MOE_FLAG_PREFETCH_NEXT;
+  if (form != 0 && form != MOE_FLAG_DEQUANT_LITERAL && form != MOE_FLAG_DEQUANT_NAIVE) {
+    *why = "flags must be 0, MOE_FLAG_DEQUANT_LITERAL or MOE_FLAG_DEQUANT_NAIVE, optionally with MOE_FLAG_PREFETCH_NEXT";
     return false;
   }
-  g->form = L->flags == MOE_FLAG_DEQUANT_LITERAL ? 1 : L->flags == MOE_FLAG_DEQUANT_NAIVE ? 2 : 0;
+  g->form = form == MOE_FLAG_DEQUANT_LITERAL ? 1 : form == MOE_FLAG_DEQUANT_NAIVE ? 2 : 0;
   g->H = L->hidden; g->I = L->inter; g->E = L->n_experts; g->K = L->top_k;
   g->has_shared = L->has_shared; g->NE = g->K + g->has_shared;
   g->bits = L->bits; g->G = L->group;
@@ -378,6 +380,44 @@ int moe_layer_forward_timed(const moe_layer_t* layer, const float* x, const floa
   return hip_status(e);
 }
 
+}  // extern "C"
+
+namespace bqmoe {
+namespace {
+// The side stream of the cross-layer prefetch, one per device, created on first use and kept until
+// the process ends, with the event that forks it off the caller's stream.
+constexpr int kMaxDevices = 64;
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+SideStream g_side[kMaxDevices];
+std::mutex g_side_mu;
+
+hipError_t side_stream(SideStream** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  SideStream& ss = g_side[dev];
+  if (ss.s == nullptr) {
+    if ((e = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming)) != hipSuccess) return e;
+  }
+  *out = &ss;
+  return hipSuccess;
+}
+}  // namespace
+}  // namespace bqmoe
+
+using namespace bqmoe;
+extern "C" {
+
+#ifndef BQ_PREFETCH_BLOCKS
+#define BQ_PREFETCH_BLOCKS 64
+#endif
 int moe_stack_forward(const moe_layer_t* layers, int L, float eps, const float* x, int T, float* out,
                       int32_t* idx_out, void* ws, size_t ws_bytes, void* stream) {
   if (layers == nullptr || L < 1) return fail(MOE_EINVAL, "layers must be non-NULL and L >= 1");
@@ -407,8 +447,23 @@ int moe_stack_forward(const moe_layer_t* layers, int L, float eps, const float* 
   const int nsq = down_blocks(g);
   if (nsq < 1 || nsq > max_norm_partials()) return fail(MOE_EUNSUPPORTED, "layer shape has too many down blocks");
   hipError_t e = hipSuccess;
+  // Cross-layer prefetch: at the start of layer l, a side stream forked off the caller's stream reads
+  // layer l+1's router and shared expert; it runs beside layer l's kernels and joins the caller's
+  // stream once, after the last layer.
+  SideStream* side = nullptr;
+  const bool prefetch = (layers[0].flags & MOE_FLAG_PREFETCH_NEXT) != 0 && L > 1;
+  if (prefetch && (e = side_stream(&side)) != hipSuccess) return hip_status(e);
   for (int l = 0; l < L && e == hipSuccess; ++l) {
     const LayerPtrs p = ptrs_of(&layers[l]);
+    if (prefetch && l + 1 < L) {
+      const LayerPtrs pn = ptrs_of(&layers[l + 1]);
+      const Prefetch pf{{reinterpret_cast<const uint8_t*>(pn.router), pn.shared},
+                        {(uint64_t)g.E * g.H * 2, pn.shared != nullptr ? g.blob_bytes : 0}};
+      e = hipEventRecord(side->fork, s);
+      if (e == hipSuccess) e = hipStreamWaitEvent(side->s, side->fork, 0);
+      if (e == hipSuccess) e = launch_prefetch(pf, BQ_PREFETCH_BLOCKS, side->s);
+      if (e != hipSuccess) break;
+    }
     float* h_next = (l == L - 1) ? out : hbuf[l & 1];
     const float* norm_src = (l == 0) ? nullptr : h;
     const float* xin = (l == 0) ? x : W.u;
@@ -418,6 +473,10 @@ int moe_stack_forward(const moe_layer_t* layers, int L, float eps, const float* 
     if (e == hipSuccess) e = launch_gateup(g, p, xin, T, W, nullptr, io, true, s);
     if (e == hipSuccess) e = launch_down(g, p, T, W, W.idx, h, h_next, nullptr, (l + 1 < L) ? W.sq : nullptr, s);
     h = h_next;
+  }
+  if (prefetch && e == hipSuccess) {
+    e = hipEventRecord(side->join, side->s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(s, side->join, 0);
   }
   return hip_status(e);
 }

@@ -120,6 +120,8 @@ def _layer(**kw):
     (dict(shared_gate=FAKE + 2), bq.MOE_EINVAL),
     (dict(flags=3), bq.MOE_EUNSUPPORTED),
     (dict(flags=-1), bq.MOE_EUNSUPPORTED),
+    (dict(flags=7), bq.MOE_EUNSUPPORTED),
+    (dict(flags=8), bq.MOE_EUNSUPPORTED),
 ])
 def test_layer_validation(kw, code):
     layer = _layer(**kw)

@@ -72,6 +72,37 @@ def test_stack_single_layer_equals_layer_forward(gpu_device):
     assert np.array_equal(out_s, out.cpu().numpy()) and np.array_equal(idx_s[0], idx.cpu().numpy())
 
 
+def test_stack_prefetch_leaves_results_unchanged(gpu_device):
+    """MOE_FLAG_PREFETCH_NEXT only adds reads on a side stream: eager calls and graph replays give
+    the same bits as the plain stack."""
+    w = TINYSTACK
+    layers = [DeviceLayer(w, l) for l in range(w.layers)]
+    x = torch.from_numpy(synth.tokens_x(w, 0, w.tokens)).cuda()
+    out0, idx0 = _run_stack(layers, x, w.tokens)
+    layers[0].desc.flags = bq.MOE_FLAG_PREFETCH_NEXT
+    try:
+        out1, idx1 = _run_stack(layers, x, w.tokens)  # eager: also creates the side stream
+        assert np.array_equal(out0, out1) and np.array_equal(idx0, idx1)
+        n = bq.moe_stack_workspace_bytes(layers[0].desc, w.tokens)
+        ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+        out = torch.empty_like(x)
+        idx = torch.empty(len(layers), w.tokens, w.top_k, dtype=torch.int32, device="cuda")
+        s = torch.cuda.Stream()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            bq.moe_stack_forward([L.desc for L in layers], EPS, x, w.tokens, out, idx, ws, n, stream=s)
+        for rep in range(3):
+            out.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            assert np.array_equal(out.cpu().numpy(), out0), f"replay {rep}"
+            assert np.array_equal(idx.cpu().numpy(), idx0), f"replay {rep}"
+            _run_stack(layers, x, w.tokens)  # eager work between replays
+    finally:
+        layers[0].desc.flags = 0
+
+
 def test_stack60_sequence(gpu_device):
     """The full 60-layer stack with every expert resident (about 218 GB), as 128 sequential
     single-token calls in one graph; sampled tokens are checked against the oracle's stack."""
