@@ -57,9 +57,10 @@ def kernel_hash():
     return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
 
 
-def load_traffic(kernel_label):
-    """HBM traffic per launch from committed rocprofv3 --pmc summaries, if taken on this kernel source."""
-    path = os.path.join(ROOT, "profiles", "decode4_traffic.json")
+def load_traffic(kernel_label, workload):
+    """HBM traffic per launch from committed rocprofv3 --pmc summaries, if taken on this workload and on
+    this kernel source."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     try:
@@ -119,7 +120,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="decode4", choices=["decode4", "decode2", "prefill4", "stack60"])
+    ap.add_argument("--workload", default="decode4", choices=["decode4", "decode2", "decodemx", "prefill4", "stack60"])
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cold", action="store_true")
@@ -230,7 +231,7 @@ def main():
                                  "GB/s": round(per_kernel_bytes[k] / avg[k] / 1e9, 1)} for k in range(3)}
     print(f"[bench] kernels: {json.dumps(kernels)}", file=sys.stderr, flush=True)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(KERNEL_NAMES[dom]),
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(KERNEL_NAMES[dom], w.name),
                 "kernel": KERNEL_NAMES[dom], "algorithmic_bytes_per_launch": per_kernel_bytes[dom],
                 "avg_launch_us": round(avg[dom] * 1e6, 3),
                 "timing": f"start/stop HIP events recorded by each dispatch itself (hipExtLaunchKernel) on the "
@@ -270,7 +271,7 @@ def main():
                                f"top-{w.top_k} + shared, {w.bits}-bit group-{w.group} experts; a step is {N} "
                                f"sequential single-token calls in one HIP graph",
                    "tokens_per_step": N, "hidden": w.hidden, "n_experts": w.n_experts, "inter": w.inter,
-                   "top_k": w.top_k, "bits": w.bits, "group": w.group, "dequant_form": args.dequant,
+                   "top_k": w.top_k, "bits": w.bits, "group": w.group, "dequant_form": args.dequant if w.fmt == "affine" else "mxfp4: e2m1(q) * 2^(e - 127)",
                    "parallelism": "single GPU"},
         "us_per_token": round(us_tok, 3),
         "expert_GB/s": round(expert_bytes / (us_tok * 1e-6) / 1e9, 1),

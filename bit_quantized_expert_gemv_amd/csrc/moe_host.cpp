@@ -80,7 +80,11 @@ int check_act(const void* p, const char* name) {
 
 bool geometry_from(const moe_layer_t* L, Geometry* g, const char** why) {
   if (L->bits != 2 && L->bits != 4) { *why = "bits must be 2 or 4"; return false; }
-  if (L->group != 64) { *why = "group must be 64"; return false; }
+  if (L->group != 64 && !(L->group == 32 && L->bits == 4)) {
+    *why = "group must be 64 (affine), or 32 with bits 4 (MXFP4)";
+    return false;
+  }
+  const bool mx = L->group == 32;
   if (!pow2_in(L->hidden, 256, 8192)) { *why = "hidden must be a power of two in [256, 8192]"; return false; }
   if (!pow2_in(L->inter, 64, 2048)) { *why = "inter must be a power of two in [64, 2048]"; return false; }
   if (L->n_experts < 1 || L->n_experts > MOE_MAX_EXPERTS) { *why = "n_experts must be in [1, 1024]"; return false; }
@@ -94,12 +98,13 @@ bool geometry_from(const moe_layer_t* L, Geometry* g, const char** why) {
     *why = "flags must be 0, MOE_FLAG_DEQUANT_LITERAL or MOE_FLAG_DEQUANT_NAIVE, optionally with MOE_FLAG_PREFETCH_NEXT";
     return false;
   }
-  g->form = form == MOE_FLAG_DEQUANT_LITERAL ? 1 : form == MOE_FLAG_DEQUANT_NAIVE ? 2 : 0;
+  if (mx && form != 0) { *why = "the dequant-form flags apply to the affine format only"; return false; }
+  g->form = mx ? 3 : form == MOE_FLAG_DEQUANT_LITERAL ? 1 : form == MOE_FLAG_DEQUANT_NAIVE ? 2 : 0;
   g->H = L->hidden; g->I = L->inter; g->E = L->n_experts; g->K = L->top_k;
   g->has_shared = L->has_shared; g->NE = g->K + g->has_shared;
   g->bits = L->bits; g->G = L->group;
   const uint64_t cb = (uint64_t)g->I * g->H * g->bits / 8;
-  const uint64_t sbb = (uint64_t)g->I * (g->H / g->G) * 4;
+  const uint64_t sbb = (uint64_t)g->I * (g->H / g->G) * (mx ? 1 : 4);  // (scale, bias) words or E8M0 bytes
   for (int m = 0; m < 3; ++m) {
     g->off_codes[m] = m * cb;
     g->off_sb[m] = 3 * cb + m * sbb;
@@ -186,10 +191,10 @@ using namespace bqmoe;
 extern "C" {
 
 size_t moe_blob_bytes(int hidden, int inter, int bits, int group) {
-  if ((bits != 2 && bits != 4) || group != 64) return 0;
-  if (hidden <= 0 || inter <= 0 || hidden % group != 0 || inter % group != 0) return 0;
+  if ((bits != 2 && bits != 4) || (group != 64 && !(group == 32 && bits == 4))) return 0;
+  if (hidden <= 0 || inter <= 0 || hidden % 64 != 0 || inter % 64 != 0) return 0;
   const uint64_t w = (uint64_t)hidden * inter;
-  return (size_t)(3 * w * bits / 8 + 3 * (w / group) * 4);
+  return (size_t)(3 * w * bits / 8 + 3 * (w / group) * (group == 32 ? 1 : 4));
 }
 
 size_t moe_workspace_bytes(const moe_layer_t* layer, int T) {
@@ -213,12 +218,18 @@ size_t moe_stack_workspace_bytes(const moe_layer_t* layer, int T) {
 
 int moe_pack_expert(int hidden, int inter, int bits, int group, const moe_expert_arrays_t* a, void* blob_host) {
   const size_t bytes = moe_blob_bytes(hidden, inter, bits, group);
-  if (bytes == 0) return fail(MOE_EUNSUPPORTED, "unsupported blob shape (bits 2/4, group 64, dims multiple of 64)");
+  if (bytes == 0)
+    return fail(MOE_EUNSUPPORTED, "unsupported blob shape (bits 2/4 with group 64, or bits 4 with group 32; dims multiple of 64)");
   if (a == nullptr || blob_host == nullptr) return fail(MOE_EINVAL, "arrays and blob must be non-NULL");
+  const bool mx = group == 32;
   for (int m = 0; m < 3; ++m)
-    if (a->q[m] == nullptr || a->scale[m] == nullptr || a->bias[m] == nullptr)
-      return fail(MOE_EINVAL, "every q/scale/bias array must be non-NULL");
+    if (a->q[m] == nullptr || a->scale[m] == nullptr || (!mx && a->bias[m] == nullptr))
+      return fail(MOE_EINVAL, "every q/scale array (and bias, for the affine format) must be non-NULL");
   const int64_t n = (int64_t)hidden * inter;
+  if (mx)
+    for (int m = 0; m < 3; ++m)
+      for (int64_t i = 0; i < n / group; ++i)
+        if (a->scale[m][i] > 255) return fail(MOE_EINVAL, "an E8M0 scale does not fit in 8 bits");
   const int per = 8 / bits;
   const uint8_t lim = (uint8_t)(1u << bits);
   for (int m = 0; m < 3; ++m)
@@ -234,6 +245,11 @@ int moe_pack_expert(int hidden, int inter, int bits, int group, const moe_expert
       for (int j = 0; j < per; ++j) v |= (uint32_t)a->q[m][k * per + j] << (bits * j);
       codes[k] = (uint8_t)v;
     }
+    if (mx) {
+      uint8_t* sc = out + 3 * cb + m * ng;
+      for (int64_t k = 0; k < ng; ++k) sc[k] = (uint8_t)a->scale[m][k];
+      continue;
+    }
     uint8_t* sb = out + 3 * cb + m * ng * 4;
     for (int64_t k = 0; k < ng; ++k) {
       const uint32_t word = (uint32_t)a->scale[m][k] | ((uint32_t)a->bias[m][k] << 16);
@@ -246,11 +262,11 @@ int moe_pack_expert(int hidden, int inter, int bits, int group, const moe_expert
 int moe_pack_expert_device(int hidden, int inter, int bits, int group, const moe_expert_arrays_t* a, void* blob_dev,
                            void* stream) {
   if (moe_blob_bytes(hidden, inter, bits, group) == 0)
-    return fail(MOE_EUNSUPPORTED, "unsupported blob shape (bits 2/4, group 64, dims multiple of 64)");
+    return fail(MOE_EUNSUPPORTED, "unsupported blob shape (bits 2/4 with group 64, or bits 4 with group 32; dims multiple of 64)");
   if (a == nullptr || blob_dev == nullptr) return fail(MOE_EINVAL, "arrays and blob must be non-NULL");
   for (int m = 0; m < 3; ++m)
-    if (a->q[m] == nullptr || a->scale[m] == nullptr || a->bias[m] == nullptr)
-      return fail(MOE_EINVAL, "every q/scale/bias array must be non-NULL");
+    if (a->q[m] == nullptr || a->scale[m] == nullptr || (group != 32 && a->bias[m] == nullptr))
+      return fail(MOE_EINVAL, "every q/scale array (and bias, for the affine format) must be non-NULL");
   if (!aligned(blob_dev, 4)) return fail(MOE_EINVAL, "blob_dev must be 4-byte aligned");
   return hip_status(launch_pack(hidden, inter, bits, group, a, static_cast<uint8_t*>(blob_dev),
                                 static_cast<hipStream_t>(stream)));
@@ -271,6 +287,10 @@ int moe_dequant(const moe_layer_t* layer, int expert, int matrix, int out_dtype,
 }
 
 namespace {
+// The grouped (prefill) path: affine layers from MOE_PREFILL_MIN_TOKENS tokens. MXFP4 layers run the
+// per-token kernels at every T.
+bool use_prefill(const Geometry& g, int T) { return T >= MOE_PREFILL_MIN_TOKENS && g.form != 3; }
+
 size_t needed_ws(const Geometry& g, int T) {
   size_t n = workspace_layer_bytes(g, T);
   if (T >= MOE_PREFILL_MIN_TOKENS) {
@@ -313,7 +333,7 @@ int moe_expert_ffn(const moe_layer_t* layer, const float* x, int T, const int32_
   if (ws_bytes < needed_ws(g, T)) return fail(MOE_ENOSPC, "workspace smaller than moe_workspace_bytes()");
   hipStream_t s = static_cast<hipStream_t>(stream);
   const LayerPtrs p = ptrs_of(layer);
-  if (T >= MOE_PREFILL_MIN_TOKENS)
+  if (use_prefill(g, T))
     return hip_status(launch_prefill(g, p, x, nullptr, T, carve_prefill(g, T, ws), idx, nullptr, nullptr, y, s));
   const Workspace W = carve_workspace(g, T, ws);
   hipError_t e = launch_gateup(g, p, x, T, W, idx, nullptr, true, s);
@@ -363,7 +383,7 @@ int moe_layer_forward_timed(const moe_layer_t* layer, const float* x, const floa
     }
     return e;
   };
-  if (T >= MOE_PREFILL_MIN_TOKENS) {
+  if (use_prefill(g, T)) {
     // many kernels: events[0] and events[5] are recorded around all of them
     hipError_t e = hipSuccess;
     if (events != nullptr && events[0] != nullptr) e = hipEventRecord(static_cast<hipEvent_t>(events[0]), s);

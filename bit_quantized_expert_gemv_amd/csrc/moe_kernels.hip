@@ -119,6 +119,33 @@ __device__ __forceinline__ float chunk_dot2(const uint4 w, const float* x) {
   return acc;
 }
 
+// sum_j e2m1(q_j) x_j over the 32 E2M1 codes of one MXFP4 block (byte k holds elements 2k, 2k+1,
+// lower nibble first). The hardware conversion decodes E2M1 exactly (sign, 2 exponent bits with
+// bias 1, 1 mantissa bit; the values 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives).
+template <int N>
+__device__ __forceinline__ float mx_byte(uint32_t w, const float* x, float acc) {
+  const auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, N);  // byte N: elements 2N, 2N+1
+  acc = fmaf(v[0], x[2 * N], acc);
+  return fmaf(v[1], x[2 * N + 1], acc);
+}
+__device__ __forceinline__ float chunk_dot_mx(const uint4 w, const float* x) {
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    acc = mx_byte<0>(ws[i], x + 8 * i, acc);
+    acc = mx_byte<1>(ws[i], x + 8 * i, acc);
+    acc = mx_byte<2>(ws[i], x + 8 * i, acc);
+    acc = mx_byte<3>(ws[i], x + 8 * i, acc);
+  }
+  return acc;
+}
+
+// E8M0 block scale 2^(s - 127); 255 is NaN.
+__device__ __forceinline__ float e8m0_value(uint32_t s) {
+  return s == 0u ? 0x1p-127f : (s == 255u ? __uint_as_float(0x7FC00000u) : __uint_as_float(s << 23));
+}
+
 template <int BITS>
 __device__ __forceinline__ float chunk_dot(const uint4 w, const float* x) {
   if constexpr (BITS == 4) return chunk_dot4(w, x);
@@ -186,8 +213,9 @@ __device__ __forceinline__ float chunk_lit2(const uint4 w, const float* x, float
   return acc;
 }
 
-// This lane's share of one row: sum over its chunks of s * sum(q x) + b * S (FORM 0), or one of the
-// per-element forms of the ablation (FORM 1, 2).
+// This lane's share of one row: sum over its chunks of s * sum(q x) + b * S (FORM 0), one of the
+// per-element forms of the ablation (FORM 1, 2), or for MXFP4 (FORM 3, one block per chunk)
+// 2^(e - 127) * sum(e2m1(q) x) with the block's E8M0 byte e in sb.
 template <int BITS, class C, int FORM = 0>
 __device__ __forceinline__ float row_partial(const uint4 (&cw)[C::CPL], const uint32_t (&sb)[C::CPL],
                                              const float (&xr)[C::XPL], const float (&S)[C::CPL]) {
@@ -195,7 +223,9 @@ __device__ __forceinline__ float row_partial(const uint4 (&cw)[C::CPL], const ui
   float a = 0.0f;
 #pragma unroll
   for (int j = 0; j < C::CPL; ++j) {
-    if constexpr (FORM != 0) {
+    if constexpr (FORM == 3) {
+      a = fmaf(e8m0_value(sb[j]), chunk_dot_mx(cw[j], &xr[j * C::CH]), a);
+    } else if constexpr (FORM != 0) {
       if constexpr (BITS == 4) a = chunk_lit4<FORM>(cw[j], &xr[j * C::CH], bf16_lo(sb[j]) * kCvt, bf16_hi(sb[j]), a);
       else a = chunk_lit2<FORM>(cw[j], &xr[j * C::CH], bf16_lo(sb[j]) * kCvt, bf16_hi(sb[j]), a);
     } else {
@@ -206,15 +236,18 @@ __device__ __forceinline__ float row_partial(const uint4 (&cw)[C::CPL], const ui
   return a;
 }
 
-template <class C>
-__device__ __forceinline__ void load_row(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ sbp, int r,
+// One row's chunks for this lane, with each chunk's (scale, bias) word, or for MXFP4 (MX) its E8M0
+// byte (at 4-bit a 16-byte chunk is one block of 32).
+template <class C, bool MX = false>
+__device__ __forceinline__ void load_row(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ sbp, int r,
                                          int lir, uint4 (&cw)[C::CPL], uint32_t (&sb)[C::CPL]) {
   const uint8_t* row = codes + (size_t)r * C::ROW_BYTES;
 #pragma unroll
   for (int j = 0; j < C::CPL; ++j) {
     const int c = lir + j * C::LPR;
     cw[j] = *reinterpret_cast<const uint4*>(row + (size_t)c * 16);
-    sb[j] = sbp[(size_t)r * C::GROUPS + (c * C::CH) / 64];
+    if constexpr (MX) sb[j] = sbp[(size_t)r * C::NC + c];
+    else sb[j] = reinterpret_cast<const uint32_t*>(sbp)[(size_t)r * C::GROUPS + (c * C::CH) / 64];
   }
 }
 
@@ -470,15 +503,15 @@ __device__ __forceinline__ void gateup_block(const LayerArgs& a, const uint8_t* 
   using C = RowCfg<BITS, H>;
   const uint8_t* gc = blob + a.off_codes[0];
   const uint8_t* uc = blob + a.off_codes[1];
-  const uint32_t* gs = reinterpret_cast<const uint32_t*>(blob + a.off_sb[0]);
-  const uint32_t* us = reinterpret_cast<const uint32_t*>(blob + a.off_sb[1]);
+  const uint8_t* gs = blob + a.off_sb[0];
+  const uint8_t* us = blob + a.off_sb[1];
   uint4 cg[P][C::CPL], cu[P][C::CPL];
   uint32_t sg[P][C::CPL], su[P][C::CPL];
 #pragma unroll
   for (int p = 0; p < P; ++p) {
     const int r = min((step0 + p) * C::RPW + rig, a.I - 1);  // rows past the end re-read the last row
-    load_row<C>(gc, gs, r, lir, cg[p], sg[p]);
-    load_row<C>(uc, us, r, lir, cu[p], su[p]);
+    load_row<C, FORM == 3>(gc, gs, r, lir, cg[p], sg[p]);
+    load_row<C, FORM == 3>(uc, us, r, lir, cu[p], su[p]);
   }
   __builtin_amdgcn_sched_barrier(0);
   st.template store<C>(xs, threadIdx.x, scale);
@@ -663,11 +696,12 @@ __global__ __launch_bounds__(kBlock) void k_down(LayerArgs a, const int32_t* __r
     float yv[P];
     if (valid) {
       const uint8_t* dc = blob + a.off_codes[2];
-      const uint32_t* ds = reinterpret_cast<const uint32_t*>(blob + a.off_sb[2]);
+      const uint8_t* ds = blob + a.off_sb[2];
       uint4 cw[P][C::CPL];
       uint32_t sb[P][C::CPL];
 #pragma unroll
-      for (int p = 0; p < P; ++p) load_row<C>(dc, ds, min(row0 + p * C::RPW + rig, a.H - 1), lir, cw[p], sb[p]);
+      for (int p = 0; p < P; ++p)
+        load_row<C, FORM == 3>(dc, ds, min(row0 + p * C::RPW + rig, a.H - 1), lir, cw[p], sb[p]);
       __builtin_amdgcn_sched_barrier(0);
       st.template store<C>(hs[wave], lane, 1.0f);
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -765,6 +799,29 @@ __global__ void k_dequant(int rows, int cols, int bits, const uint8_t* __restric
   }
 }
 
+// MXFP4: w = e2m1(q) * 2^(e - 127), exact in fp32 for the E8M0 range of normal floats.
+__global__ void k_dequant_mx(int rows, int cols, const uint8_t* __restrict__ codes, const uint8_t* __restrict__ sc,
+                             int out_dtype, void* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)rows * cols) return;
+  const int64_t r = i / cols, c = i % cols;
+  const uint32_t byte = codes[(r * cols + c) / 2];
+  const auto v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(byte, 1.0f, 0);
+  const float v = (c & 1 ? v2[1] : v2[0]) * e8m0_value(sc[r * (cols / 32) + c / 32]);
+  if (out_dtype == 0) {
+    static_cast<float*>(out)[i] = v;
+  } else {
+    uint32_t b = __float_as_uint(v);
+    b += 0x7FFFu + ((b >> 16) & 1u);  // round to nearest even (finite values)
+    static_cast<uint16_t*>(out)[i] = (uint16_t)(b >> 16);
+  }
+}
+
+__global__ void k_pack_e8m0(int64_t n, const uint16_t* __restrict__ s, uint8_t* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = (uint8_t)s[i];
+}
+
 __global__ void k_pack_codes(int64_t nbytes_out, int bits, const uint8_t* __restrict__ q, uint8_t* __restrict__ out) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= nbytes_out) return;
@@ -835,6 +892,9 @@ hipError_t gateup_impl(const LayerArgs& a, const float* x, int T, const int32_t*
   const int slots = a.K + ((with_shared && a.has_shared) ? 1 : 0);
   const dim3 grid(nb, slots, T);
 #define BQ_GU(PL, F) launch_timed(k_gateup<BITS, H, kP2, PL, F>, grid, dim3(kBlock), s, ev, a, x, idx_in, idx_out)
+  if constexpr (BITS == 4) {
+    if (a.form == 3) return a.E <= 512 ? BQ_GU(8, 3) : BQ_GU(16, 3);
+  }
   if (a.E <= 512) return a.form == 1 ? BQ_GU(8, 1) : a.form == 2 ? BQ_GU(8, 2) : BQ_GU(8, 0);
   return a.form == 1 ? BQ_GU(16, 1) : a.form == 2 ? BQ_GU(16, 2) : BQ_GU(16, 0);
 #undef BQ_GU
@@ -847,6 +907,9 @@ hipError_t down_impl(const LayerArgs& a, int T, const int32_t* idx, const float*
   constexpr int RB = C::RPW * kP3;
   const int nb = (a.H + RB - 1) / RB;
 #define BQ_DN(F) launch_timed(k_down<BITS, I, kP3, F>, dim3(nb, T), dim3(kBlock), s, ev, a, idx, residual, out, y, sq_out)
+  if constexpr (BITS == 4) {
+    if (a.form == 3) return BQ_DN(3);
+  }
   return a.form == 1 ? BQ_DN(1) : a.form == 2 ? BQ_DN(2) : BQ_DN(0);
 #undef BQ_DN
 }
@@ -939,6 +1002,11 @@ hipError_t launch_dequant(const Geometry& g, const uint8_t* blob, int matrix, in
   const int rows = matrix == 2 ? g.H : g.I;
   const int cols = matrix == 2 ? g.I : g.H;
   const int64_t n = (int64_t)rows * cols;
+  if (g.form == 3) {
+    hipLaunchKernelGGL(k_dequant_mx, dim3(blocks_for(n, 256)), dim3(256), 0, s, rows, cols, blob + g.off_codes[matrix],
+                       blob + g.off_sb[matrix], out_dtype, out);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(k_dequant, dim3(blocks_for(n, 256)), dim3(256), 0, s, rows, cols, g.bits,
                      blob + g.off_codes[matrix], reinterpret_cast<const uint32_t*>(blob + g.off_sb[matrix]), out_dtype,
                      out);
@@ -951,6 +1019,11 @@ hipError_t launch_pack(int H, int I, int bits, int G, const moe_expert_arrays_t*
   for (int m = 0; m < 3; ++m) {
     hipLaunchKernelGGL(k_pack_codes, dim3(blocks_for(code_bytes, 256)), dim3(256), 0, s, code_bytes, bits, arr->q[m],
                        blob + m * code_bytes);
+    if (G == 32) {  // MXFP4: one E8M0 byte per block
+      hipLaunchKernelGGL(k_pack_e8m0, dim3(blocks_for(ngroups, 256)), dim3(256), 0, s, ngroups, arr->scale[m],
+                         blob + 3 * code_bytes + m * ngroups);
+      continue;
+    }
     hipLaunchKernelGGL(k_pack_sb, dim3(blocks_for(ngroups, 256)), dim3(256), 0, s, ngroups, arr->scale[m],
                        arr->bias[m], reinterpret_cast<uint32_t*>(blob + 3 * code_bytes + m * ngroups * 4));
   }

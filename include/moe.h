@@ -34,6 +34,17 @@
  *     nibble*scale + bias ("Kernel de dequantización optimizado con FMA").
  *   - Size: 3*I*H*b/8 + 3*I*(H/G)*4 bytes, which is 7,077,888 B (6.75 MiB) at 4-bit and
  *     3,932,160 B at 2-bit for H = 4096, I = 1024.
+ *
+ * MXFP4 expert blob (bits 4, group 32): the expert format of the page "300b on 32gb MoE-streaming
+ * findings + optimisations" (its summary), as the OCP Microscaling (MX) format defines it:
+ *   [gate codes][up codes][down codes][gate scales][up scales][down scales]
+ *   - codes: 4-bit E2M1 values (sign bit, 2 exponent bits with bias 1, 1 mantissa bit), packed as
+ *     above (element c at byte c/2, lower nibble first).
+ *   - scales: one E8M0 byte per (row, block of 32 columns), row-major [rows][cols/32]; 255 is NaN.
+ *   - W[r][c] = e2m1(q[r][c]) * 2^(e[r][c/32] - 127); there is no bias.
+ *   - Size: 3*I*H/2 + 3*I*H/32 bytes, 6,684,672 B for H = 4096, I = 1024.
+ * A layer in this format runs the per-token kernels at every T, with exact fp32 products of the
+ * dequantised weights and the fp32 activations.
  */
 #ifndef BQ_MOE_H
 #define BQ_MOE_H
@@ -74,15 +85,16 @@ extern "C" {
 #define MOE_FLAG_PREFETCH_NEXT 4
 
 /* One MoE layer.
- *   hidden H, inter I: powers of two with 256 <= H <= 8192 and 64 <= I <= 2048. group must be 64, bits 2 or 4.
+ *   hidden H, inter I: powers of two with 256 <= H <= 8192 and 64 <= I <= 2048. bits 2 or 4 with
+ *   group 64 (affine format), or bits 4 with group 32 (MXFP4 format).
  *   n_experts E: 1..MOE_MAX_EXPERTS. top_k K: 1..min(E, MOE_MAX_TOP_K).
  *   experts_dev: E packed blobs, expert e at experts_dev + e*expert_stride. expert_stride is at
  *   least moe_blob_bytes(H, I, bits, group) and a multiple of 256.
  *   shared_blob_dev and shared_gate_dev: the shared expert's blob and its gate vector (bf16 [H]).
  *   Required when has_shared is 1, ignored when it is 0.
  *   router_dev: bf16 [E][H] row-major; logit e = row e . x, with no bias.
- *   flags: 0, MOE_FLAG_DEQUANT_LITERAL or MOE_FLAG_DEQUANT_NAIVE, optionally or-ed with
- *   MOE_FLAG_PREFETCH_NEXT (other values: MOE_EUNSUPPORTED). */
+ *   flags: 0, MOE_FLAG_DEQUANT_LITERAL or MOE_FLAG_DEQUANT_NAIVE (the latter two affine only),
+ *   optionally or-ed with MOE_FLAG_PREFETCH_NEXT (other values: MOE_EUNSUPPORTED). */
 typedef struct moe_layer_t {
   int32_t hidden;
   int32_t inter;
@@ -122,7 +134,8 @@ size_t moe_stack_workspace_bytes(const moe_layer_t* layer, int T);
 /* ---- packing -------------------------------------------------------------------------------------- */
 
 /* Pack one expert from canonical host arrays into a host blob of moe_blob_bytes() bytes.
- * Codes must be < 2^bits (MOE_EINVAL otherwise). Pure host code; usable without a GPU. */
+ * Codes must be < 2^bits (MOE_EINVAL otherwise). For MXFP4 (group 32), scale[m] holds the E8M0
+ * bytes as uint16 values <= 255 and bias may be NULL. Pure host code; usable without a GPU. */
 int moe_pack_expert(int hidden, int inter, int bits, int group, const moe_expert_arrays_t* arrays_host,
                     void* blob_host);
 
@@ -135,7 +148,7 @@ int moe_pack_expert_device(int hidden, int inter, int bits, int group, const moe
  * 0 gate, 1 up, 2 down. out_dtype 0 writes fp32 [rows][cols]. out_dtype 1 writes the bf16
  * (round-to-nearest-even) of each weight. Every 2-bit and 4-bit weight in the supported ranges is
  * exact in fp32. The pages' form: nibble*scale + bias ("Kernel de dequantización optimizado con
- * FMA"). */
+ * FMA"); for MXFP4, e2m1(q) * 2^(e - 127). */
 int moe_dequant(const moe_layer_t* layer, int expert, int matrix, int out_dtype, void* w_out_dev, void* stream);
 
 /* ---- the layer, step by step --------------------------------------------------------------------- */

@@ -41,8 +41,11 @@ def lib():
         L.oracle_expert.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, vp]
         L.oracle_combine.argtypes = [i64, i64, vp, vp, vp, dbl, vp, vp]
         L.oracle_rmsnorm.argtypes = [i64, dbl, vp, vp]
+        L.oracle_dequant_mx.argtypes = [i64, i64, vp, vp, vp]
+        L.oracle_expert_mx.argtypes = [i64, i64, vp, vp, vp, vp, vp]
         for f in (L.oracle_dequant, L.oracle_matvec, L.oracle_router_logits, L.oracle_topk,
-                  L.oracle_route_weights, L.oracle_expert, L.oracle_combine, L.oracle_rmsnorm):
+                  L.oracle_route_weights, L.oracle_expert, L.oracle_combine, L.oracle_rmsnorm,
+                  L.oracle_dequant_mx, L.oracle_expert_mx):
             f.restype = None
         _lib = L
     return _lib
@@ -63,6 +66,17 @@ def dequant(q, scale, bias, group: int) -> np.ndarray:
     assert s.shape == (rows, cols // group) and b.shape == s.shape
     W = np.empty((rows, cols), dtype=np.float64)
     lib().oracle_dequant(rows, cols, group, _p(q), _p(s), _p(b), _p(W))
+    return W
+
+
+def dequant_mx(q, scale) -> np.ndarray:
+    """MXFP4: W = e2m1(q) * 2^(scale - 127), one E8M0 scale per block of 32 along a row (see oracle.h)."""
+    q = _c(q, np.uint8)
+    rows, cols = q.shape
+    s = _c(scale, np.uint16)
+    assert s.shape == (rows, cols // 32)
+    W = np.empty((rows, cols), dtype=np.float64)
+    lib().oracle_dequant_mx(rows, cols, _p(q), _p(s), _p(W))
     return W
 
 
@@ -100,7 +114,10 @@ def shared_gate(gs, x) -> float:
 
 
 def expert(x, ex, group: int, want_h: bool = False):
-    """ex: an object with .mats = [gate, up, down], each with .q, .scale, .bias canonical arrays."""
+    """ex: an object with .mats = [gate, up, down], each with .q, .scale, .bias canonical arrays, and
+    .fmt ("affine", or "mxfp4": E2M1 codes with E8M0 scales per 32 and no bias; group is then unused)."""
+    if getattr(ex, "fmt", "affine") == "mxfp4":
+        return _expert_mx(x, ex, want_h)
     x = _c(x, np.float64)
     mats = [(_c(m.q, np.uint8), _c(m.scale, np.uint16), _c(m.bias, np.uint16)) for m in ex.mats]
     I, H = mats[0][0].shape
@@ -111,6 +128,19 @@ def expert(x, ex, group: int, want_h: bool = False):
     y = np.empty(H, dtype=np.float64)
     h = np.empty(I, dtype=np.float64) if want_h else None
     lib().oracle_expert(H, I, group, _p(x), qs, ss, bs, _p(y), _p(h))
+    return (y, h) if want_h else y
+
+
+def _expert_mx(x, ex, want_h: bool):
+    x = _c(x, np.float64)
+    mats = [(_c(m.q, np.uint8), _c(m.scale, np.uint16)) for m in ex.mats]
+    I, H = mats[0][0].shape
+    assert mats[1][0].shape == (I, H) and mats[2][0].shape == (H, I) and x.shape == (H,)
+    qs = (ctypes.c_void_p * 3)(*[m[0].ctypes.data for m in mats])
+    ss = (ctypes.c_void_p * 3)(*[m[1].ctypes.data for m in mats])
+    y = np.empty(H, dtype=np.float64)
+    h = np.empty(I, dtype=np.float64) if want_h else None
+    lib().oracle_expert_mx(H, I, _p(x), qs, ss, _p(y), _p(h))
     return (y, h) if want_h else y
 
 

@@ -124,6 +124,50 @@ void oracle_expert(int64_t H, int64_t I, int64_t group, const double* x, const u
   free(h);
 }
 
+/* E2M1 (OCP MX element format for FP4): sign bit 3, exponent bits 2-1 (bias 1), mantissa bit 0.
+ * Exponent 0 is subnormal: value = mantissa * 2^-1. Otherwise value = (1 + mantissa/2) * 2^(e - 1). */
+static double e2m1_value(uint8_t q) {
+  const int sign = (q >> 3) & 1, e = (q >> 1) & 3, m = q & 1;
+  const double v = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+  return sign ? -v : v;
+}
+
+/* E8M0 (OCP MX scale format): 2^(s - 127), and 255 is NaN. */
+static double e8m0_value(uint16_t s) { return s == 255 ? NAN : ldexp(1.0, (int)s - 127); }
+
+/* The page "300b on 32gb MoE-streaming findings + optimisations": MXFP4 experts. A block of 32
+ * consecutive elements along a row shares one E8M0 scale. */
+void oracle_dequant_mx(int64_t rows, int64_t cols, const uint8_t* q, const uint16_t* scale, double* W) {
+  const int64_t nb = cols / 32;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t c = 0; c < cols; ++c) W[r * cols + c] = e2m1_value(q[r * cols + c]) * e8m0_value(scale[r * nb + c / 32]);
+}
+
+void oracle_expert_mx(int64_t H, int64_t I, const double* x, const uint8_t* const q[3], const uint16_t* const scale[3],
+                      double* y, double* h_out) {
+  double* Wg = (double*)malloc((size_t)(I * H) * sizeof(double));
+  double* Wu = (double*)malloc((size_t)(I * H) * sizeof(double));
+  double* Wd = (double*)malloc((size_t)(H * I) * sizeof(double));
+  double* a = (double*)malloc((size_t)I * sizeof(double));
+  double* c = (double*)malloc((size_t)I * sizeof(double));
+  double* h = (double*)malloc((size_t)I * sizeof(double));
+  oracle_dequant_mx(I, H, q[0], scale[0], Wg);
+  oracle_dequant_mx(I, H, q[1], scale[1], Wu);
+  oracle_dequant_mx(H, I, q[2], scale[2], Wd);
+  oracle_matvec(I, H, Wg, x, a);
+  oracle_matvec(I, H, Wu, x, c);
+  for (int64_t i = 0; i < I; ++i) h[i] = a[i] / (1.0 + exp(-a[i])) * c[i];
+  oracle_matvec(H, I, Wd, h, y);
+  if (h_out) memcpy(h_out, h, (size_t)I * sizeof(double));
+  free(Wg);
+  free(Wu);
+  free(Wd);
+  free(a);
+  free(c);
+  free(h);
+}
+
 /* GN+ summary, "Metal Compute Shaders" (MoE combine + residual + gate). */
 void oracle_combine(int64_t H, int64_t K, const double* res, const double* y, const double* w, double g,
                     const double* ys, double* out) {

@@ -52,6 +52,16 @@ double oracle_shared_gate(int64_t H, const uint16_t* gs, const double* x);
  * q/scale/bias point to the canonical arrays of gate, up, down (index 0, 1, 2). h_out may be NULL. */
 void oracle_expert(int64_t H, int64_t I, int64_t group, const double* x, const uint8_t* const q[3],
                    const uint16_t* const scale[3], const uint16_t* const bias[3], double* y, double* h_out);
+/* MXFP4 experts (the page "300b on 32gb MoE-streaming findings + optimisations", its summary: the
+ * expert pool is stored as MXFP4; the format is read as the OCP Microscaling specification defines
+ * MXFP4). q holds one E2M1 code per byte (sign bit 3, exponent bits 2-1 with bias 1, mantissa bit 0;
+ * exponent 0 is subnormal, value mantissa/2); scale holds one E8M0 byte per (row, block of 32
+ * columns) in uint16 slots, value 2^(s - 127), with 255 meaning NaN. There is no bias.
+ * W[r][c] = e2m1(q[r][c]) * 2^(scale[r][c/32] - 127), dense, rows x cols, fp64 (exact). */
+void oracle_dequant_mx(int64_t rows, int64_t cols, const uint8_t* q, const uint16_t* scale, double* W);
+/* One MXFP4 expert: as oracle_expert with oracle_dequant_mx weights. */
+void oracle_expert_mx(int64_t H, int64_t I, const double* x, const uint8_t* const q[3], const uint16_t* const scale[3],
+                      double* y, double* h_out);
 /* out = res + sum_k w[k] * y[k] + g * ys (the shared term only when ys != NULL); y is K x H. */
 void oracle_combine(int64_t H, int64_t K, const double* res, const double* y, const double* w, double g,
                     const double* ys, double* out);

@@ -10,7 +10,9 @@ pages describe (GN+ summary, "Arquitectura del modelo" / "Arsitektur model": 60 
 512 experts per layer, 4 active per token counting one shared expert, hidden 4096). The
 4-bit and 2-bit expert formats are the two configurations on those pages ("Resultados de
 rendimiento"). The value distributions are the synthetic stand-ins for the missing trained
-weights.
+weights. The MXFP4 workloads take the expert format and the top-6 routing of the page "300b on
+32gb MoE-streaming findings + optimisations" (its summary) at the same layer shape: E2M1 codes in
+blocks of 32 with an E8M0 scale per block, no bias.
 """
 from __future__ import annotations
 
@@ -51,6 +53,8 @@ class Workload:
     weight_family: int = 0  # key family of the weights (layer l uses layer index l)
     x_family: int = 0  # key family of the activations
     prefill: bool = False
+    fmt: str = "affine"  # "affine" (bf16 scale + bias per group) or "mxfp4" (E8M0 scale per 32, group 32)
+    mx_scale_range: tuple = (118, 122)  # E8M0 scale bytes: 2^-9 .. 2^-5
 
     def matrix_shape(self, m: int) -> tuple:
         return (self.inter, self.hidden) if m in (GATE, UP) else (self.hidden, self.inter)
@@ -73,6 +77,17 @@ WORKLOADS = {
     "stack60": Workload("stack60", 4096, 512, 1024, 3, tokens=128, layers=60, weight_family=1, x_family=4,
                         **_FOUR_BIT),
 }
+
+_MX = dict(bits=4, group=32, fmt="mxfp4")
+WORKLOADS.update({
+    # tiny MXFP4 layer, top-6 of 8 experts + shared
+    "tinymx": Workload("tinymx", 256, 8, 128, 6, tokens=1, weight_family=6, x_family=6, **_MX),
+    # single-token decode at the model's shape with MXFP4 experts and top-6 routing
+    "decodemx": Workload("decodemx", 4096, 512, 1024, 6, tokens=1000, weight_family=7, x_family=7, **_MX),
+    # 2048-token prefill through the decodemx layer
+    "prefillmx": Workload("prefillmx", 4096, 512, 1024, 6, tokens=2048, weight_family=7, x_family=8,
+                          prefill=True, **_MX),
+})
 
 _host = None
 _gpu = None
@@ -98,6 +113,7 @@ def host_lib():
         lib.bq_gen_uniform_bf16.argtypes, lib.bq_gen_uniform_bf16.restype = [u64, dbl, dbl, i64, i64, vp], None
         lib.bq_gen_normal_bf16.argtypes, lib.bq_gen_normal_bf16.restype = [u64, dbl, i64, i64, vp], None
         lib.bq_gen_normal_f32.argtypes, lib.bq_gen_normal_f32.restype = [u64, dbl, i64, i64, vp], None
+        lib.bq_gen_ints_u16.argtypes, lib.bq_gen_ints_u16.restype = [u64, i32, i32, i64, i64, vp], None
         _host = lib
     return _host
 
@@ -109,6 +125,7 @@ def gpu_lib():
         u64, i64, i32, dbl, vp = ctypes.c_uint64, ctypes.c_int64, ctypes.c_int, ctypes.c_double, ctypes.c_void_p
         lib.bqgen_fill_codes.argtypes, lib.bqgen_fill_codes.restype = [u64, i32, i64, vp, vp], i32
         lib.bqgen_fill_uniform_bf16.argtypes, lib.bqgen_fill_uniform_bf16.restype = [u64, dbl, dbl, i64, vp, vp], i32
+        lib.bqgen_fill_ints_u16.argtypes, lib.bqgen_fill_ints_u16.restype = [u64, i32, i32, i64, vp, vp], i32
         _gpu = lib
     return _gpu
 
@@ -135,6 +152,12 @@ def uniform_bf16(k: int, lo: float, hi: float, n: int, start: int = 0) -> np.nda
     return out
 
 
+def ints_u16(k: int, lo: int, hi: int, n: int, start: int = 0) -> np.ndarray:
+    out = np.empty(n, dtype=np.uint16)
+    host_lib().bq_gen_ints_u16(k, lo, hi, start, n, _ptr(out))
+    return out
+
+
 def normal_bf16(k: int, sigma: float, n: int, start: int = 0) -> np.ndarray:
     out = np.empty(n, dtype=np.uint16)
     host_lib().bq_gen_normal_bf16(k, sigma, start, n, _ptr(out))
@@ -149,11 +172,13 @@ def normal_f32(k: int, sigma: float, n: int, start: int = 0) -> np.ndarray:
 
 @dataclass
 class MatrixArrays:
-    """Canonical arrays of one quantised matrix: q[rows][cols] codes, scale/bias[rows][cols/group] bf16."""
+    """Canonical arrays of one quantised matrix: q[rows][cols] codes, scale/bias[rows][cols/group] bf16
+    (affine). For MXFP4, q holds E2M1 codes, scale the E8M0 bytes (uint16 each) and bias is None."""
 
     q: np.ndarray
     scale: np.ndarray
-    bias: np.ndarray
+    bias: np.ndarray | None
+    fmt: str = "affine"
 
 
 @dataclass
@@ -166,12 +191,19 @@ class ExpertArrays:
     def __post_init__(self):
         self.mats = [self.gate, self.up, self.down]
 
+    @property
+    def fmt(self) -> str:
+        return self.gate.fmt
+
 
 def matrix_arrays(w: Workload, layer: int, expert: int, m: int) -> MatrixArrays:
     rows, cols = w.matrix_shape(m)
     fam = w.weight_family
     q = codes(key(w, fam, layer, T_CODES, expert, m), w.bits, rows * cols).reshape(rows, cols)
     ng = rows * (cols // w.group)
+    if w.fmt == "mxfp4":
+        s = ints_u16(key(w, fam, layer, T_SCALE, expert, m), *w.mx_scale_range, ng).reshape(rows, cols // w.group)
+        return MatrixArrays(q, s, None, "mxfp4")
     s = uniform_bf16(key(w, fam, layer, T_SCALE, expert, m), *w.scale_range, ng).reshape(rows, cols // w.group)
     b = uniform_bf16(key(w, fam, layer, T_BIAS, expert, m), *w.bias_range, ng).reshape(rows, cols // w.group)
     return MatrixArrays(q, s, b)
@@ -214,6 +246,11 @@ def fill_matrix_device(w: Workload, layer: int, expert: int, m: int, q_ptr: int,
     fam = w.weight_family
     ng = rows * (cols // w.group)
     rc = g.bqgen_fill_codes(key(w, fam, layer, T_CODES, expert, m), w.bits, rows * cols, q_ptr, stream)
+    if w.fmt == "mxfp4":
+        rc = rc or g.bqgen_fill_ints_u16(key(w, fam, layer, T_SCALE, expert, m), *w.mx_scale_range, ng, s_ptr, stream)
+        if rc != 0:
+            raise RuntimeError(f"synthetic fill failed with code {rc}")
+        return
     rc = rc or g.bqgen_fill_uniform_bf16(key(w, fam, layer, T_SCALE, expert, m), *w.scale_range, ng, s_ptr, stream)
     rc = rc or g.bqgen_fill_uniform_bf16(key(w, fam, layer, T_BIAS, expert, m), *w.bias_range, ng, b_ptr, stream)
     if rc != 0:

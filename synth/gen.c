@@ -69,6 +69,12 @@ void bq_gen_uniform_bf16(uint64_t key, double lo, double hi, int64_t start, int6
   }
 }
 
+void bq_gen_ints_u16(uint64_t key, int lo, int hi, int64_t start, int64_t n, uint16_t* out) {
+  const uint64_t span = (uint64_t)(hi - lo) + 1u;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) out[i] = (uint16_t)(lo + (int)(bq_draw(key, (uint64_t)(start + i)) % span));
+}
+
 static double normal_at(uint64_t key, int64_t m) {
   const double u1 = (double)((bq_draw(key, (uint64_t)(2 * m)) >> 11) + 1) * 0x1p-53;
   const double u2 = (double)(bq_draw(key, (uint64_t)(2 * m + 1)) >> 11) * 0x1p-53;

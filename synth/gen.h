@@ -14,6 +14,8 @@
  *  - uniform: element m is lo + (hi-lo)*t with t = (draw(key, m) >> 11) * 2^-53, evaluated in IEEE
  *             double with one rounding per operation (no fused multiply-add), then rounded to bf16
  *             with round-to-nearest-even.
+ *  - ints:    element m is lo + (draw(key, m) mod (hi - lo + 1)), an integer in [lo, hi] (the
+ *             E8M0 block scales of MXFP4 experts).
  *  - normal:  element m is sigma*sqrt(-2 ln u1)*cos(2 pi u2) (Box and Muller, 1958) with
  *             u1 = ((draw(key,2m) >> 11) + 1) * 2^-53 and u2 = (draw(key,2m+1) >> 11) * 2^-53; host only.
  */
@@ -44,6 +46,8 @@ uint16_t bq_bf16_rne(double v);
 void bq_gen_codes(uint64_t key, int bits, int64_t start, int64_t n, uint8_t* out);
 /* uniform bf16 in [lo, hi] (before rounding): elements [start, start+n). */
 void bq_gen_uniform_bf16(uint64_t key, double lo, double hi, int64_t start, int64_t n, uint16_t* out);
+/* integers in [lo, hi] (0 <= lo <= hi <= 65535), one uint16 each: elements [start, start+n). */
+void bq_gen_ints_u16(uint64_t key, int lo, int hi, int64_t start, int64_t n, uint16_t* out);
 /* normal(0, sigma) rounded to bf16 / to fp32 / left in fp64: elements [start, start+n). */
 void bq_gen_normal_bf16(uint64_t key, double sigma, int64_t start, int64_t n, uint16_t* out);
 void bq_gen_normal_f32(uint64_t key, double sigma, int64_t start, int64_t n, float* out);

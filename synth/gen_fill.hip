@@ -70,6 +70,12 @@ __global__ void fill_uniform_bf16_kernel(uint64_t key, double lo, double hi, int
   }
 }
 
+__global__ void fill_ints_u16_kernel(uint64_t key, int lo, uint64_t span, int64_t n, uint16_t* __restrict__ out) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t m = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; m < n; m += stride)
+    out[m] = (uint16_t)(lo + (int)(draw(key, (uint64_t)m) % span));
+}
+
 int grid_for(int64_t work) {
   int64_t g = (work + 255) / 256;
   if (g > 65536) g = 65536;
@@ -102,6 +108,15 @@ int bqgen_fill_uniform_bf16(uint64_t key, double lo, double hi, int64_t n, void*
   if (n == 0) return 0;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   fill_uniform_bf16_kernel<<<grid_for(n), 256, 0, s>>>(key, lo, hi, n, static_cast<uint16_t*>(out));
+  return (int)hipGetLastError();
+}
+
+// Integers [0, n) in [lo, hi] (0 <= lo <= hi <= 65535), one uint16 each, into device memory `out`.
+int bqgen_fill_ints_u16(uint64_t key, int lo, int hi, int64_t n, void* out, void* stream) {
+  if (out == nullptr || n < 0 || lo < 0 || hi < lo || hi > 65535 || (reinterpret_cast<uintptr_t>(out) & 1u)) return -1;
+  if (n == 0) return 0;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  fill_ints_u16_kernel<<<grid_for(n), 256, 0, s>>>(key, lo, (uint64_t)(hi - lo) + 1u, n, static_cast<uint16_t*>(out));
   return (int)hipGetLastError();
 }
 

@@ -31,13 +31,14 @@ class DeviceLayer:
         s = bq.stream_handle(stream)
         q = [torch.empty(r * c, dtype=torch.uint8, device=device) for r, c in map(w.matrix_shape, range(3))]
         sc = [torch.empty(r * c // w.group, dtype=torch.int16, device=device) for r, c in map(w.matrix_shape, range(3))]
-        bi = [torch.empty_like(t) for t in sc]
+        bi = [torch.empty_like(t) for t in sc] if w.fmt == "affine" else [None] * 3
         targets = [(e, self.experts.data_ptr() + e * self.stride) for e in range(E)]
         if w.has_shared:
             targets.append((synth.SHARED, self.shared.data_ptr()))
         for e, dst in targets:
             for m in range(3):
-                synth.fill_matrix_device(w, layer, e, m, q[m].data_ptr(), sc[m].data_ptr(), bi[m].data_ptr(), s)
+                synth.fill_matrix_device(w, layer, e, m, q[m].data_ptr(), sc[m].data_ptr(),
+                                         bi[m].data_ptr() if bi[m] is not None else 0, s)
             bq.moe_pack_expert_device(H, I, w.bits, w.group, q, sc, bi, dst, s)
         self.router = _i16(synth.router_weights(w, layer)).to(device)
         self.shared_gate = _i16(synth.shared_gate_weights(w, layer)).to(device) if w.has_shared else None

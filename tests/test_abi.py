@@ -50,7 +50,13 @@ def test_blob_bytes_closed_form():
     assert bq.moe_blob_bytes(4096, 1024, 2) == 3_932_160
     assert bq.moe_blob_bytes(256, 128, 4) == 55_296
     assert bq.moe_blob_bytes(4096, 1024, 3) == 0
-    assert bq.moe_blob_bytes(4096, 1024, 4, 32) == 0
+    # MXFP4: 4-bit codes plus one E8M0 byte per block of 32
+    for H, I in ((256, 128), (4096, 1024)):
+        n = 3 * H * I
+        assert bq.moe_blob_bytes(H, I, 4, 32) == n // 2 + n // 32
+    assert bq.moe_blob_bytes(4096, 1024, 4, 32) == 6_684_672
+    assert bq.moe_blob_bytes(4096, 1024, 2, 32) == 0
+    assert bq.moe_blob_bytes(4096, 1024, 4, 16) == 0
     assert bq.moe_blob_bytes(100, 1024, 4) == 0
 
 
@@ -81,6 +87,23 @@ def test_host_pack_roundtrip(name):
         assert np.array_equal((sb >> 16).astype(np.uint16), mat.bias.reshape(-1))
 
 
+def test_host_pack_roundtrip_mx():
+    w = synth.WORKLOADS["tinymx"]
+    ex = synth.expert_arrays(w, 0, 1)
+    H, I = w.hidden, w.inter
+    blob = np.zeros(bq.moe_blob_bytes(H, I, 4, 32), dtype=np.uint8)
+    bq.moe_pack_expert(H, I, 4, 32, [m.q for m in ex.mats], [m.scale for m in ex.mats], [None] * 3, blob)
+    cb, nb = I * H // 2, I * H // 32
+    for m, mat in enumerate(ex.mats):
+        assert np.array_equal(_unpack_codes(blob[m * cb:(m + 1) * cb], 4, I * H), mat.q.reshape(-1))
+        assert np.array_equal(blob[3 * cb + m * nb: 3 * cb + (m + 1) * nb], mat.scale.reshape(-1).astype(np.uint8))
+    big = [m.scale.copy() for m in ex.mats]
+    big[1][0, 0] = 256
+    with pytest.raises(bq.MoeError) as e:
+        bq.moe_pack_expert(H, I, 4, 32, [m.q for m in ex.mats], big, [None] * 3, blob)
+    assert e.value.code == bq.MOE_EINVAL
+
+
 def test_host_pack_rejects_wide_codes():
     H, I = 256, 64
     q = [np.zeros(H * I, np.uint8) for _ in range(3)]
@@ -104,7 +127,7 @@ def _layer(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(bits=3), bq.MOE_EUNSUPPORTED),
-    (dict(group=32), bq.MOE_EUNSUPPORTED),
+    (dict(group=16), bq.MOE_EUNSUPPORTED),
     (dict(hidden=3000), bq.MOE_EUNSUPPORTED),
     (dict(hidden=128), bq.MOE_EUNSUPPORTED),
     (dict(inter=96), bq.MOE_EUNSUPPORTED),
@@ -122,6 +145,8 @@ def _layer(**kw):
     (dict(flags=-1), bq.MOE_EUNSUPPORTED),
     (dict(flags=7), bq.MOE_EUNSUPPORTED),
     (dict(flags=8), bq.MOE_EUNSUPPORTED),
+    (dict(bits=2, group=32), bq.MOE_EUNSUPPORTED),
+    (dict(group=32, expert_stride=6_684_672 + 256, flags=1), bq.MOE_EUNSUPPORTED),
 ])
 def test_layer_validation(kw, code):
     layer = _layer(**kw)

@@ -268,10 +268,68 @@ def pin_zero_input():
     assert np.array_equal(got.out, res)
 
 
+# ---- MXFP4 pins --------------------------------------------------------------------------------
+# The values E2M1 defines (sign, 2 exponent bits, 1 mantissa bit), written out as the list the
+# format specifies rather than derived from bit fields, and E8M0 = 2^(s - 127).
+E2M1_TABLE = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0, -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0]
+TINYMX = synth.WORKLOADS["tinymx"]
+
+
+def _dense_mx(m):
+    return np.array(E2M1_TABLE)[m.q] * np.ldexp(1.0, np.repeat(m.scale.astype(np.int64) - 127, 32, axis=1))
+
+
+def pin_mx_e2m1_table():
+    q = np.tile(np.arange(16, dtype=np.uint8), 2).reshape(1, 32)
+    W = oracle.dequant_mx(q, np.full((1, 1), 127, np.uint16))
+    assert np.array_equal(W[0], np.array(E2M1_TABLE * 2))
+    assert np.signbit(W[0, 8]) and not np.signbit(W[0, 0])
+
+
+def pin_mx_e8m0_scales():
+    q = np.full((6, 64), 2, np.uint8)  # E2M1 1.0 everywhere
+    s = np.array([[127, 128], [120, 0], [254, 127], [255, 127], [1, 2], [126, 125]], np.uint16)
+    W = oracle.dequant_mx(q, s)
+    assert W[0, 0] == 1.0 and W[0, 40] == 2.0
+    assert W[1, 0] == 2.0 ** -7 and W[1, 40] == 2.0 ** -127
+    assert W[2, 0] == 2.0 ** 127 and W[2, 40] == 1.0
+    assert np.all(np.isnan(W[3, :32])) and np.all(W[3, 32:] == 1.0)
+    assert W[4, 0] == 2.0 ** -126 and W[4, 63] == 2.0 ** -125
+    assert W[5, 31] == 0.5 and W[5, 32] == 0.25
+
+
+def pin_mx_dequant_bruteforce():
+    ex = synth.expert_arrays(TINYMX, 0, 3)
+    for m in ex.mats:
+        assert np.array_equal(oracle.dequant_mx(m.q, m.scale), _dense_mx(m))
+
+
+def pin_mx_expert_bruteforce():
+    ex = synth.expert_arrays(TINYMX, 0, 5)
+    x = synth.tokens_x(TINYMX, 0, 1)[0].astype(np.float64)
+    Wg, Wu, Wd = (_dense_mx(m) for m in ex.mats)
+    a, c = Wg @ x, Wu @ x
+    want = Wd @ (a * sp.expit(a) * c)
+    got = oracle.expert(x, ex, 32)
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-13)
+
+
+def pin_mx_expert_closed_form():
+    # every weight 1.0 (code 2, scale 127), x = ones: a = c = H, h = H^2 * sigmoid(H), y = I * h
+    H, I = 64, 96
+    mk = lambda r, cc: synth.MatrixArrays(np.full((r, cc), 2, np.uint8), np.full((r, cc // 32), 127, np.uint16),
+                                          None, "mxfp4")
+    ex = synth.ExpertArrays(mk(I, H), mk(I, H), mk(H, I))
+    y = oracle.expert(np.ones(H), ex, 32)
+    h = H * H * sp.expit(H)
+    assert np.allclose(y, I * h, rtol=1e-14)
+
+
 PINS = [pin_dequant_special_cases, pin_dequant_bruteforce, pin_matvec_onehot, pin_router_logits,
         pin_topk_sorted, pin_topk_duplicate_rows_tie, pin_route_weights, pin_shared_gate,
         pin_expert_bruteforce, pin_expert_bias_only, pin_swiglu_points, pin_combine, pin_rmsnorm,
-        pin_tiny_layer_bruteforce, pin_zero_input]
+        pin_tiny_layer_bruteforce, pin_zero_input, pin_mx_e2m1_table, pin_mx_e8m0_scales,
+        pin_mx_dequant_bruteforce, pin_mx_expert_bruteforce, pin_mx_expert_closed_form]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -349,6 +407,12 @@ MUTANTS = {
     "combine drops residual": ("double acc = res[r];", "double acc = 0.0;"),
     "combine transposes y": ("acc += w[k] * y[k * H + r];", "acc += w[k] * y[r * K + k];"),
     "rmsnorm without mean": ("ss / (double)H + eps", "ss + eps"),
+    "e2m1 exponent bias 0": ("ldexp(1.0 + 0.5 * m, e - 1)", "ldexp(1.0 + 0.5 * m, e)"),
+    "e2m1 no subnormals": ("e == 0 ? 0.5 * m", "e == 0 ? 1.0 * m"),
+    "e2m1 sign ignored": ("return sign ? -v : v;", "return v;"),
+    "e8m0 bias 128": ("ldexp(1.0, (int)s - 127)", "ldexp(1.0, (int)s - 128)"),
+    "mx block of 64": ("scale[r * nb + c / 32]", "scale[r * nb + c / 64]"),
+    "mx down uses gate codes": ("oracle_dequant_mx(H, I, q[2], scale[2], Wd);", "oracle_dequant_mx(H, I, q[0], scale[2], Wd);"),
 }
 
 
@@ -370,7 +434,8 @@ def test_mutants_are_caught(name, tmp_path):
     real = oracle.lib()  # rebuild the argtypes on the mutant by swapping the path
     mut = ctypes.CDLL(str(so))
     for fname in ("oracle_dequant", "oracle_matvec", "oracle_router_logits", "oracle_topk", "oracle_route_weights",
-                  "oracle_shared_gate", "oracle_expert", "oracle_combine", "oracle_rmsnorm"):
+                  "oracle_shared_gate", "oracle_expert", "oracle_combine", "oracle_rmsnorm", "oracle_dequant_mx",
+                  "oracle_expert_mx"):
         getattr(mut, fname).argtypes = getattr(real, fname).argtypes
         getattr(mut, fname).restype = getattr(real, fname).restype
     oracle._lib = mut
