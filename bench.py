@@ -120,7 +120,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="decode4", choices=["decode4", "decode2", "decodemx", "prefill4", "stack60"])
+    ap.add_argument("--workload", default="decode4", choices=["decode4", "decode2", "decodemx", "prefill4", "prefillmx", "stack60"])
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cold", action="store_true")

@@ -141,8 +141,11 @@ PrefillWorkspace carve_prefill_impl(const Geometry& g, int T, void* base, size_t
   w.layer.g = c.take<float>(t);
   w.layer.h = nullptr;
   w.layer.u = nullptr;
-  w.xq = c.take<uint16_t>(t * g.H);
-  w.xs = c.take<float>(t * (g.H / 64));
+  const bool mx = g.form == 3;
+  w.xq = mx ? nullptr : c.take<uint16_t>(t * g.H);
+  w.xs = mx ? nullptr : c.take<float>(t * (g.H / 64));
+  w.x8 = mx ? c.take<uint8_t>(3 * t * g.H) : nullptr;
+  w.xsc = mx ? c.take<uint8_t>(3 * t * (g.H / 32)) : nullptr;
   w.hist = c.take<int32_t>(((N + 255) / 256) * g.E);
   w.counts = c.take<int32_t>(g.E);
   w.offsets = c.take<int32_t>(g.E + 1);
@@ -151,8 +154,11 @@ PrefillWorkspace carve_prefill_impl(const Geometry& g, int T, void* base, size_t
   w.ntiles = c.take<int32_t>(1);
   w.pos = c.take<int32_t>(N);
   w.perm = c.take<int32_t>(N);
-  w.hq = c.take<uint16_t>(R * g.I);
-  w.hs = c.take<float>(R * (g.I / 64));
+  w.hq = mx ? nullptr : c.take<uint16_t>(R * g.I);
+  w.hs = mx ? nullptr : c.take<float>(R * (g.I / 64));
+  w.h32 = mx ? c.take<float>(R * g.I) : nullptr;
+  w.h8 = mx ? c.take<uint8_t>(3 * R * g.I) : nullptr;
+  w.hsc = mx ? c.take<uint8_t>(3 * R * (g.I / 32)) : nullptr;
   w.y = c.take<float>(R * g.H);
   *total = c.used;
   return w;
@@ -287,9 +293,9 @@ int moe_dequant(const moe_layer_t* layer, int expert, int matrix, int out_dtype,
 }
 
 namespace {
-// The grouped (prefill) path: affine layers from MOE_PREFILL_MIN_TOKENS tokens. MXFP4 layers run the
-// per-token kernels at every T.
-bool use_prefill(const Geometry& g, int T) { return T >= MOE_PREFILL_MIN_TOKENS && g.form != 3; }
+// The grouped (prefill) path, from MOE_PREFILL_MIN_TOKENS tokens (MXFP4 layers need inter >= 128:
+// their grouped GEMM steps K by 128).
+bool use_prefill(const Geometry& g, int T) { return T >= MOE_PREFILL_MIN_TOKENS && (g.form != 3 || g.I >= 128); }
 
 size_t needed_ws(const Geometry& g, int T) {
   size_t n = workspace_layer_bytes(g, T);

@@ -55,6 +55,13 @@ struct PrefillWorkspace {
   uint16_t* hq;     // [R][I] SwiGLU outputs in fp16 (same 8-block order as xq)
   float* hs;        // [R][I/64] group sums of the fp16 SwiGLU outputs
   float* y;         // [R][H] down outputs
+  // MXFP4 layers only (null otherwise): 3-term MXFP8 expansions of the activations and of the
+  // SwiGLU outputs (term planes of E4M3 bytes, E8M0 scales per 32), and the fp32 SwiGLU outputs
+  uint8_t* x8;      // [3][T][H]
+  uint8_t* xsc;     // [3][T][H/32]
+  float* h32;       // [R][I]
+  uint8_t* h8;      // [3][R][I]
+  uint8_t* hsc;     // [3][R][I/32]
 };
 
 bool geometry_from(const moe_layer_t* L, Geometry* g, const char** why);

@@ -269,6 +269,12 @@ struct GroupArgs {
   float* os;
   float* oy;  // down: [rows][nout]
   int nout;
+  // MXFP4 layers: activations as kMxTerms planes of E4M3 bytes [rows][KDIM] (a_plane bytes apart)
+  // with E8M0 scales [rows][KDIM/32] (sc_plane bytes apart); gate/up writes fp32 SwiGLU outputs
+  const uint8_t* a8;
+  const uint8_t* asc;
+  uint64_t a_plane, sc_plane;
+  float* oh32;
 };
 
 constexpr int kTileM = 32;  // token rows per tile
@@ -708,6 +714,256 @@ __global__ __launch_bounds__(kThreads, GATEUP ? BQ_LB_GU : BQ_LB_DOWN) void k_gr
   }
 }
 
+
+// ---- MXFP4 experts on the scaled MX MFMA ------------------------------------------------------------
+// v_mfma_scale_f32_16x16x128_f8f6f4 with A = E4M3 activations and B = E2M1 codes, block scales
+// applied by the matrix core (lane layout checked on the device): B lane j + 16q holds block q
+// (32 codes = 16 bytes, lower nibble first) of column j with that block's scale; A lane i + 16q
+// holds K = 16q..16q+15 (bytes 0-15) and K = 64+16q..64+16q+15 (bytes 16-31) of row i, with the
+// scale of block q; D as for the other 16 x 16 MFMAs.
+constexpr int kMxTerms = 3;
+
+// 3-term MXFP8 expansion of fp32 rows (E4M3 values, one E8M0 scale per block of 32):
+// x = sum_t q_t * 2^(e_t - 127) + r. Term t quantises what terms 0..t-1 left, with the block scale
+// chosen so that the block's largest magnitude falls in [128, 256) (no E4M3 saturation); the
+// residual is exact in fp32, and after three terms |r| is about 2^-12 of each element (less
+// than fp16's rounding). Lanes are elements; each 32-lane half of a wave is one block.
+__global__ __launch_bounds__(kThreads) void k_prep_mx(int64_t nblk, const float* __restrict__ x, uint8_t* __restrict__ q8,
+                                                      uint8_t* __restrict__ sc, uint64_t q_plane, uint64_t sc_plane) {
+  const int lane = threadIdx.x & 63;
+  const int64_t blk = (((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6) * 2 + (lane >> 5);
+  if (blk >= nblk) return;  // whole 32-lane halves
+  const int64_t i = blk * 32 + (lane & 31);
+  float r = x[i];
+#pragma unroll
+  for (int t = 0; t < kMxTerms; ++t) {
+    float a = fabsf(r);
+#pragma unroll
+    for (int m = 16; m >= 1; m >>= 1) a = fmaxf(a, __shfl_xor(a, m, 32));
+    const int e = a > 0.0f ? max(-127, min(127, ilogbf(a) - 7)) : -127;
+    const float y = r * ldexpf(1.0f, -e);  // exact, |y| < 256
+    const uint32_t code = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y, 0.0f, 0, false) & 0xFFu;
+    q8[t * q_plane + i] = (uint8_t)code;
+    if ((lane & 31) == 0) sc[t * sc_plane + blk] = (uint8_t)(e + 127);
+    r -= __builtin_amdgcn_cvt_f32_fp8((int)code, 0) * ldexpf(1.0f, e);  // exact
+  }
+}
+
+typedef int v8i_t __attribute__((ext_vector_type(8)));
+typedef float f32x4m_t __attribute__((ext_vector_type(4)));
+
+struct MxCodes {
+  u32x4_t v[2];     // [row block]: 16 code bytes (block q of the step for lane q)
+  uint32_t sc[2];   // [row block]: the step's 4 E8M0 bytes of the lane's row
+};
+struct MxAct {
+  u32x4_t v[kMxTerms];  // 16 bytes of each term: row tid/8, slot tid%8 of the step
+  uint32_t sc;          // 4 scale bytes of (term min(tid/32, 2), row tid%32)
+};
+
+// Block: as k_grouped (4 waves, a tile of up to 32 tokens as one or two 16-token halves, each wave
+// 32 rows of one matrix per slab, slabs walked in order, XCD-aware tile placement). Step: K = 128,
+// i.e. 4 MX blocks: per row block one 16-byte code load and one scale dword; the tile's three
+// activation terms (12 KiB) through an LDS ring. Codes keep three register stages and
+// activations two sets, so every load has two steps to land. No dequantisation on the VALU: the
+// MFMA consumes the packed codes and both scale sets.
+template <int KDIM, bool GATEUP, bool SHARED>
+__global__ __launch_bounds__(kThreads, GATEUP ? BQ_LB_GU : BQ_LB_DOWN) void k_grouped_mx(GroupArgs g, int sgroups) {
+  static_assert(KDIM % 128 == 0, "K steps of 128");
+  constexpr int NSTEP = KDIM / 128;          // steps per slab
+  constexpr int ROWB = KDIM / 2;             // code bytes per row
+  constexpr int NB = KDIM / 32;              // scale bytes per row
+  constexpr int ROWS_B = GATEUP ? 64 : 128;  // rows per matrix per slab
+  __shared__ u32x4_t a_lds[2][kMxTerms][kTileM][8];  // [parity][term][row][16-byte slot ^ swizzle]
+  __shared__ uint32_t sc_lds[2][kMxTerms][kTileM];
+  __shared__ float x_lds[GATEUP ? 2 : 1][16][64];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int c16 = lane & 15, q = lane >> 4;
+  const int mi = GATEUP ? (wave >> 1) : 0;
+  const int wrow = (GATEUP ? (wave & 1) : wave) * 32;
+  const int b8 = 8 * sgroups;
+  const int tau = (int)(blockIdx.x / b8) * 8 + (int)(blockIdx.x & 7);
+  const int gy = (int)(blockIdx.x % b8) >> 3;
+  int first, count;
+  const uint8_t* blob;
+  if constexpr (SHARED) {
+    first = tau * kTileM;
+    if (first >= g.T) return;  // uniform per block
+    count = min(kTileM, g.T - first);
+    blob = g.shared;
+  } else {
+    if (tau >= *g.ntiles) return;  // uniform per block
+    const int e = g.tile_e[tau];
+    first = g.tile_first[tau];
+    count = min(kTileM, g.offsets[e + 1] - first);
+    blob = g.experts + (size_t)e * g.stride;
+  }
+  const int nh = count > 16 ? 2 : 1;
+  auto arow = [&](int m) -> int {
+    const int mm = first + min(m, count - 1);
+    if constexpr (SHARED) return GATEUP ? mm : g.shared_base + mm;
+    else return GATEUP ? g.perm[mm] / g.K : mm;
+  };
+  auto orow = [&](int m) -> int { return SHARED ? g.shared_base + first + m : first + m; };
+
+  // activation loads: row tid/8, 16-byte slot tid%8 of each term; scale dword of (term, row)
+  const int a_row = tid >> 3, a_slot = tid & 7;
+  const uint8_t* a_src = g.a8 + (size_t)arow(a_row) * KDIM + a_slot * 16;
+  const int s_term = min(tid >> 5, kMxTerms - 1), s_row = tid & 31;
+  const uint8_t* s_src = g.asc + s_term * g.sc_plane + (size_t)arow(s_row) * NB;
+  auto load_act = [&](MxAct& r, int s) {
+    const int k = s % NSTEP;
+#pragma unroll
+    for (int t = 0; t < kMxTerms; ++t) r.v[t] = *reinterpret_cast<const u32x4_t*>(a_src + t * g.a_plane + k * 128);
+    r.sc = *reinterpret_cast<const uint32_t*>(s_src + k * 4);
+  };
+  // slot swizzle: the 16 rows a fragment read touches hit distinct banks
+  auto park_act = [&](const MxAct& r, int s) {
+#pragma unroll
+    for (int t = 0; t < kMxTerms; ++t) a_lds[s & 1][t][a_row][a_slot ^ ((a_row >> 1) & 7)] = r.v[t];
+    if (tid < kMxTerms * 32) sc_lds[s & 1][s_term][s_row] = r.sc;
+  };
+
+  const int nslab = (g.nout + ROWS_B - 1) / ROWS_B;
+  const int spb = (nslab + sgroups - 1) / sgroups;
+  const int slab0 = gy * spb;
+  const int ntot = (min(nslab, slab0 + spb) - slab0) * NSTEP;
+  if (ntot <= 0) return;  // uniform per block
+  const __amdgpu_buffer_rsrc_t crs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(blob + g.off_codes[mi]), (short)0, g.nout * ROWB, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t srs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(blob + g.off_sb[mi]), (short)0, g.nout * NB, kRsrcWord3);
+  // clamped rows and steps: every path issues the same loads (exact wait counts)
+  auto load_codes = [&](MxCodes& st, int s) {
+    const int slab = slab0 + s / NSTEP, k = s % NSTEP;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int row = min(slab * ROWS_B + wrow + 16 * rb + c16, g.nout - 1);
+      st.v[rb] = __builtin_amdgcn_raw_buffer_load_b128(crs, row * ROWB + 16 * q, k * 64, 0);
+      st.sc[rb] = __builtin_amdgcn_raw_buffer_load_b32(srs, row * NB, k * 4, 0);
+    }
+  };
+
+  f32x4m_t acc[2][2];
+#pragma unroll
+  for (int th = 0; th < 2; ++th)
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) acc[th][rb] = f32x4m_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  auto compute = [&](const MxCodes& st, int s) __attribute__((always_inline)) {
+    v8i_t b[2];
+    int sb[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      b[rb] = v8i_t{(int)st.v[rb][0], (int)st.v[rb][1], (int)st.v[rb][2], (int)st.v[rb][3], 0, 0, 0, 0};
+      sb[rb] = (int)((st.sc[rb] >> (8 * q)) & 0xFFu);
+    }
+#pragma unroll
+    for (int th = 0; th < 2; ++th) {
+      if (th < nh) {
+        const int row = 16 * th + c16, sw = (row >> 1) & 7;
+#pragma unroll
+        for (int t = 0; t < kMxTerms; ++t) {
+          const u32x4_t lo = a_lds[s & 1][t][row][q ^ sw], hi = a_lds[s & 1][t][row][(4 + q) ^ sw];
+          const v8i_t a = v8i_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+          const int sa = (int)((sc_lds[s & 1][t][row] >> (8 * q)) & 0xFFu);
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
+            acc[th][rb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b[rb], acc[th][rb], 0, 4, 0, sa, 0, sb[rb]);
+        }
+      }
+    }
+  };
+
+  // End of a slab: element e of acc[th][rb] is token 16*th + 4*q + e, row slab*ROWS_B + wrow + 16*rb + c16.
+  auto finish_slab = [&](int slab) __attribute__((always_inline)) {
+    if constexpr (GATEUP) {
+      if (mi == 0) {
+#pragma unroll
+        for (int th = 0; th < 2; ++th)
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x_lds[wave][8 * th + 4 * rb + e][lane] = acc[th][rb][e];
+      }
+      __syncthreads();
+      if (mi == 1 && slab * ROWS_B + wrow < g.nout) {
+#pragma unroll
+        for (int th = 0; th < 2; ++th) {
+          if (th < nh) {
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+              const int row = slab * ROWS_B + wrow + 16 * rb + c16;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int m = 16 * th + 4 * q + e;
+                const float a = x_lds[wave - 2][8 * th + 4 * rb + e][lane], c = acc[th][rb][e];
+                if (m < count) g.oh32[(size_t)orow(m) * g.nout + row] = a / (1.0f + expf(-a)) * c;
+              }
+            }
+          }
+        }
+      }
+      __syncthreads();
+    } else {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const int row = slab * ROWS_B + wrow + 16 * rb + c16;
+        if (row < g.nout) {
+#pragma unroll
+          for (int th = 0; th < 2; ++th)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int m = 16 * th + 4 * q + e;
+              if (m < count) g.oy[(size_t)orow(m) * g.nout + row] = acc[th][rb][e];
+            }
+        }
+      }
+    }
+#pragma unroll
+    for (int th = 0; th < 2; ++th)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) acc[th][rb] = f32x4m_t{0.0f, 0.0f, 0.0f, 0.0f};
+  };
+
+  MxCodes c0, c1, c2;
+  MxAct a0, a1;
+  auto body = [&](auto ci, auto ai, int s) __attribute__((always_inline)) {
+    constexpr int CI = decltype(ci)::value, AI = decltype(ai)::value;
+    MxCodes& cur = CI == 0 ? c0 : (CI == 1 ? c1 : c2);
+    MxCodes& ahead = CI == 0 ? c2 : (CI == 1 ? c0 : c1);
+    MxAct& aload = AI == 0 ? a0 : a1;
+    MxAct& apark = AI == 0 ? a1 : a0;
+    load_act(aload, min(s + 2, ntot - 1));
+    load_codes(ahead, min(s + 2, ntot - 1));
+    if (s < ntot) {  // uniform per block
+      compute(cur, s);
+      if (s % NSTEP == NSTEP - 1) finish_slab(slab0 + s / NSTEP);
+    }
+    park_act(apark, s + 1);
+    __syncthreads();
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  load_act(a0, 0);
+  load_act(a1, min(1, ntot - 1));
+  load_codes(c0, 0);
+  load_codes(c1, min(1, ntot - 1));
+  park_act(a0, 0);
+  __syncthreads();
+#pragma unroll 1
+  for (int s = 0; s < ntot; s += 6) {
+    body(I0{}, I0{}, s);
+    body(I1{}, I1{}, s + 1);
+    body(I2{}, I0{}, s + 2);
+    body(I0{}, I1{}, s + 3);
+    body(I1{}, I0{}, s + 4);
+    body(I2{}, I1{}, s + 5);
+  }
+}
+
 // ---- 6. combine (gather) / scatter ------------------------------------------------------------------
 // out[t][r] = residual[t][r] + sum_k w[t][k] * y[pos[t*K+k]][r] + g[t] * y[T*K + t][r]   (combine)
 // y_out[t][k][r] = y[pos[t*K+k]][r], y_out[t][K][r] = y[T*K + t][r]                       (scatter)
@@ -773,8 +1029,41 @@ hipError_t launch_grouped(const GroupArgs& ga, int nout, int T, int N, int E, bo
   return hipGetLastError();
 }
 
+template <int KDIM, bool GATEUP>
+hipError_t launch_grouped_mx(const GroupArgs& ga, int nout, int T, int N, int E, bool has_shared, hipStream_t s) {
+  constexpr int RS = GATEUP ? 64 : 128;
+  const dim3 block(kThreads);
+  const int max_tiles = E + (int)cdiv(N, kTileM);
+  const int rg = slab_groups(std::min(max_tiles, N), nout, RS);
+  hipLaunchKernelGGL((k_grouped_mx<KDIM, GATEUP, false>), dim3(grouped_grid(max_tiles, rg)), block, 0, s, ga, rg);
+  if (has_shared) {
+    const int st = (int)cdiv(T, kTileM);
+    const int sg = slab_groups(st, nout, RS);
+    hipLaunchKernelGGL((k_grouped_mx<KDIM, GATEUP, true>), dim3(grouped_grid(st, sg)), block, 0, s, ga, sg);
+  }
+  return hipGetLastError();
+}
+
 #define BQ_FOR_KDIM_GU(X) X(256) X(512) X(1024) X(2048) X(4096) X(8192)
 #define BQ_FOR_KDIM_DN(X) X(64) X(128) X(256) X(512) X(1024) X(2048)
+
+#define BQ_FOR_KDIM_MX(X) X(128) X(256) X(512) X(1024) X(2048) X(4096) X(8192)
+hipError_t dispatch_mx(bool gateup, int kdim, const GroupArgs& ga, int nout, int T, int N, int E, bool hs, hipStream_t s) {
+#define BQ_CASE(KV)                                                                        \
+  case KV:                                                                                 \
+    return gateup ? launch_grouped_mx<KV, true>(ga, nout, T, N, E, hs, s)                  \
+                  : launch_grouped_mx<KV, false>(ga, nout, T, N, E, hs, s);
+  switch (kdim) { BQ_FOR_KDIM_MX(BQ_CASE) }
+#undef BQ_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_prep_mx(int rows, int cols, const float* x, uint8_t* q8, uint8_t* sc, hipStream_t s) {
+  const int64_t nblk = (int64_t)rows * cols / 32;
+  hipLaunchKernelGGL(k_prep_mx, dim3(cdiv(nblk, 2 * (kThreads / 64))), dim3(kThreads), 0, s, nblk, x, q8, sc,
+                     (uint64_t)rows * cols, (uint64_t)nblk);
+  return hipGetLastError();
+}
 
 hipError_t dispatch_gateup(int bits, int H, const GroupArgs& ga, int I, int T, int N, int E, bool hs, hipStream_t s) {
 #define BQ_CASE(KV)                                                                   \
@@ -818,7 +1107,13 @@ hipError_t launch_prefill(const Geometry& g, const LayerPtrs& p, const float* x,
   const int H = g.H, I = g.I, E = g.E, K = g.K;
   const int N = T * K;
   const int nchunks = (int)cdiv(N, kChunk);
-  hipLaunchKernelGGL(k_prep, dim3(T), dim3(kThreads), 0, s, H, x, reinterpret_cast<_Float16*>(w.xq), w.xs);
+  const bool mx = g.form == 3;
+  if (mx) {
+    hipError_t e = launch_prep_mx(T, H, x, w.x8, w.xsc, s);
+    if (e != hipSuccess) return e;
+  } else {
+    hipLaunchKernelGGL(k_prep, dim3(T), dim3(kThreads), 0, s, H, x, reinterpret_cast<_Float16*>(w.xq), w.xs);
+  }
   const int32_t* idx = idx_in;
   if (idx_in == nullptr) {
     // the fp64 GEMM fills the chip only for many tokens; below that, per-token router rows win
@@ -838,6 +1133,24 @@ hipError_t launch_prefill(const Geometry& g, const LayerPtrs& p, const float* x,
   // gate/up + SwiGLU
   ga.off_codes[0] = g.off_codes[0]; ga.off_codes[1] = g.off_codes[1];
   ga.off_sb[0] = g.off_sb[0]; ga.off_sb[1] = g.off_sb[1];
+  if (mx) {
+    const int R = N + (g.has_shared ? T : 0);
+    ga.a8 = w.x8; ga.asc = w.xsc; ga.a_plane = (uint64_t)T * H; ga.sc_plane = (uint64_t)T * H / 32;
+    ga.oh32 = w.h32; ga.nout = I;
+    hipError_t e = dispatch_mx(true, H, ga, I, T, N, E, g.has_shared != 0, s);
+    if (e == hipSuccess) e = launch_prep_mx(R, I, w.h32, w.h8, w.hsc, s);
+    if (e != hipSuccess) return e;
+    ga.off_codes[0] = g.off_codes[2]; ga.off_sb[0] = g.off_sb[2];
+    ga.a8 = w.h8; ga.asc = w.hsc; ga.a_plane = (uint64_t)R * I; ga.sc_plane = (uint64_t)R * I / 32;
+    ga.oy = w.y; ga.nout = H;
+    e = dispatch_mx(false, I, ga, H, T, N, E, g.has_shared != 0, s);
+    if (e != hipSuccess) return e;
+    if (idx_out && idx_in == nullptr)
+      hipLaunchKernelGGL(k_copy_i32, dim3(cdiv(N, kThreads)), dim3(kThreads), 0, s, N, w.layer.idx, idx_out);
+    hipLaunchKernelGGL(k_prefill_out, dim3(cdiv(H, kThreads), T), dim3(kThreads), 0, s, T, H, K, g.has_shared, w.pos,
+                       w.y, w.layer.w, w.layer.g, residual, out, y_out);
+    return hipGetLastError();
+  }
   ga.a = reinterpret_cast<const _Float16*>(w.xq); ga.as = w.xs;
   ga.oh = reinterpret_cast<_Float16*>(w.hq); ga.os = w.hs; ga.nout = I;
   hipError_t e = dispatch_gateup(g.bits, H, ga, I, T, N, E, g.has_shared != 0, s);

@@ -1,5 +1,6 @@
 """GPU parity of MXFP4 expert layers (E2M1 codes, one E8M0 scale per 32, top-6 routing) against the
-fp64 oracle, through the C ABI on an MI355X.
+fp64 oracle, through the C ABI on an MI355X. From 56 tokens the layer runs the grouped path on the
+scaled MX MFMA, with the activations as 3-term MXFP8 expansions.
 
 Bar as for the affine layers: bit-exact top-K indices and dequantised weights; outputs within
 2e-3*max|oracle| + 1e-5 per token vector.
@@ -95,8 +96,8 @@ def test_mx_expert_ffn_and_combine(which, T, request):
             assert_close(yn[t, k], ref.expert_out(xs[t], int(e)), f"y[{t}][{k}]")
 
 
-@pytest.mark.parametrize("which,t0,T", [("tinymx", 0, 1), ("tinymx", 1, 24), ("tinymx", 30, 64), ("decmx", 0, 1),
-                                         ("decmx", 500, 4), ("decmx", 700, 64)])
+@pytest.mark.parametrize("which,t0,T", [("tinymx", 0, 1), ("tinymx", 1, 24), ("tinymx", 30, 64), ("tinymx", 3, 200),
+                                         ("decmx", 0, 1), ("decmx", 500, 4), ("decmx", 700, 64), ("decmx", 0, 2048)])
 def test_mx_layer_forward(which, t0, T, request):
     L, ref = request.getfixturevalue(which)
     w = L.w
