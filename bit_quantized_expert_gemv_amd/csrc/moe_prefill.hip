@@ -79,76 +79,129 @@ __global__ __launch_bounds__(kThreads) void k_prep(int H, const float* __restric
 // v_mfma_f64_16x16x4_f64: every bf16 x fp32 product is exact in fp64 and the sums are fp64, so the
 // top-K decision is exact up to fp64 rounding. Lane layout (checked on the device): A[i][k] in lane
 // i + 16k, B[k][j] in lane j + 16k, D[i][j] in lane j + 16*(i%4), element i/4.
-// Block: 4 waves, 64 tokens x 32 rows; wave (wt, wr) owns tokens 32wt..32wt+31 x rows 16wr..16wr+15
-// as two 16 x 16 tiles that share the row operand. Operands are staged in LDS as fp64, token- or
-// row-major with a 34-double stride: a fragment read (16 rows x 4 consecutive k per 32-lane pass)
-// and the 16-byte staging writes both touch distinct banks. The next k-slice is in flight during
-// the MFMAs.
+// Each wave owns 32 tokens x 32 rows as 2 x 2 tiles over a quarter of K; the four waves of a block split
+// K and add their parts in a fixed order (((q0 + q1) + q2) + q3). There is no LDS staging: within each
+// 32-wide K slice, MFMA step s of lane (i, kk) takes k = 8*kk + s instead of 4*s + kk (both operands
+// use the same order, so every product is still paired), so a lane's operands are 8 contiguous
+// elements of its token or row: two 16-byte loads of x, one of the router row. Three register stages
+// keep two slices in flight during the MFMAs; the bf16 and fp32 values widen to fp64 exactly, one
+// step at a time.
 typedef double f64x4_t __attribute__((ext_vector_type(4)));
-typedef double f64x2_t __attribute__((ext_vector_type(2)));
-constexpr int kRTok = 64, kRRow = 32, kRK = 32, kRS = kRK + 2;
+constexpr int kRW = 32;      // tokens and rows per wave
+#ifndef BQ_ROUTER_SPLITK
+#define BQ_ROUTER_SPLITK 4
+#endif
+constexpr int kRSplit = BQ_ROUTER_SPLITK;  // waves per block, each with 1/kRSplit of K
+constexpr int kRSlice = 32;  // K per slice
 #ifndef BQ_ROUTER_GEMM_MIN
 #define BQ_ROUTER_GEMM_MIN 256
 #endif
 constexpr int kRouterGemmMinTokens = BQ_ROUTER_GEMM_MIN;
-__global__ __launch_bounds__(kThreads) void k_router_gemm(int T, int H, int E, int has_shared,
-                                                          const float* __restrict__ x,
-                                                          const uint16_t* __restrict__ router,
-                                                          const uint16_t* __restrict__ sgate,
-                                                          double* __restrict__ logits) {
-  __shared__ double xs[kRTok][kRS];
-  __shared__ double rs[kRRow][kRS];
-  const int t0 = blockIdx.y * kRTok, e0 = blockIdx.x * kRRow;
-  const int nrows = E + has_shared;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+
+struct RouterRaw {
+  float4 x[2][2];  // [token tile][half]: 8 consecutive x of the lane's token
+  uint4 r[2];      // [row tile]: 8 consecutive bf16 of the lane's row
+};
+
+__global__ __launch_bounds__(64 * kRSplit) void k_router_gemm(int T, int H, int E, int has_shared,
+                                                              const float* __restrict__ x,
+                                                              const uint16_t* __restrict__ router,
+                                                              const uint16_t* __restrict__ sgate,
+                                                              double* __restrict__ logits) {
+  __shared__ f64x4_t part[kRSplit - 1][2][2][64];  // the partial tiles of waves 1..kRSplit-1
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15, kk = lane >> 4;
-  const int wt = wave >> 1, wr = wave & 1;
-  // staging: x as (token tid/4, k 8*(tid%4) .. +7); R as (row tid/8, k 4*(tid%8) .. +3)
-  const int xt = tid >> 2, xk = (tid & 3) * 8;
-  const int rr = tid >> 3, rk = (tid & 7) * 4;
-  const float* xp = x + (size_t)min(t0 + xt, T - 1) * H + xk;
-  const int er = min(e0 + rr, nrows - 1);
-  const uint16_t* rp = ((er < E) ? router + (size_t)er * H : sgate) + rk;
-  float4 xv[2];
+  const int t0 = blockIdx.y * kRW, e0 = blockIdx.x * kRW;
+  const int nrows = E + has_shared;
+  const int kh = H / kRSplit;
+  const int kbeg = wave * kh + 8 * kk;
+  // operand rows of this lane (clamped ones are computed and never stored)
+  const float* xp[2];
+  const uint16_t* rp[2];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) xv[q] = *reinterpret_cast<const float4*>(xp + 4 * q);
-  uint2 rv = *reinterpret_cast<const uint2*>(rp);
-  f64x4_t acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = {0.0, 0.0, 0.0, 0.0};
-  for (int k0 = 0; k0 < H; k0 += kRK) {
-    f64x2_t* xw = reinterpret_cast<f64x2_t*>(&xs[xt][xk]);
+  for (int ti = 0; ti < 2; ++ti) xp[ti] = x + (size_t)min(t0 + 16 * ti + c, T - 1) * H + kbeg;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      xw[2 * q] = f64x2_t{(double)xv[q].x, (double)xv[q].y};
-      xw[2 * q + 1] = f64x2_t{(double)xv[q].z, (double)xv[q].w};
-    }
-    f64x2_t* rw = reinterpret_cast<f64x2_t*>(&rs[rr][rk]);
-    const uint32_t rw32[2] = {rv.x, rv.y};
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-      rw[q] = f64x2_t{(double)bf16_val((uint16_t)(rw32[q] & 0xFFFFu)), (double)bf16_val((uint16_t)(rw32[q] >> 16))};
-    __syncthreads();
-    if (k0 + kRK < H) {  // next slice in flight during the MFMAs
-#pragma unroll
-      for (int q = 0; q < 2; ++q) xv[q] = *reinterpret_cast<const float4*>(xp + k0 + kRK + 4 * q);
-      rv = *reinterpret_cast<const uint2*>(rp + k0 + kRK);
-    }
-#pragma unroll
-    for (int s4 = 0; s4 < kRK / 4; ++s4) {
-      const double bv = rs[wr * 16 + c][4 * s4 + kk];
-      const double a0 = xs[wt * 32 + c][4 * s4 + kk];
-      const double a1 = xs[wt * 32 + 16 + c][4 * s4 + kk];
-      acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, bv, acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, bv, acc1, 0, 0, 0);
-    }
-    __syncthreads();
+  for (int rj = 0; rj < 2; ++rj) {
+    const int e = min(e0 + 16 * rj + c, nrows - 1);
+    rp[rj] = (e < E ? router + (size_t)e * H : sgate) + kbeg;
   }
-  const int e = e0 + wr * 16 + c;
-  if (e >= nrows) return;
+  const int nsl = kh / kRSlice;
+  auto load = [&](RouterRaw& R, int sl) __attribute__((always_inline)) {
+    const int off = sl * kRSlice;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int ta = t0 + wt * 32 + kk + 4 * q;
-    if (ta < T) logits[(size_t)ta * (E + 1) + e] = acc0[q];
-    if (ta + 16 < T) logits[(size_t)(ta + 16) * (E + 1) + e] = acc1[q];
+    for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) R.x[ti][h] = *reinterpret_cast<const float4*>(xp[ti] + off + 4 * h);
+#pragma unroll
+    for (int rj = 0; rj < 2; ++rj) R.r[rj] = *reinterpret_cast<const uint4*>(rp[rj] + off);
+  };
+  f64x4_t acc[2][2];
+#pragma unroll
+  for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+    for (int rj = 0; rj < 2; ++rj) acc[ti][rj] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+  auto compute = [&](const RouterRaw& R) __attribute__((always_inline)) {
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      double a[2], b[2];
+#pragma unroll
+      for (int ti = 0; ti < 2; ++ti) {
+        const float4 v = R.x[ti][st >> 2];
+        const int e = st & 3;
+        a[ti] = (double)(e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w);
+      }
+#pragma unroll
+      for (int rj = 0; rj < 2; ++rj) {
+        const uint4 w = R.r[rj];
+        const uint32_t d = (st >> 1) == 0 ? w.x : (st >> 1) == 1 ? w.y : (st >> 1) == 2 ? w.z : w.w;
+        b[rj] = (double)__uint_as_float((st & 1) ? (d & 0xFFFF0000u) : (d << 16));
+      }
+#pragma unroll
+      for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+        for (int rj = 0; rj < 2; ++rj) acc[ti][rj] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[ti], b[rj], acc[ti][rj], 0, 0, 0);
+    }
+  };
+  RouterRaw r0, r1, r2;
+  load(r0, 0);
+  load(r1, min(1, nsl - 1));
+#pragma unroll 1
+  for (int sl = 0; sl < nsl; sl += 3) {
+    // every load is issued on every path (clamped past the end), so the wait counts stay exact
+    load(r2, min(sl + 2, nsl - 1));
+    compute(r0);
+    load(r0, min(sl + 3, nsl - 1));
+    if (sl + 1 < nsl) compute(r1);
+    load(r1, min(sl + 4, nsl - 1));
+    if (sl + 2 < nsl) compute(r2);
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+      for (int rj = 0; rj < 2; ++rj) part[wave - 1][ti][rj][lane] = acc[ti][rj];
+  }
+  __syncthreads();
+  if (wave > 0) return;
+#pragma unroll
+  for (int w = 0; w < kRSplit - 1; ++w)
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+      for (int rj = 0; rj < 2; ++rj) acc[ti][rj] += part[w][ti][rj][lane];
+  // element q of tile (ti, rj) in lane (c, kk): token t0 + 16ti + kk + 4q, row e0 + 16rj + c
+#pragma unroll
+  for (int rj = 0; rj < 2; ++rj) {
+    const int e = e0 + 16 * rj + c;
+    if (e >= nrows) continue;
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int t = t0 + 16 * ti + kk + 4 * q;
+        if (t < T) logits[(size_t)t * (E + 1) + e] = acc[ti][rj][q];
+      }
+    }
   }
 }
 
@@ -1089,8 +1142,8 @@ hipError_t dispatch_down(int bits, int I, const GroupArgs& ga, int H, int T, int
 
 hipError_t launch_router_gemm(const Geometry& g, const LayerPtrs& p, const float* x, int T, const Workspace& ws,
                               hipStream_t s) {
-  hipLaunchKernelGGL(k_router_gemm, dim3(cdiv(g.E + g.has_shared, kRRow), cdiv(T, kRTok)), dim3(kThreads), 0, s, T, g.H,
-                     g.E, g.has_shared, x, p.router, p.sgate, ws.logits);
+  hipLaunchKernelGGL(k_router_gemm, dim3(cdiv(g.E + g.has_shared, kRW), cdiv(T, kRW)), dim3(64 * kRSplit), 0, s, T,
+                     g.H, g.E, g.has_shared, x, p.router, p.sgate, ws.logits);
   return hipGetLastError();
 }
 
