@@ -805,30 +805,46 @@ __global__ __launch_bounds__(kThreads) void k_prep_mx(int64_t nblk, const float*
 typedef int v8i_t __attribute__((ext_vector_type(8)));
 typedef float f32x4m_t __attribute__((ext_vector_type(4)));
 
+// KB MX K-blocks of 128 per step (KB = 2 wherever K allows): per row block KB code loads of 16 bytes
+// and KB scale dwords in one load.
+template <int KB>
 struct MxCodes {
-  u32x4_t v[2];     // [row block]: 16 code bytes (block q of the step for lane q)
-  uint32_t sc[2];   // [row block]: the step's 4 E8M0 bytes of the lane's row
+  u32x4_t v[2][KB];   // [row block][K-block]: 16 code bytes (block q of the K-block for lane q)
+  uint32_t sc[2][KB]; // [row block][K-block]: the 4 E8M0 bytes of the lane's row
 };
+template <int KB>
 struct MxAct {
-  u32x4_t v[kMxTerms];  // 16 bytes of each term: row tid/8, slot tid%8 of the step
-  uint32_t sc;          // 4 scale bytes of (term min(tid/32, 2), row tid%32)
+  u32x4_t v[kMxTerms][KB];  // 16 bytes of each term: row tid/(8KB) + (32/KB)h, slot tid%(8KB)
+  uint32_t sc[KB];          // scale bytes of (term min(tid/32, 2), row tid%32), 4 per K-block
 };
 
+template <int KB>
+__device__ __forceinline__ void mx_load_scales(uint32_t (&d)[KB], __amdgpu_buffer_rsrc_t rs, int voff, int soff) {
+  if constexpr (KB == 2) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, 0);
+    d[0] = v[0];
+    d[1] = v[1];
+  } else {
+    d[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, 0);
+  }
+}
+
 // Block: as k_grouped (4 waves, a tile of up to 32 tokens as one or two 16-token halves, each wave
-// 32 rows of one matrix per slab, slabs walked in order, XCD-aware tile placement). Step: K = 128,
-// i.e. 4 MX blocks: per row block one 16-byte code load and one scale dword; the tile's three
-// activation terms (12 KiB) through an LDS ring. Codes keep three register stages and
-// activations two sets, so every load has two steps to land. No dequantisation on the VALU: the
-// MFMA consumes the packed codes and both scale sets.
+// 32 rows of one matrix per slab, slabs walked in order, XCD-aware tile placement). Step: K = 128 KB,
+// i.e. 4 KB MX blocks: per row block KB 16-byte code loads (a whole 128-byte line of the row when
+// KB = 2) and one scale load; the tile's three activation terms (12 KiB per K-block) through an LDS ring.
+// No dequantisation on the VALU: the MFMA consumes the packed codes and both scale sets.
 template <int KDIM, bool GATEUP, bool SHARED>
 __global__ __launch_bounds__(kThreads, GATEUP ? BQ_LB_GU : BQ_LB_DOWN) void k_grouped_mx(GroupArgs g, int sgroups) {
   static_assert(KDIM % 128 == 0, "K steps of 128");
-  constexpr int NSTEP = KDIM / 128;          // steps per slab
-  constexpr int ROWB = KDIM / 2;             // code bytes per row
-  constexpr int NB = KDIM / 32;              // scale bytes per row
-  constexpr int ROWS_B = GATEUP ? 64 : 128;  // rows per matrix per slab
-  __shared__ u32x4_t a_lds[2][kMxTerms][kTileM][8];  // [parity][term][row][16-byte slot ^ swizzle]
-  __shared__ uint32_t sc_lds[2][kMxTerms][kTileM];
+  constexpr int KB = (KDIM % 256 == 0) ? 2 : 1;  // K-blocks per step
+  constexpr int SLOTS = 8 * KB;                  // 16-byte activation slots per row and step
+  constexpr int NSTEP = KDIM / (128 * KB);       // steps per slab
+  constexpr int ROWB = KDIM / 2;                 // code bytes per row
+  constexpr int NB = KDIM / 32;                  // scale bytes per row
+  constexpr int ROWS_B = GATEUP ? 64 : 128;      // rows per matrix per slab
+  __shared__ u32x4_t a_lds[2][kMxTerms][kTileM][SLOTS];  // [parity][term][row][16-byte slot ^ swizzle]
+  __shared__ uint32_t sc_lds[2][kMxTerms][kTileM][KB];
   __shared__ float x_lds[GATEUP ? 2 : 1][16][64];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -859,23 +875,39 @@ __global__ __launch_bounds__(kThreads, GATEUP ? BQ_LB_GU : BQ_LB_DOWN) void k_gr
     else return GATEUP ? g.perm[mm] / g.K : mm;
   };
   auto orow = [&](int m) -> int { return SHARED ? g.shared_base + first + m : first + m; };
+  // LDS slot swizzle: the 16 rows of a fragment read (and of a 16-lane write) hit distinct banks.
+  // Rows of 128 bytes (KB = 1) alternate bank halves; rows of 256 bytes all start at bank 0.
+  auto swz = [](int row, int slot) -> int { return KB == 2 ? (slot ^ (row & 15)) : (slot ^ ((row >> 1) & 7)); };
 
-  // activation loads: row tid/8, 16-byte slot tid%8 of each term; scale dword of (term, row)
-  const int a_row = tid >> 3, a_slot = tid & 7;
-  const uint8_t* a_src = g.a8 + (size_t)arow(a_row) * KDIM + a_slot * 16;
+  // activation loads: row tid/SLOTS + (32/KB)h, slot tid%SLOTS of each term; the scales of (term, row)
+  const int a_row = tid / SLOTS, a_slot = tid % SLOTS;
+  const uint8_t* a_src[KB];
+#pragma unroll
+  for (int h = 0; h < KB; ++h) a_src[h] = g.a8 + (size_t)arow(a_row + (32 / KB) * h) * KDIM + a_slot * 16;
   const int s_term = min(tid >> 5, kMxTerms - 1), s_row = tid & 31;
   const uint8_t* s_src = g.asc + s_term * g.sc_plane + (size_t)arow(s_row) * NB;
-  auto load_act = [&](MxAct& r, int s) {
+  auto load_act = [&](MxAct<KB>& r, int s) __attribute__((always_inline)) {
     const int k = s % NSTEP;
 #pragma unroll
-    for (int t = 0; t < kMxTerms; ++t) r.v[t] = *reinterpret_cast<const u32x4_t*>(a_src + t * g.a_plane + k * 128);
-    r.sc = *reinterpret_cast<const uint32_t*>(s_src + k * 4);
-  };
-  // slot swizzle: the 16 rows a fragment read touches hit distinct banks
-  auto park_act = [&](const MxAct& r, int s) {
+    for (int t = 0; t < kMxTerms; ++t)
 #pragma unroll
-    for (int t = 0; t < kMxTerms; ++t) a_lds[s & 1][t][a_row][a_slot ^ ((a_row >> 1) & 7)] = r.v[t];
-    if (tid < kMxTerms * 32) sc_lds[s & 1][s_term][s_row] = r.sc;
+      for (int h = 0; h < KB; ++h)
+        r.v[t][h] = *reinterpret_cast<const u32x4_t*>(a_src[h] + t * g.a_plane + k * 128 * KB);
+#pragma unroll
+    for (int j = 0; j < KB; ++j) r.sc[j] = *reinterpret_cast<const uint32_t*>(s_src + k * 4 * KB + 4 * j);
+  };
+  auto park_act = [&](const MxAct<KB>& r, int s) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < kMxTerms; ++t)
+#pragma unroll
+      for (int h = 0; h < KB; ++h) {
+        const int row = a_row + (32 / KB) * h;
+        a_lds[s & 1][t][row][swz(row, a_slot)] = r.v[t][h];
+      }
+    if (tid < kMxTerms * 32) {
+#pragma unroll
+      for (int j = 0; j < KB; ++j) sc_lds[s & 1][s_term][s_row][j] = r.sc[j];
+    }
   };
 
   const int nslab = (g.nout + ROWS_B - 1) / ROWS_B;
@@ -888,13 +920,15 @@ __global__ __launch_bounds__(kThreads, GATEUP ? BQ_LB_GU : BQ_LB_DOWN) void k_gr
   const __amdgpu_buffer_rsrc_t srs =
       __builtin_amdgcn_make_buffer_rsrc((void*)(blob + g.off_sb[mi]), (short)0, g.nout * NB, kRsrcWord3);
   // clamped rows and steps: every path issues the same loads (exact wait counts)
-  auto load_codes = [&](MxCodes& st, int s) {
+  auto load_codes = [&](MxCodes<KB>& st, int s) __attribute__((always_inline)) {
     const int slab = slab0 + s / NSTEP, k = s % NSTEP;
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       const int row = min(slab * ROWS_B + wrow + 16 * rb + c16, g.nout - 1);
-      st.v[rb] = __builtin_amdgcn_raw_buffer_load_b128(crs, row * ROWB + 16 * q, k * 64, 0);
-      st.sc[rb] = __builtin_amdgcn_raw_buffer_load_b32(srs, row * NB, k * 4, 0);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        st.v[rb][kb] = __builtin_amdgcn_raw_buffer_load_b128(crs, row * ROWB + 16 * q, (k * KB + kb) * 64, 0);
+      mx_load_scales<KB>(st.sc[rb], srs, row * NB, k * 4 * KB);
     }
   };
 
@@ -904,26 +938,30 @@ __global__ __launch_bounds__(kThreads, GATEUP ? BQ_LB_GU : BQ_LB_DOWN) void k_gr
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) acc[th][rb] = f32x4m_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  auto compute = [&](const MxCodes& st, int s) __attribute__((always_inline)) {
-    v8i_t b[2];
-    int sb[2];
+  auto compute = [&](const MxCodes<KB>& st, int s) __attribute__((always_inline)) {
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      b[rb] = v8i_t{(int)st.v[rb][0], (int)st.v[rb][1], (int)st.v[rb][2], (int)st.v[rb][3], 0, 0, 0, 0};
-      sb[rb] = (int)((st.sc[rb] >> (8 * q)) & 0xFFu);
-    }
+    for (int kb = 0; kb < KB; ++kb) {
+      v8i_t b[2];
+      int sb[2];
 #pragma unroll
-    for (int th = 0; th < 2; ++th) {
-      if (th < nh) {
-        const int row = 16 * th + c16, sw = (row >> 1) & 7;
+      for (int rb = 0; rb < 2; ++rb) {
+        b[rb] = v8i_t{(int)st.v[rb][kb][0], (int)st.v[rb][kb][1], (int)st.v[rb][kb][2], (int)st.v[rb][kb][3], 0, 0, 0, 0};
+        sb[rb] = (int)((st.sc[rb][kb] >> (8 * q)) & 0xFFu);
+      }
 #pragma unroll
-        for (int t = 0; t < kMxTerms; ++t) {
-          const u32x4_t lo = a_lds[s & 1][t][row][q ^ sw], hi = a_lds[s & 1][t][row][(4 + q) ^ sw];
-          const v8i_t a = v8i_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-          const int sa = (int)((sc_lds[s & 1][t][row] >> (8 * q)) & 0xFFu);
+      for (int th = 0; th < 2; ++th) {
+        if (th < nh) {
+          const int row = 16 * th + c16;
 #pragma unroll
-          for (int rb = 0; rb < 2; ++rb)
-            acc[th][rb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b[rb], acc[th][rb], 0, 4, 0, sa, 0, sb[rb]);
+          for (int t = 0; t < kMxTerms; ++t) {
+            const u32x4_t lo = a_lds[s & 1][t][row][swz(row, 8 * kb + q)];
+            const u32x4_t hi = a_lds[s & 1][t][row][swz(row, 8 * kb + 4 + q)];
+            const v8i_t a = v8i_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+            const int sa = (int)((sc_lds[s & 1][t][row][kb] >> (8 * q)) & 0xFFu);
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+              acc[th][rb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b[rb], acc[th][rb], 0, 4, 0, sa, 0, sb[rb]);
+          }
         }
       }
     }
@@ -980,40 +1018,37 @@ __global__ __launch_bounds__(kThreads, GATEUP ? BQ_LB_GU : BQ_LB_DOWN) void k_gr
       for (int rb = 0; rb < 2; ++rb) acc[th][rb] = f32x4m_t{0.0f, 0.0f, 0.0f, 0.0f};
   };
 
-  MxCodes c0, c1, c2;
-  MxAct a0, a1;
-  auto body = [&](auto ci, auto ai, int s) __attribute__((always_inline)) {
-    constexpr int CI = decltype(ci)::value, AI = decltype(ai)::value;
-    MxCodes& cur = CI == 0 ? c0 : (CI == 1 ? c1 : c2);
-    MxCodes& ahead = CI == 0 ? c2 : (CI == 1 ? c0 : c1);
-    MxAct& aload = AI == 0 ? a0 : a1;
-    MxAct& apark = AI == 0 ? a1 : a0;
-    load_act(aload, min(s + 2, ntot - 1));
+  // Codes: three register stages, loaded two steps ahead. Activations: one register set, loaded at
+  // the start of a step and parked at its end (loads retire in order, so parking waits for the
+  // activations and not for the codes issued after them).
+  MxCodes<KB> c0, c1, c2;
+  MxAct<KB> act;
+  auto body = [&](auto ci, int s) __attribute__((always_inline)) {
+    constexpr int CI = decltype(ci)::value;
+    MxCodes<KB>& cur = CI == 0 ? c0 : (CI == 1 ? c1 : c2);
+    MxCodes<KB>& ahead = CI == 0 ? c2 : (CI == 1 ? c0 : c1);
+    load_act(act, min(s + 1, ntot - 1));
     load_codes(ahead, min(s + 2, ntot - 1));
     if (s < ntot) {  // uniform per block
       compute(cur, s);
       if (s % NSTEP == NSTEP - 1) finish_slab(slab0 + s / NSTEP);
     }
-    park_act(apark, s + 1);
+    park_act(act, s + 1);
     __syncthreads();
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
-  load_act(a0, 0);
-  load_act(a1, min(1, ntot - 1));
+  load_act(act, 0);
   load_codes(c0, 0);
   load_codes(c1, min(1, ntot - 1));
-  park_act(a0, 0);
+  park_act(act, 0);
   __syncthreads();
 #pragma unroll 1
-  for (int s = 0; s < ntot; s += 6) {
-    body(I0{}, I0{}, s);
-    body(I1{}, I1{}, s + 1);
-    body(I2{}, I0{}, s + 2);
-    body(I0{}, I1{}, s + 3);
-    body(I1{}, I0{}, s + 4);
-    body(I2{}, I1{}, s + 5);
+  for (int s = 0; s < ntot; s += 3) {
+    body(I0{}, s);
+    body(I1{}, s + 1);
+    body(I2{}, s + 2);
   }
 }
 
