@@ -436,11 +436,16 @@ __global__ __launch_bounds__(kThreads, GATEUP ? BQ_LB_GU : BQ_LB_DOWN) void k_gr
   constexpr int ROWS_B = GATEUP ? 64 : 128;   // rows per matrix per slab
   constexpr int AS = U * 8;                   // 16-byte activation slots per row and step
   constexpr int ASW = AS >= 16 ? 15 : AS - 1; // slot swizzle: 16 consecutive rows hit distinct banks
+  // Down projections (K <= 1024) keep the tile's whole activation rows in LDS (64 KiB at K = 1024),
+  // loaded once per block: the steps then issue only weight loads and need no barrier.
+  constexpr bool RESIDENT = !GATEUP && KDIM <= 1024;
+  constexpr int RS = KDIM / 8;                // 16-byte slots per resident row
   using Codes = GCodes<NI>;
   using Act = GAct<U>;
   __shared__ float s_lds[NG * kTileM];             // group sums of the tile's activations, [group][row]
-  __shared__ u32x4_t a_lds[2][kTileM * AS];        // activation ring: [step parity][row][slot ^ swizzle]
-  __shared__ float x_lds[GATEUP ? 2 : 1][16][64];  // gate/up: gate results handed to the up waves
+  __shared__ u32x4_t a_lds[RESIDENT ? kTileM * RS : 2 * kTileM * AS];  // resident rows, or a ring
+                                                   // [step parity][row][slot ^ swizzle]
+  __shared__ float x_lds[GATEUP ? 2 : 1][GATEUP ? 16 : 1][64];  // gate/up: gate results for the up waves
   __shared__ float h_lds[GATEUP ? 2 : 1][kTileM];  // gate/up: per-wave sums of the fp16 SwiGLU outputs
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -490,8 +495,24 @@ __global__ __launch_bounds__(kThreads, GATEUP ? BQ_LB_GU : BQ_LB_DOWN) void k_gr
   };
   auto park_act = [&](const Act& r, int s) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) a_lds[s & 1][a_row * AS + ((u * 8 + a_slot) ^ (a_row & ASW))] = r.v[u];
+    for (int u = 0; u < U; ++u) a_lds[(s & 1) * kTileM * AS + a_row * AS + ((u * 8 + a_slot) ^ (a_row & ASW))] = r.v[u];
   };
+  if constexpr (RESIDENT) {
+    // whole rows, 16-byte slot j of row m at slot j ^ (m & 15): 16 consecutive rows of a fragment read
+    // hit distinct banks (every 2 KiB row starts at bank 0)
+    constexpr int PER = kTileM * RS / kThreads;
+    u32x4_t v[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int idx = tid + i * kThreads, m = idx / RS, j = idx % RS;
+      v[i] = reinterpret_cast<const u32x4_t*>(g.a + (size_t)arow(m) * KDIM)[j];
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int idx = tid + i * kThreads, m = idx / RS, j = idx % RS;
+      a_lds[m * RS + (j ^ (m & 15))] = v[i];
+    }
+  }
 
   // this block's slabs: range gy of sgroups equal ranges
   const int nslab = (g.nout + ROWS_B - 1) / ROWS_B;
@@ -552,7 +573,12 @@ __global__ __launch_bounds__(kThreads, GATEUP ? BQ_LB_GU : BQ_LB_DOWN) void k_gr
 
   auto a_frag = [&](int s, int th, int G, int h) __attribute__((always_inline)) {
     const int row = 16 * th + c16;
-    return __builtin_bit_cast(f16x8_t, a_lds[s & 1][row * AS + ((G * 8 + kblock<BITS>(q, h)) ^ (row & ASW))]);
+    if constexpr (RESIDENT) {
+      const int j = ((s % NSTEP) * U + G) * 8 + kblock<BITS>(q, h);
+      return __builtin_bit_cast(f16x8_t, a_lds[row * RS + (j ^ (row & 15))]);
+    } else {
+      return __builtin_bit_cast(f16x8_t, a_lds[(s & 1) * kTileM * AS + row * AS + ((G * 8 + kblock<BITS>(q, h)) ^ (row & ASW))]);
+    }
   };
   // One step: regroup the codes, then per group the MFMAs of every token half and row block and the
   // scale epilogue; the bias MFMAs first.
@@ -736,25 +762,29 @@ __global__ __launch_bounds__(kThreads, GATEUP ? BQ_LB_GU : BQ_LB_DOWN) void k_gr
     Act& aload = AI == 0 ? a0 : a1;
     Act& apark = AI == 0 ? a1 : a0;
     if constexpr (AI == 0) split_words(wp, wx);
-    load_act(aload, min(s + 2, ntot - 1));
+    if constexpr (!RESIDENT) load_act(aload, min(s + 2, ntot - 1));
     load_codes(ahead, min(s + 2, ntot - 1));
     if constexpr (AI == 0) load_words(wp, s / 2 + 1);
     if (s < ntot) {  // uniform per block
       compute(cur, wx.w[AI], s);
       if (s % NSTEP == NSTEP - 1) finish_slab(slab0 + s / NSTEP);
     }
-    park_act(apark, s + 1);
-    __syncthreads();
+    if constexpr (!RESIDENT) {
+      park_act(apark, s + 1);
+      __syncthreads();
+    }
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
-  load_act(a0, 0);
-  load_act(a1, min(1, ntot - 1));
+  if constexpr (!RESIDENT) {
+    load_act(a0, 0);
+    load_act(a1, min(1, ntot - 1));
+  }
   load_codes(c0, 0);
   load_words(wp, 0);
   load_codes(c1, min(1, ntot - 1));
-  park_act(a0, 0);
+  if constexpr (!RESIDENT) park_act(a0, 0);
   __syncthreads();
 #pragma unroll 1
   for (int s = 0; s < ntot; s += 6) {
