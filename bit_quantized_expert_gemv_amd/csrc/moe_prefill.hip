@@ -94,7 +94,7 @@ constexpr int kRW = 32;      // tokens and rows per wave
 constexpr int kRSplit = BQ_ROUTER_SPLITK;  // waves per block, each with 1/kRSplit of K
 constexpr int kRSlice = 32;  // K per slice
 #ifndef BQ_ROUTER_GEMM_MIN
-#define BQ_ROUTER_GEMM_MIN 256
+#define BQ_ROUTER_GEMM_MIN 96
 #endif
 constexpr int kRouterGemmMinTokens = BQ_ROUTER_GEMM_MIN;
 
