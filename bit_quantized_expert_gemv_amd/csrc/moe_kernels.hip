@@ -485,13 +485,13 @@ __device__ __forceinline__ void write_routing(const LayerArgs& a, int t, const i
 // (fp64). Lane l holds partials l, l + 64, ...; every wave adds them in the same fixed order, so
 // every wave of every block gets the same value without a barrier.
 constexpr int kNormSqPerLane = 16;  // partial sums per lane: up to 1024 phase-3 blocks (H 8192, I 2048)
-__device__ __forceinline__ float wave_rms_inv(double ss, int H, float eps) {
+__device__ __forceinline__ double wave_rms_inv(double ss, int H, float eps) {
   ss = seg_sum<64>(ss);
   const long long b = __double_as_longlong(ss);
   const int lo = __builtin_amdgcn_readlane((int)(b & 0xFFFFFFFF), 63);
   const int hi = __builtin_amdgcn_readlane((int)(b >> 32), 63);
   const double tot = __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
-  return (float)(1.0 / sqrt(tot / (double)H + (double)eps));
+  return 1.0 / sqrt(tot / (double)H + (double)eps);
 }
 
 // gate/up/SwiGLU for P row steps of one expert, for a whole block: weight loads go out first,
@@ -557,9 +557,10 @@ __global__ __launch_bounds__(kBlock) void k_router_phase(LayerArgs a, const floa
 #pragma unroll
     for (int j = 0; j < CPW; ++j) w[j] = *reinterpret_cast<const uint4*>(row + (lir + (j * SPLIT + piece) * R::LPR) * 8);
   };
-  // Order of requests: the norm's partial sums, then the first router rows, then (after the scale
-  // is known) the activations. Loads retire in order, so reducing the partial sums never waits for
-  // the router rows.
+  // Order of requests: the norm's partial sums, then the first router rows and the activations.
+  // Loads retire in order, so reducing the partial sums never waits for the rows. The norm's scale
+  // is a scalar, so a row's dot product with the raw input is taken first and scaled at the end:
+  // sum_j R[e][j] (s h_j) = s sum_j R[e][j] h_j, with every product exact in fp64.
   const bool norm = norm_src != nullptr;
   double sqv[kNormSqPerLane];
   if (norm) {
@@ -571,12 +572,18 @@ __global__ __launch_bounds__(kBlock) void k_router_phase(LayerArgs a, const floa
       sqv[i] = k < nsq ? v : 0.0;
     }
   }
+  const float* src = (norm ? norm_src : x) + (size_t)t * H;
   uint4 w[CPW];
+  float4 xr[CPW][2];
   load_w(0, w);
-  float scale = 1.0f;
-  const float* src = x + (size_t)t * H;
+#pragma unroll
+  for (int j = 0; j < CPW; ++j) {
+    const float4* p = reinterpret_cast<const float4*>(src + (lir + (j * SPLIT + piece) * R::LPR) * 8);
+    xr[j][0] = p[0];
+    xr[j][1] = p[1];
+  }
+  double scale = 1.0;
   if (norm) {
-    src = norm_src + (size_t)t * H;
     double ss = 0.0;
 #pragma unroll
     for (int i = 0; i < kNormSqPerLane; ++i) ss += sqv[i];
@@ -588,10 +595,8 @@ __global__ __launch_bounds__(kBlock) void k_router_phase(LayerArgs a, const floa
     double acc[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int j = 0; j < CPW; ++j) {
-      const float4* p = reinterpret_cast<const float4*>(src + (lir + (j * SPLIT + piece) * R::LPR) * 8);
-      const float4 u0 = p[0], u1 = p[1];
-      const float xv[8] = {u0.x * scale, u0.y * scale, u0.z * scale, u0.w * scale,
-                           u1.x * scale, u1.y * scale, u1.z * scale, u1.w * scale};
+      const float xv[8] = {xr[j][0].x, xr[j][0].y, xr[j][0].z, xr[j][0].w,
+                           xr[j][1].x, xr[j][1].y, xr[j][1].z, xr[j][1].w};
       const uint32_t ww[4] = {w[j].x, w[j].y, w[j].z, w[j].w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -601,21 +606,23 @@ __global__ __launch_bounds__(kBlock) void k_router_phase(LayerArgs a, const floa
     }
     const double tot = seg_sum<R::LPR>((acc[0] + acc[1]) + (acc[2] + acc[3]));
     if constexpr (SPLIT == 1) {
-      if (lir == R::LPR - 1 && r < nrows) a.ws.logits[(size_t)t * (a.E + 1) + r] = tot;
+      if (lir == R::LPR - 1 && r < nrows) a.ws.logits[(size_t)t * (a.E + 1) + r] = norm ? tot * scale : tot;
     } else {
       if (lane == 63) part[wave] = tot;
       __syncthreads();
       if (piece == 0 && lane == 63 && r < nrows) {
         double v = part[wave];
         for (int q = 1; q < SPLIT; ++q) v += part[wave + q];
-        a.ws.logits[(size_t)t * (a.E + 1) + r] = v;
+        a.ws.logits[(size_t)t * (a.E + 1) + r] = norm ? v * scale : v;
       }
       __syncthreads();
     }
   }
   // the normalised input for phase 2 (block 0 only, off the router's critical path)
-  if (norm && blockIdx.x == 0)
-    for (int i = threadIdx.x; i < H; i += kBlock) a.ws.u[(size_t)t * H + i] = src[i] * scale;
+  if (norm && blockIdx.x == 0) {
+    const float fs = (float)scale;
+    for (int i = threadIdx.x; i < H; i += kBlock) a.ws.u[(size_t)t * H + i] = src[i] * fs;
+  }
 }
 
 // Kernel 2: gate/up/SwiGLU of the routed experts (blockIdx.y = slot) and, as slot K, of the shared
