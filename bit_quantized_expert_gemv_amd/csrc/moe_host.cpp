@@ -297,6 +297,18 @@ namespace {
 // their grouped GEMM steps K by 128).
 bool use_prefill(const Geometry& g, int T) { return T >= MOE_PREFILL_MIN_TOKENS && (g.form != 3 || g.I >= 128); }
 
+// The MXFP4 grouped GEMMs address their activation planes (3 E4M3 terms of [rows][K]) with 32-bit
+// buffer offsets: both the input's planes (T rows of H) and the SwiGLU outputs' (T*(K+shared)
+// rows of I) must stay under 2^31 bytes.
+int check_prefill_size(const Geometry& g, int T) {
+  if (!use_prefill(g, T) || g.form != 3) return MOE_OK;
+  const uint64_t rows = (uint64_t)T * (g.K + g.has_shared);
+  if (3ull * T * g.H >= (1ull << 31) || 3ull * rows * g.I >= (1ull << 31))
+    return fail(MOE_EUNSUPPORTED, "too many tokens for one MXFP4 prefill call (3*T*hidden and "
+                                  "3*T*(top_k+shared)*inter must stay below 2^31)");
+  return MOE_OK;
+}
+
 size_t needed_ws(const Geometry& g, int T) {
   size_t n = workspace_layer_bytes(g, T);
   if (T >= MOE_PREFILL_MIN_TOKENS) {
@@ -339,6 +351,7 @@ int moe_expert_ffn(const moe_layer_t* layer, const float* x, int T, const int32_
   if (ws_bytes < needed_ws(g, T)) return fail(MOE_ENOSPC, "workspace smaller than moe_workspace_bytes()");
   hipStream_t s = static_cast<hipStream_t>(stream);
   const LayerPtrs p = ptrs_of(layer);
+  if ((rc = check_prefill_size(g, T))) return rc;
   if (use_prefill(g, T))
     return hip_status(launch_prefill(g, p, x, nullptr, T, carve_prefill(g, T, ws), idx, nullptr, nullptr, y, s));
   const Workspace W = carve_workspace(g, T, ws);
@@ -389,6 +402,7 @@ int moe_layer_forward_timed(const moe_layer_t* layer, const float* x, const floa
     }
     return e;
   };
+  if ((rc = check_prefill_size(g, T))) return rc;
   if (use_prefill(g, T)) {
     // many kernels: events[0] and events[5] are recorded around all of them
     hipError_t e = hipSuccess;

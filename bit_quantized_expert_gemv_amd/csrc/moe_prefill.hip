@@ -845,7 +845,6 @@ struct MxCodes {
 template <int KB>
 struct MxAct {
   u32x4_t v[kMxTerms][KB];  // 16 bytes of each term: row tid/(8KB) + (32/KB)h, slot tid%(8KB)
-  uint32_t sc[KB];          // scale bytes of (term min(tid/32, 2), row tid%32), 4 per K-block
 };
 
 template <int KB>
@@ -863,6 +862,7 @@ __device__ __forceinline__ void mx_load_scales(uint32_t (&d)[KB], __amdgpu_buffe
 // 32 rows of one matrix per slab, slabs walked in order, XCD-aware tile placement). Step: K = 128 KB,
 // i.e. 4 KB MX blocks: per row block KB 16-byte code loads (a whole 128-byte line of the row when
 // KB = 2) and one scale load; the tile's three activation terms (12 KiB per K-block) through an LDS ring.
+// The activations' E8M0 scales (3 KiB per 1024 of K) sit in LDS for the whole block.
 // No dequantisation on the VALU: the MFMA consumes the packed codes and both scale sets.
 template <int KDIM, bool GATEUP, bool SHARED>
 __global__ __launch_bounds__(kThreads, GATEUP ? BQ_LB_GU : BQ_LB_DOWN) void k_grouped_mx(GroupArgs g, int sgroups) {
@@ -874,7 +874,9 @@ __global__ __launch_bounds__(kThreads, GATEUP ? BQ_LB_GU : BQ_LB_DOWN) void k_gr
   constexpr int NB = KDIM / 32;                  // scale bytes per row
   constexpr int ROWS_B = GATEUP ? 64 : 128;      // rows per matrix per slab
   __shared__ u32x4_t a_lds[2][kMxTerms][kTileM][SLOTS];  // [parity][term][row][16-byte slot ^ swizzle]
-  __shared__ uint32_t sc_lds[2][kMxTerms][kTileM][KB];
+  // every activation scale of the tile, loaded once; rows padded by a dword so that the 16 rows of a
+  // fragment read hit distinct banks
+  __shared__ uint32_t sc_lds[kMxTerms][kTileM][NB / 4 + 1];
   __shared__ float x_lds[GATEUP ? 2 : 1][16][64];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -911,20 +913,28 @@ __global__ __launch_bounds__(kThreads, GATEUP ? BQ_LB_GU : BQ_LB_DOWN) void k_gr
 
   // activation loads: row tid/SLOTS + (32/KB)h, slot tid%SLOTS of each term; the scales of (term, row)
   const int a_row = tid / SLOTS, a_slot = tid % SLOTS;
-  const uint8_t* a_src[KB];
+  // buffer loads: the planes' base in scalar registers, a 32-bit offset per lane, term and step as
+  // scalar offsets (the host keeps the three planes under 2^31 bytes)
+  const __amdgpu_buffer_rsrc_t ars =
+      __builtin_amdgcn_make_buffer_rsrc((void*)g.a8, (short)0, (int)(kMxTerms * g.a_plane), kRsrcWord3);
+  int a_off[KB];
 #pragma unroll
-  for (int h = 0; h < KB; ++h) a_src[h] = g.a8 + (size_t)arow(a_row + (32 / KB) * h) * KDIM + a_slot * 16;
-  const int s_term = min(tid >> 5, kMxTerms - 1), s_row = tid & 31;
-  const uint8_t* s_src = g.asc + s_term * g.sc_plane + (size_t)arow(s_row) * NB;
+  for (int h = 0; h < KB; ++h) a_off[h] = arow(a_row + (32 / KB) * h) * KDIM + a_slot * 16;
+  // the tile's activation scales are the same for every slab: all of them go to LDS once
+  {
+    constexpr int NW = kMxTerms * kTileM * (NB / 4);
+    for (int i = tid; i < NW; i += kThreads) {
+      const int t = i / (kTileM * (NB / 4)), m = (i / (NB / 4)) % kTileM, d = i % (NB / 4);
+      sc_lds[t][m][d] = *reinterpret_cast<const uint32_t*>(g.asc + t * g.sc_plane + (size_t)arow(m) * NB + 4 * d);
+    }
+  }
   auto load_act = [&](MxAct<KB>& r, int s) __attribute__((always_inline)) {
     const int k = s % NSTEP;
 #pragma unroll
     for (int t = 0; t < kMxTerms; ++t)
 #pragma unroll
       for (int h = 0; h < KB; ++h)
-        r.v[t][h] = *reinterpret_cast<const u32x4_t*>(a_src[h] + t * g.a_plane + k * 128 * KB);
-#pragma unroll
-    for (int j = 0; j < KB; ++j) r.sc[j] = *reinterpret_cast<const uint32_t*>(s_src + k * 4 * KB + 4 * j);
+        r.v[t][h] = __builtin_amdgcn_raw_buffer_load_b128(ars, a_off[h], (int)(t * g.a_plane) + k * 128 * KB, 0);
   };
   auto park_act = [&](const MxAct<KB>& r, int s) __attribute__((always_inline)) {
 #pragma unroll
@@ -934,10 +944,6 @@ __global__ __launch_bounds__(kThreads, GATEUP ? BQ_LB_GU : BQ_LB_DOWN) void k_gr
         const int row = a_row + (32 / KB) * h;
         a_lds[s & 1][t][row][swz(row, a_slot)] = r.v[t][h];
       }
-    if (tid < kMxTerms * 32) {
-#pragma unroll
-      for (int j = 0; j < KB; ++j) sc_lds[s & 1][s_term][s_row][j] = r.sc[j];
-    }
   };
 
   const int nslab = (g.nout + ROWS_B - 1) / ROWS_B;
@@ -987,7 +993,7 @@ __global__ __launch_bounds__(kThreads, GATEUP ? BQ_LB_GU : BQ_LB_DOWN) void k_gr
             const u32x4_t lo = a_lds[s & 1][t][row][swz(row, 8 * kb + q)];
             const u32x4_t hi = a_lds[s & 1][t][row][swz(row, 8 * kb + 4 + q)];
             const v8i_t a = v8i_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-            const int sa = (int)((sc_lds[s & 1][t][row][kb] >> (8 * q)) & 0xFFu);
+            const int sa = (int)((sc_lds[t][row][(s % NSTEP) * KB + kb] >> (8 * q)) & 0xFFu);
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb)
               acc[th][rb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b[rb], acc[th][rb], 0, 4, 0, sa, 0, sb[rb]);

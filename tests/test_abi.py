@@ -180,6 +180,12 @@ def test_call_validation():
     assert L.moe_dequant(ref, 0, 0, 2, FAKE, None) == bq.MOE_EINVAL
     no_shared = _layer(shared_blob=None, shared_gate=None)
     assert L.moe_dequant(ctypes.byref(no_shared), -1, 0, 0, FAKE, None) == bq.MOE_EINVAL
+    # an MXFP4 prefill whose activation planes would pass 2^31 bytes is refused before any HIP call
+    mx = _layer(group=32, expert_stride=6_684_672 + 256, top_k=6)
+    big = 180_000  # 3 * T * 4096 >= 2^31
+    assert L.moe_layer_forward(ctypes.byref(mx), FAKE, FAKE, big, FAKE + (1 << 36), None, FAKE, 1 << 62,
+                               None) == bq.MOE_EUNSUPPORTED
+    assert "2^31" in bq.moe_last_error()
     # the stack: mismatched layers, bad eps, small workspace
     other = _layer(top_k=2)
     arr = (bq.moe_layer_t * 2)(layer, other)
