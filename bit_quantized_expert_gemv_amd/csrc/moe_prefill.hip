@@ -440,6 +440,7 @@ __global__ __launch_bounds__(kThreads, GATEUP ? BQ_LB_GU : BQ_LB_DOWN) void k_gr
   // loaded once per block: the steps then issue only weight loads and need no barrier.
   constexpr bool RESIDENT = !GATEUP && KDIM <= 1024;
   constexpr int RS = KDIM / 8;                // 16-byte slots per resident row
+  constexpr int RSW = RS >= 16 ? 15 : RS - 1; // its slot swizzle stays inside the row (RS is 8 at K = 64)
   using Codes = GCodes<NI>;
   using Act = GAct<U>;
   __shared__ float s_lds[NG * kTileM];             // group sums of the tile's activations, [group][row]
@@ -498,8 +499,8 @@ __global__ __launch_bounds__(kThreads, GATEUP ? BQ_LB_GU : BQ_LB_DOWN) void k_gr
     for (int u = 0; u < U; ++u) a_lds[(s & 1) * kTileM * AS + a_row * AS + ((u * 8 + a_slot) ^ (a_row & ASW))] = r.v[u];
   };
   if constexpr (RESIDENT) {
-    // whole rows, 16-byte slot j of row m at slot j ^ (m & 15): 16 consecutive rows of a fragment read
-    // hit distinct banks (every 2 KiB row starts at bank 0)
+    // whole rows, 16-byte slot j of row m at slot j ^ (m & RSW): 16 consecutive rows of a fragment read
+    // hit distinct banks (a row of 256 bytes or more starts at bank 0)
     constexpr int PER = kTileM * RS / kThreads;
     u32x4_t v[PER];
 #pragma unroll
@@ -510,7 +511,7 @@ __global__ __launch_bounds__(kThreads, GATEUP ? BQ_LB_GU : BQ_LB_DOWN) void k_gr
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int idx = tid + i * kThreads, m = idx / RS, j = idx % RS;
-      a_lds[m * RS + (j ^ (m & 15))] = v[i];
+      a_lds[m * RS + (j ^ (m & RSW))] = v[i];
     }
   }
 
@@ -575,7 +576,7 @@ __global__ __launch_bounds__(kThreads, GATEUP ? BQ_LB_GU : BQ_LB_DOWN) void k_gr
     const int row = 16 * th + c16;
     if constexpr (RESIDENT) {
       const int j = ((s % NSTEP) * U + G) * 8 + kblock<BITS>(q, h);
-      return __builtin_bit_cast(f16x8_t, a_lds[row * RS + (j ^ (row & 15))]);
+      return __builtin_bit_cast(f16x8_t, a_lds[row * RS + (j ^ (row & RSW))]);
     } else {
       return __builtin_bit_cast(f16x8_t, a_lds[(s & 1) * kTileM * AS + row * AS + ((G * 8 + kblock<BITS>(q, h)) ^ (row & ASW))]);
     }
