@@ -2,8 +2,9 @@
 
 - 1024 experts (MOE_MAX_EXPERTS), top-8 (MOE_MAX_TOP_K): the decode top-K holds 16 logits per lane.
 - top-K = E (every expert routed; the weights are the full softmax) and top-1 (weight 1).
-- hidden 8192 x inter 2048, the largest rows the kernels take, in the affine 4-bit and MXFP4
-  formats.
+- hidden 8192 x inter 2048, the largest rows the kernels take, in the affine 4-bit, 2-bit and
+  MXFP4 formats; hidden 1024 and 2048 (other lane-per-row layouts of the decode GEMVs); MXFP4 with
+  inter 64, which stays on the per-token path at every T.
 Each runs the decode path and the prefill path. Bar as elsewhere: bit-exact top-K indices;
 outputs within 2e-3*max|oracle| + 1e-5 per token vector.
 """
@@ -30,6 +31,10 @@ SHAPES = {
     "max4": synth.Workload("max4", 8192, 12, 2048, 3, weight_family=14, x_family=14, **_4),
     "maxmx": synth.Workload("maxmx", 8192, 8, 2048, 6, bits=4, group=32, fmt="mxfp4", weight_family=15,
                             x_family=15),
+    "max2": synth.Workload("max2", 8192, 8, 2048, 3, weight_family=16, x_family=16, **_2),
+    "mid2": synth.Workload("mid2", 1024, 32, 512, 4, weight_family=17, x_family=17, **_2),
+    "mid4": synth.Workload("mid4", 2048, 16, 256, 2, weight_family=18, x_family=18, **_4),
+    "mx64": synth.Workload("mx64", 256, 8, 64, 2, bits=4, group=32, fmt="mxfp4", weight_family=19, x_family=19),
 }
 
 
@@ -71,11 +76,15 @@ def _forward(L, x):
     ("k1", 1, (0,)), ("k1", 4, (0, 1, 2, 3)), ("k1", 48, (0, 47)),
     ("max4", 1, (0,)), ("max4", 48, (0, 47)),
     ("maxmx", 1, (0,)), ("maxmx", 48, (0, 47)),
+    ("max2", 1, (0,)), ("max2", 48, (0, 47)),
+    ("mid2", 3, (0, 1, 2)), ("mid2", 100, (0, 50, 99)),
+    ("mid4", 2, (0, 1)), ("mid4", 64, (0, 33, 63)),
+    ("mx64", 1, (0,)), ("mx64", 60, (0, 30, 59)),  # MXFP4 below inter 128 decodes at every T
 ])
 def test_edge_shape_layer_forward(layers, name, T, check):
     L, ref = layers(name)
     w = L.w
-    path = "prefill" if T >= bq.MOE_PREFILL_MIN_TOKENS else "decode"
+    path = "prefill" if T >= bq.MOE_PREFILL_MIN_TOKENS and (w.fmt != "mxfp4" or w.inter >= 128) else "decode"
     _log(f"{name}: {T} tokens ({path})")
     x = torch.from_numpy(synth.tokens_x(w, 0, T)).cuda()
     out, idx = _forward(L, x)
