@@ -66,7 +66,7 @@ extern "C" {
 #define MOE_MAX_EXPERTS 1024
 /* Token counts at or above this run the prefill path in moe_layer_forward (grouped by expert). Below
  * it, per-token streaming is faster on MI355X for a 512-expert, top-3 layer (measured crossover). */
-#define MOE_PREFILL_MIN_TOKENS 48
+#define MOE_PREFILL_MIN_TOKENS 64
 
 /* moe_layer_t.flags values, an A/B ablation of the one kernel claim on the pages ("Kernel de
  * dequantización optimizado con FMA"). By default the decode GEMVs use the per-chunk form

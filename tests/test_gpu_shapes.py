@@ -72,11 +72,11 @@ def _forward(L, x):
 
 @pytest.mark.parametrize("name,T,check", [
     ("e1024", 1, (0,)), ("e1024", 5, (0, 2, 4)), ("e1024", 100, (0, 31, 32, 99)),
-    ("kall", 2, (0, 1)), ("kall", 50, (0, 25, 49)),
-    ("k1", 1, (0,)), ("k1", 4, (0, 1, 2, 3)), ("k1", 48, (0, 47)),
-    ("max4", 1, (0,)), ("max4", 48, (0, 47)),
-    ("maxmx", 1, (0,)), ("maxmx", 48, (0, 47)),
-    ("max2", 1, (0,)), ("max2", 48, (0, 47)),
+    ("kall", 2, (0, 1)), ("kall", 70, (0, 35, 69)),
+    ("k1", 1, (0,)), ("k1", 4, (0, 1, 2, 3)), ("k1", 64, (0, 63)),
+    ("max4", 1, (0,)), ("max4", 64, (0, 63)),
+    ("maxmx", 1, (0,)), ("maxmx", 64, (0, 63)),
+    ("max2", 1, (0,)), ("max2", 64, (0, 63)),
     ("mid2", 3, (0, 1, 2)), ("mid2", 100, (0, 50, 99)),
     ("mid4", 2, (0, 1)), ("mid4", 64, (0, 33, 63)),
     ("mx64", 1, (0,)), ("mx64", 60, (0, 30, 59)),  # MXFP4 below inter 128 decodes at every T
