@@ -630,6 +630,81 @@ __global__ __launch_bounds__(kBlock) void k_router_phase(LayerArgs a, const floa
   }
 }
 
+// Kernel 1 for several tokens without the stack's norm: each block reads its router row once for a
+// group of TG tokens, and every lane accumulates one fp64 dot product per token. A token's logits
+// are summed in the same order as in k_router_phase, so they are bitwise the same; only the row
+// traffic drops, from T reads of the router to T / TG.
+template <int H, int TG>
+__global__ __launch_bounds__(kBlock) void k_router_group(LayerArgs a, const float* __restrict__ x, int T) {
+  using R = RouterCfg<H>;
+  constexpr int SPLIT = (R::CPL % BQ_ROUTER_SPLIT == 0) ? BQ_ROUTER_SPLIT : 1;  // waves per row
+  constexpr int CPW = R::CPL / SPLIT;                                            // chunks per lane
+  __shared__ double part[TG][kWaves];
+  const int t0 = blockIdx.y * TG;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int lir = lane % R::LPR, rig = lane / R::LPR;
+  const int nrows = a.E + a.has_shared;
+  const int piece = wave % SPLIT;
+  const int r = (blockIdx.x * (kWaves / SPLIT) + wave / SPLIT) * R::RPW + rig;  // one row step per block
+  uint4 w[CPW];
+  {
+    const int rr = min(r, nrows - 1);
+    const uint16_t* row = (rr < a.E) ? a.router + (size_t)rr * H : a.sgate;
+#pragma unroll
+    for (int j = 0; j < CPW; ++j) w[j] = *reinterpret_cast<const uint4*>(row + (lir + (j * SPLIT + piece) * R::LPR) * 8);
+  }
+  float4 xr[TG][CPW][2];
+#pragma unroll
+  for (int g = 0; g < TG; ++g) {
+    const float* src = x + (size_t)min(t0 + g, T - 1) * H;  // tokens past T re-read the last one
+#pragma unroll
+    for (int j = 0; j < CPW; ++j) {
+      const float4* p = reinterpret_cast<const float4*>(src + (lir + (j * SPLIT + piece) * R::LPR) * 8);
+      xr[g][j][0] = p[0];
+      xr[g][j][1] = p[1];
+    }
+  }
+  double tot[TG];
+#pragma unroll
+  for (int g = 0; g < TG; ++g) {
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int j = 0; j < CPW; ++j) {
+      const float xv[8] = {xr[g][j][0].x, xr[g][j][0].y, xr[g][j][0].z, xr[g][j][0].w,
+                           xr[g][j][1].x, xr[g][j][1].y, xr[g][j][1].z, xr[g][j][1].w};
+      const uint32_t ww[4] = {w[j].x, w[j].y, w[j].z, w[j].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[q] = fma((double)bf16_lo(ww[q]), (double)xv[2 * q], acc[q]);
+        acc[q] = fma((double)bf16_hi(ww[q]), (double)xv[2 * q + 1], acc[q]);
+      }
+    }
+    tot[g] = seg_sum<R::LPR>((acc[0] + acc[1]) + (acc[2] + acc[3]));
+  }
+  if constexpr (SPLIT == 1) {
+    if (lir == R::LPR - 1 && r < nrows) {
+#pragma unroll
+      for (int g = 0; g < TG; ++g)
+        if (t0 + g < T) a.ws.logits[(size_t)(t0 + g) * (a.E + 1) + r] = tot[g];
+    }
+  } else {
+    if (lane == 63) {
+#pragma unroll
+      for (int g = 0; g < TG; ++g) part[g][wave] = tot[g];
+    }
+    __syncthreads();
+    if (piece == 0 && lane == 63 && r < nrows) {
+#pragma unroll
+      for (int g = 0; g < TG; ++g) {
+        if (t0 + g >= T) continue;
+        double v = part[g][wave];
+        for (int q = 1; q < SPLIT; ++q) v += part[g][wave + q];
+        a.ws.logits[(size_t)(t0 + g) * (a.E + 1) + r] = v;
+      }
+    }
+  }
+}
+
 // Kernel 2: gate/up/SwiGLU of the routed experts (blockIdx.y = slot) and, as slot K, of the shared
 // expert. The shared slot needs no routing, so its blocks stream weights while the routed blocks are
 // still picking their experts.
@@ -881,6 +956,14 @@ constexpr int kP3 = BQ_P3;  // down
 #define BQ_WIDE_MIN_TOKENS 4
 #endif
 constexpr int kP2Wide = BQ_P2_WIDE;
+// Tokens per block of the multi-token router (k_router_group).
+#ifndef BQ_ROUTER_GROUP
+#define BQ_ROUTER_GROUP 4
+#endif
+#ifndef BQ_ROUTER_GROUP_MIN_TOKENS
+#define BQ_ROUTER_GROUP_MIN_TOKENS BQ_ROUTER_GROUP
+#endif
+constexpr int kRouterGroup = BQ_ROUTER_GROUP;
 
 // A launch that, when events are given, has the dispatch itself record its start and end time
 // (the same timestamps a kernel-trace profiler reports), not separate event packets around it.
@@ -902,6 +985,10 @@ hipError_t router_phase_impl(const LayerArgs& a, const float* x, const float* no
   constexpr int SPLIT = (R::CPL % BQ_ROUTER_SPLIT == 0) ? BQ_ROUTER_SPLIT : 1;
   const int rows_per_block = kWaves / SPLIT * router_steps * R::RPW;
   const int nrb = (nrows + rows_per_block - 1) / rows_per_block;
+  if (norm_src == nullptr && T >= BQ_ROUTER_GROUP_MIN_TOKENS && router_steps == 1) {  // one read per token group
+    return launch_timed(k_router_group<H, kRouterGroup>, dim3(nrb, (T + kRouterGroup - 1) / kRouterGroup),
+                        dim3(kBlock), s, ev, a, x, T);
+  }
   return launch_timed(k_router_phase<H>, dim3(nrb, T), dim3(kBlock), s, ev, a, x, norm_src, norm_sq, nsq, eps,
                       router_steps);
 }

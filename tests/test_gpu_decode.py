@@ -314,3 +314,29 @@ def test_per_element_dequant_forms_parity(which, tokens, flag, request):
         assert_close(out[t], r.out, f"{w.name} literal out[{t}]")
         assert_close(out[t], base_out[t], f"{w.name} literal vs default out[{t}]")
 
+
+
+@pytest.mark.parametrize("which,T", [("tiny", 9), ("dec4", 8), ("dec2", 6)])
+def test_router_token_groups_bitwise(which, T, request):
+    """Several tokens per call read each router row once for a group of tokens; every token's
+    logits are summed in the single-token order, so they equal one-token calls bitwise (T not a
+    multiple of the group size leaves a partial group)."""
+    L, _ = request.getfixturevalue(which)
+    w = L.w
+    x = _x(w, 60, T)
+    n = bq.moe_workspace_bytes(L.desc, T)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    idx = torch.empty(T, w.top_k, dtype=torch.int32, device="cuda")
+    wt = torch.empty(T, w.top_k, dtype=torch.float32, device="cuda")
+    lg = torch.empty(T, w.n_experts, dtype=torch.float64, device="cuda")
+    bq.moe_router(L.desc, x, T, idx, wt, None, lg, ws, n)
+    one = torch.empty(1, w.n_experts, dtype=torch.float64, device="cuda")
+    i1 = torch.empty(1, w.top_k, dtype=torch.int32, device="cuda")
+    w1 = torch.empty(1, w.top_k, dtype=torch.float32, device="cuda")
+    n1 = bq.moe_workspace_bytes(L.desc, 1)
+    ws1 = torch.empty(n1, dtype=torch.uint8, device="cuda")
+    for t in range(T):
+        bq.moe_router(L.desc, x[t:t + 1].contiguous(), 1, i1, w1, None, one, ws1, n1)
+        torch.cuda.synchronize()
+        assert torch.equal(lg[t], one[0]), f"token {t}"
+        assert torch.equal(idx[t], i1[0]) and torch.equal(wt[t], w1[0])
