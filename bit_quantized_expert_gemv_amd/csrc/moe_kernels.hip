@@ -623,10 +623,22 @@ __global__ __launch_bounds__(kBlock) void k_router_phase(LayerArgs a, const floa
       __syncthreads();
     }
   }
-  // the normalised input for phase 2 (block 0 only, off the router's critical path)
-  if (norm && blockIdx.x == 0) {
+  // The normalised input for phase 2, written from the activations already in registers: block b
+  // writes 8-float chunks b, b + gridDim.x, ..., each from the one lane that holds it (row group 0).
+  // Spread this way no block waits on extra loads, and the next kernel does not wait on a straggler.
+  if (norm) {
     const float fs = (float)scale;
-    for (int i = threadIdx.x; i < H; i += kBlock) a.ws.u[(size_t)t * H + i] = src[i] * fs;
+    for (int c = blockIdx.x; c < R::NC; c += gridDim.x) {
+      const int jp = c / R::LPR;  // chunk position j * SPLIT + piece
+      if (rig != 0 || lir != c % R::LPR || piece != jp % SPLIT || wave / SPLIT != 0) continue;
+#pragma unroll
+      for (int j = 0; j < CPW; ++j) {
+        if (j != jp / SPLIT) continue;
+        float4* dst = reinterpret_cast<float4*>(a.ws.u + (size_t)t * H + (size_t)c * 8);
+        dst[0] = make_float4(xr[j][0].x * fs, xr[j][0].y * fs, xr[j][0].z * fs, xr[j][0].w * fs);
+        dst[1] = make_float4(xr[j][1].x * fs, xr[j][1].y * fs, xr[j][1].z * fs, xr[j][1].w * fs);
+      }
+    }
   }
 }
 
