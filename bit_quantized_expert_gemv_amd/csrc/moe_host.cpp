@@ -116,7 +116,7 @@ bool geometry_from(const moe_layer_t* L, Geometry* g, const char** why) {
 size_t workspace_layer_bytes(const Geometry& g, int T) {
   const size_t t = (size_t)T;
   return align256(t * (g.E + 1) * 8) + align256(t * g.K * 4) + align256(t * g.K * 4) + align256(t * 4) +
-         align256(t * g.NE * g.I * 4) + align256(t * g.H * 4) + align256(t * g.H * 8);
+         align256(t * g.NE * g.I * 4) + align256(t * g.H * 4);
 }
 
 namespace {
@@ -185,8 +185,7 @@ Workspace carve_workspace(const Geometry& g, int T, void* base) {
   ws.w = reinterpret_cast<float*>(p); p += align256(t * g.K * 4);
   ws.g = reinterpret_cast<float*>(p); p += align256(t * 4);
   ws.h = reinterpret_cast<float*>(p); p += align256(t * g.NE * g.I * 4);
-  ws.u = reinterpret_cast<float*>(p); p += align256(t * g.H * 4);
-  ws.sq = reinterpret_cast<double*>(p);  // [T][down blocks], at most H per token
+  ws.u = reinterpret_cast<float*>(p);
   return ws;
 }
 
@@ -356,7 +355,7 @@ int moe_expert_ffn(const moe_layer_t* layer, const float* x, int T, const int32_
     return hip_status(launch_prefill(g, p, x, nullptr, T, carve_prefill(g, T, ws), idx, nullptr, nullptr, y, s));
   const Workspace W = carve_workspace(g, T, ws);
   hipError_t e = launch_gateup(g, p, x, T, W, idx, nullptr, true, s);
-  if (e == hipSuccess) e = launch_down(g, p, T, W, idx, nullptr, nullptr, y, nullptr, s);
+  if (e == hipSuccess) e = launch_down(g, p, T, W, idx, nullptr, nullptr, y, s);
   return hip_status(e);
 }
 
@@ -414,9 +413,9 @@ int moe_layer_forward_timed(const moe_layer_t* layer, const float* x, const floa
     return hip_status(e);
   }
   const Workspace W = carve_workspace(g, T, ws);
-  hipError_t e = launch_router_phase(g, p, x, nullptr, nullptr, 0, 0.0f, T, W, s, ev(0));
+  hipError_t e = launch_router_phase(g, p, x, nullptr, 0.0f, T, W, s, ev(0));
   if (e == hipSuccess) e = launch_gateup(g, p, x, T, W, nullptr, idx_out, true, s, ev(1));
-  if (e == hipSuccess) e = launch_down(g, p, T, W, W.idx, residual, out, nullptr, nullptr, s, ev(2));
+  if (e == hipSuccess) e = launch_down(g, p, T, W, W.idx, residual, out, nullptr, s, ev(2));
   return hip_status(e);
 }
 
@@ -484,8 +483,6 @@ int moe_stack_forward(const moe_layer_t* layers, int L, float eps, const float* 
                     reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + base + hb)};
   hipStream_t s = static_cast<hipStream_t>(stream);
   const float* h = x;  // h_l
-  const int nsq = down_blocks(g);
-  if (nsq < 1 || nsq > max_norm_partials()) return fail(MOE_EUNSUPPORTED, "layer shape has too many down blocks");
   hipError_t e = hipSuccess;
   // Cross-layer prefetch: at the start of layer l, a side stream forked off the caller's stream reads
   // layer l+1's router and shared expert; it runs beside layer l's kernels and joins the caller's
@@ -508,10 +505,9 @@ int moe_stack_forward(const moe_layer_t* layers, int L, float eps, const float* 
     const float* norm_src = (l == 0) ? nullptr : h;
     const float* xin = (l == 0) ? x : W.u;
     int32_t* io = idx_out ? idx_out + (size_t)l * T * g.K : nullptr;
-    // the norm of layer l reads the partial sums of h_l^2 that layer l-1's phase 3 wrote
-    e = launch_router_phase(g, p, x, norm_src, W.sq, nsq, eps, T, W, s);
+    e = launch_router_phase(g, p, x, norm_src, eps, T, W, s);
     if (e == hipSuccess) e = launch_gateup(g, p, xin, T, W, nullptr, io, true, s);
-    if (e == hipSuccess) e = launch_down(g, p, T, W, W.idx, h, h_next, nullptr, (l + 1 < L) ? W.sq : nullptr, s);
+    if (e == hipSuccess) e = launch_down(g, p, T, W, W.idx, h, h_next, nullptr, s);
     h = h_next;
   }
   if (prefetch && e == hipSuccess) {

@@ -36,7 +36,6 @@ struct Workspace {
   float* g;        // [T]
   float* h;        // [T][NE][I]: SwiGLU outputs
   float* u;        // [T][H]: normalised layer input (stack only)
-  double* sq;      // [T][down blocks]: per-block sums of the layer output squared (stack only)
 };
 
 // Prefill (grouped) workspace for T tokens; N = T*K routed entries, R = N + T*has_shared rows.
@@ -89,25 +88,17 @@ struct Prefetch {
 hipError_t launch_prefetch(const Prefetch& pf, int blocks, hipStream_t s);
 
 // Phase 1: router logits and the shared-gate logit into ws.logits. If norm_src is non-null the layer
-// input is RMSNorm(norm_src) (also written to ws.u), with the mean square taken from norm_sq[T][nsq],
-// the previous phase 3's per-block partial sums; otherwise the input is x.
+// input is RMSNorm(norm_src) with the given eps (also written to ws.u); otherwise the input is x.
 hipError_t launch_router_phase(const Geometry& g, const LayerPtrs& p, const float* x, const float* norm_src,
-                               const double* norm_sq, int nsq, float eps, int T, const Workspace& ws, hipStream_t s,
-                               const KernelEvents& ev = {});
+                               float eps, int T, const Workspace& ws, hipStream_t s, const KernelEvents& ev = {});
 // Phase 2: gate/up SwiGLU of the routed experts (slots 0..K-1), plus slot K (shared) if with_shared.
 // If idx_in is null the top-K is computed from ws.logits and written to ws.idx/w/g (and idx_out).
 hipError_t launch_gateup(const Geometry& g, const LayerPtrs& p, const float* x, int T, const Workspace& ws,
                          const int32_t* idx_in, int32_t* idx_out, bool with_shared, hipStream_t s,
                          const KernelEvents& ev = {});
 // Phase 3: down projections. combine: out = residual + sum_k w_k y_k + g y_s; otherwise y[t][k][:] = y_k.
-// With combine and sq_out non-null, also sq_out[t][block] = sum over the block's rows of out^2.
 hipError_t launch_down(const Geometry& g, const LayerPtrs& p, int T, const Workspace& ws, const int32_t* idx,
-                       const float* residual, float* out, float* y, double* sq_out, hipStream_t s,
-                       const KernelEvents& ev = {});
-// Number of phase-3 blocks per token (the partial-sum count of sq_out), and the most partial sums
-// phase 1's norm reads.
-int down_blocks(const Geometry& g);
-int max_norm_partials();
+                       const float* residual, float* out, float* y, hipStream_t s, const KernelEvents& ev = {});
 // Top-K + weights from ws.logits (router-only path).
 hipError_t launch_topk(const Geometry& g, int T, const Workspace& ws, int32_t* idx, float* w, float* sg,
                        double* logits_out, hipStream_t s);

@@ -486,17 +486,17 @@ __device__ __forceinline__ void write_routing(const LayerArgs& a, int t, const i
   if (g_out && a.has_shared) g_out[t] = (float)(1.0 / (1.0 + exp(-lg[a.E])));
 }
 
-// RMS norm scale 1/sqrt(mean(h^2) + eps) from the previous layer's per-block partial sums of h^2
-// (fp64). Lane l holds partials l, l + 64, ...; every wave adds them in the same fixed order, so
-// every wave of every block gets the same value without a barrier.
-constexpr int kNormSqPerLane = 16;  // partial sums per lane: up to 1024 phase-3 blocks (H 8192, I 2048)
-__device__ __forceinline__ double wave_rms_inv(double ss, int H, float eps) {
-  ss = seg_sum<64>(ss);
-  const long long b = __double_as_longlong(ss);
-  const int lo = __builtin_amdgcn_readlane((int)(b & 0xFFFFFFFF), 63);
-  const int hi = __builtin_amdgcn_readlane((int)(b >> 32), 63);
-  const double tot = __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
-  return 1.0 / sqrt(tot / (double)H + (double)eps);
+// RMS norm scale 1/sqrt(mean(h^2) + eps) from the fp64 sum of h^2 over the whole vector.
+__device__ __forceinline__ double rms_inv(double ss, int H, float eps) {
+  return 1.0 / sqrt(ss / (double)H + (double)eps);
+}
+
+// An fp64 value of one lane, made uniform across the wave.
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane((int)(b & 0xFFFFFFFF), lane);
+  const int hi = __builtin_amdgcn_readlane((int)(b >> 32), lane);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
 }
 
 // gate/up/SwiGLU for P row steps of one expert, for a whole block: weight loads go out first,
@@ -534,19 +534,19 @@ __device__ __forceinline__ void gateup_block(const LayerArgs& a, const uint8_t* 
 
 // ---------------------------------------------------------------------------------------------
 // Kernel 1: router logits and the shared-gate logit (row E), accumulated in fp64. In a stack the
-// input is RMS-normalised first; block 0 stores the normalised vector for kernel 2.
+// input is RMS-normalised first, and the blocks together store the normalised vector for kernel 2.
 #ifndef BQ_ROUTER_SPLIT
 #define BQ_ROUTER_SPLIT 4
 #endif
 template <int H>
 __global__ __launch_bounds__(kBlock) void k_router_phase(LayerArgs a, const float* __restrict__ x,
-                                                         const float* __restrict__ norm_src,
-                                                         const double* __restrict__ norm_sq, int nsq, float eps,
+                                                         const float* __restrict__ norm_src, float eps,
                                                          int router_steps) {
   using R = RouterCfg<H>;
   constexpr int SPLIT = (R::CPL % BQ_ROUTER_SPLIT == 0) ? BQ_ROUTER_SPLIT : 1;  // waves per row
   constexpr int CPW = R::CPL / SPLIT;                                            // chunks per lane
   __shared__ double part[kWaves];
+  __shared__ double psq[kWaves];
   const int t = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int lir = lane % R::LPR, rig = lane / R::LPR;
@@ -562,21 +562,9 @@ __global__ __launch_bounds__(kBlock) void k_router_phase(LayerArgs a, const floa
 #pragma unroll
     for (int j = 0; j < CPW; ++j) w[j] = *reinterpret_cast<const uint4*>(row + (lir + (j * SPLIT + piece) * R::LPR) * 8);
   };
-  // Order of requests: the norm's partial sums, then the first router rows and the activations.
-  // Loads retire in order, so reducing the partial sums never waits for the rows. The norm's scale
-  // is a scalar, so a row's dot product with the raw input is taken first and scaled at the end:
-  // sum_j R[e][j] (s h_j) = s sum_j R[e][j] h_j, with every product exact in fp64.
+  // The norm's scale is a scalar, so a row's dot product with the raw input is taken first and
+  // scaled at the end: sum_j R[e][j] (s h_j) = s sum_j R[e][j] h_j, with every product exact in fp64.
   const bool norm = norm_src != nullptr;
-  double sqv[kNormSqPerLane];
-  if (norm) {
-    const double* sq = norm_sq + (size_t)t * nsq;
-#pragma unroll
-    for (int i = 0; i < kNormSqPerLane; ++i) {
-      const int k = lane + 64 * i;
-      const double v = sq[min(k, nsq - 1)];
-      sqv[i] = k < nsq ? v : 0.0;
-    }
-  }
   const float* src = (norm ? norm_src : x) + (size_t)t * H;
   uint4 w[CPW];
   float4 xr[CPW][2];
@@ -587,12 +575,25 @@ __global__ __launch_bounds__(kBlock) void k_router_phase(LayerArgs a, const floa
     xr[j][0] = p[0];
     xr[j][1] = p[1];
   }
+  // The mean square of h, from the activations already in registers: the SPLIT waves of a row set
+  // hold the whole vector between them (each row group of a wave the same share), so every block
+  // adds the same squares in the same order and gets the same scale, bit for bit.
   double scale = 1.0;
   if (norm) {
     double ss = 0.0;
 #pragma unroll
-    for (int i = 0; i < kNormSqPerLane; ++i) ss += sqv[i];
-    scale = wave_rms_inv(ss, H, eps);
+    for (int j = 0; j < CPW; ++j) {
+      const float xv[8] = {xr[j][0].x, xr[j][0].y, xr[j][0].z, xr[j][0].w,
+                           xr[j][1].x, xr[j][1].y, xr[j][1].z, xr[j][1].w};
+#pragma unroll
+      for (int q = 0; q < 8; ++q) ss = fma((double)xv[q], (double)xv[q], ss);
+    }
+    ss = seg_sum<R::LPR>(ss);  // the wave's share, complete in lane LPR - 1 of each row group
+    if constexpr (SPLIT == 1) {
+      scale = rms_inv(readlane_f64(ss, R::LPR - 1), H, eps);
+    } else {
+      if (lane == 63) psq[wave] = ss;  // summed after the first row step's barrier
+    }
   }
   for (int s = 0; s < router_steps; ++s) {
     if (s > 0) load_w(s, w);
@@ -615,6 +616,11 @@ __global__ __launch_bounds__(kBlock) void k_router_phase(LayerArgs a, const floa
     } else {
       if (lane == 63) part[wave] = tot;
       __syncthreads();
+      if (norm && s == 0) {
+        double v = psq[wave - piece];
+        for (int q = 1; q < SPLIT; ++q) v += psq[wave - piece + q];
+        scale = rms_inv(v, H, eps);
+      }
       if (piece == 0 && lane == 63 && r < nrows) {
         double v = part[wave];
         for (int q = 1; q < SPLIT; ++q) v += part[wave + q];
@@ -767,7 +773,7 @@ __global__ __launch_bounds__(kBlock) void k_gateup(LayerArgs a, const float* __r
 template <int BITS, int I, int P, int FORM>
 __global__ __launch_bounds__(kBlock) void k_down(LayerArgs a, const int32_t* __restrict__ idx,
                                                  const float* __restrict__ residual, float* __restrict__ out,
-                                                 float* __restrict__ y, double* __restrict__ sq_out) {
+                                                 float* __restrict__ y) {
   using C = RowCfg<BITS, I>;
   constexpr int RB = C::RPW * P;
   __shared__ float4 hs[kWaves][I / 4];
@@ -832,23 +838,13 @@ __global__ __launch_bounds__(kBlock) void k_down(LayerArgs a, const int32_t* __r
   }
   if (!combine) return;
   __syncthreads();
-  double ss = 0.0;
   for (int i = threadIdx.x; i < RB; i += kBlock) {
     const int r = row0 + i;
     if (r >= a.H) continue;
     float acc = residual[(size_t)t * a.H + r];
     for (int w = 0; w < kWaves && w < a.NE; ++w) acc += part[w][i];
     out[(size_t)t * a.H + r] = acc;
-    ss += (double)acc * (double)acc;
   }
-  if (sq_out == nullptr) return;
-  // this block's sum of out^2 for the next layer's RMS norm (fixed order: DPP within each wave,
-  // then the waves in index order)
-  __shared__ double wsq[kWaves];
-  ss = seg_sum<64>(ss);
-  if (lane == 63) wsq[wave] = ss;
-  __syncthreads();
-  if (threadIdx.x == 0) sq_out[(size_t)t * gridDim.x + blockIdx.x] = (wsq[0] + wsq[1]) + (wsq[2] + wsq[3]);
 }
 
 // Router-only top-K: one wave per token.
@@ -989,8 +985,8 @@ hipError_t launch_timed(F kernel, dim3 grid, dim3 block, hipStream_t s, const Ke
 }
 
 template <int BITS, int H>
-hipError_t router_phase_impl(const LayerArgs& a, const float* x, const float* norm_src, const double* norm_sq,
-                             int nsq, float eps, int T, hipStream_t s, const KernelEvents& ev) {
+hipError_t router_phase_impl(const LayerArgs& a, const float* x, const float* norm_src, float eps, int T,
+                             hipStream_t s, const KernelEvents& ev) {
   using R = RouterCfg<H>;
   const int router_steps = BQ_ROUTER_STEPS;
   const int nrows = a.E + a.has_shared;
@@ -1001,8 +997,7 @@ hipError_t router_phase_impl(const LayerArgs& a, const float* x, const float* no
     return launch_timed(k_router_group<H, kRouterGroup>, dim3(nrb, (T + kRouterGroup - 1) / kRouterGroup),
                         dim3(kBlock), s, ev, a, x, T);
   }
-  return launch_timed(k_router_phase<H>, dim3(nrb, T), dim3(kBlock), s, ev, a, x, norm_src, norm_sq, nsq, eps,
-                      router_steps);
+  return launch_timed(k_router_phase<H>, dim3(nrb, T), dim3(kBlock), s, ev, a, x, norm_src, eps, router_steps);
 }
 
 template <int BITS, int H>
@@ -1031,11 +1026,11 @@ hipError_t gateup_impl(const LayerArgs& a, const float* x, int T, const int32_t*
 
 template <int BITS, int I>
 hipError_t down_impl(const LayerArgs& a, int T, const int32_t* idx, const float* residual, float* out, float* y,
-                     double* sq_out, hipStream_t s, const KernelEvents& ev) {
+                     hipStream_t s, const KernelEvents& ev) {
   using C = RowCfg<BITS, I>;
   constexpr int RB = C::RPW * kP3;
   const int nb = (a.H + RB - 1) / RB;
-#define BQ_DN(F) launch_timed(k_down<BITS, I, kP3, F>, dim3(nb, T), dim3(kBlock), s, ev, a, idx, residual, out, y, sq_out)
+#define BQ_DN(F) launch_timed(k_down<BITS, I, kP3, F>, dim3(nb, T), dim3(kBlock), s, ev, a, idx, residual, out, y)
   if constexpr (BITS == 4) {
     if (a.form == 3) return BQ_DN(3);
   }
@@ -1043,23 +1038,15 @@ hipError_t down_impl(const LayerArgs& a, int T, const int32_t* idx, const float*
 #undef BQ_DN
 }
 
-template <int BITS, int I>
-int down_blocks_impl(int H) {
-  using C = RowCfg<BITS, I>;
-  constexpr int RB = C::RPW * kP3;
-  return (H + RB - 1) / RB;
-}
-
 }  // namespace
 
 hipError_t launch_router_phase(const Geometry& g, const LayerPtrs& p, const float* x, const float* norm_src,
-                               const double* norm_sq, int nsq, float eps, int T, const Workspace& ws, hipStream_t s,
-                               const KernelEvents& ev) {
+                               float eps, int T, const Workspace& ws, hipStream_t s, const KernelEvents& ev) {
   const LayerArgs a = make_args(g, p, ws);
 #define BQ_CASE(HV)                                                                                  \
   case HV:                                                                                           \
-    return g.bits == 4 ? router_phase_impl<4, HV>(a, x, norm_src, norm_sq, nsq, eps, T, s, ev)       \
-                       : router_phase_impl<2, HV>(a, x, norm_src, norm_sq, nsq, eps, T, s, ev);
+    return g.bits == 4 ? router_phase_impl<4, HV>(a, x, norm_src, eps, T, s, ev)                     \
+                       : router_phase_impl<2, HV>(a, x, norm_src, eps, T, s, ev);
   switch (g.H) { BQ_FOR_H(BQ_CASE) }
 #undef BQ_CASE
   return hipErrorInvalidValue;
@@ -1079,33 +1066,21 @@ hipError_t launch_gateup(const Geometry& g, const LayerPtrs& p, const float* x, 
 }
 
 hipError_t launch_down(const Geometry& g, const LayerPtrs& p, int T, const Workspace& ws, const int32_t* idx,
-                       const float* residual, float* out, float* y, double* sq_out, hipStream_t s,
-                       const KernelEvents& ev) {
+                       const float* residual, float* out, float* y, hipStream_t s, const KernelEvents& ev) {
   const LayerArgs a = make_args(g, p, ws);
 #define BQ_CASE(IV)                                                                        \
   case IV:                                                                                 \
-    return g.bits == 4 ? down_impl<4, IV>(a, T, idx, residual, out, y, sq_out, s, ev)      \
-                       : down_impl<2, IV>(a, T, idx, residual, out, y, sq_out, s, ev);
+    return g.bits == 4 ? down_impl<4, IV>(a, T, idx, residual, out, y, s, ev)              \
+                       : down_impl<2, IV>(a, T, idx, residual, out, y, s, ev);
   switch (g.I) { BQ_FOR_I(BQ_CASE) }
 #undef BQ_CASE
   return hipErrorInvalidValue;
 }
 
-int max_norm_partials() { return 64 * kNormSqPerLane; }
-
 hipError_t launch_prefetch(const Prefetch& pf, int blocks, hipStream_t s) {
   if (pf.bytes[0] + pf.bytes[1] == 0) return hipSuccess;
   hipLaunchKernelGGL(k_prefetch, dim3(blocks), dim3(kBlock), 0, s, pf);
   return hipGetLastError();
-}
-
-int down_blocks(const Geometry& g) {
-#define BQ_CASE(IV) \
-  case IV:          \
-    return g.bits == 4 ? down_blocks_impl<4, IV>(g.H) : down_blocks_impl<2, IV>(g.H);
-  switch (g.I) { BQ_FOR_I(BQ_CASE) }
-#undef BQ_CASE
-  return 0;
 }
 
 hipError_t launch_topk(const Geometry& g, int T, const Workspace& ws, int32_t* idx, float* w, float* sg,

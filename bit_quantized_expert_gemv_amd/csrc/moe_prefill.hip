@@ -1223,7 +1223,7 @@ hipError_t launch_router_tokens(const Geometry& g, const LayerPtrs& p, const flo
                                 hipStream_t s) {
   // the fp64 GEMM fills the chip only for many tokens; below that, per-token router rows win
   if (T >= kRouterGemmMinTokens) return launch_router_gemm(g, p, x, T, ws, s);
-  return launch_router_phase(g, p, x, nullptr, nullptr, 0, 0.0f, T, ws, s);
+  return launch_router_phase(g, p, x, nullptr, 0.0f, T, ws, s);
 }
 
 hipError_t launch_prefill(const Geometry& g, const LayerPtrs& p, const float* x, const float* residual, int T,
