@@ -15,6 +15,8 @@ from ._binding import (  # noqa: F401
     MOE_MAX_TOP_K,
     MOE_OK,
     MOE_PREFILL_MIN_TOKENS,
+    MOE_ROUTER_BATCH_MIN_TOKENS,
+    MOE_ROUTER_CERTIFIED_MIN_TOKENS,
     MOE_FLAG_DEQUANT_LITERAL,
     MOE_FLAG_DEQUANT_NAIVE,
     MOE_FLAG_PREFETCH_NEXT,

@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(_HERE, "libbqmoe.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ENOSPC, MOE_EHIP = 0, -1, -2, -3, -4
 MOE_MAX_TOP_K, MOE_MAX_EXPERTS, MOE_PREFILL_MIN_TOKENS = 8, 1024, 64
+MOE_ROUTER_BATCH_MIN_TOKENS, MOE_ROUTER_CERTIFIED_MIN_TOKENS = 96, 512
 MOE_FLAG_DEQUANT_LITERAL, MOE_FLAG_DEQUANT_NAIVE, MOE_FLAG_PREFETCH_NEXT = 1, 2, 4
 
 c_i32, c_u64, c_size, c_vp, c_f32 = ctypes.c_int32, ctypes.c_uint64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float

@@ -116,7 +116,7 @@ bool geometry_from(const moe_layer_t* L, Geometry* g, const char** why) {
 size_t workspace_layer_bytes(const Geometry& g, int T) {
   const size_t t = (size_t)T;
   return align256(t * (g.E + 1) * 8) + align256(t * g.K * 4) + align256(t * g.K * 4) + align256(t * 4) +
-         align256(t * g.NE * g.I * 4) + align256(t * g.H * 4);
+         align256(t * g.NE * g.I * 4) + align256(t * g.H * 4) + align256((size_t)g.E * 8);
 }
 
 namespace {
@@ -141,6 +141,7 @@ PrefillWorkspace carve_prefill_impl(const Geometry& g, int T, void* base, size_t
   w.layer.g = c.take<float>(t);
   w.layer.h = nullptr;
   w.layer.u = nullptr;
+  w.layer.rnorm = c.take<double>(g.E);
   const bool mx = g.form == 3;
   w.xq = mx ? nullptr : c.take<uint16_t>(t * g.H);
   w.xs = mx ? nullptr : c.take<float>(t * (g.H / 64));
@@ -185,7 +186,8 @@ Workspace carve_workspace(const Geometry& g, int T, void* base) {
   ws.w = reinterpret_cast<float*>(p); p += align256(t * g.K * 4);
   ws.g = reinterpret_cast<float*>(p); p += align256(t * 4);
   ws.h = reinterpret_cast<float*>(p); p += align256(t * g.NE * g.I * 4);
-  ws.u = reinterpret_cast<float*>(p);
+  ws.u = reinterpret_cast<float*>(p); p += align256(t * g.H * 4);
+  ws.rnorm = reinterpret_cast<double*>(p);
   return ws;
 }
 
@@ -331,8 +333,7 @@ int moe_router(const moe_layer_t* layer, const float* x, int T, int32_t* idx, fl
   if (ws_bytes < needed_ws(g, T)) return fail(MOE_ENOSPC, "workspace smaller than moe_workspace_bytes()");
   const Workspace W = carve_workspace(g, T, ws);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = launch_router_tokens(g, ptrs_of(layer), x, T, W, s);
-  if (e == hipSuccess) e = launch_topk(g, T, W, idx, w, shared_g, logits, s);
+  hipError_t e = launch_router_select(g, ptrs_of(layer), x, T, W, idx, w, shared_g, logits, s);
   return hip_status(e);
 }
 

@@ -36,6 +36,7 @@ struct Workspace {
   float* g;        // [T]
   float* h;        // [T][NE][I]: SwiGLU outputs
   float* u;        // [T][H]: normalised layer input (stack only)
+  double* rnorm;   // [E]: router row norms (certified top-K only)
 };
 
 // Prefill (grouped) workspace for T tokens; N = T*K routed entries, R = N + T*has_shared rows.
@@ -99,6 +100,15 @@ hipError_t launch_gateup(const Geometry& g, const LayerPtrs& p, const float* x, 
 // Phase 3: down projections. combine: out = residual + sum_k w_k y_k + g y_s; otherwise y[t][k][:] = y_k.
 hipError_t launch_down(const Geometry& g, const LayerPtrs& p, int T, const Workspace& ws, const int32_t* idx,
                        const float* residual, float* out, float* y, hipStream_t s, const KernelEvents& ev = {});
+// Certified top-K (many tokens, no logits output): ws.logits must hold approximate logits whose
+// error is at most kc * |r_e| * |x_t| (plus a subnormal slack); computes the router row norms into
+// ws.rnorm, recomputes in fp64 the rows the bound cannot rule out, and writes idx, w and sg.
+hipError_t launch_topk_certified(const Geometry& g, const LayerPtrs& p, const float* x, int T, const Workspace& ws,
+                                 double kc, int32_t* idx, float* w, float* sg, hipStream_t s);
+// Routing of T tokens into idx/w/sg (and the fp64 logits into logits_out when non-null): the
+// certified bf16-MFMA path for many tokens without logits_out, otherwise fp64 logits then the top-K.
+hipError_t launch_router_select(const Geometry& g, const LayerPtrs& p, const float* x, int T, const Workspace& ws,
+                                int32_t* idx, float* w, float* sg, double* logits_out, hipStream_t s);
 // Top-K + weights from ws.logits (router-only path).
 hipError_t launch_topk(const Geometry& g, int T, const Workspace& ws, int32_t* idx, float* w, float* sg,
                        double* logits_out, hipStream_t s);

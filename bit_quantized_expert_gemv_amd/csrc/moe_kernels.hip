@@ -863,6 +863,181 @@ __global__ __launch_bounds__(64) void k_topk(LayerArgs a, int32_t* __restrict__ 
   if (lane == 0) write_routing(a, t, sel, val, lg, idx, w, nullptr, sg);
 }
 
+// fp64 norm of each bf16 router row (one wave per row), for the certified top-K's error bound.
+__global__ __launch_bounds__(kBlock) void k_row_norms(int E, int H, const uint16_t* __restrict__ router,
+                                                      double* __restrict__ rnorm) {
+  const int e = blockIdx.x * kWaves + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (e >= E) return;
+  const uint16_t* row = router + (size_t)e * H;
+  double ss = 0.0;
+  for (int c = lane; c < H / 8; c += 64) {
+    const uint4 w = *reinterpret_cast<const uint4*>(row + c * 8);
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const double lo = bf16_lo(ww[q]), hi = bf16_hi(ww[q]);
+      ss = fma(lo, lo, ss);
+      ss = fma(hi, hi, ss);
+    }
+  }
+  ss = readlane_f64(seg_sum<64>(ss), 63);
+  if (lane == 0) rnorm[e] = sqrt(ss);
+}
+
+// fp64 dot products of NR bf16 rows with the token's activations held in registers (chunk
+// lane + 64j, 8 values each). The rows' loads are issued together; every lane returns the totals.
+template <int H, int NR>
+__device__ __forceinline__ void wave_rows_dot(const uint16_t* const (&rows)[NR],
+                                              const float4 (&xr)[(H / 8 + 63) / 64][2], int lane, double (&out)[NR]) {
+  constexpr int NCH = H / 8, XC = (NCH + 63) / 64;
+  double acc[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) acc[r] = 0.0;
+#pragma unroll
+  for (int j = 0; j < XC; ++j) {
+    const int ch = lane + 64 * j;
+    if (NCH % 64 != 0 && ch >= NCH) continue;
+    const float xv[8] = {xr[j][0].x, xr[j][0].y, xr[j][0].z, xr[j][0].w,
+                         xr[j][1].x, xr[j][1].y, xr[j][1].z, xr[j][1].w};
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const uint4 w = *reinterpret_cast<const uint4*>(rows[r] + ch * 8);
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[r] = fma((double)bf16_lo(ww[q]), (double)xv[2 * q], acc[r]);
+        acc[r] = fma((double)bf16_hi(ww[q]), (double)xv[2 * q + 1], acc[r]);
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < NR; ++r) out[r] = readlane_f64(seg_sum<64>(acc[r]), 63);
+}
+
+__device__ __forceinline__ double wave_min_f64(double v) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v = fmin(v, __shfl_xor(v, m));
+  return v;
+}
+
+// Certified top-K from approximate logits (one wave per token). ws.logits holds approximations
+// l~_e with |l~_e - l_e| <= b_e = kc * |r_e| * |x| + (|r_e| + 1) * 2^-100 (Cauchy-Schwarz on the
+// approximation's error bound, with the row norms |r_e| from k_row_norms). With A the K rows of
+// largest l~ and LB = min over A of (l~_a - b_a), every a in A has l_a >= LB, so a row with
+// l~_i + b_i < LB lies strictly below K rows and cannot be chosen. The other rows (A itself and
+// any row the bound cannot separate) are recomputed exactly in fp64 and the top-K is taken over
+// them: the same choice as a top-K over every row's fp64 logit. A non-finite approximation or
+// bound makes every row a candidate. The shared-gate logit (row id E in the list) is computed in
+// fp64 with A's rows.
+constexpr int kCertBatch = 4;  // rows recomputed together
+template <int PL, int H>
+__global__ __launch_bounds__(kBlock) void k_topk_certified(LayerArgs a, const float* __restrict__ x,
+                                                           const double* __restrict__ rnorm, double kc, int T,
+                                                           int32_t* __restrict__ idx, float* __restrict__ w,
+                                                           float* __restrict__ sg) {
+  constexpr int NCH = H / 8, XC = (NCH + 63) / 64;
+  constexpr int kList = 64 * PL + MOE_MAX_TOP_K + 1;  // every row, the gate row, and room for A twice
+  __shared__ int32_t sel[kWaves][MOE_MAX_TOP_K];
+  __shared__ double val[kWaves][MOE_MAX_TOP_K];
+  __shared__ int32_t list[kWaves][kList];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * kWaves + wave;
+  if (t >= T) return;  // wave-uniform; the kernel has no block barrier
+  const double* lg = a.ws.logits + (size_t)t * (a.E + 1);
+  double la[PL], rn[PL];
+  load_topk_values<PL>(lg, a.E, lane, la);
+#pragma unroll
+  for (int i = 0; i < PL; ++i) rn[i] = rnorm[min(lane + 64 * i, a.E - 1)];
+  float4 xr[XC][2];
+  double xx = 0.0;
+#pragma unroll
+  for (int j = 0; j < XC; ++j) {
+    const int ch = min(lane + 64 * j, NCH - 1);
+    const float4* p = reinterpret_cast<const float4*>(x + (size_t)t * H + ch * 8);
+    xr[j][0] = p[0];
+    xr[j][1] = p[1];
+    if (NCH % 64 != 0 && lane + 64 * j >= NCH) continue;
+    const float xv[8] = {xr[j][0].x, xr[j][0].y, xr[j][0].z, xr[j][0].w,
+                         xr[j][1].x, xr[j][1].y, xr[j][1].z, xr[j][1].w};
+#pragma unroll
+    for (int q = 0; q < 8; ++q) xx = fma((double)xv[q], (double)xv[q], xx);
+  }
+  const double xn = sqrt(readlane_f64(seg_sum<64>(xx), 63));
+  double bnd[PL];
+  bool bad = false;
+#pragma unroll
+  for (int i = 0; i < PL; ++i) {
+    bnd[i] = kc * rn[i] * xn + (rn[i] + 1.0) * 0x1p-100;
+    if (lane + 64 * i < a.E && !(__builtin_isfinite(la[i]) && __builtin_isfinite(bnd[i]))) bad = true;
+  }
+  // The list of rows to recompute: A (or, after a non-finite value, every row), the gate row
+  // (id E), then the rows the bound cannot separate from A.
+  int32_t* lst = list[wave];
+  int n = 0;
+  bool extra[PL];
+  if (__ballot(bad) == 0) {
+    double v[PL];
+#pragma unroll
+    for (int i = 0; i < PL; ++i) v[i] = la[i];
+    wave_topk<PL>(v, a.E, a.K, lane, -1, true, sel[wave], val[wave]);  // the K best become -inf
+    double lb = INFINITY;
+#pragma unroll
+    for (int i = 0; i < PL; ++i)
+      if (lane + 64 * i < a.E && v[i] == -INFINITY) lb = fmin(lb, la[i] - bnd[i]);
+    lb = wave_min_f64(lb);
+#pragma unroll
+    for (int i = 0; i < PL; ++i) extra[i] = lane + 64 * i < a.E && v[i] != -INFINITY && la[i] + bnd[i] >= lb;
+    if (lane < a.K) lst[lane] = sel[wave][lane];
+    n = a.K;
+  } else {
+#pragma unroll
+    for (int i = 0; i < PL; ++i) extra[i] = lane + 64 * i < a.E;
+  }
+  if (a.has_shared) {  // the shared-gate row
+    if (lane == 0) lst[n] = a.E;
+    n += 1;
+  }
+#pragma unroll
+  for (int i = 0; i < PL; ++i) {
+    const uint64_t m = __ballot(extra[i]);
+    if (extra[i]) lst[n + __popcll(m & ((1ull << lane) - 1))] = lane + 64 * i;
+    n += __popcll(m);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  double ex[PL];
+#pragma unroll
+  for (int i = 0; i < PL; ++i) ex[i] = -INFINITY;
+  double gl = 0.0;
+  for (int b = 0; b < n; b += kCertBatch) {
+    int id[kCertBatch];
+    const uint16_t* rows[kCertBatch];
+#pragma unroll
+    for (int q = 0; q < kCertBatch; ++q) {
+      id[q] = lst[min(b + q, n - 1)];  // past the end: the last row again, its result unused
+      rows[q] = id[q] < a.E ? a.router + (size_t)id[q] * H : a.sgate;  // id E only with a shared gate
+    }
+    double d[kCertBatch];
+    wave_rows_dot<H, kCertBatch>(rows, xr, lane, d);
+#pragma unroll
+    for (int q = 0; q < kCertBatch; ++q) {
+      if (id[q] == a.E) {
+        gl = d[q];
+        continue;
+      }
+#pragma unroll
+      for (int i = 0; i < PL; ++i)
+        if (id[q] == lane + 64 * i) ex[i] = d[q];
+    }
+  }
+  wave_topk<PL>(ex, a.E, a.K, lane, -1, true, sel[wave], val[wave]);
+  if (lane == 0) {
+    write_routing(a, t, sel[wave], val[wave], nullptr, idx, w, nullptr, nullptr);
+    if (sg && a.has_shared) sg[t] = (float)(1.0 / (1.0 + exp(-gl)));
+  }
+}
+
 __global__ void k_combine(int T, int H, int K, int has_shared, const float* __restrict__ res,
                           const float* __restrict__ y, const float* __restrict__ w, const float* __restrict__ sg,
                           float* __restrict__ out) {
@@ -1092,6 +1267,23 @@ hipError_t launch_topk(const Geometry& g, int T, const Workspace& ws, int32_t* i
   else
     hipLaunchKernelGGL(k_topk<16>, dim3(T), dim3(64), 0, s, a, idx, w, sg, logits_out);
   return hipGetLastError();
+}
+
+hipError_t launch_topk_certified(const Geometry& g, const LayerPtrs& p, const float* x, int T, const Workspace& ws,
+                                 double kc, int32_t* idx, float* w, float* sg, hipStream_t s) {
+  const LayerArgs a = make_args(g, p, ws);
+  hipLaunchKernelGGL(k_row_norms, dim3((g.E + kWaves - 1) / kWaves), dim3(kBlock), 0, s, g.E, g.H, p.router, ws.rnorm);
+  const dim3 grid((T + kWaves - 1) / kWaves);
+#define BQ_CASE(HV)                                                                                              \
+  case HV:                                                                                                       \
+    if (g.E <= 512)                                                                                              \
+      hipLaunchKernelGGL((k_topk_certified<8, HV>), grid, dim3(kBlock), 0, s, a, x, ws.rnorm, kc, T, idx, w, sg); \
+    else                                                                                                         \
+      hipLaunchKernelGGL((k_topk_certified<16, HV>), grid, dim3(kBlock), 0, s, a, x, ws.rnorm, kc, T, idx, w, sg); \
+    return hipGetLastError();
+  switch (g.H) { BQ_FOR_H(BQ_CASE) }
+#undef BQ_CASE
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_combine(const Geometry& g, int T, const float* residual, const float* y, const float* w,

@@ -94,9 +94,13 @@ constexpr int kRW = 32;      // tokens and rows per wave
 constexpr int kRSplit = BQ_ROUTER_SPLITK;  // waves per block, each with 1/kRSplit of K
 constexpr int kRSlice = 32;  // K per slice
 #ifndef BQ_ROUTER_GEMM_MIN
-#define BQ_ROUTER_GEMM_MIN 96
+#define BQ_ROUTER_GEMM_MIN MOE_ROUTER_BATCH_MIN_TOKENS
 #endif
 constexpr int kRouterGemmMinTokens = BQ_ROUTER_GEMM_MIN;
+#ifndef BQ_ROUTER_CERTIFIED_MIN
+#define BQ_ROUTER_CERTIFIED_MIN MOE_ROUTER_CERTIFIED_MIN_TOKENS
+#endif
+constexpr int kRouterCertifiedMinTokens = BQ_ROUTER_CERTIFIED_MIN;
 
 struct RouterRaw {
   float4 x[2][2];  // [token tile][half]: 8 consecutive x of the lane's token
@@ -200,6 +204,150 @@ __global__ __launch_bounds__(64 * kRSplit) void k_router_gemm(int T, int H, int 
       for (int q = 0; q < 4; ++q) {
         const int t = t0 + 16 * ti + kk + 4 * q;
         if (t < T) logits[(size_t)t * (E + 1) + e] = acc[ti][rj][q];
+      }
+    }
+  }
+}
+
+// ---- 2b. certified router: approximate logits on bf16 MFMAs -------------------------------------
+// For a top-K alone the fp64 GEMM above does far more exact work than the decision needs. Here the
+// logits are first approximated on bf16 MFMAs, then a per-token kernel recomputes in fp64 only the
+// rows that the approximation's error bound cannot rule out. Each x is split into two bf16 values,
+// x = hi + lo + d with |d| <= 2^-16 |x| (round to nearest even twice), so the MFMAs see products
+// that are exact in fp32; the only other error is the fp32 accumulation inside the MFMA chain.
+// D = A B with A = router rows (16 x 32 bf16) and B = activations (32 x 16). A[i][k] sits in lane
+// i + 16*(k/8), element k%8; B[k][j] in lane j + 16*(k/8), element k%8; D[i][j] in lane
+// j + 16*(i/4), element i%4. A block computes kAR rows x 32 tokens; its kASplit waves take equal
+// slices of K, and their partial tiles are added in fp64 in wave order.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+#ifndef BQ_ROUTER_APPROX_RT
+#define BQ_ROUTER_APPROX_RT 8
+#endif
+constexpr int kART = BQ_ROUTER_APPROX_RT;  // row tiles of 16 per wave
+constexpr int kAR = 16 * kART;             // router rows per block
+constexpr int kAT = 32;     // tokens per block (2 token tiles)
+#ifndef BQ_ROUTER_APPROX_SPLITK
+#define BQ_ROUTER_APPROX_SPLITK 4
+#endif
+constexpr int kASplit = BQ_ROUTER_APPROX_SPLITK;  // waves per block, each with 1/kASplit of K
+
+struct ApproxRaw {
+  uint4 r[kART];   // [row tile]: 8 consecutive bf16 of the lane's row
+  float4 x[2][2];  // [token tile][half]: 8 consecutive x of the lane's token
+};
+
+__device__ __forceinline__ void split_bf16(const float4& a, const float4& b, bf16x8_t& hi, bf16x8_t& lo) {
+  const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const __bf16 h = (__bf16)v[i];  // round to nearest even
+    hi[i] = h;
+    lo[i] = (__bf16)(v[i] - (float)h);  // the difference is exact in fp32
+  }
+}
+
+__global__ __launch_bounds__(64 * kASplit) void k_router_approx(int T, int H, int E, const float* __restrict__ x,
+                                                                const uint16_t* __restrict__ router,
+                                                                double* __restrict__ logits) {
+  __shared__ f32x4_t part[kASplit - 1][kART][2][64];  // the partial tiles of waves 1..kASplit-1
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane & 15, kk = lane >> 4;
+  // XCD-aware order: blocks are dealt to the 8 XCDs in turn, so when the count allows, the blocks
+  // of one XCD take consecutive tiles (a few token tiles, every row tile) and share them in its L2.
+  const int nbx = gridDim.x, total = gridDim.x * gridDim.y;
+  int id = blockIdx.x + nbx * blockIdx.y;
+  if (total % 8 == 0) id = (id & 7) * (total / 8) + (id >> 3);
+  const int e0 = (id % nbx) * kAR, t0 = (id / nbx) * kAT;
+  const int kh = H / kASplit;
+  const int kbeg = wave * kh + 8 * kk;
+  const uint16_t* rp[kART];
+  const float* xp[2];
+#pragma unroll
+  for (int i = 0; i < kART; ++i) rp[i] = router + (size_t)min(e0 + 16 * i + c, E - 1) * H + kbeg;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) xp[j] = x + (size_t)min(t0 + 16 * j + c, T - 1) * H + kbeg;
+  const int nst = kh / 32;
+  auto load = [&](ApproxRaw& R, int st) __attribute__((always_inline)) {
+    const int off = st * 32;
+#pragma unroll
+    for (int i = 0; i < kART; ++i) R.r[i] = *reinterpret_cast<const uint4*>(rp[i] + off);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) R.x[j][h] = *reinterpret_cast<const float4*>(xp[j] + off + 4 * h);
+  };
+  f32x4_t acc[kART][2];
+#pragma unroll
+  for (int i = 0; i < kART; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  auto compute = [&](const ApproxRaw& R) __attribute__((always_inline)) {
+    bf16x8_t hi[2], lo[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) split_bf16(R.x[j][0], R.x[j][1], hi[j], lo[j]);
+#pragma unroll
+    for (int i = 0; i < kART; ++i) {
+      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, R.r[i]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, hi[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, lo[j], acc[i][j], 0, 0, 0);
+      }
+    }
+  };
+  ApproxRaw r0, r1, r2;
+  load(r0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  load(r1, min(1, nst - 1));
+  __builtin_amdgcn_sched_barrier(0);
+  // The scheduling barriers keep each stage's loads where they are written: left to itself, the
+  // scheduler sinks them into the MFMA stream of the previous stage, and each stage then waits for
+  // loads issued just before it.
+#pragma unroll 1
+  for (int st = 0; st < nst; st += 3) {
+    // every load is issued on every path (clamped past the end), so the wait counts stay exact
+    load(r2, min(st + 2, nst - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    compute(r0);
+    __builtin_amdgcn_sched_barrier(0);
+    load(r0, min(st + 3, nst - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    if (st + 1 < nst) compute(r1);
+    __builtin_amdgcn_sched_barrier(0);
+    load(r1, min(st + 4, nst - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    if (st + 2 < nst) compute(r2);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int i = 0; i < kART; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) part[wave - 1][i][j][lane] = acc[i][j];
+  }
+  __syncthreads();
+  if (wave > 0) return;
+  // element q of tile (i, j) in lane (c, kk): row e0 + 16i + 4kk + q, token t0 + 16j + c
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int t = t0 + 16 * j + c;
+    if (t >= T) continue;
+#pragma unroll
+    for (int i = 0; i < kART; ++i) {
+      double v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = (double)acc[i][j][q];
+#pragma unroll
+      for (int w = 0; w < kASplit - 1; ++w) {
+        const f32x4_t p = part[w][i][j][lane];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] += (double)p[q];
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = e0 + 16 * i + 4 * kk + q;
+        if (e < E) logits[(size_t)t * (E + 1) + e] = v[q];
       }
     }
   }
@@ -1226,6 +1374,32 @@ hipError_t launch_router_tokens(const Geometry& g, const LayerPtrs& p, const flo
   return launch_router_phase(g, p, x, nullptr, 0.0f, T, ws, s);
 }
 
+hipError_t launch_router_select(const Geometry& g, const LayerPtrs& p, const float* x, int T, const Workspace& ws,
+                                int32_t* idx, float* w, float* sg, double* logits_out, hipStream_t s) {
+  if (logits_out != nullptr || T < kRouterCertifiedMinTokens) {
+    hipError_t e = launch_router_tokens(g, p, x, T, ws, s);
+    return e == hipSuccess ? launch_topk(g, T, ws, idx, w, sg, logits_out, s) : e;
+  }
+  hipLaunchKernelGGL(k_router_approx, dim3(cdiv(g.E, kAR), cdiv(T, kAT)), dim3(64 * kASplit), 0, s, T, g.H, g.E, x,
+                     p.router, ws.logits);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // Error bound of the approximate logits, relative to |r_e| |x_t|:
+  //  - splitting x into two bf16 values leaves |d| <= 2^-16 |x|, and |hi| + |lo| <= 1.01 |x|;
+  //  - one MFMA adds 32 exact products to its accumulator with an error of at most 34 * 2^-23 times
+  //    the sum of the magnitudes it adds (per-addition rounding, to nearest or toward zero, or
+  //    operands aligned and truncated to fp32 precision);
+  //  - a wave chains n = 2 H / (32 * kASplit) MFMAs (hi and lo parts), so its error is at most
+  //    34 * 2^-23 * n * (1 + 34 * 2^-23 * n) times its sum of |r| (|hi| + |lo|);
+  //  - the sum of |r_j| |x_j| is at most |r| |x| (Cauchy-Schwarz), and the fp64 sums around
+  //    this (the waves' partial sums, the norms, the exact recomputation) are far below it.
+  // The factor 1.25 is a safety margin on all of it.
+  const double n = 2.0 * g.H / (32.0 * kASplit);
+  const double u = std::ldexp(1.0, -23);
+  const double kc = 1.25 * (std::ldexp(1.0, -16) * 1.01 + 34.0 * u * n * (1.0 + 34.0 * u * n) * 1.01);
+  return launch_topk_certified(g, p, x, T, ws, kc, idx, w, sg, s);
+}
+
 hipError_t launch_prefill(const Geometry& g, const LayerPtrs& p, const float* x, const float* residual, int T,
                           const PrefillWorkspace& w, const int32_t* idx_in, int32_t* idx_out, float* out,
                           float* y_out, hipStream_t s) {
@@ -1241,9 +1415,7 @@ hipError_t launch_prefill(const Geometry& g, const LayerPtrs& p, const float* x,
   }
   const int32_t* idx = idx_in;
   if (idx_in == nullptr) {
-    // the fp64 GEMM fills the chip only for many tokens; below that, per-token router rows win
-    hipError_t e = launch_router_tokens(g, p, x, T, w.layer, s);
-    if (e == hipSuccess) e = launch_topk(g, T, w.layer, w.layer.idx, w.layer.w, w.layer.g, nullptr, s);
+    hipError_t e = launch_router_select(g, p, x, T, w.layer, w.layer.idx, w.layer.w, w.layer.g, nullptr, s);
     if (e != hipSuccess) return e;
     idx = w.layer.idx;
   }

@@ -67,6 +67,14 @@ extern "C" {
 /* Token counts at or above this run the prefill path in moe_layer_forward (grouped by expert). Below
  * it, per-token streaming is faster on MI355X for a 512-expert, top-3 layer (measured crossover). */
 #define MOE_PREFILL_MIN_TOKENS 64
+/* Token counts at or above this route all tokens in one fp64 router GEMM instead of per-token
+ * router rows. */
+#define MOE_ROUTER_BATCH_MIN_TOKENS 96
+/* Token counts at or above this, when moe_router is not asked for the logits (and in
+ * moe_layer_forward's prefill), take the certified router instead: bf16 MFMA logits with an error
+ * bound, then fp64 for every row the bound cannot rule out (measured crossover with the fp64 GEMM
+ * on a 512 x 4096 router: between 384 and 512 tokens). */
+#define MOE_ROUTER_CERTIFIED_MIN_TOKENS 512
 
 /* moe_layer_t.flags values, an A/B ablation of the one kernel claim on the pages ("Kernel de
  * dequantización optimizado con FMA"). By default the decode GEMVs use the per-chunk form
@@ -159,7 +167,10 @@ int moe_dequant(const moe_layer_t* layer, int expert, int matrix, int out_dtype,
  *   w_dev fp32 [T][K] (softmax over all E logits renormalised over the K chosen),
  *   shared_g_dev fp32 [T] (sigmoid(shared_gate . x); may be NULL; ignored if !has_shared),
  *   logits_dev fp64 [T][E] (may be NULL).
- * Logits are accumulated in fp64, so the top-K decision is exact up to fp64 rounding. */
+ * Logits are accumulated in fp64, so the top-K decision is exact up to fp64 rounding. From
+ * MOE_ROUTER_CERTIFIED_MIN_TOKENS tokens with logits_dev NULL (and in moe_layer_forward's prefill), the
+ * logits are first approximated on bf16 MFMAs and only the rows whose error bound overlaps the K-th
+ * are recomputed in fp64; the choice is the same as the top-K of the fp64 logits. */
 int moe_router(const moe_layer_t* layer, const float* x_dev, int T, int32_t* idx_dev, float* w_dev,
                float* shared_g_dev, double* logits_dev, void* ws_dev, size_t ws_bytes, void* stream);
 

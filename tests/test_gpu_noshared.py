@@ -2,9 +2,9 @@
 
 The shared expert changes slot counts, the router's extra gate row, the combine and the
 grouping's shared tiles, so every path runs here once without it: decode (one token and a
-ragged handful), the router and expert entry points, and prefill with each of its two routers
-(per-token rows below 96 tokens, the fp64 GEMM from 96, with a ragged last token tile), for the
-affine 4-bit format and for MXFP4. Bar as elsewhere: bit-exact top-K indices; outputs within
+ragged handful), the router and expert entry points, and prefill with each of its three routers
+(per-token rows below 96 tokens, the fp64 GEMM from 96, the certified bf16 router from 512, each
+with a ragged last token tile), for the affine 4-bit format and for MXFP4. Bar as elsewhere: bit-exact top-K indices; outputs within
 2e-3*max|oracle| + 1e-5 per token vector.
 """
 from __future__ import annotations
@@ -64,10 +64,11 @@ def test_descriptor_has_no_shared_expert(ns4, nsmx):
 
 
 @pytest.mark.parametrize("which", ["ns4", "nsmx"])
-@pytest.mark.parametrize("t0,T", [(0, 1), (3, 7), (20, 70), (100, 130)])
+@pytest.mark.parametrize("t0,T", [(0, 1), (3, 7), (20, 70), (100, 130), (300, 600)])
 def test_layer_forward(which, t0, T, request):
-    """T = 1 and 7 run the decode path, 70 the prefill path with per-token router rows, and 130 the
-    prefill path with the fp64 router GEMM (four full token tiles and a ragged one of 2)."""
+    """T = 1 and 7 run the decode path, 70 the prefill path with per-token router rows, 130 the
+    prefill path with the fp64 router GEMM (four full token tiles and a ragged one of 2), and 600
+    the prefill path with the certified router (no shared-gate row to recompute)."""
     L, ref = request.getfixturevalue(which)
     w = L.w
     _log(f"{w.name}: layer forward tokens [{t0}, {t0 + T})")
