@@ -217,23 +217,25 @@ __global__ __launch_bounds__(64 * kRSplit) void k_router_gemm(int T, int H, int 
 // that are exact in fp32; the only other error is the fp32 accumulation inside the MFMA chain.
 // D = A B with A = router rows (16 x 32 bf16) and B = activations (32 x 16). A[i][k] sits in lane
 // i + 16*(k/8), element k%8; B[k][j] in lane j + 16*(k/8), element k%8; D[i][j] in lane
-// j + 16*(i/4), element i%4. A block computes kAR rows x 32 tokens; its kASplit waves take equal
+// j + 16*(i/4), element i%4. A block computes 16 RT rows x 32 tokens; its kASplit waves take equal
 // slices of K, and their partial tiles are added in fp64 in wave order.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+// Row tiles of 16 per wave (RT = 2, 4 or 8). The approximation is latency-bound per block, so the
+// launch takes the smallest tile whose grid still fits one block per CU: a grid past 256 blocks
+// puts two blocks on some CUs, and those finish last.
 #ifndef BQ_ROUTER_APPROX_RT
-#define BQ_ROUTER_APPROX_RT 8
+#define BQ_ROUTER_APPROX_RT 0  // 0: chosen per launch
 #endif
-constexpr int kART = BQ_ROUTER_APPROX_RT;  // row tiles of 16 per wave
-constexpr int kAR = 16 * kART;             // router rows per block
 constexpr int kAT = 32;     // tokens per block (2 token tiles)
 #ifndef BQ_ROUTER_APPROX_SPLITK
 #define BQ_ROUTER_APPROX_SPLITK 4
 #endif
 constexpr int kASplit = BQ_ROUTER_APPROX_SPLITK;  // waves per block, each with 1/kASplit of K
 
+template <int RT>
 struct ApproxRaw {
-  uint4 r[kART];   // [row tile]: 8 consecutive bf16 of the lane's row
+  uint4 r[RT];     // [row tile]: 8 consecutive bf16 of the lane's row
   float4 x[2][2];  // [token tile][half]: 8 consecutive x of the lane's token
 };
 
@@ -247,10 +249,12 @@ __device__ __forceinline__ void split_bf16(const float4& a, const float4& b, bf1
   }
 }
 
+template <int RT>
 __global__ __launch_bounds__(64 * kASplit) void k_router_approx(int T, int H, int E, const float* __restrict__ x,
                                                                 const uint16_t* __restrict__ router,
                                                                 double* __restrict__ logits) {
-  __shared__ f32x4_t part[kASplit - 1][kART][2][64];  // the partial tiles of waves 1..kASplit-1
+  constexpr int kAR = 16 * RT;  // router rows per block
+  __shared__ f32x4_t part[kASplit - 1][RT][2][64];  // the partial tiles of waves 1..kASplit-1
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15, kk = lane >> 4;
   // XCD-aware order: blocks are dealt to the 8 XCDs in turn, so when the count allows, the blocks
@@ -261,33 +265,33 @@ __global__ __launch_bounds__(64 * kASplit) void k_router_approx(int T, int H, in
   const int e0 = (id % nbx) * kAR, t0 = (id / nbx) * kAT;
   const int kh = H / kASplit;
   const int kbeg = wave * kh + 8 * kk;
-  const uint16_t* rp[kART];
+  const uint16_t* rp[RT];
   const float* xp[2];
 #pragma unroll
-  for (int i = 0; i < kART; ++i) rp[i] = router + (size_t)min(e0 + 16 * i + c, E - 1) * H + kbeg;
+  for (int i = 0; i < RT; ++i) rp[i] = router + (size_t)min(e0 + 16 * i + c, E - 1) * H + kbeg;
 #pragma unroll
   for (int j = 0; j < 2; ++j) xp[j] = x + (size_t)min(t0 + 16 * j + c, T - 1) * H + kbeg;
   const int nst = kh / 32;
-  auto load = [&](ApproxRaw& R, int st) __attribute__((always_inline)) {
+  auto load = [&](ApproxRaw<RT>& R, int st) __attribute__((always_inline)) {
     const int off = st * 32;
 #pragma unroll
-    for (int i = 0; i < kART; ++i) R.r[i] = *reinterpret_cast<const uint4*>(rp[i] + off);
+    for (int i = 0; i < RT; ++i) R.r[i] = *reinterpret_cast<const uint4*>(rp[i] + off);
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int h = 0; h < 2; ++h) R.x[j][h] = *reinterpret_cast<const float4*>(xp[j] + off + 4 * h);
   };
-  f32x4_t acc[kART][2];
+  f32x4_t acc[RT][2];
 #pragma unroll
-  for (int i = 0; i < kART; ++i)
+  for (int i = 0; i < RT; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  auto compute = [&](const ApproxRaw& R) __attribute__((always_inline)) {
+  auto compute = [&](const ApproxRaw<RT>& R) __attribute__((always_inline)) {
     bf16x8_t hi[2], lo[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) split_bf16(R.x[j][0], R.x[j][1], hi[j], lo[j]);
 #pragma unroll
-    for (int i = 0; i < kART; ++i) {
+    for (int i = 0; i < RT; ++i) {
       const bf16x8_t a = __builtin_bit_cast(bf16x8_t, R.r[i]);
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
@@ -296,7 +300,7 @@ __global__ __launch_bounds__(64 * kASplit) void k_router_approx(int T, int H, in
       }
     }
   };
-  ApproxRaw r0, r1, r2;
+  ApproxRaw<RT> r0, r1, r2;
   load(r0, 0);
   __builtin_amdgcn_sched_barrier(0);
   load(r1, min(1, nst - 1));
@@ -322,7 +326,7 @@ __global__ __launch_bounds__(64 * kASplit) void k_router_approx(int T, int H, in
   }
   if (wave > 0) {
 #pragma unroll
-    for (int i = 0; i < kART; ++i)
+    for (int i = 0; i < RT; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) part[wave - 1][i][j][lane] = acc[i][j];
   }
@@ -334,7 +338,7 @@ __global__ __launch_bounds__(64 * kASplit) void k_router_approx(int T, int H, in
     const int t = t0 + 16 * j + c;
     if (t >= T) continue;
 #pragma unroll
-    for (int i = 0; i < kART; ++i) {
+    for (int i = 0; i < RT; ++i) {
       double v[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) v[q] = (double)acc[i][j][q];
@@ -1380,8 +1384,22 @@ hipError_t launch_router_select(const Geometry& g, const LayerPtrs& p, const flo
     hipError_t e = launch_router_tokens(g, p, x, T, ws, s);
     return e == hipSuccess ? launch_topk(g, T, ws, idx, w, sg, logits_out, s) : e;
   }
-  hipLaunchKernelGGL(k_router_approx, dim3(cdiv(g.E, kAR), cdiv(T, kAT)), dim3(64 * kASplit), 0, s, T, g.H, g.E, x,
-                     p.router, ws.logits);
+  int rt = BQ_ROUTER_APPROX_RT;
+  if (rt == 0) {  // the smallest tile whose grid fits one block per CU (256), else the largest
+    rt = 8;
+    for (int c : {2, 4})
+      if (cdiv(g.E, 16 * c) * cdiv(T, kAT) <= 256) {
+        rt = c;
+        break;
+      }
+  }
+  const dim3 ag(cdiv(g.E, 16 * rt), cdiv(T, kAT)), ab(64 * kASplit);
+  if (rt == 8)
+    hipLaunchKernelGGL(k_router_approx<8>, ag, ab, 0, s, T, g.H, g.E, x, p.router, ws.logits);
+  else if (rt == 4)
+    hipLaunchKernelGGL(k_router_approx<4>, ag, ab, 0, s, T, g.H, g.E, x, p.router, ws.logits);
+  else
+    hipLaunchKernelGGL(k_router_approx<2>, ag, ab, 0, s, T, g.H, g.E, x, p.router, ws.logits);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // Error bound of the approximate logits, relative to |r_e| |x_t|:
