@@ -93,6 +93,9 @@ constexpr int kRW = 32;      // tokens and rows per wave
 #endif
 constexpr int kRSplit = BQ_ROUTER_SPLITK;  // waves per block, each with 1/kRSplit of K
 constexpr int kRSlice = 32;  // K per slice
+#ifndef BQ_APPROX_QUAD
+#define BQ_APPROX_QUAD 1
+#endif
 #ifndef BQ_ROUTER_GEMM_MIN
 #define BQ_ROUTER_GEMM_MIN MOE_ROUTER_BATCH_MIN_TOKENS
 #endif
@@ -263,14 +266,29 @@ __global__ __launch_bounds__(64 * kASplit) void k_router_approx(int T, int H, in
   int id = blockIdx.x + nbx * blockIdx.y;
   if (total % 8 == 0) id = (id & 7) * (total / 8) + (id >> 3);
   const int e0 = (id % nbx) * kAR, t0 = (id / nbx) * kAT;
+  // Loads: each group of 4 lanes reads 64 (router) or 128 (x) contiguous bytes of one row, lane
+  // 4r + j taking chunk j of row r; the compute moves chunk kk of row c to lane c + 16 kk, the MFMA
+  // operand layout, with ds_bpermute. Loading in the operand layout directly (16 rows per 4-lane
+  // group of 16-byte reads) halves what L2 delivers per cycle.
+  const int lr = BQ_APPROX_QUAD ? (lane >> 2) : c, lk = BQ_APPROX_QUAD ? (lane & 3) : kk;
   const int kh = H / kASplit;
-  const int kbeg = wave * kh + 8 * kk;
+  const int kbeg = wave * kh + 8 * lk;
   const uint16_t* rp[RT];
   const float* xp[2];
 #pragma unroll
-  for (int i = 0; i < RT; ++i) rp[i] = router + (size_t)min(e0 + 16 * i + c, E - 1) * H + kbeg;
+  for (int i = 0; i < RT; ++i) rp[i] = router + (size_t)min(e0 + 16 * i + lr, E - 1) * H + kbeg;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) xp[j] = x + (size_t)min(t0 + 16 * j + c, T - 1) * H + kbeg;
+  for (int j = 0; j < 2; ++j) xp[j] = x + (size_t)min(t0 + 16 * j + lr, T - 1) * H + kbeg;
+  const int src = (4 * c + kk) << 2;  // the lane that loaded this lane's operand chunk
+  auto move4 = [&](uint4 v) __attribute__((always_inline)) {
+    if constexpr (BQ_APPROX_QUAD) {
+      v.x = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)v.x);
+      v.y = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)v.y);
+      v.z = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)v.z);
+      v.w = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)v.w);
+    }
+    return v;
+  };
   const int nst = kh / 32;
   auto load = [&](ApproxRaw<RT>& R, int st) __attribute__((always_inline)) {
     const int off = st * 32;
@@ -289,10 +307,12 @@ __global__ __launch_bounds__(64 * kASplit) void k_router_approx(int T, int H, in
   auto compute = [&](const ApproxRaw<RT>& R) __attribute__((always_inline)) {
     bf16x8_t hi[2], lo[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) split_bf16(R.x[j][0], R.x[j][1], hi[j], lo[j]);
+    for (int j = 0; j < 2; ++j)
+      split_bf16(__builtin_bit_cast(float4, move4(__builtin_bit_cast(uint4, R.x[j][0]))),
+                 __builtin_bit_cast(float4, move4(__builtin_bit_cast(uint4, R.x[j][1]))), hi[j], lo[j]);
 #pragma unroll
     for (int i = 0; i < RT; ++i) {
-      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, R.r[i]);
+      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, move4(R.r[i]));
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, hi[j], acc[i][j], 0, 0, 0);
