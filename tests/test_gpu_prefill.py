@@ -50,8 +50,11 @@ def _forward(L, x, res=None):
     return out.cpu().numpy(), idx.cpu().numpy()
 
 
-@pytest.mark.parametrize("T", [bq.MOE_PREFILL_MIN_TOKENS, 100, 300])
+@pytest.mark.parametrize("T", [bq.MOE_PREFILL_MIN_TOKENS, 100, 300, bq.MOE_ROUTER_CERTIFIED_MIN_TOKENS + 88])
 def test_prefill_tiny_all_tokens(tiny, T):
+    """Every token against the oracle, through each prefill router: per-token rows (64), the fp64
+    GEMM (100, 300) and the certified router (600, with 8 experts: one 32-row tile, mostly
+    clamped rows)."""
     L, ref = tiny
     x = torch.from_numpy(synth.tokens_x(TINY, 7, T)).cuda()
     out, idx = _forward(L, x)

@@ -156,3 +156,16 @@ def test_certified_router_degenerate_tokens(layers):
     i_c, w_c = _check(L, x, _router_u16(L), [0, 10, 11, 76, 77, 78, T - 1])
     assert list(i_c[10]) == list(range(w.top_k))
     assert np.allclose(w_c[10], 1.0 / w.top_k, atol=1e-7)
+
+
+def test_certified_router_bitwise_repeatable(layers):
+    """Two calls on the same inputs give the same indices, weights and gate bit for bit: the
+    approximation's partial sums, the candidate list and the fp64 recomputation all run in a fixed
+    order."""
+    L = layers("c4096")
+    x = torch.from_numpy(synth.tokens_x(L.w, 3000, 1024)).cuda()
+    _log("c4096: certified router twice on 1024 tokens")
+    a = _route(L, x, with_logits=False)
+    b = _route(L, x, with_logits=False)
+    for u, v in zip(a[:3], b[:3]):
+        assert np.array_equal(u, v)
