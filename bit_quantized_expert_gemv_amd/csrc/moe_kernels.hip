@@ -980,6 +980,10 @@ __global__ __launch_bounds__(kBlock) void k_topk_certified(LayerArgs a, const fl
 #pragma unroll
     for (int i = 0; i < PL; ++i) v[i] = la[i];
     wave_topk<PL>(v, a.E, a.K, lane, -1, true, sel[wave], val[wave]);  // the K best become -inf
+    // lane 0 recorded the choices in LDS; the other lanes read them below
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     double lb = INFINITY;
 #pragma unroll
     for (int i = 0; i < PL; ++i)
