@@ -4,7 +4,9 @@
 //   1. prep: activations to fp16 (each 8-block stored in the order 0,2,4,6,1,3,5,7, the order in
 //      which the code widening below produces weights) and per-64-group sums of the fp16 values;
 //   2. router: logits = X . [R; gate]^T as an fp64 tiled GEMM, so the top-K decision is exact
-//      up to fp64 rounding; then the top-K and weights per token (the decode top-K kernel);
+//      up to fp64 rounding, then the top-K and weights per token (the decode top-K kernel); or,
+//      from MOE_ROUTER_CERTIFIED_MIN_TOKENS tokens, approximate logits on bf16 MFMAs with an error
+//      bound, and fp64 only for the rows the bound cannot rule out (the same choice);
 //   3. grouping: per-expert counts, exclusive scan and a stable permutation by token index,
 //      built from per-chunk histograms so that the result is deterministic;
 //   4. gate/up: an MFMA grouped GEMM per expert tile with SwiGLU in the epilogue; the routed
