@@ -1303,9 +1303,15 @@ constexpr int kULine = BQ_U_LINE * 4;
 // Blocks: one per tile, times enough slab groups that a launch has about BQ_GROUP_TARGET working
 // blocks when tiles are few (the shared expert's 64 tiles at 2048 tokens; small batches). `tiles`
 // is the number expected to hold tokens: for the routed experts at most one per routed entry.
-int slab_groups(int tiles, int nout, int rows_per_slab) {
+// The shared expert's launch (every token, 64 tiles at 2048 tokens) does best with half the
+// target: two blocks per CU, each with twice the slabs, so the pipeline fills half as often
+// (measured at 2048 tokens: gate/up 97 -> 93 us, down 52 -> 43 us; 256 and 2048 were slower).
+#ifndef BQ_SHARED_GROUP_TARGET
+#define BQ_SHARED_GROUP_TARGET 512
+#endif
+int slab_groups(int tiles, int nout, int rows_per_slab, int target = BQ_GROUP_TARGET) {
   const int nslab = (nout + rows_per_slab - 1) / rows_per_slab;
-  return std::max(1, std::min(nslab, BQ_GROUP_TARGET / std::max(1, tiles)));
+  return std::max(1, std::min(nslab, target / std::max(1, tiles)));
 }
 // 1-D grid for `tiles` tile slots with `sg` slab groups each, in runs of 8 tiles (see k_grouped).
 unsigned grouped_grid(int tiles, int sg) { return cdiv(tiles, 8) * 8u * (unsigned)sg; }
@@ -1321,7 +1327,7 @@ hipError_t launch_grouped(const GroupArgs& ga, int nout, int T, int N, int E, bo
                      ga, rg);
   if (has_shared) {
     const int st = (int)cdiv(T, kTileM);
-    const int sg = slab_groups(st, nout, RS);
+    const int sg = slab_groups(st, nout, RS, BQ_SHARED_GROUP_TARGET);
     hipLaunchKernelGGL((k_grouped<BITS, KDIM, UM, GATEUP, true>), dim3(grouped_grid(st, sg)), block, 0, s, ga,
                        sg);
   }
@@ -1337,7 +1343,7 @@ hipError_t launch_grouped_mx(const GroupArgs& ga, int nout, int T, int N, int E,
   hipLaunchKernelGGL((k_grouped_mx<KDIM, GATEUP, false>), dim3(grouped_grid(max_tiles, rg)), block, 0, s, ga, rg);
   if (has_shared) {
     const int st = (int)cdiv(T, kTileM);
-    const int sg = slab_groups(st, nout, RS);
+    const int sg = slab_groups(st, nout, RS, BQ_SHARED_GROUP_TARGET);
     hipLaunchKernelGGL((k_grouped_mx<KDIM, GATEUP, true>), dim3(grouped_grid(st, sg)), block, 0, s, ga, sg);
   }
   return hipGetLastError();
