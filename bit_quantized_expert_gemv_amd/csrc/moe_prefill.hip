@@ -1297,15 +1297,17 @@ unsigned cdiv(long long a, long long b) { return (unsigned)((a + b - 1) / b); }
 template <int BITS>
 constexpr int kULine = BQ_U_LINE * 4;
 
-#ifndef BQ_GROUP_TARGET
-#define BQ_GROUP_TARGET 1024
-#endif
 // Blocks: one per tile, times enough slab groups that a launch has about BQ_GROUP_TARGET working
-// blocks when tiles are few (the shared expert's 64 tiles at 2048 tokens; small batches). `tiles`
-// is the number expected to hold tokens: for the routed experts at most one per routed entry.
-// The shared expert's launch (every token, 64 tiles at 2048 tokens) does best with half the
-// target: two blocks per CU, each with twice the slabs, so the pipeline fills half as often
-// (measured at 2048 tokens: gate/up 97 -> 93 us, down 52 -> 43 us; 256 and 2048 were slower).
+// blocks. `tiles` is the number expected to hold tokens: for the routed experts at most one per
+// routed entry. Measured at 2048 tokens (704 tile slots for the routed experts):
+//  - routed: a target of 3072 (4 slab groups per tile) balances the launch's tail better than one
+//    block per tile: gate/up 670-690 -> 607-622 us, down 307 -> 287 us; 5 groups measured the
+//    same, 8 groups slower for gate/up;
+//  - shared (64 tiles): 512, two blocks per CU with two slabs each, so the pipeline fills half as
+//    often as with 1024 (gate/up 97 -> 93 us, down 52 -> 43 us; 256 and 2048 were slower).
+#ifndef BQ_GROUP_TARGET
+#define BQ_GROUP_TARGET 3072
+#endif
 #ifndef BQ_SHARED_GROUP_TARGET
 #define BQ_SHARED_GROUP_TARGET 512
 #endif
