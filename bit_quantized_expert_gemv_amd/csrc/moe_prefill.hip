@@ -1300,9 +1300,10 @@ constexpr int kULine = BQ_U_LINE * 4;
 // Blocks: one per tile, times enough slab groups that a launch has about BQ_GROUP_TARGET working
 // blocks. `tiles` is the number expected to hold tokens: for the routed experts at most one per
 // routed entry. Measured at 2048 tokens (704 tile slots for the routed experts):
-//  - routed: a target of 3072 (4 slab groups per tile) balances the launch's tail better than one
-//    block per tile: gate/up 670-690 -> 607-622 us, down 307 -> 287 us; 5 groups measured the
-//    same, 8 groups slower for gate/up;
+//  - routed: at least 4 slab groups per tile (BQ_ROUTED_MIN_GROUPS) balance the launch's tail
+//    better than one block per tile: gate/up 670-690 -> 607-622 us, down 307 -> 287 us; 5 groups
+//    measured the same, 8 slower for gate/up; prefillmx (896 tile slots) 1.83 -> 1.54 ms per step
+//    with 4 groups, 1.58 with 3;
 //  - shared (64 tiles): 512, two blocks per CU with two slabs each, so the pipeline fills half as
 //    often as with 1024 (gate/up 97 -> 93 us, down 52 -> 43 us; 256 and 2048 were slower).
 #ifndef BQ_GROUP_TARGET
@@ -1311,9 +1312,12 @@ constexpr int kULine = BQ_U_LINE * 4;
 #ifndef BQ_SHARED_GROUP_TARGET
 #define BQ_SHARED_GROUP_TARGET 512
 #endif
-int slab_groups(int tiles, int nout, int rows_per_slab, int target = BQ_GROUP_TARGET) {
+#ifndef BQ_ROUTED_MIN_GROUPS
+#define BQ_ROUTED_MIN_GROUPS 4
+#endif
+int slab_groups(int tiles, int nout, int rows_per_slab, int target, int min_groups) {
   const int nslab = (nout + rows_per_slab - 1) / rows_per_slab;
-  return std::max(1, std::min(nslab, target / std::max(1, tiles)));
+  return std::max(1, std::min(nslab, std::max(min_groups, target / std::max(1, tiles))));
 }
 // 1-D grid for `tiles` tile slots with `sg` slab groups each, in runs of 8 tiles (see k_grouped).
 unsigned grouped_grid(int tiles, int sg) { return cdiv(tiles, 8) * 8u * (unsigned)sg; }
@@ -1324,12 +1328,12 @@ hipError_t launch_grouped(const GroupArgs& ga, int nout, int T, int N, int E, bo
   constexpr int RS = GATEUP ? 64 : 128;  // rows per matrix per slab
   const dim3 block(kThreads);
   const int max_tiles = E + (int)cdiv(N, kTileM);
-  const int rg = slab_groups(std::min(max_tiles, N), nout, RS);
+  const int rg = slab_groups(std::min(max_tiles, N), nout, RS, BQ_GROUP_TARGET, BQ_ROUTED_MIN_GROUPS);
   hipLaunchKernelGGL((k_grouped<BITS, KDIM, UM, GATEUP, false>), dim3(grouped_grid(max_tiles, rg)), block, 0, s,
                      ga, rg);
   if (has_shared) {
     const int st = (int)cdiv(T, kTileM);
-    const int sg = slab_groups(st, nout, RS, BQ_SHARED_GROUP_TARGET);
+    const int sg = slab_groups(st, nout, RS, BQ_SHARED_GROUP_TARGET, 1);
     hipLaunchKernelGGL((k_grouped<BITS, KDIM, UM, GATEUP, true>), dim3(grouped_grid(st, sg)), block, 0, s, ga,
                        sg);
   }
@@ -1341,11 +1345,11 @@ hipError_t launch_grouped_mx(const GroupArgs& ga, int nout, int T, int N, int E,
   constexpr int RS = GATEUP ? 64 : 128;
   const dim3 block(kThreads);
   const int max_tiles = E + (int)cdiv(N, kTileM);
-  const int rg = slab_groups(std::min(max_tiles, N), nout, RS);
+  const int rg = slab_groups(std::min(max_tiles, N), nout, RS, BQ_GROUP_TARGET, BQ_ROUTED_MIN_GROUPS);
   hipLaunchKernelGGL((k_grouped_mx<KDIM, GATEUP, false>), dim3(grouped_grid(max_tiles, rg)), block, 0, s, ga, rg);
   if (has_shared) {
     const int st = (int)cdiv(T, kTileM);
-    const int sg = slab_groups(st, nout, RS, BQ_SHARED_GROUP_TARGET);
+    const int sg = slab_groups(st, nout, RS, BQ_SHARED_GROUP_TARGET, 1);
     hipLaunchKernelGGL((k_grouped_mx<KDIM, GATEUP, true>), dim3(grouped_grid(st, sg)), block, 0, s, ga, sg);
   }
   return hipGetLastError();
