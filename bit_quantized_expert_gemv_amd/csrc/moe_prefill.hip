@@ -1272,18 +1272,32 @@ __global__ __launch_bounds__(kThreads) void k_prefill_out(int T, int H, int K, i
                                                           const float* __restrict__ sg,
                                                           const float* __restrict__ residual,
                                                           float* __restrict__ out, float* __restrict__ y_out) {
+  // 4 consecutive rows per thread (H is a multiple of 64): 16-byte loads of y (workspace) and
+  // stores of out and y_out (16-byte aligned by the entry points' checks); the residual, which
+  // carries no alignment requirement, is read as 4 floats
   const int t = blockIdx.y;
-  const int r = blockIdx.x * kThreads + threadIdx.x;
+  const int r = 4 * (blockIdx.x * kThreads + threadIdx.x);
   if (r >= H) return;
   const int NE = K + has_shared;
+  auto row4 = [&](size_t row) { return *reinterpret_cast<const float4*>(y + row * H + r); };
   if (out != nullptr) {
-    float acc = residual[(size_t)t * H + r];
-    for (int k = 0; k < K; ++k) acc += w[(size_t)t * K + k] * y[(size_t)pos[(size_t)t * K + k] * H + r];
-    if (has_shared) acc += sg[t] * y[((size_t)T * K + t) * H + r];
-    out[(size_t)t * H + r] = acc;
+    const float* rs = residual + (size_t)t * H + r;
+    float4 acc = make_float4(rs[0], rs[1], rs[2], rs[3]);
+    for (int k = 0; k < K; ++k) {
+      const float wk = w[(size_t)t * K + k];
+      const float4 v = row4((size_t)pos[(size_t)t * K + k]);
+      acc.x += wk * v.x; acc.y += wk * v.y; acc.z += wk * v.z; acc.w += wk * v.w;
+    }
+    if (has_shared) {
+      const float gs = sg[t];
+      const float4 v = row4((size_t)T * K + t);
+      acc.x += gs * v.x; acc.y += gs * v.y; acc.z += gs * v.z; acc.w += gs * v.w;
+    }
+    *reinterpret_cast<float4*>(out + (size_t)t * H + r) = acc;
   } else {
-    for (int k = 0; k < K; ++k) y_out[((size_t)t * NE + k) * H + r] = y[(size_t)pos[(size_t)t * K + k] * H + r];
-    if (has_shared) y_out[((size_t)t * NE + K) * H + r] = y[((size_t)T * K + t) * H + r];
+    for (int k = 0; k < K; ++k)
+      *reinterpret_cast<float4*>(y_out + ((size_t)t * NE + k) * H + r) = row4((size_t)pos[(size_t)t * K + k]);
+    if (has_shared) *reinterpret_cast<float4*>(y_out + ((size_t)t * NE + K) * H + r) = row4((size_t)T * K + t);
   }
 }
 
@@ -1496,7 +1510,7 @@ hipError_t launch_prefill(const Geometry& g, const LayerPtrs& p, const float* x,
     if (e != hipSuccess) return e;
     if (idx_out && idx_in == nullptr)
       hipLaunchKernelGGL(k_copy_i32, dim3(cdiv(N, kThreads)), dim3(kThreads), 0, s, N, w.layer.idx, idx_out);
-    hipLaunchKernelGGL(k_prefill_out, dim3(cdiv(H, kThreads), T), dim3(kThreads), 0, s, T, H, K, g.has_shared, w.pos,
+    hipLaunchKernelGGL(k_prefill_out, dim3(cdiv(H / 4, kThreads), T), dim3(kThreads), 0, s, T, H, K, g.has_shared, w.pos,
                        w.y, w.layer.w, w.layer.g, residual, out, y_out);
     return hipGetLastError();
   }
@@ -1513,7 +1527,7 @@ hipError_t launch_prefill(const Geometry& g, const LayerPtrs& p, const float* x,
   // combine or scatter
   if (idx_out && idx_in == nullptr)
     hipLaunchKernelGGL(k_copy_i32, dim3(cdiv(N, kThreads)), dim3(kThreads), 0, s, N, w.layer.idx, idx_out);
-  hipLaunchKernelGGL(k_prefill_out, dim3(cdiv(H, kThreads), T), dim3(kThreads), 0, s, T, H, K, g.has_shared, w.pos,
+  hipLaunchKernelGGL(k_prefill_out, dim3(cdiv(H / 4, kThreads), T), dim3(kThreads), 0, s, T, H, K, g.has_shared, w.pos,
                      w.y, w.layer.w, w.layer.g, residual, out, y_out);
   return hipGetLastError();
 }
