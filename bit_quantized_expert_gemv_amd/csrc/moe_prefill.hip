@@ -59,21 +59,29 @@ __device__ __forceinline__ float bf16_val(uint16_t h) { return __uint_as_float((
 __device__ __forceinline__ int perm8(int e) { return (e >> 1) + 4 * (e & 1); }
 
 // ---- 1. activation prep -------------------------------------------------------------------------
-// One block per token: fp16 copy (8-blocks permuted) and per-64-group sums of the fp16 values.
-__global__ __launch_bounds__(kThreads) void k_prep(int H, const float* __restrict__ x, _Float16* __restrict__ xq,
-                                                   float* __restrict__ xs) {
-  const int t = blockIdx.x;
-  const float* xr = x + (size_t)t * H;
-  const int ng = H / 64;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  for (int gi = wave; gi < ng; gi += kThreads / 64) {
-    const int j = gi * 64 + lane;
-    const _Float16 q = (_Float16)xr[j];
-    xq[(size_t)t * H + (j & ~7) + perm8(j & 7)] = q;
-    float v = (float)q;
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-    if (lane == 0) xs[(size_t)t * ng + gi] = v;
+// fp16 copy (8-blocks stored in the order 0,2,4,6,1,3,5,7) and per-64-group sums of the fp16
+// values. Thread i takes 8-block i of the whole [T][H] array: two 16-byte loads, one 16-byte store;
+// the 8 threads of a group add their sums with 3 butterfly steps, in a fixed order.
+__global__ __launch_bounds__(kThreads) void k_prep(int64_t nblk8, const float* __restrict__ x,
+                                                   _Float16* __restrict__ xq, float* __restrict__ xs) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const bool live = i < nblk8;  // nblk8 is a multiple of 8, so a group's 8 threads agree
+  const int64_t ib = live ? i : 0;
+  const float4* src = reinterpret_cast<const float4*>(x) + 2 * ib;
+  const float4 a = src[0], b = src[1];
+  const _Float16 h[8] = {(_Float16)a.x, (_Float16)a.y, (_Float16)a.z, (_Float16)a.w,
+                         (_Float16)b.x, (_Float16)b.y, (_Float16)b.z, (_Float16)b.w};
+  if (live) {
+    f16x8_t o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[perm8(e)] = h[e];
+    reinterpret_cast<f16x8_t*>(xq)[ib] = o;
   }
+  float v = (((float)h[0] + (float)h[1]) + ((float)h[2] + (float)h[3])) +
+            (((float)h[4] + (float)h[5]) + ((float)h[6] + (float)h[7]));
+#pragma unroll
+  for (int m = 1; m < 8; m <<= 1) v += __shfl_xor(v, m, 8);
+  if (live && (i & 7) == 0) xs[i >> 3] = v;
 }
 
 // ---- 2. router GEMM (fp64 MFMA) ---------------------------------------------------------------------
@@ -1477,7 +1485,9 @@ hipError_t launch_prefill(const Geometry& g, const LayerPtrs& p, const float* x,
     hipError_t e = launch_prep_mx(T, H, x, w.x8, w.xsc, s);
     if (e != hipSuccess) return e;
   } else {
-    hipLaunchKernelGGL(k_prep, dim3(T), dim3(kThreads), 0, s, H, x, reinterpret_cast<_Float16*>(w.xq), w.xs);
+    const int64_t nblk8 = (int64_t)T * H / 8;
+    hipLaunchKernelGGL(k_prep, dim3((unsigned)cdiv(nblk8, kThreads)), dim3(kThreads), 0, s, nblk8, x,
+                       reinterpret_cast<_Float16*>(w.xq), w.xs);
   }
   const int32_t* idx = idx_in;
   if (idx_in == nullptr) {
