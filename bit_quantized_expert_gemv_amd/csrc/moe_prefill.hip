@@ -993,25 +993,42 @@ constexpr int kMxTerms = 3;
 // x = sum_t q_t * 2^(e_t - 127) + r. Term t quantises what terms 0..t-1 left, with the block scale
 // chosen so that the block's largest magnitude falls in [128, 256) (no E4M3 saturation); the
 // residual is exact in fp32, and after three terms |r| is about 2^-12 of each element (less
-// than fp16's rounding). Lanes are elements; each 32-lane half of a wave is one block.
+// than fp16's rounding). A thread takes 8 consecutive elements (two 16-byte loads, one 8-byte store
+// per term); 4 threads hold one block and share its maximum in 2 butterfly steps.
 __global__ __launch_bounds__(kThreads) void k_prep_mx(int64_t nblk, const float* __restrict__ x, uint8_t* __restrict__ q8,
                                                       uint8_t* __restrict__ sc, uint64_t q_plane, uint64_t sc_plane) {
-  const int lane = threadIdx.x & 63;
-  const int64_t blk = (((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6) * 2 + (lane >> 5);
-  if (blk >= nblk) return;  // whole 32-lane halves
-  const int64_t i = blk * 32 + (lane & 31);
-  float r = x[i];
+  const int64_t i8 = (int64_t)blockIdx.x * kThreads + threadIdx.x;  // 8-element chunk
+  const bool live = i8 < nblk * 4;  // a block's 4 threads agree (kThreads is a multiple of 4)
+  const int64_t ib = live ? i8 : 0;
+  const float4* src = reinterpret_cast<const float4*>(x) + 2 * ib;
+  const float4 p0 = src[0], p1 = src[1];
+  float r[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
 #pragma unroll
   for (int t = 0; t < kMxTerms; ++t) {
-    float a = fabsf(r);
+    float a = 0.0f;
 #pragma unroll
-    for (int m = 16; m >= 1; m >>= 1) a = fmaxf(a, __shfl_xor(a, m, 32));
+    for (int k = 0; k < 8; ++k) a = fmaxf(a, fabsf(r[k]));
+    a = fmaxf(a, __shfl_xor(a, 1, 4));
+    a = fmaxf(a, __shfl_xor(a, 2, 4));
     const int e = a > 0.0f ? max(-127, min(127, ilogbf(a) - 7)) : -127;
-    const float y = r * ldexpf(1.0f, -e);  // exact, |y| < 256
-    const uint32_t code = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y, 0.0f, 0, false) & 0xFFu;
-    q8[t * q_plane + i] = (uint8_t)code;
-    if ((lane & 31) == 0) sc[t * sc_plane + blk] = (uint8_t)(e + 127);
-    r -= __builtin_amdgcn_cvt_f32_fp8((int)code, 0) * ldexpf(1.0f, e);  // exact
+    const float down = ldexpf(1.0f, -e), up = ldexpf(1.0f, e);
+    uint32_t w[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {  // y = r * 2^-e is exact, |y| < 256; bytes in element order
+      w[h] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(r[4 * h] * down, r[4 * h + 1] * down, 0, false);
+      w[h] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(r[4 * h + 2] * down, r[4 * h + 3] * down, (int)w[h], true);
+    }
+    if (live) {
+      *reinterpret_cast<uint2*>(q8 + t * q_plane + 8 * ib) = make_uint2(w[0], w[1]);
+      if ((i8 & 3) == 0) sc[t * sc_plane + (ib >> 2)] = (uint8_t)(e + 127);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {  // the residual, exact
+      r[4 * h] -= __builtin_amdgcn_cvt_f32_fp8((int)w[h], 0) * up;
+      r[4 * h + 1] -= __builtin_amdgcn_cvt_f32_fp8((int)w[h], 1) * up;
+      r[4 * h + 2] -= __builtin_amdgcn_cvt_f32_fp8((int)w[h], 2) * up;
+      r[4 * h + 3] -= __builtin_amdgcn_cvt_f32_fp8((int)w[h], 3) * up;
+    }
   }
 }
 
@@ -1393,7 +1410,7 @@ hipError_t dispatch_mx(bool gateup, int kdim, const GroupArgs& ga, int nout, int
 
 hipError_t launch_prep_mx(int rows, int cols, const float* x, uint8_t* q8, uint8_t* sc, hipStream_t s) {
   const int64_t nblk = (int64_t)rows * cols / 32;
-  hipLaunchKernelGGL(k_prep_mx, dim3(cdiv(nblk, 2 * (kThreads / 64))), dim3(kThreads), 0, s, nblk, x, q8, sc,
+  hipLaunchKernelGGL(k_prep_mx, dim3(cdiv(nblk * 4, kThreads)), dim3(kThreads), 0, s, nblk, x, q8, sc,
                      (uint64_t)rows * cols, (uint64_t)nblk);
   return hipGetLastError();
 }
