@@ -333,7 +333,7 @@ int moe_router(const moe_layer_t* layer, const float* x, int T, int32_t* idx, fl
   if (ws_bytes < needed_ws(g, T)) return fail(MOE_ENOSPC, "workspace smaller than moe_workspace_bytes()");
   const Workspace W = carve_workspace(g, T, ws);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = launch_router_select(g, ptrs_of(layer), x, T, W, idx, w, shared_g, logits, s);
+  hipError_t e = launch_router_select(g, ptrs_of(layer), x, T, W, idx, w, shared_g, logits, nullptr, s);
   return hip_status(e);
 }
 

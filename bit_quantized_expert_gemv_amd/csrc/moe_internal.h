@@ -104,14 +104,16 @@ hipError_t launch_down(const Geometry& g, const LayerPtrs& p, int T, const Works
 // error is at most kc * |r_e| * |x_t| (plus a subnormal slack); computes the router row norms into
 // ws.rnorm, recomputes in fp64 the rows the bound cannot rule out, and writes idx, w and sg.
 hipError_t launch_topk_certified(const Geometry& g, const LayerPtrs& p, const float* x, int T, const Workspace& ws,
-                                 double kc, int32_t* idx, float* w, float* sg, hipStream_t s);
-// Routing of T tokens into idx/w/sg (and the fp64 logits into logits_out when non-null): the
-// certified bf16-MFMA path for many tokens without logits_out, otherwise fp64 logits then the top-K.
+                                 double kc, int32_t* idx, float* w, float* sg, int32_t* idx_b, hipStream_t s);
+// Routing of T tokens into idx/w/sg (and the fp64 logits into logits_out, a copy of idx into idx_b,
+// each when non-null): the certified bf16-MFMA path for many tokens without logits_out, otherwise
+// fp64 logits then the top-K.
 hipError_t launch_router_select(const Geometry& g, const LayerPtrs& p, const float* x, int T, const Workspace& ws,
-                                int32_t* idx, float* w, float* sg, double* logits_out, hipStream_t s);
-// Top-K + weights from ws.logits (router-only path).
+                                int32_t* idx, float* w, float* sg, double* logits_out, int32_t* idx_b,
+                                hipStream_t s);
+// Top-K + weights from ws.logits (router-only path); idx_b, if non-null, receives a copy of idx.
 hipError_t launch_topk(const Geometry& g, int T, const Workspace& ws, int32_t* idx, float* w, float* sg,
-                       double* logits_out, hipStream_t s);
+                       double* logits_out, int32_t* idx_b, hipStream_t s);
 hipError_t launch_combine(const Geometry& g, int T, const float* residual, const float* y, const float* w,
                           const float* sg, float* out, hipStream_t s);
 hipError_t launch_dequant(const Geometry& g, const uint8_t* blob, int matrix, int out_dtype, void* out, hipStream_t s);

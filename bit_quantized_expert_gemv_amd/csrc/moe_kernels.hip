@@ -850,7 +850,8 @@ __global__ __launch_bounds__(kBlock) void k_down(LayerArgs a, const int32_t* __r
 // Router-only top-K: one wave per token.
 template <int PL>
 __global__ __launch_bounds__(64) void k_topk(LayerArgs a, int32_t* __restrict__ idx, float* __restrict__ w,
-                                             float* __restrict__ sg, double* __restrict__ logits_out) {
+                                             float* __restrict__ sg, double* __restrict__ logits_out,
+                                             int32_t* __restrict__ idx_b) {
   __shared__ int32_t sel[MOE_MAX_TOP_K];
   __shared__ double val[MOE_MAX_TOP_K];
   const int t = blockIdx.x, lane = threadIdx.x;
@@ -860,7 +861,7 @@ __global__ __launch_bounds__(64) void k_topk(LayerArgs a, int32_t* __restrict__ 
   wave_topk<PL>(v, a.E, a.K, lane, -1, true, sel, val);
   if (logits_out)
     for (int e = lane; e < a.E; e += 64) logits_out[(size_t)t * a.E + e] = lg[e];
-  if (lane == 0) write_routing(a, t, sel, val, lg, idx, w, nullptr, sg);
+  if (lane == 0) write_routing(a, t, sel, val, lg, idx, w, idx_b, sg);
 }
 
 // fp64 norm of each bf16 router row (one wave per row), for the certified top-K's error bound.
@@ -934,7 +935,7 @@ template <int PL, int H>
 __global__ __launch_bounds__(kBlock) void k_topk_certified(LayerArgs a, const float* __restrict__ x,
                                                            const double* __restrict__ rnorm, double kc, int T,
                                                            int32_t* __restrict__ idx, float* __restrict__ w,
-                                                           float* __restrict__ sg) {
+                                                           float* __restrict__ sg, int32_t* __restrict__ idx_b) {
   constexpr int NCH = H / 8, XC = (NCH + 63) / 64;
   constexpr int kList = 64 * PL + MOE_MAX_TOP_K + 1;  // every row, the gate row, and room for A twice
   __shared__ int32_t sel[kWaves][MOE_MAX_TOP_K];
@@ -1037,7 +1038,7 @@ __global__ __launch_bounds__(kBlock) void k_topk_certified(LayerArgs a, const fl
   }
   wave_topk<PL>(ex, a.E, a.K, lane, -1, true, sel[wave], val[wave]);
   if (lane == 0) {
-    write_routing(a, t, sel[wave], val[wave], nullptr, idx, w, nullptr, nullptr);
+    write_routing(a, t, sel[wave], val[wave], nullptr, idx, w, idx_b, nullptr);
     if (sg && a.has_shared) sg[t] = (float)(1.0 / (1.0 + exp(-gl)));
   }
 }
@@ -1263,27 +1264,27 @@ hipError_t launch_prefetch(const Prefetch& pf, int blocks, hipStream_t s) {
 }
 
 hipError_t launch_topk(const Geometry& g, int T, const Workspace& ws, int32_t* idx, float* w, float* sg,
-                       double* logits_out, hipStream_t s) {
+                       double* logits_out, int32_t* idx_b, hipStream_t s) {
   LayerPtrs p{};
   const LayerArgs a = make_args(g, p, ws);
   if (g.E <= 512)
-    hipLaunchKernelGGL(k_topk<8>, dim3(T), dim3(64), 0, s, a, idx, w, sg, logits_out);
+    hipLaunchKernelGGL(k_topk<8>, dim3(T), dim3(64), 0, s, a, idx, w, sg, logits_out, idx_b);
   else
-    hipLaunchKernelGGL(k_topk<16>, dim3(T), dim3(64), 0, s, a, idx, w, sg, logits_out);
+    hipLaunchKernelGGL(k_topk<16>, dim3(T), dim3(64), 0, s, a, idx, w, sg, logits_out, idx_b);
   return hipGetLastError();
 }
 
 hipError_t launch_topk_certified(const Geometry& g, const LayerPtrs& p, const float* x, int T, const Workspace& ws,
-                                 double kc, int32_t* idx, float* w, float* sg, hipStream_t s) {
+                                 double kc, int32_t* idx, float* w, float* sg, int32_t* idx_b, hipStream_t s) {
   const LayerArgs a = make_args(g, p, ws);
   hipLaunchKernelGGL(k_row_norms, dim3((g.E + kWaves - 1) / kWaves), dim3(kBlock), 0, s, g.E, g.H, p.router, ws.rnorm);
   const dim3 grid((T + kWaves - 1) / kWaves);
 #define BQ_CASE(HV)                                                                                              \
   case HV:                                                                                                       \
     if (g.E <= 512)                                                                                              \
-      hipLaunchKernelGGL((k_topk_certified<8, HV>), grid, dim3(kBlock), 0, s, a, x, ws.rnorm, kc, T, idx, w, sg); \
+      hipLaunchKernelGGL((k_topk_certified<8, HV>), grid, dim3(kBlock), 0, s, a, x, ws.rnorm, kc, T, idx, w, sg, idx_b); \
     else                                                                                                         \
-      hipLaunchKernelGGL((k_topk_certified<16, HV>), grid, dim3(kBlock), 0, s, a, x, ws.rnorm, kc, T, idx, w, sg); \
+      hipLaunchKernelGGL((k_topk_certified<16, HV>), grid, dim3(kBlock), 0, s, a, x, ws.rnorm, kc, T, idx, w, sg, idx_b); \
     return hipGetLastError();
   switch (g.H) { BQ_FOR_H(BQ_CASE) }
 #undef BQ_CASE

@@ -1326,11 +1326,6 @@ __global__ __launch_bounds__(kThreads) void k_prefill_out(int T, int H, int K, i
   }
 }
 
-__global__ void k_copy_i32(int n, const int32_t* __restrict__ src, int32_t* __restrict__ dst) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) dst[i] = src[i];
-}
-
 unsigned cdiv(long long a, long long b) { return (unsigned)((a + b - 1) / b); }
 
 template <int BITS>
@@ -1452,10 +1447,11 @@ hipError_t launch_router_tokens(const Geometry& g, const LayerPtrs& p, const flo
 }
 
 hipError_t launch_router_select(const Geometry& g, const LayerPtrs& p, const float* x, int T, const Workspace& ws,
-                                int32_t* idx, float* w, float* sg, double* logits_out, hipStream_t s) {
+                                int32_t* idx, float* w, float* sg, double* logits_out, int32_t* idx_b,
+                                hipStream_t s) {
   if (logits_out != nullptr || T < kRouterCertifiedMinTokens) {
     hipError_t e = launch_router_tokens(g, p, x, T, ws, s);
-    return e == hipSuccess ? launch_topk(g, T, ws, idx, w, sg, logits_out, s) : e;
+    return e == hipSuccess ? launch_topk(g, T, ws, idx, w, sg, logits_out, idx_b, s) : e;
   }
   int rt = BQ_ROUTER_APPROX_RT;
   if (rt == 0) {  // the smallest tile whose grid fits one block per CU (256), else the largest
@@ -1488,7 +1484,7 @@ hipError_t launch_router_select(const Geometry& g, const LayerPtrs& p, const flo
   const double n = 2.0 * g.H / (32.0 * kASplit);
   const double u = std::ldexp(1.0, -23);
   const double kc = 1.25 * (std::ldexp(1.0, -16) * 1.01 + 34.0 * u * n * (1.0 + 34.0 * u * n) * 1.01);
-  return launch_topk_certified(g, p, x, T, ws, kc, idx, w, sg, s);
+  return launch_topk_certified(g, p, x, T, ws, kc, idx, w, sg, idx_b, s);
 }
 
 hipError_t launch_prefill(const Geometry& g, const LayerPtrs& p, const float* x, const float* residual, int T,
@@ -1508,7 +1504,7 @@ hipError_t launch_prefill(const Geometry& g, const LayerPtrs& p, const float* x,
   }
   const int32_t* idx = idx_in;
   if (idx_in == nullptr) {
-    hipError_t e = launch_router_select(g, p, x, T, w.layer, w.layer.idx, w.layer.w, w.layer.g, nullptr, s);
+    hipError_t e = launch_router_select(g, p, x, T, w.layer, w.layer.idx, w.layer.w, w.layer.g, nullptr, idx_out, s);
     if (e != hipSuccess) return e;
     idx = w.layer.idx;
   }
@@ -1535,8 +1531,6 @@ hipError_t launch_prefill(const Geometry& g, const LayerPtrs& p, const float* x,
     ga.oy = w.y; ga.nout = H;
     e = dispatch_mx(false, I, ga, H, T, N, E, g.has_shared != 0, s);
     if (e != hipSuccess) return e;
-    if (idx_out && idx_in == nullptr)
-      hipLaunchKernelGGL(k_copy_i32, dim3(cdiv(N, kThreads)), dim3(kThreads), 0, s, N, w.layer.idx, idx_out);
     hipLaunchKernelGGL(k_prefill_out, dim3(cdiv(H / 4, kThreads), T), dim3(kThreads), 0, s, T, H, K, g.has_shared, w.pos,
                        w.y, w.layer.w, w.layer.g, residual, out, y_out);
     return hipGetLastError();
@@ -1552,8 +1546,6 @@ hipError_t launch_prefill(const Geometry& g, const LayerPtrs& p, const float* x,
   e = dispatch_down(g.bits, I, ga, H, T, N, E, g.has_shared != 0, s);
   if (e != hipSuccess) return e;
   // combine or scatter
-  if (idx_out && idx_in == nullptr)
-    hipLaunchKernelGGL(k_copy_i32, dim3(cdiv(N, kThreads)), dim3(kThreads), 0, s, N, w.layer.idx, idx_out);
   hipLaunchKernelGGL(k_prefill_out, dim3(cdiv(H / 4, kThreads), T), dim3(kThreads), 0, s, T, H, K, g.has_shared, w.pos,
                      w.y, w.layer.w, w.layer.g, residual, out, y_out);
   return hipGetLastError();
