@@ -739,6 +739,10 @@ __global__ __launch_bounds__(kBlock) void k_gateup(LayerArgs a, const float* __r
   const int step0 = (blockIdx.x * kWaves + wave) * P;
   const uint8_t* blob = a.shared;
   Stage<H, kBlock> st;
+  // One wave records the choices (LDS) and writes the routing for the next kernel after its block's
+  // gate/up work: written before it, the softmax's fp64 exps and the gate logit's load would hold
+  // back this block's weight loads, and the block's barrier the other waves'.
+  bool writer = false;
   if (slot < a.K) {
     int e;
     if (idx_in != nullptr) {
@@ -750,9 +754,8 @@ __global__ __launch_bounds__(kBlock) void k_gateup(LayerArgs a, const float* __r
       double v[PL];
       load_topk_values<PL>(lg, a.E, lane, v);
       st.load(x + (size_t)t * H, threadIdx.x);
-      const bool writer = blockIdx.x == 0 && blockIdx.y == 0 && wave == 0;
+      writer = blockIdx.x == 0 && blockIdx.y == 0 && wave == 0;
       e = wave_topk<PL>(v, a.E, a.K, lane, slot, writer, sel, val);
-      if (writer && lane == 0) write_routing(a, t, sel, val, lg, a.ws.idx, a.ws.w, idx_out, a.ws.g);
     }
     if (e < 0 || e >= a.E) {  // never read outside the pool: mark the slot's output as invalid
       for (int p = 0; p < P; ++p) {
@@ -766,6 +769,8 @@ __global__ __launch_bounds__(kBlock) void k_gateup(LayerArgs a, const float* __r
     st.load(x + (size_t)t * H, threadIdx.x);
   }
   gateup_block<BITS, H, P, FORM>(a, blob, st, 1.0f, xs, step0, lir, rig, a.ws.h + ((size_t)t * a.NE + slot) * a.I);
+  if (writer && lane == 0)
+    write_routing(a, t, sel, val, a.ws.logits + (size_t)t * (a.E + 1), a.ws.idx, a.ws.w, idx_out, a.ws.g);
 }
 
 // Kernel 3: down projections of all expert slots for a block of output rows; combine or store.
