@@ -426,7 +426,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* __restrict__ wsu
 }
 
 // One block of 1024 threads, thread e for expert e: per-expert prefix over chunks (in place),
-// counts, offsets and the tile list (tiles of BM entries per expert, in expert order). The chunk
+// counts, offsets and the tile list (tiles of BM entries per expert; those above BM/2 first). The chunk
 // column is read eight loads at a time, and the expert scans are block-wide.
 __global__ __launch_bounds__(1024) void k_group_scan(int nchunks, int E, int BM, int32_t* __restrict__ hist,
                                                      int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
@@ -448,20 +448,28 @@ __global__ __launch_bounds__(1024) void k_group_scan(int nchunks, int E, int BM,
     }
     counts[e] = run;
   }
-  const int nt = (e < E) ? (run + BM - 1) / BM : 0;
-  int total_entries, total_tiles;
+  // Tiles with more than BM/2 tokens run both token halves and take longer, so they go first (a
+  // stable partition, each class in expert order): the launch then ends on the light tiles.
+  const int full = (e < E) ? run / BM : 0, rem = (e < E) ? run % BM : 0;
+  const int heavy = full + (rem > BM / 2 ? 1 : 0), light = (rem > 0 && rem <= BM / 2) ? 1 : 0;
+  int total_entries, total_heavy, total_light;
   const int off = block_exclusive_scan(e < E ? run : 0, wsum, &total_entries);
-  const int t0 = block_exclusive_scan(nt, wsum, &total_tiles);
+  const int h0 = block_exclusive_scan(heavy, wsum, &total_heavy);
+  const int l0 = block_exclusive_scan(light, wsum, &total_light);
   if (e < E) {
     offsets[e] = off;
-    for (int j = 0; j < nt; ++j) {
-      tile_e[t0 + j] = e;
-      tile_first[t0 + j] = off + j * BM;
+    for (int j = 0; j < heavy; ++j) {  // the full tiles, then a partial one above BM/2
+      tile_e[h0 + j] = e;
+      tile_first[h0 + j] = off + j * BM;
+    }
+    if (light) {
+      tile_e[total_heavy + l0] = e;
+      tile_first[total_heavy + l0] = off + full * BM;
     }
   }
   if (e == 0) {
     offsets[E] = total_entries;
-    *ntiles = total_tiles;
+    *ntiles = total_heavy + total_light;
   }
 }
 
