@@ -1365,14 +1365,16 @@ int slab_groups(int tiles, int nout, int rows_per_slab, int target, int min_grou
 unsigned grouped_grid(int tiles, int sg) { return cdiv(tiles, 8) * 8u * (unsigned)sg; }
 
 template <int BITS, int KDIM, bool GATEUP>
-hipError_t launch_grouped(const GroupArgs& ga, int nout, int T, int N, int E, bool has_shared, hipStream_t s) {
+hipError_t launch_grouped(const GroupArgs& ga, int nout, int T, int N, int E, bool routed, bool has_shared,
+                          hipStream_t s) {
   constexpr int UM = kULine<BITS>;
   constexpr int RS = GATEUP ? 64 : 128;  // rows per matrix per slab
   const dim3 block(kThreads);
   const int max_tiles = E + (int)cdiv(N, kTileM);
   const int rg = slab_groups(std::min(max_tiles, N), nout, RS, BQ_GROUP_TARGET, BQ_ROUTED_MIN_GROUPS);
-  hipLaunchKernelGGL((k_grouped<BITS, KDIM, UM, GATEUP, false>), dim3(grouped_grid(max_tiles, rg)), block, 0, s,
-                     ga, rg);
+  if (routed)
+    hipLaunchKernelGGL((k_grouped<BITS, KDIM, UM, GATEUP, false>), dim3(grouped_grid(max_tiles, rg)), block, 0, s,
+                       ga, rg);
   if (has_shared) {
     const int st = (int)cdiv(T, kTileM);
     const int sg = slab_groups(st, nout, RS, BQ_SHARED_GROUP_TARGET, 1);
@@ -1418,24 +1420,53 @@ hipError_t launch_prep_mx(int rows, int cols, const float* x, uint8_t* q8, uint8
   return hipGetLastError();
 }
 
-hipError_t dispatch_gateup(int bits, int H, const GroupArgs& ga, int I, int T, int N, int E, bool hs, hipStream_t s) {
+hipError_t dispatch_gateup(int bits, int H, const GroupArgs& ga, int I, int T, int N, int E, bool routed, bool hs,
+                           hipStream_t s) {
 #define BQ_CASE(KV)                                                                   \
   case KV:                                                                            \
-    return bits == 4 ? launch_grouped<4, KV, true>(ga, I, T, N, E, hs, s)             \
-                     : launch_grouped<2, KV, true>(ga, I, T, N, E, hs, s);
+    return bits == 4 ? launch_grouped<4, KV, true>(ga, I, T, N, E, routed, hs, s)     \
+                     : launch_grouped<2, KV, true>(ga, I, T, N, E, routed, hs, s);
   switch (H) { BQ_FOR_KDIM_GU(BQ_CASE) }
 #undef BQ_CASE
   return hipErrorInvalidValue;
 }
 
-hipError_t dispatch_down(int bits, int I, const GroupArgs& ga, int H, int T, int N, int E, bool hs, hipStream_t s) {
+hipError_t dispatch_down(int bits, int I, const GroupArgs& ga, int H, int T, int N, int E, bool routed, bool hs,
+                         hipStream_t s) {
 #define BQ_CASE(KV)                                                                   \
   case KV:                                                                            \
-    return bits == 4 ? launch_grouped<4, KV, false>(ga, H, T, N, E, hs, s)            \
-                     : launch_grouped<2, KV, false>(ga, H, T, N, E, hs, s);
+    return bits == 4 ? launch_grouped<4, KV, false>(ga, H, T, N, E, routed, hs, s)    \
+                     : launch_grouped<2, KV, false>(ga, H, T, N, E, routed, hs, s);
   switch (I) { BQ_FOR_KDIM_DN(BQ_CASE) }
 #undef BQ_CASE
   return hipErrorInvalidValue;
+}
+
+// The prefill's side stream for the shared expert: one per host thread and device, created on first
+// use and kept (never destroyed, so that no thread's exit races the runtime's teardown). Its fork
+// and join events are the thread's own, so concurrent calls from other threads never share them.
+#ifndef BQ_SHARED_SIDE
+#define BQ_SHARED_SIDE 1
+#endif
+struct PrefillSide {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kSideDevices = 16;
+hipError_t prefill_side(PrefillSide** out) {
+  thread_local PrefillSide side[kSideDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kSideDevices) return hipErrorInvalidDevice;
+  PrefillSide& ps = side[dev];
+  if (ps.s == nullptr) {
+    if ((e = hipStreamCreateWithFlags(&ps.s, hipStreamNonBlocking)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&ps.fork, hipEventDisableTiming)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&ps.join, hipEventDisableTiming)) != hipSuccess) return e;
+  }
+  *out = &ps;
+  return hipSuccess;
 }
 
 }  // namespace
@@ -1510,6 +1541,31 @@ hipError_t launch_prefill(const Geometry& g, const LayerPtrs& p, const float* x,
     hipLaunchKernelGGL(k_prep, dim3((unsigned)cdiv(nblk8, kThreads)), dim3(kThreads), 0, s, nblk8, x,
                        reinterpret_cast<_Float16*>(w.xq), w.xs);
   }
+  // The shared expert needs no routing: with BQ_SHARED_SIDE its gate/up and down run on a side
+  // stream forked here, beside the router, the grouping and the routed GEMMs, and join before the
+  // combine. It writes only its own rows (N + t) of the SwiGLU and output buffers.
+  PrefillSide* side = nullptr;
+  if (BQ_SHARED_SIDE && !mx && g.has_shared) {
+    hipError_t e = prefill_side(&side);
+    if (e == hipSuccess) e = hipEventRecord(side->fork, s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(side->s, side->fork, 0);
+    if (e != hipSuccess) return e;
+    GroupArgs gs{};
+    gs.shared = p.shared; gs.K = K; gs.shared_base = N; gs.T = T;
+    gs.off_codes[0] = g.off_codes[0]; gs.off_codes[1] = g.off_codes[1];
+    gs.off_sb[0] = g.off_sb[0]; gs.off_sb[1] = g.off_sb[1];
+    gs.a = reinterpret_cast<const _Float16*>(w.xq); gs.as = w.xs;
+    gs.oh = reinterpret_cast<_Float16*>(w.hq); gs.os = w.hs; gs.nout = I;
+    e = dispatch_gateup(g.bits, H, gs, I, T, N, E, false, true, side->s);
+    if (e != hipSuccess) return e;
+    gs.off_codes[0] = g.off_codes[2]; gs.off_sb[0] = g.off_sb[2];
+    gs.a = reinterpret_cast<const _Float16*>(w.hq); gs.as = w.hs;
+    gs.oy = w.y; gs.nout = H;
+    e = dispatch_down(g.bits, I, gs, H, T, N, E, false, true, side->s);
+    if (e == hipSuccess) e = hipEventRecord(side->join, side->s);
+    if (e != hipSuccess) return e;
+  }
+  const bool shared_here = g.has_shared && side == nullptr;
   const int32_t* idx = idx_in;
   if (idx_in == nullptr) {
     hipError_t e = launch_router_select(g, p, x, T, w.layer, w.layer.idx, w.layer.w, w.layer.g, nullptr, idx_out, s);
@@ -1545,13 +1601,14 @@ hipError_t launch_prefill(const Geometry& g, const LayerPtrs& p, const float* x,
   }
   ga.a = reinterpret_cast<const _Float16*>(w.xq); ga.as = w.xs;
   ga.oh = reinterpret_cast<_Float16*>(w.hq); ga.os = w.hs; ga.nout = I;
-  hipError_t e = dispatch_gateup(g.bits, H, ga, I, T, N, E, g.has_shared != 0, s);
+  hipError_t e = dispatch_gateup(g.bits, H, ga, I, T, N, E, true, shared_here, s);
   if (e != hipSuccess) return e;
   // down
   ga.off_codes[0] = g.off_codes[2]; ga.off_sb[0] = g.off_sb[2];
   ga.a = reinterpret_cast<const _Float16*>(w.hq); ga.as = w.hs;
   ga.oy = w.y; ga.nout = H;
-  e = dispatch_down(g.bits, I, ga, H, T, N, E, g.has_shared != 0, s);
+  e = dispatch_down(g.bits, I, ga, H, T, N, E, true, shared_here, s);
+  if (e == hipSuccess && side != nullptr) e = hipStreamWaitEvent(s, side->join, 0);
   if (e != hipSuccess) return e;
   // combine or scatter
   hipLaunchKernelGGL(k_prefill_out, dim3(cdiv(H / 4, kThreads), T), dim3(kThreads), 0, s, T, H, K, g.has_shared, w.pos,

@@ -169,3 +169,34 @@ def test_prefill_duplicate_router_rows_tie_to_lower_index(gpu_device):
     assert tied_tokens >= 1  # the tie decides at least token 0's choice
     for t in (0, 31, T - 1):
         assert_close(out[t], ref.token(xs[t]).out, f"out[{t}]")
+
+
+@pytest.mark.parametrize("which,T", [("tiny", bq.MOE_ROUTER_CERTIFIED_MIN_TOKENS + 88),
+                                     ("pre4", bq.MOE_ROUTER_CERTIFIED_MIN_TOKENS)])
+def test_prefill_graph_replays_match_eager(which, T, request):
+    """One prefill call captured in a HIP graph: its shared expert runs on the library's side stream,
+    forked from and joined back to the caller's stream, so the capture holds both. Three replays,
+    with eager work on the device between them, each equal the eager call bit for bit."""
+    L, _ = request.getfixturevalue(which)
+    w = L.w
+    _log(f"{w.name}: graph of one {T}-token prefill call")
+    x = torch.from_numpy(synth.tokens_x(w, 4000, T)).cuda()
+    eager, eager_idx = _forward(L, x)
+    n = bq.moe_workspace_bytes(L.desc, T)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(x)
+    idx = torch.empty(T, w.top_k, dtype=torch.int32, device="cuda")
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        bq.moe_layer_forward(L.desc, x, x, T, out, idx, ws, n, stream=s)
+    for rep in range(3):
+        out.fill_(float(rep + 1))
+        idx.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), eager), f"replay {rep}"
+        assert np.array_equal(idx.cpu().numpy(), eager_idx), f"replay {rep}"
+        _forward(L, x[: T // 2].contiguous())  # eager work between replays
