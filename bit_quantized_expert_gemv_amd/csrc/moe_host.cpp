@@ -210,7 +210,7 @@ size_t moe_workspace_bytes(const moe_layer_t* layer, int T) {
   if (layer == nullptr || T < 0 || !geometry_from(layer, &g, &why)) return 0;
   const int t = T < 1 ? 1 : T;
   size_t n = workspace_layer_bytes(g, t);
-  if (t >= MOE_PREFILL_MIN_TOKENS) {
+  if (t >= BQ_PREFILL_MIN) {
     const size_t pf = workspace_prefill_bytes(g, t);
     if (pf > n) n = pf;
   }
@@ -296,7 +296,7 @@ int moe_dequant(const moe_layer_t* layer, int expert, int matrix, int out_dtype,
 namespace {
 // The grouped (prefill) path, from MOE_PREFILL_MIN_TOKENS tokens (MXFP4 layers need inter >= 128:
 // their grouped GEMM steps K by 128).
-bool use_prefill(const Geometry& g, int T) { return T >= MOE_PREFILL_MIN_TOKENS && (g.form != 3 || g.I >= 128); }
+bool use_prefill(const Geometry& g, int T) { return T >= BQ_PREFILL_MIN && (g.form != 3 || g.I >= 128); }
 
 // The MXFP4 grouped GEMMs address their activation planes (3 E4M3 terms of [rows][K]) with 32-bit
 // buffer offsets: both the input's planes (T rows of H) and the SwiGLU outputs' (T*(K+shared)
@@ -312,7 +312,7 @@ int check_prefill_size(const Geometry& g, int T) {
 
 size_t needed_ws(const Geometry& g, int T) {
   size_t n = workspace_layer_bytes(g, T);
-  if (T >= MOE_PREFILL_MIN_TOKENS) {
+  if (T >= BQ_PREFILL_MIN) {
     const size_t pf = workspace_prefill_bytes(g, T);
     if (pf > n) n = pf;
   }

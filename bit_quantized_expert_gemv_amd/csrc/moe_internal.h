@@ -8,6 +8,12 @@
 
 #include "moe.h"
 
+// The token count from which moe_layer_forward and moe_expert_ffn take the prefill path (a build
+// may set another value to time both paths at the same T).
+#ifndef BQ_PREFILL_MIN
+#define BQ_PREFILL_MIN MOE_PREFILL_MIN_TOKENS
+#endif
+
 namespace bqmoe {
 
 // Shape and blob layout of one layer, validated on the host.
