@@ -13,7 +13,12 @@
  *
  * Conventions
  *  - Pointers named *_dev are device (HBM) pointers. The caller allocates and owns every buffer;
- *    the library never allocates or frees memory and keeps no mutable global state.
+ *    the library never allocates or frees device memory. Its only state is side streams: the
+ *    prefill path of an affine layer with a shared expert runs that expert on a side stream,
+ *    forked from the caller's stream and joined back within the call. The stream and its two
+ *    events are created on the calling host thread's first such call on a device, and live until
+ *    the process ends; make that first call outside stream capture. Calls from one thread share
+ *    its side stream, so their shared-expert work runs in call order.
  *  - Calls that take a stream enqueue work on it (a hipStream_t; NULL means the default stream)
  *    and return at once. Results are valid once the stream has reached that point. No call
  *    synchronises the host, so calls can be captured into a HIP graph.
