@@ -1385,12 +1385,14 @@ hipError_t launch_grouped(const GroupArgs& ga, int nout, int T, int N, int E, bo
 }
 
 template <int KDIM, bool GATEUP>
-hipError_t launch_grouped_mx(const GroupArgs& ga, int nout, int T, int N, int E, bool has_shared, hipStream_t s) {
+hipError_t launch_grouped_mx(const GroupArgs& ga, int nout, int T, int N, int E, bool routed, bool has_shared,
+                             hipStream_t s) {
   constexpr int RS = GATEUP ? 64 : 128;
   const dim3 block(kThreads);
   const int max_tiles = E + (int)cdiv(N, kTileM);
   const int rg = slab_groups(std::min(max_tiles, N), nout, RS, BQ_GROUP_TARGET, BQ_ROUTED_MIN_GROUPS);
-  hipLaunchKernelGGL((k_grouped_mx<KDIM, GATEUP, false>), dim3(grouped_grid(max_tiles, rg)), block, 0, s, ga, rg);
+  if (routed)
+    hipLaunchKernelGGL((k_grouped_mx<KDIM, GATEUP, false>), dim3(grouped_grid(max_tiles, rg)), block, 0, s, ga, rg);
   if (has_shared) {
     const int st = (int)cdiv(T, kTileM);
     const int sg = slab_groups(st, nout, RS, BQ_SHARED_GROUP_TARGET, 1);
@@ -1403,20 +1405,25 @@ hipError_t launch_grouped_mx(const GroupArgs& ga, int nout, int T, int N, int E,
 #define BQ_FOR_KDIM_DN(X) X(64) X(128) X(256) X(512) X(1024) X(2048)
 
 #define BQ_FOR_KDIM_MX(X) X(128) X(256) X(512) X(1024) X(2048) X(4096) X(8192)
-hipError_t dispatch_mx(bool gateup, int kdim, const GroupArgs& ga, int nout, int T, int N, int E, bool hs, hipStream_t s) {
+hipError_t dispatch_mx(bool gateup, int kdim, const GroupArgs& ga, int nout, int T, int N, int E, bool routed, bool hs,
+                       hipStream_t s) {
 #define BQ_CASE(KV)                                                                        \
   case KV:                                                                                 \
-    return gateup ? launch_grouped_mx<KV, true>(ga, nout, T, N, E, hs, s)                  \
-                  : launch_grouped_mx<KV, false>(ga, nout, T, N, E, hs, s);
+    return gateup ? launch_grouped_mx<KV, true>(ga, nout, T, N, E, routed, hs, s)          \
+                  : launch_grouped_mx<KV, false>(ga, nout, T, N, E, routed, hs, s);
   switch (kdim) { BQ_FOR_KDIM_MX(BQ_CASE) }
 #undef BQ_CASE
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_prep_mx(int rows, int cols, const float* x, uint8_t* q8, uint8_t* sc, hipStream_t s) {
-  const int64_t nblk = (int64_t)rows * cols / 32;
-  hipLaunchKernelGGL(k_prep_mx, dim3(cdiv(nblk * 4, kThreads)), dim3(kThreads), 0, s, nblk, x, q8, sc,
-                     (uint64_t)rows * cols, (uint64_t)nblk);
+// Rows [row0, row0 + nrows) of a [rows][cols] array into planes of rows * cols codes and
+// rows * cols / 32 scales.
+hipError_t launch_prep_mx(int rows, int row0, int nrows, int cols, const float* x, uint8_t* q8, uint8_t* sc,
+                          hipStream_t s) {
+  const int64_t nblk = (int64_t)nrows * cols / 32, off = (int64_t)row0 * cols;
+  if (nblk == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_prep_mx, dim3(cdiv(nblk * 4, kThreads)), dim3(kThreads), 0, s, nblk, x + off, q8 + off,
+                     sc + off / 32, (uint64_t)rows * cols, (uint64_t)rows * cols / 32);
   return hipGetLastError();
 }
 
@@ -1533,8 +1540,9 @@ hipError_t launch_prefill(const Geometry& g, const LayerPtrs& p, const float* x,
   const int N = T * K;
   const int nchunks = (int)cdiv(N, kChunk);
   const bool mx = g.form == 3;
+  const int R = N + (g.has_shared ? T : 0);  // SwiGLU rows: the routed entries, then the shared expert's
   if (mx) {
-    hipError_t e = launch_prep_mx(T, H, x, w.x8, w.xsc, s);
+    hipError_t e = launch_prep_mx(T, 0, T, H, x, w.x8, w.xsc, s);
     if (e != hipSuccess) return e;
   } else {
     const int64_t nblk8 = (int64_t)T * H / 8;
@@ -1545,7 +1553,7 @@ hipError_t launch_prefill(const Geometry& g, const LayerPtrs& p, const float* x,
   // stream forked here, beside the router, the grouping and the routed GEMMs, and join before the
   // combine. It writes only its own rows (N + t) of the SwiGLU and output buffers.
   PrefillSide* side = nullptr;
-  if (BQ_SHARED_SIDE && !mx && g.has_shared) {
+  if (BQ_SHARED_SIDE && g.has_shared) {
     hipError_t e = prefill_side(&side);
     if (e == hipSuccess) e = hipEventRecord(side->fork, s);
     if (e == hipSuccess) e = hipStreamWaitEvent(side->s, side->fork, 0);
@@ -1554,14 +1562,26 @@ hipError_t launch_prefill(const Geometry& g, const LayerPtrs& p, const float* x,
     gs.shared = p.shared; gs.K = K; gs.shared_base = N; gs.T = T;
     gs.off_codes[0] = g.off_codes[0]; gs.off_codes[1] = g.off_codes[1];
     gs.off_sb[0] = g.off_sb[0]; gs.off_sb[1] = g.off_sb[1];
-    gs.a = reinterpret_cast<const _Float16*>(w.xq); gs.as = w.xs;
-    gs.oh = reinterpret_cast<_Float16*>(w.hq); gs.os = w.hs; gs.nout = I;
-    e = dispatch_gateup(g.bits, H, gs, I, T, N, E, false, true, side->s);
-    if (e != hipSuccess) return e;
-    gs.off_codes[0] = g.off_codes[2]; gs.off_sb[0] = g.off_sb[2];
-    gs.a = reinterpret_cast<const _Float16*>(w.hq); gs.as = w.hs;
-    gs.oy = w.y; gs.nout = H;
-    e = dispatch_down(g.bits, I, gs, H, T, N, E, false, true, side->s);
+    if (mx) {  // gate/up, the expansion of the shared rows (N + t) of the SwiGLU outputs, down
+      gs.a8 = w.x8; gs.asc = w.xsc; gs.a_plane = (uint64_t)T * H; gs.sc_plane = (uint64_t)T * H / 32;
+      gs.oh32 = w.h32; gs.nout = I;
+      e = dispatch_mx(true, H, gs, I, T, N, E, false, true, side->s);
+      if (e == hipSuccess) e = launch_prep_mx(R, N, T, I, w.h32, w.h8, w.hsc, side->s);
+      if (e != hipSuccess) return e;
+      gs.off_codes[0] = g.off_codes[2]; gs.off_sb[0] = g.off_sb[2];
+      gs.a8 = w.h8; gs.asc = w.hsc; gs.a_plane = (uint64_t)R * I; gs.sc_plane = (uint64_t)R * I / 32;
+      gs.oy = w.y; gs.nout = H;
+      e = dispatch_mx(false, I, gs, H, T, N, E, false, true, side->s);
+    } else {
+      gs.a = reinterpret_cast<const _Float16*>(w.xq); gs.as = w.xs;
+      gs.oh = reinterpret_cast<_Float16*>(w.hq); gs.os = w.hs; gs.nout = I;
+      e = dispatch_gateup(g.bits, H, gs, I, T, N, E, false, true, side->s);
+      if (e != hipSuccess) return e;
+      gs.off_codes[0] = g.off_codes[2]; gs.off_sb[0] = g.off_sb[2];
+      gs.a = reinterpret_cast<const _Float16*>(w.hq); gs.as = w.hs;
+      gs.oy = w.y; gs.nout = H;
+      e = dispatch_down(g.bits, I, gs, H, T, N, E, false, true, side->s);
+    }
     if (e == hipSuccess) e = hipEventRecord(side->join, side->s);
     if (e != hipSuccess) return e;
   }
@@ -1584,16 +1604,16 @@ hipError_t launch_prefill(const Geometry& g, const LayerPtrs& p, const float* x,
   ga.off_codes[0] = g.off_codes[0]; ga.off_codes[1] = g.off_codes[1];
   ga.off_sb[0] = g.off_sb[0]; ga.off_sb[1] = g.off_sb[1];
   if (mx) {
-    const int R = N + (g.has_shared ? T : 0);
     ga.a8 = w.x8; ga.asc = w.xsc; ga.a_plane = (uint64_t)T * H; ga.sc_plane = (uint64_t)T * H / 32;
     ga.oh32 = w.h32; ga.nout = I;
-    hipError_t e = dispatch_mx(true, H, ga, I, T, N, E, g.has_shared != 0, s);
-    if (e == hipSuccess) e = launch_prep_mx(R, I, w.h32, w.h8, w.hsc, s);
+    hipError_t e = dispatch_mx(true, H, ga, I, T, N, E, true, shared_here, s);
+    if (e == hipSuccess) e = launch_prep_mx(R, 0, shared_here ? R : N, I, w.h32, w.h8, w.hsc, s);
     if (e != hipSuccess) return e;
     ga.off_codes[0] = g.off_codes[2]; ga.off_sb[0] = g.off_sb[2];
     ga.a8 = w.h8; ga.asc = w.hsc; ga.a_plane = (uint64_t)R * I; ga.sc_plane = (uint64_t)R * I / 32;
     ga.oy = w.y; ga.nout = H;
-    e = dispatch_mx(false, I, ga, H, T, N, E, g.has_shared != 0, s);
+    e = dispatch_mx(false, I, ga, H, T, N, E, true, shared_here, s);
+    if (e == hipSuccess && side != nullptr) e = hipStreamWaitEvent(s, side->join, 0);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_prefill_out, dim3(cdiv(H / 4, kThreads), T), dim3(kThreads), 0, s, T, H, K, g.has_shared, w.pos,
                        w.y, w.layer.w, w.layer.g, residual, out, y_out);

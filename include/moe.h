@@ -14,7 +14,7 @@
  * Conventions
  *  - Pointers named *_dev are device (HBM) pointers. The caller allocates and owns every buffer;
  *    the library never allocates or frees device memory. Its only state is side streams: the
- *    prefill path of an affine layer with a shared expert runs that expert on a side stream,
+ *    prefill path of a layer with a shared expert runs that expert on a side stream,
  *    forked from the caller's stream and joined back within the call. The stream and its two
  *    events are created on the calling host thread's first such call on a device, and live until
  *    the process ends; make that first call outside stream capture. Calls from one thread share
