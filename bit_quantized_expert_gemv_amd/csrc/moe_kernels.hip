@@ -755,7 +755,8 @@ __global__ __launch_bounds__(kBlock) void k_gateup(LayerArgs a, const float* __r
       load_topk_values<PL>(lg, a.E, lane, v);
       st.load(x + (size_t)t * H, threadIdx.x);
       writer = blockIdx.x == 0 && blockIdx.y == 0 && wave == 0;
-      e = wave_topk<PL>(v, a.E, a.K, lane, slot, writer, sel, val);
+      // slot s needs rounds 0..s only; the writer takes all K to record the routing
+      e = wave_topk<PL>(v, a.E, writer ? a.K : slot + 1, lane, slot, writer, sel, val);
     }
     if (e < 0 || e >= a.E) {  // never read outside the pool: mark the slot's output as invalid
       for (int p = 0; p < P; ++p) {
