@@ -733,7 +733,13 @@ __global__ __launch_bounds__(kBlock) void k_gateup(LayerArgs a, const float* __r
   __shared__ float4 xs[H / 4];
   __shared__ int32_t sel[MOE_MAX_TOP_K];
   __shared__ double val[MOE_MAX_TOP_K];
-  const int t = blockIdx.z, slot = blockIdx.y;
+  // Dispatch order of the routed slots. Slot s needs top-K rounds 0..s. With many routed experts
+  // (K > 4) the slots go in reverse, so the ones with the most rounds start first; with few, in
+  // order. Measured: top-6 40.7k -> 43.9k tokens/s reversed; top-3 64.7k in order against 63.7k.
+  // The first slot dispatched records the routing; the shared expert's slot K stays last.
+  const int t = blockIdx.z;
+  const bool reversed = a.K > 4;
+  const int slot = reversed && (int)blockIdx.y < a.K ? a.K - 1 - (int)blockIdx.y : (int)blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int lir = lane % C::LPR, rig = lane / C::LPR;
   const int step0 = (blockIdx.x * kWaves + wave) * P;
@@ -754,7 +760,7 @@ __global__ __launch_bounds__(kBlock) void k_gateup(LayerArgs a, const float* __r
       double v[PL];
       load_topk_values<PL>(lg, a.E, lane, v);
       st.load(x + (size_t)t * H, threadIdx.x);
-      writer = blockIdx.x == 0 && blockIdx.y == 0 && wave == 0;
+      writer = blockIdx.x == 0 && blockIdx.y == 0 && wave == 0;  // the first routed slot dispatched
       // slot s needs rounds 0..s only; the writer takes all K to record the routing
       e = wave_topk<PL>(v, a.E, writer ? a.K : slot + 1, lane, slot, writer, sel, val);
     }
