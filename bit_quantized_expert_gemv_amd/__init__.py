@@ -29,6 +29,7 @@ from ._binding import (  # noqa: F401
     moe_dequant,
     moe_expert_arrays_t,
     moe_expert_ffn,
+    moe_expert_ffn_checked,
     moe_last_error,
     moe_layer_forward,
     moe_layer_forward_timed,

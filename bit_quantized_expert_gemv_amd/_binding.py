@@ -43,6 +43,8 @@ SIGNATURES = {
     "moe_router": (ctypes.c_int, [ctypes.POINTER(moe_layer_t), c_vp, ctypes.c_int, c_vp, c_vp, c_vp, c_vp, c_vp,
                                   c_size, c_vp]),
     "moe_expert_ffn": (ctypes.c_int, [ctypes.POINTER(moe_layer_t), c_vp, ctypes.c_int, c_vp, c_vp, c_vp, c_size, c_vp]),
+    "moe_expert_ffn_checked": (ctypes.c_int, [ctypes.POINTER(moe_layer_t), c_vp, ctypes.c_int, c_vp, c_vp, c_vp, c_size,
+                                              c_vp, c_vp]),
     "moe_combine": (ctypes.c_int, [ctypes.POINTER(moe_layer_t), c_vp, c_vp, c_vp, c_vp, ctypes.c_int, c_vp, c_vp]),
     "moe_layer_forward": (ctypes.c_int, [ctypes.POINTER(moe_layer_t), c_vp, c_vp, ctypes.c_int, c_vp, c_vp, c_vp,
                                          c_size, c_vp]),
@@ -159,6 +161,11 @@ def moe_router(layer, x, T, idx, w, shared_g, logits, ws, ws_bytes, stream=None)
 def moe_expert_ffn(layer, x, T, idx, y, ws, ws_bytes, stream=None) -> None:
     _check(lib().moe_expert_ffn(_ref(layer), ptr(x), T, ptr(idx), ptr(y), ptr(ws), ws_bytes, stream_handle(stream)),
            "moe_expert_ffn")
+
+
+def moe_expert_ffn_checked(layer, x, T, idx, y, ws, ws_bytes, err, stream=None) -> None:
+    _check(lib().moe_expert_ffn_checked(_ref(layer), ptr(x), T, ptr(idx), ptr(y), ptr(ws), ws_bytes, ptr(err),
+                                        stream_handle(stream)), "moe_expert_ffn_checked")
 
 
 def moe_combine(layer, residual, y, w, shared_g, T, out, stream=None) -> None:

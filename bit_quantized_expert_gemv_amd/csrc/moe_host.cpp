@@ -339,6 +339,11 @@ int moe_router(const moe_layer_t* layer, const float* x, int T, int32_t* idx, fl
 
 int moe_expert_ffn(const moe_layer_t* layer, const float* x, int T, const int32_t* idx, float* y, void* ws,
                    size_t ws_bytes, void* stream) {
+  return moe_expert_ffn_checked(layer, x, T, idx, y, ws, ws_bytes, nullptr, stream);
+}
+
+int moe_expert_ffn_checked(const moe_layer_t* layer, const float* x, int T, const int32_t* idx, float* y, void* ws,
+                           size_t ws_bytes, int32_t* err, void* stream) {
   Geometry g;
   int rc = check_layer(layer, &g);
   if (rc) return rc;
@@ -352,10 +357,11 @@ int moe_expert_ffn(const moe_layer_t* layer, const float* x, int T, const int32_
   hipStream_t s = static_cast<hipStream_t>(stream);
   const LayerPtrs p = ptrs_of(layer);
   if ((rc = check_prefill_size(g, T))) return rc;
+  if (err != nullptr && !aligned(err, 4)) return fail(MOE_EINVAL, "err must be 4-byte aligned");
   if (use_prefill(g, T))
-    return hip_status(launch_prefill(g, p, x, nullptr, T, carve_prefill(g, T, ws), idx, nullptr, nullptr, y, s));
+    return hip_status(launch_prefill(g, p, x, nullptr, T, carve_prefill(g, T, ws), idx, nullptr, nullptr, y, err, s));
   const Workspace W = carve_workspace(g, T, ws);
-  hipError_t e = launch_gateup(g, p, x, T, W, idx, nullptr, true, s);
+  hipError_t e = launch_gateup(g, p, x, T, W, idx, nullptr, true, err, s);
   if (e == hipSuccess) e = launch_down(g, p, T, W, idx, nullptr, nullptr, y, s);
   return hip_status(e);
 }
@@ -408,14 +414,14 @@ int moe_layer_forward_timed(const moe_layer_t* layer, const float* x, const floa
     hipError_t e = hipSuccess;
     if (events != nullptr && events[0] != nullptr) e = hipEventRecord(static_cast<hipEvent_t>(events[0]), s);
     if (e == hipSuccess)
-      e = launch_prefill(g, p, x, residual, T, carve_prefill(g, T, ws), nullptr, idx_out, out, nullptr, s);
+      e = launch_prefill(g, p, x, residual, T, carve_prefill(g, T, ws), nullptr, idx_out, out, nullptr, nullptr, s);
     if (e == hipSuccess && events != nullptr && events[5] != nullptr)
       e = hipEventRecord(static_cast<hipEvent_t>(events[5]), s);
     return hip_status(e);
   }
   const Workspace W = carve_workspace(g, T, ws);
   hipError_t e = launch_router_phase(g, p, x, nullptr, 0.0f, T, W, s, ev(0));
-  if (e == hipSuccess) e = launch_gateup(g, p, x, T, W, nullptr, idx_out, true, s, ev(1));
+  if (e == hipSuccess) e = launch_gateup(g, p, x, T, W, nullptr, idx_out, true, nullptr, s, ev(1));
   if (e == hipSuccess) e = launch_down(g, p, T, W, W.idx, residual, out, nullptr, s, ev(2));
   return hip_status(e);
 }
@@ -507,7 +513,7 @@ int moe_stack_forward(const moe_layer_t* layers, int L, float eps, const float* 
     const float* xin = (l == 0) ? x : W.u;
     int32_t* io = idx_out ? idx_out + (size_t)l * T * g.K : nullptr;
     e = launch_router_phase(g, p, x, norm_src, eps, T, W, s);
-    if (e == hipSuccess) e = launch_gateup(g, p, xin, T, W, nullptr, io, true, s);
+    if (e == hipSuccess) e = launch_gateup(g, p, xin, T, W, nullptr, io, true, nullptr, s);
     if (e == hipSuccess) e = launch_down(g, p, T, W, W.idx, h, h_next, nullptr, s);
     h = h_next;
   }

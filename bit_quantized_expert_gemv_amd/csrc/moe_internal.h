@@ -99,9 +99,11 @@ hipError_t launch_prefetch(const Prefetch& pf, int blocks, hipStream_t s);
 hipError_t launch_router_phase(const Geometry& g, const LayerPtrs& p, const float* x, const float* norm_src,
                                float eps, int T, const Workspace& ws, hipStream_t s, const KernelEvents& ev = {});
 // Phase 2: gate/up SwiGLU of the routed experts (slots 0..K-1), plus slot K (shared) if with_shared.
-// If idx_in is null the top-K is computed from ws.logits and written to ws.idx/w/g (and idx_out).
+// If idx_in is null the top-K is computed from ws.logits and written to ws.idx/w/g (and idx_out). A
+// caller's index outside [0, E) makes that slot's h NaN (nothing is read) and, if err is non-null,
+// stores MOE_EINVAL to *err.
 hipError_t launch_gateup(const Geometry& g, const LayerPtrs& p, const float* x, int T, const Workspace& ws,
-                         const int32_t* idx_in, int32_t* idx_out, bool with_shared, hipStream_t s,
+                         const int32_t* idx_in, int32_t* idx_out, bool with_shared, int32_t* err, hipStream_t s,
                          const KernelEvents& ev = {});
 // Phase 3: down projections. combine: out = residual + sum_k w_k y_k + g y_s; otherwise y[t][k][:] = y_k.
 hipError_t launch_down(const Geometry& g, const LayerPtrs& p, int T, const Workspace& ws, const int32_t* idx,
@@ -130,7 +132,7 @@ hipError_t launch_pack(int H, int I, int bits, int G, const moe_expert_arrays_t*
 // y_out[t][k][:] = expert outputs (y_out non-null).
 hipError_t launch_prefill(const Geometry& g, const LayerPtrs& p, const float* x, const float* residual, int T,
                           const PrefillWorkspace& w, const int32_t* idx_in, int32_t* idx_out, float* out,
-                          float* y_out, hipStream_t s);
+                          float* y_out, int32_t* err, hipStream_t s);
 // Router logits of T tokens into ws.logits: the fp64 MFMA GEMM for many tokens, per-token router
 // rows (phase 1) for few.
 hipError_t launch_router_tokens(const Geometry& g, const LayerPtrs& p, const float* x, int T, const Workspace& ws,

@@ -373,6 +373,7 @@ struct LayerArgs {
   const uint16_t* router;
   const uint16_t* sgate;
   Workspace ws;
+  int32_t* err;  // optional error word: set to MOE_EINVAL when a caller's expert index is out of range
 };
 
 // Cross-layer prefetch: the grid reads the two regions (as one concatenated range, split evenly over
@@ -404,6 +405,7 @@ LayerArgs make_args(const Geometry& g, const LayerPtrs& p, const Workspace& ws) 
   for (int m = 0; m < 3; ++m) { a.off_codes[m] = g.off_codes[m]; a.off_sb[m] = g.off_sb[m]; }
   a.experts = p.experts; a.stride = p.stride; a.shared = p.shared; a.router = p.router; a.sgate = p.sgate;
   a.ws = ws;
+  a.err = nullptr;
   return a;
 }
 
@@ -470,20 +472,115 @@ __device__ __forceinline__ int wave_topk(double (&v)[PL], int E, int K, int lane
   return chosen;
 }
 
+// The same top-K (descending value, ties to the lower index; the same choices, bit for bit) with a
+// shorter dependent chain per round. Each fp64 logit becomes an order-preserving 64-bit key (the sign
+// bit flips non-negative values, every bit flips negative ones; NaN, and the slots past E, become
+// key 0, the lowest). A round first takes the wave maximum M of the keys' upper 32 bits with six
+// one-instruction DPP steps. If exactly one key has upper half M, it is the round's winner, and no
+// fp64 compare runs at all; only keys tied in their upper 32 bits (distinct logits agreeing in sign,
+// exponent and 20 mantissa bits, or equal logits) take the full (key, index) comparison.
+__device__ __forceinline__ double wave_read_f64(double v, int lane) {  // lane's v, wave-uniform
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane((int)(b & 0xFFFFFFFF), lane);
+  const int hi = __builtin_amdgcn_readlane((int)(b >> 32), lane);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {  // complete in lane 63
+  v = max(v, (uint32_t)dpp_i<kDppQuadXor1, 0xF>(0, (int)v));
+  v = max(v, (uint32_t)dpp_i<kDppQuadXor2, 0xF>(0, (int)v));
+  v = max(v, (uint32_t)dpp_i<kDppHalfMirror, 0xF>(0, (int)v));
+  v = max(v, (uint32_t)dpp_i<kDppRowMirror, 0xF>(0, (int)v));
+  v = max(v, (uint32_t)dpp_i<kDppBcast15, 0xA>(0, (int)v));
+  v = max(v, (uint32_t)dpp_i<kDppBcast31, 0xC>(0, (int)v));
+  return v;
+}
+// (key, index) argmax step for the tie case: larger key first, then lower index
+template <int CTRL, int ROWS>
+__device__ __forceinline__ void keymax_step(uint64_t& k, int& i) {
+  const uint32_t ohi = (uint32_t)dpp_i<CTRL, ROWS>(0, (int)(k >> 32));
+  const uint32_t olo = (uint32_t)dpp_i<CTRL, ROWS>(0, (int)(uint32_t)k);
+  const int oi = dpp_i<CTRL, ROWS>(0x7FFFFFFF, i);
+  const uint64_t ok = ((uint64_t)ohi << 32) | olo;
+  if (ok > k || (ok == k && oi < i)) { k = ok; i = oi; }
+}
+template <int PL>
+__device__ __forceinline__ int wave_topk_fast(const double (&v)[PL], int E, int K, int lane, int want, bool record,
+                                              int32_t* __restrict__ sel, double* __restrict__ val) {
+  uint64_t key[PL];
+#pragma unroll
+  for (int i = 0; i < PL; ++i) {
+    const uint64_t b = (uint64_t)__double_as_longlong(v[i]);
+    const uint64_t k = (b >> 63) ? ~b : (b | (1ull << 63));
+    key[i] = (lane + 64 * i < E && !__builtin_isnan(v[i])) ? k : 0ull;
+  }
+  int chosen = 0;
+  for (int r = 0; r < K; ++r) {
+    uint32_t m = (uint32_t)(key[0] >> 32);
+#pragma unroll
+    for (int i = 1; i < PL; ++i) m = max(m, (uint32_t)(key[i] >> 32));
+    const uint32_t M = (uint32_t)__builtin_amdgcn_readlane((int)wave_max_u32(m), 63);
+    uint32_t cm = 0;  // this lane's values whose upper half is M
+#pragma unroll
+    for (int i = 0; i < PL; ++i) cm |= ((uint32_t)(key[i] >> 32) == M ? 1u : 0u) << i;
+    const uint64_t lanes = __ballot(cm != 0);
+    const int wl0 = __builtin_ctzll(lanes);
+    const uint32_t cm0 = (uint32_t)__builtin_amdgcn_readlane((int)cm, wl0);
+    int win;
+    if ((lanes & (lanes - 1)) == 0 && (cm0 & (cm0 - 1)) == 0) {
+      win = wl0 + 64 * __builtin_ctz(cm0);  // a unique upper half decides the round
+    } else {  // tied upper halves: the full (key, index) argmax over the tied keys
+      uint64_t bk = 0;
+      int bi = 0x7FFFFFFF;
+#pragma unroll
+      for (int i = 0; i < PL; ++i) {
+        const bool c = ((cm >> i) & 1u) && (bi == 0x7FFFFFFF || key[i] > bk);  // strict: the lower index keeps a tie
+        bk = c ? key[i] : bk;
+        bi = c ? lane + 64 * i : bi;
+      }
+      keymax_step<kDppQuadXor1, 0xF>(bk, bi);
+      keymax_step<kDppQuadXor2, 0xF>(bk, bi);
+      keymax_step<kDppHalfMirror, 0xF>(bk, bi);
+      keymax_step<kDppRowMirror, 0xF>(bk, bi);
+      keymax_step<kDppBcast15, 0xA>(bk, bi);
+      keymax_step<kDppBcast31, 0xC>(bk, bi);
+      win = __builtin_amdgcn_readlane(bi, 63);
+    }
+    win = min(max(win, 0), E - 1);
+    if (r == want) chosen = win;
+    if (record) {  // the winner's fp64 value, from its lane
+      double wv = v[0];
+#pragma unroll
+      for (int i = 1; i < PL; ++i) wv = (win / 64 == i) ? v[i] : wv;
+      wv = wave_read_f64(wv, win % 64);
+      if (lane == 0) {
+        sel[r] = win;
+        val[r] = wv;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < PL; ++i) key[i] = (lane + 64 * i == win) ? 0ull : key[i];
+  }
+  return chosen;
+}
+
 // Softmax of the K chosen logits (the full softmax over E renormalised over the chosen set reduces to
-// this), written with the choices and the shared gate for token t. One lane calls this.
-__device__ __forceinline__ void write_routing(const LayerArgs& a, int t, const int32_t* __restrict__ sel,
-                                              const double* __restrict__ val, const double* __restrict__ lg,
+// this), written with the choices and the shared gate for token t. A whole wave calls this: lane k < K
+// computes exp(l_k - l_0) in fp32 (l_k - l_0 <= 0 is formed in fp64, then rounded), the lanes' terms
+// are added in slot order, and lane k writes slot k. In fp32 and across lanes, the routing write
+// costs one exp's latency instead of K + 1 serial fp64 exps at the end of the block's work.
+__device__ __forceinline__ void write_routing(const LayerArgs& a, int t, int lane, const int32_t* __restrict__ sel,
+                                              const double* __restrict__ val, double gate_logit,
                                               int32_t* __restrict__ idx_a, float* __restrict__ w_a,
                                               int32_t* __restrict__ idx_b, float* __restrict__ g_out) {
-  double z = 0.0;
-  for (int k = 0; k < a.K; ++k) z += exp(val[k] - val[0]);
-  for (int k = 0; k < a.K; ++k) {
-    idx_a[(size_t)t * a.K + k] = sel[k];
-    w_a[(size_t)t * a.K + k] = (float)(exp(val[k] - val[0]) / z);
-    if (idx_b) idx_b[(size_t)t * a.K + k] = sel[k];
+  const float e = lane < a.K ? expf((float)(val[min(lane, a.K - 1)] - val[0])) : 0.0f;
+  float z = 0.0f;
+  for (int k = 0; k < a.K; ++k) z += __shfl(e, k);
+  if (lane < a.K) {
+    idx_a[(size_t)t * a.K + lane] = sel[lane];
+    w_a[(size_t)t * a.K + lane] = e / z;
+    if (idx_b) idx_b[(size_t)t * a.K + lane] = sel[lane];
   }
-  if (g_out && a.has_shared) g_out[t] = (float)(1.0 / (1.0 + exp(-lg[a.E])));
+  if (lane == 0 && g_out && a.has_shared) g_out[t] = 1.0f / (1.0f + expf(-(float)gate_logit));
 }
 
 // RMS norm scale 1/sqrt(mean(h^2) + eps) from the fp64 sum of h^2 over the whole vector.
@@ -497,39 +594,6 @@ __device__ __forceinline__ double readlane_f64(double v, int lane) {
   const int lo = __builtin_amdgcn_readlane((int)(b & 0xFFFFFFFF), lane);
   const int hi = __builtin_amdgcn_readlane((int)(b >> 32), lane);
   return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
-}
-
-// gate/up/SwiGLU for P row steps of one expert, for a whole block: weight loads go out first,
-// then the staged activations are parked in LDS (one barrier) and read back per lane.
-template <int BITS, int H, int P, int FORM>
-__device__ __forceinline__ void gateup_block(const LayerArgs& a, const uint8_t* __restrict__ blob,
-                                             const Stage<H, kBlock>& st, float scale, float4* __restrict__ xs,
-                                             int step0, int lir, int rig, float* __restrict__ h) {
-  using C = RowCfg<BITS, H>;
-  const uint8_t* gc = blob + a.off_codes[0];
-  const uint8_t* uc = blob + a.off_codes[1];
-  const uint8_t* gs = blob + a.off_sb[0];
-  const uint8_t* us = blob + a.off_sb[1];
-  uint4 cg[P][C::CPL], cu[P][C::CPL];
-  uint32_t sg[P][C::CPL], su[P][C::CPL];
-#pragma unroll
-  for (int p = 0; p < P; ++p) {
-    const int r = min((step0 + p) * C::RPW + rig, a.I - 1);  // rows past the end re-read the last row
-    load_row<C, FORM == 3>(gc, gs, r, lir, cg[p], sg[p]);
-    load_row<C, FORM == 3>(uc, us, r, lir, cu[p], su[p]);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  st.template store<C>(xs, threadIdx.x, scale);
-  __syncthreads();
-  float xr[C::XPL], S[C::CPL];
-  read_act<C>(xs, lir, xr, S);
-#pragma unroll
-  for (int p = 0; p < P; ++p) {
-    const int r = (step0 + p) * C::RPW + rig;
-    const float ga = seg_sum<C::LPR>(row_partial<BITS, C, FORM>(cg[p], sg[p], xr, S));
-    const float ua = seg_sum<C::LPR>(row_partial<BITS, C, FORM>(cu[p], su[p], xr, S));
-    if (lir == C::LPR - 1 && r < a.I) h[r] = silu_mul(ga, ua);
-  }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -724,60 +788,124 @@ __global__ __launch_bounds__(kBlock) void k_router_group(LayerArgs a, const floa
 }
 
 // Kernel 2: gate/up/SwiGLU of the routed experts (blockIdx.y = slot) and, as slot K, of the shared
-// expert. The shared slot needs no routing, so its blocks stream weights while the routed blocks are
-// still picking their experts.
-template <int BITS, int H, int P, int PL, int FORM>
-__global__ __launch_bounds__(kBlock) void k_gateup(LayerArgs a, const float* __restrict__ x,
-                                                   const int32_t* __restrict__ idx_in, int32_t* __restrict__ idx_out) {
+// expert; blockIdx.x is a slice of kSlice rows, blockIdx.z the token. One block per CU reads the
+// activations once per CU (every row of gate and up needs all of them): a CU can keep only a limited
+// number of cache lines in flight, so its time tracks the lines it touches, and the activations were
+// most of them when four 4-wave blocks shared a CU. Wave 0 of a routed block picks the expert with
+// the two-phase top-K and shares it through LDS; the shared slot's blocks, which need no routing,
+// stream their weights meanwhile. h goes straight from the row lanes to memory.
+constexpr int kSlice = 16;  // rows of gate and up per block
+template <int BITS, int H, int FORM, int PL, int NW>
+__global__ __launch_bounds__(64 * NW) void k_gateup(LayerArgs a, const float* __restrict__ x,
+                                                    const int32_t* __restrict__ idx_in, int32_t* __restrict__ idx_out) {
   using C = RowCfg<BITS, H>;
+  constexpr int NT = 64 * NW;
+  constexpr bool MX = FORM == 3;
+  const int I = a.I;
+  const int NSL = I / kSlice;                            // slices per expert
+  constexpr int STEPS = kSlice / C::RPW;                 // row steps of a slice (gate and up rows)
+  constexpr int PW = (STEPS + NW - 1) / NW;              // row steps per wave
+  constexpr int PP0 = 8 / C::CPL > 0 ? 8 / C::CPL : 1;   // steps in registers at once
+  constexpr int PP = PW < PP0 ? PW : PP0;
+  constexpr int NPASS = (PW + PP - 1) / PP;
+  static_assert(kSlice % C::RPW == 0, "a row step covers whole rows of the slice");
   __shared__ float4 xs[H / 4];
   __shared__ int32_t sel[MOE_MAX_TOP_K];
   __shared__ double val[MOE_MAX_TOP_K];
-  // Dispatch order of the routed slots. Slot s needs top-K rounds 0..s. With many routed experts
-  // (K > 4) the slots go in reverse, so the ones with the most rounds start first; with few, in
-  // order. Measured: top-6 40.7k -> 43.9k tokens/s reversed; top-3 64.7k in order against 63.7k.
-  // The first slot dispatched records the routing; the shared expert's slot K stays last.
+
   const int t = blockIdx.z;
+  // Routed slots in reverse when K > 4 (slot s needs top-K rounds 0..s, so the ones with the most
+  // rounds start first); the shared expert's slot K stays last.
   const bool reversed = a.K > 4;
   const int slot = reversed && (int)blockIdx.y < a.K ? a.K - 1 - (int)blockIdx.y : (int)blockIdx.y;
+  const int bx = blockIdx.x;
+  const int slice = (NSL & 7) == 0 ? (bx & 7) * (NSL >> 3) + (bx >> 3) : bx;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int lir = lane % C::LPR, rig = lane / C::LPR;
-  const int step0 = (blockIdx.x * kWaves + wave) * P;
+  float* hout = a.ws.h + ((size_t)t * a.NE + slot) * I + (size_t)slice * kSlice;  // this block's rows of h
   const uint8_t* blob = a.shared;
-  Stage<H, kBlock> st;
-  // One wave records the choices (LDS) and writes the routing for the next kernel after its block's
-  // gate/up work: written before it, the softmax's fp64 exps and the gate logit's load would hold
-  // back this block's weight loads, and the block's barrier the other waves'.
+  Stage<H, NT> st;
+  __shared__ int32_t chosen;
+  // Wave 0 of a routed block picks the expert (the other waves would only repeat its work on the
+  // same SIMDs) and, in the first routed block dispatched, records the choices; after the block's
+  // work it writes the routing for the combine kernel (written earlier, the softmax's fp64 exps and
+  // the gate logit's load would hold back the block's weight loads).
   bool writer = false;
-  if (slot < a.K) {
-    int e;
+  double gate_logit = 0.0;
+  const bool routed = slot < a.K;
+  if (routed) {
     if (idx_in != nullptr) {
-      e = idx_in[(size_t)t * a.K + slot];
+      if (threadIdx.x == 0) chosen = idx_in[(size_t)t * a.K + slot];
       st.load(x + (size_t)t * H, threadIdx.x);
-    } else {
+    } else if (wave == 0) {
       const double* lg = a.ws.logits + (size_t)t * (a.E + 1);
       // the logits are requested first, so waiting for them never waits for the activations
       double v[PL];
       load_topk_values<PL>(lg, a.E, lane, v);
+      gate_logit = lg[a.E];  // the shared-gate logit (row E), for the routing write at the end
       st.load(x + (size_t)t * H, threadIdx.x);
-      writer = blockIdx.x == 0 && blockIdx.y == 0 && wave == 0;  // the first routed slot dispatched
+      writer = blockIdx.x == 0 && blockIdx.y == 0;  // in the first routed slot dispatched
       // slot s needs rounds 0..s only; the writer takes all K to record the routing
-      e = wave_topk<PL>(v, a.E, writer ? a.K : slot + 1, lane, slot, writer, sel, val);
+      const int e = wave_topk_fast<PL>(v, a.E, writer ? a.K : slot + 1, lane, slot, writer, sel, val);
+      if (lane == 0) chosen = e;
+    } else {
+      st.load(x + (size_t)t * H, threadIdx.x);
     }
-    if (e < 0 || e >= a.E) {  // never read outside the pool: mark the slot's output as invalid
-      for (int p = 0; p < P; ++p) {
-        const int r = (step0 + p) * C::RPW + rig;
-        if (r < a.I && lir == C::LPR - 1) a.ws.h[((size_t)t * a.NE + slot) * a.I + r] = NAN;
-      }
+    // the activations go to LDS before the weights are requested: the block then computes each row
+    // as soon as its data lands, instead of waiting at a barrier behind throttled load issue
+    st.template store<C>(xs, threadIdx.x, 1.0f);
+    __syncthreads();
+    const int e = chosen;
+    if (e < 0 || e >= a.E) {  // a caller's index outside the pool: the slot's h is NaN, nothing is read
+      if ((int)threadIdx.x < kSlice) hout[threadIdx.x] = NAN;
+      if (a.err != nullptr && threadIdx.x == 0) *a.err = MOE_EINVAL;
       return;  // the whole block takes this branch (slot is per block)
     }
     blob = a.experts + (size_t)e * a.stride;
   } else {
     st.load(x + (size_t)t * H, threadIdx.x);
   }
-  gateup_block<BITS, H, P, FORM>(a, blob, st, 1.0f, xs, step0, lir, rig, a.ws.h + ((size_t)t * a.NE + slot) * a.I);
-  if (writer && lane == 0)
-    write_routing(a, t, sel, val, a.ws.logits + (size_t)t * (a.E + 1), a.ws.idx, a.ws.w, idx_out, a.ws.g);
+
+  // 1. weight loads: gate/up rows of the first pass
+  const uint8_t* gc = blob + a.off_codes[0];
+  const uint8_t* uc = blob + a.off_codes[1];
+  const uint8_t* gs = blob + a.off_sb[0];
+  const uint8_t* us = blob + a.off_sb[1];
+  const int row0 = slice * kSlice;
+  uint4 cg[PP][C::CPL], cu[PP][C::CPL];
+  uint32_t sg[PP][C::CPL], su[PP][C::CPL];
+  auto load_pass = [&](int pass) __attribute__((always_inline)) {
+#pragma unroll
+    for (int p = 0; p < PP; ++p) {
+      const int r = min((wave * PW + pass * PP + p) * C::RPW + rig, kSlice - 1);  // past the slice: its last row again
+      load_row<C, MX>(gc, gs, row0 + r, lir, cg[p], sg[p]);
+      load_row<C, MX>(uc, us, row0 + r, lir, cu[p], su[p]);
+    }
+  };
+  load_pass(0);
+  if (!routed) {  // the shared slot requested its weights first; its activations are parked now
+    __builtin_amdgcn_sched_barrier(0);
+    st.template store<C>(xs, threadIdx.x, 1.0f);
+    __syncthreads();
+  }
+  float xr[C::XPL], S[C::CPL];
+  read_act<C>(xs, lir, xr, S);
+
+  // 2. gate/up rows and SwiGLU
+#pragma unroll
+  for (int pass = 0; pass < NPASS; ++pass) {
+    if (pass > 0) load_pass(pass);
+#pragma unroll
+    for (int p = 0; p < PP; ++p) {
+      const int step = wave * PW + pass * PP + p;
+      const int r = step * C::RPW + rig;
+      const float ga = seg_sum<C::LPR>(row_partial<BITS, C, FORM>(cg[p], sg[p], xr, S));
+      const float ua = seg_sum<C::LPR>(row_partial<BITS, C, FORM>(cu[p], su[p], xr, S));
+      if (lir == C::LPR - 1 && step < STEPS && r < kSlice)  // written through: the down kernel reads it next
+        __hip_atomic_store(&hout[r], silu_mul(ga, ua), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  if (writer) write_routing(a, t, lane, sel, val, gate_logit, a.ws.idx, a.ws.w, idx_out, a.ws.g);
 }
 
 // Kernel 3: down projections of all expert slots for a block of output rows; combine or store.
@@ -873,7 +1001,10 @@ __global__ __launch_bounds__(64) void k_topk(LayerArgs a, int32_t* __restrict__ 
   wave_topk<PL>(v, a.E, a.K, lane, -1, true, sel, val);
   if (logits_out)
     for (int e = lane; e < a.E; e += 64) logits_out[(size_t)t * a.E + e] = lg[e];
-  if (lane == 0) write_routing(a, t, sel, val, lg, idx, w, idx_b, sg);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");  // lane 0's choices in LDS, for every lane
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  write_routing(a, t, lane, sel, val, lg[a.E], idx, w, idx_b, sg);
 }
 
 // fp64 norm of each bf16 router row (one wave per row), for the certified top-K's error bound.
@@ -1049,10 +1180,10 @@ __global__ __launch_bounds__(kBlock) void k_topk_certified(LayerArgs a, const fl
     }
   }
   wave_topk<PL>(ex, a.E, a.K, lane, -1, true, sel[wave], val[wave]);
-  if (lane == 0) {
-    write_routing(a, t, sel[wave], val[wave], nullptr, idx, w, idx_b, nullptr);
-    if (sg && a.has_shared) sg[t] = (float)(1.0 / (1.0 + exp(-gl)));
-  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");  // lane 0's choices in LDS, for every lane
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  write_routing(a, t, lane, sel[wave], val[wave], gl, idx, w, idx_b, sg);
 }
 
 __global__ void k_combine(int T, int H, int K, int has_shared, const float* __restrict__ res,
@@ -1133,29 +1264,14 @@ unsigned blocks_for(int64_t n, int bs) { return (unsigned)((n + bs - 1) / bs); }
 #define BQ_FOR_H(X) X(256) X(512) X(1024) X(2048) X(4096) X(8192)
 #define BQ_FOR_I(X) X(64) X(128) X(256) X(512) X(1024) X(2048)
 
-// Row steps per wave (the bytes each wave has in flight), tuned on MI355X for the 4096/1024 shape.
-#ifndef BQ_P2
-#define BQ_P2 1
-#endif
+// Row steps per down wave (the bytes each wave has in flight), tuned on MI355X for the 4096/1024 shape.
 #ifndef BQ_P3
 #define BQ_P3 8
 #endif
 #ifndef BQ_ROUTER_STEPS
 #define BQ_ROUTER_STEPS 1
 #endif
-constexpr int kP2 = BQ_P2;  // gate/up
 constexpr int kP3 = BQ_P3;  // down
-// With several tokens per launch the grid holds a block set per token; from BQ_WIDE_MIN_TOKENS
-// tokens, gate/up waves take BQ_P2_WIDE row pairs each (fewer, longer blocks). Measured on the
-// 512-expert top-3 layer: 56.0 against 65.2 us at 8 tokens, 234 against 283 us at 40, while one
-// row pair stays best for single tokens.
-#ifndef BQ_P2_WIDE
-#define BQ_P2_WIDE 4
-#endif
-#ifndef BQ_WIDE_MIN_TOKENS
-#define BQ_WIDE_MIN_TOKENS 4
-#endif
-constexpr int kP2Wide = BQ_P2_WIDE;
 // Tokens per block of the multi-token router (k_router_group).
 #ifndef BQ_ROUTER_GROUP
 #define BQ_ROUTER_GROUP 4
@@ -1192,27 +1308,24 @@ hipError_t router_phase_impl(const LayerArgs& a, const float* x, const float* no
   return launch_timed(k_router_phase<H>, dim3(nrb, T), dim3(kBlock), s, ev, a, x, norm_src, eps, router_steps);
 }
 
+// Waves per gate/up block: 8 (two per SIMD, so one computes while the other waits), except where a
+// row's registers would not fit two waves per SIMD (hidden 8192) or a block would hold fewer rows than
+// waves' worth of lanes (hidden 256).
+#ifndef BQ_GATEUP_WAVES
+#define BQ_GATEUP_WAVES 8
+#endif
 template <int BITS, int H>
 hipError_t gateup_impl(const LayerArgs& a, const float* x, int T, const int32_t* idx_in, int32_t* idx_out,
                        bool with_shared, hipStream_t s, const KernelEvents& ev) {
-  using C = RowCfg<BITS, H>;
-  const bool wide = T >= BQ_WIDE_MIN_TOKENS && (a.form == 0 || a.form == 3);
-  const int rows_per_block = kWaves * (wide ? kP2Wide : kP2) * C::RPW;
-  const int nb = (a.I + rows_per_block - 1) / rows_per_block;
+  constexpr int NW = (H >= 64 * BQ_GATEUP_WAVES && H <= 4096) ? BQ_GATEUP_WAVES : 4;
   const int slots = a.K + ((with_shared && a.has_shared) ? 1 : 0);
-  const dim3 grid(nb, slots, T);
-#define BQ_GU(P, PL, F) launch_timed(k_gateup<BITS, H, P, PL, F>, grid, dim3(kBlock), s, ev, a, x, idx_in, idx_out)
-  if (wide) {
-    if constexpr (BITS == 4) {
-      if (a.form == 3) return a.E <= 512 ? BQ_GU(kP2Wide, 8, 3) : BQ_GU(kP2Wide, 16, 3);
-    }
-    return a.E <= 512 ? BQ_GU(kP2Wide, 8, 0) : BQ_GU(kP2Wide, 16, 0);
-  }
+  const dim3 grid(a.I / kSlice, slots, T), block(64 * NW);
+#define BQ_GU(PL, F) launch_timed(k_gateup<BITS, H, F, PL, NW>, grid, block, s, ev, a, x, idx_in, idx_out)
   if constexpr (BITS == 4) {
-    if (a.form == 3) return a.E <= 512 ? BQ_GU(kP2, 8, 3) : BQ_GU(kP2, 16, 3);
+    if (a.form == 3) return a.E <= 512 ? BQ_GU(8, 3) : BQ_GU(16, 3);
   }
-  if (a.E <= 512) return a.form == 1 ? BQ_GU(kP2, 8, 1) : a.form == 2 ? BQ_GU(kP2, 8, 2) : BQ_GU(kP2, 8, 0);
-  return a.form == 1 ? BQ_GU(kP2, 16, 1) : a.form == 2 ? BQ_GU(kP2, 16, 2) : BQ_GU(kP2, 16, 0);
+  if (a.E <= 512) return a.form == 1 ? BQ_GU(8, 1) : a.form == 2 ? BQ_GU(8, 2) : BQ_GU(8, 0);
+  return a.form == 1 ? BQ_GU(16, 1) : a.form == 2 ? BQ_GU(16, 2) : BQ_GU(16, 0);
 #undef BQ_GU
 }
 
@@ -1245,9 +1358,10 @@ hipError_t launch_router_phase(const Geometry& g, const LayerPtrs& p, const floa
 }
 
 hipError_t launch_gateup(const Geometry& g, const LayerPtrs& p, const float* x, int T, const Workspace& ws,
-                         const int32_t* idx_in, int32_t* idx_out, bool with_shared, hipStream_t s,
+                         const int32_t* idx_in, int32_t* idx_out, bool with_shared, int32_t* err, hipStream_t s,
                          const KernelEvents& ev) {
-  const LayerArgs a = make_args(g, p, ws);
+  LayerArgs a = make_args(g, p, ws);
+  a.err = err;
 #define BQ_CASE(HV)                                                                              \
   case HV:                                                                                       \
     return g.bits == 4 ? gateup_impl<4, HV>(a, x, T, idx_in, idx_out, with_shared, s, ev)        \

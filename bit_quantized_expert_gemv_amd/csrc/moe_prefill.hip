@@ -388,8 +388,11 @@ __global__ __launch_bounds__(64 * kASplit) void k_router_approx(int T, int H, in
 }
 
 // ---- 3. grouping by expert --------------------------------------------------------------------------
-// Entries i = t*K + k (token t, slot k) carry expert idx[i]. Chunks of 256 entries.
+// Entries i = t*K + k (token t, slot k) carry expert idx[i]. Chunks of 256 entries. A caller's index
+// outside [0, E) is grouped with expert 0, so that every position stays inside the buffers; the
+// output kernel writes NaN for such an entry instead of the expert 0 result computed for it.
 constexpr int kChunk = 256;
+__device__ __forceinline__ int valid_expert(int e, int E) { return (e >= 0 && e < E) ? e : 0; }
 
 __global__ __launch_bounds__(kChunk) void k_group_hist(int N, int E, const int32_t* __restrict__ idx,
                                                        int32_t* __restrict__ hist) {
@@ -397,7 +400,7 @@ __global__ __launch_bounds__(kChunk) void k_group_hist(int N, int E, const int32
   for (int e = threadIdx.x; e < E; e += kChunk) cnt[e] = 0;
   __syncthreads();
   const int i = blockIdx.x * kChunk + threadIdx.x;
-  if (i < N) atomicAdd(&cnt[idx[i]], 1);  // counts do not depend on the order of the adds
+  if (i < N) atomicAdd(&cnt[valid_expert(idx[i], E)], 1);  // counts do not depend on the order of the adds
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += kChunk) hist[(size_t)blockIdx.x * E + e] = cnt[e];
 }
@@ -481,7 +484,7 @@ __global__ __launch_bounds__(kChunk) void k_group_place(int N, int E, const int3
                                                         int32_t* __restrict__ pos, int32_t* __restrict__ perm) {
   __shared__ int32_t ex[kChunk];
   const int i = blockIdx.x * kChunk + threadIdx.x;
-  const int e = (i < N) ? idx[i] : -1;
+  const int e = (i < N) ? valid_expert(idx[i], E) : -1;
   ex[threadIdx.x] = e;
   __syncthreads();
   if (i >= N) return;
@@ -1299,7 +1302,8 @@ __global__ __launch_bounds__(kThreads, GATEUP ? BQ_LB_GU : BQ_LB_DOWN) void k_gr
 // ---- 6. combine (gather) / scatter ------------------------------------------------------------------
 // out[t][r] = residual[t][r] + sum_k w[t][k] * y[pos[t*K+k]][r] + g[t] * y[T*K + t][r]   (combine)
 // y_out[t][k][r] = y[pos[t*K+k]][r], y_out[t][K][r] = y[T*K + t][r]                       (scatter)
-__global__ __launch_bounds__(kThreads) void k_prefill_out(int T, int H, int K, int has_shared,
+__global__ __launch_bounds__(kThreads) void k_prefill_out(int T, int H, int K, int E, int has_shared,
+                                                          const int32_t* __restrict__ idx, int32_t* __restrict__ err,
                                                           const int32_t* __restrict__ pos,
                                                           const float* __restrict__ y, const float* __restrict__ w,
                                                           const float* __restrict__ sg,
@@ -1328,8 +1332,13 @@ __global__ __launch_bounds__(kThreads) void k_prefill_out(int T, int H, int K, i
     }
     *reinterpret_cast<float4*>(out + (size_t)t * H + r) = acc;
   } else {
-    for (int k = 0; k < K; ++k)
-      *reinterpret_cast<float4*>(y_out + ((size_t)t * NE + k) * H + r) = row4((size_t)pos[(size_t)t * K + k]);
+    for (int k = 0; k < K; ++k) {
+      const int e = idx[(size_t)t * K + k];
+      float4 v = make_float4(NAN, NAN, NAN, NAN);
+      if (e >= 0 && e < E) v = row4((size_t)pos[(size_t)t * K + k]);
+      else if (err != nullptr && r == 0) *err = MOE_EINVAL;
+      *reinterpret_cast<float4*>(y_out + ((size_t)t * NE + k) * H + r) = v;
+    }
     if (has_shared) *reinterpret_cast<float4*>(y_out + ((size_t)t * NE + K) * H + r) = row4((size_t)T * K + t);
   }
 }
@@ -1449,33 +1458,6 @@ hipError_t dispatch_down(int bits, int I, const GroupArgs& ga, int H, int T, int
   return hipErrorInvalidValue;
 }
 
-// The prefill's side stream for the shared expert: one per host thread and device, created on first
-// use and kept (never destroyed, so that no thread's exit races the runtime's teardown). Its fork
-// and join events are the thread's own, so concurrent calls from other threads never share them.
-#ifndef BQ_SHARED_SIDE
-#define BQ_SHARED_SIDE 1
-#endif
-struct PrefillSide {
-  hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-};
-constexpr int kSideDevices = 16;
-hipError_t prefill_side(PrefillSide** out) {
-  thread_local PrefillSide side[kSideDevices];
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= kSideDevices) return hipErrorInvalidDevice;
-  PrefillSide& ps = side[dev];
-  if (ps.s == nullptr) {
-    if ((e = hipStreamCreateWithFlags(&ps.s, hipStreamNonBlocking)) != hipSuccess) return e;
-    if ((e = hipEventCreateWithFlags(&ps.fork, hipEventDisableTiming)) != hipSuccess) return e;
-    if ((e = hipEventCreateWithFlags(&ps.join, hipEventDisableTiming)) != hipSuccess) return e;
-  }
-  *out = &ps;
-  return hipSuccess;
-}
-
 }  // namespace
 
 hipError_t launch_router_gemm(const Geometry& g, const LayerPtrs& p, const float* x, int T, const Workspace& ws,
@@ -1535,7 +1517,7 @@ hipError_t launch_router_select(const Geometry& g, const LayerPtrs& p, const flo
 
 hipError_t launch_prefill(const Geometry& g, const LayerPtrs& p, const float* x, const float* residual, int T,
                           const PrefillWorkspace& w, const int32_t* idx_in, int32_t* idx_out, float* out,
-                          float* y_out, hipStream_t s) {
+                          float* y_out, int32_t* err, hipStream_t s) {
   const int H = g.H, I = g.I, E = g.E, K = g.K;
   const int N = T * K;
   const int nchunks = (int)cdiv(N, kChunk);
@@ -1549,43 +1531,7 @@ hipError_t launch_prefill(const Geometry& g, const LayerPtrs& p, const float* x,
     hipLaunchKernelGGL(k_prep, dim3((unsigned)cdiv(nblk8, kThreads)), dim3(kThreads), 0, s, nblk8, x,
                        reinterpret_cast<_Float16*>(w.xq), w.xs);
   }
-  // The shared expert needs no routing: with BQ_SHARED_SIDE its gate/up and down run on a side
-  // stream forked here, beside the router, the grouping and the routed GEMMs, and join before the
-  // combine. It writes only its own rows (N + t) of the SwiGLU and output buffers.
-  PrefillSide* side = nullptr;
-  if (BQ_SHARED_SIDE && g.has_shared) {
-    hipError_t e = prefill_side(&side);
-    if (e == hipSuccess) e = hipEventRecord(side->fork, s);
-    if (e == hipSuccess) e = hipStreamWaitEvent(side->s, side->fork, 0);
-    if (e != hipSuccess) return e;
-    GroupArgs gs{};
-    gs.shared = p.shared; gs.K = K; gs.shared_base = N; gs.T = T;
-    gs.off_codes[0] = g.off_codes[0]; gs.off_codes[1] = g.off_codes[1];
-    gs.off_sb[0] = g.off_sb[0]; gs.off_sb[1] = g.off_sb[1];
-    if (mx) {  // gate/up, the expansion of the shared rows (N + t) of the SwiGLU outputs, down
-      gs.a8 = w.x8; gs.asc = w.xsc; gs.a_plane = (uint64_t)T * H; gs.sc_plane = (uint64_t)T * H / 32;
-      gs.oh32 = w.h32; gs.nout = I;
-      e = dispatch_mx(true, H, gs, I, T, N, E, false, true, side->s);
-      if (e == hipSuccess) e = launch_prep_mx(R, N, T, I, w.h32, w.h8, w.hsc, side->s);
-      if (e != hipSuccess) return e;
-      gs.off_codes[0] = g.off_codes[2]; gs.off_sb[0] = g.off_sb[2];
-      gs.a8 = w.h8; gs.asc = w.hsc; gs.a_plane = (uint64_t)R * I; gs.sc_plane = (uint64_t)R * I / 32;
-      gs.oy = w.y; gs.nout = H;
-      e = dispatch_mx(false, I, gs, H, T, N, E, false, true, side->s);
-    } else {
-      gs.a = reinterpret_cast<const _Float16*>(w.xq); gs.as = w.xs;
-      gs.oh = reinterpret_cast<_Float16*>(w.hq); gs.os = w.hs; gs.nout = I;
-      e = dispatch_gateup(g.bits, H, gs, I, T, N, E, false, true, side->s);
-      if (e != hipSuccess) return e;
-      gs.off_codes[0] = g.off_codes[2]; gs.off_sb[0] = g.off_sb[2];
-      gs.a = reinterpret_cast<const _Float16*>(w.hq); gs.as = w.hs;
-      gs.oy = w.y; gs.nout = H;
-      e = dispatch_down(g.bits, I, gs, H, T, N, E, false, true, side->s);
-    }
-    if (e == hipSuccess) e = hipEventRecord(side->join, side->s);
-    if (e != hipSuccess) return e;
-  }
-  const bool shared_here = g.has_shared && side == nullptr;
+  const bool shared_here = g.has_shared != 0;
   const int32_t* idx = idx_in;
   if (idx_in == nullptr) {
     hipError_t e = launch_router_select(g, p, x, T, w.layer, w.layer.idx, w.layer.w, w.layer.g, nullptr, idx_out, s);
@@ -1613,10 +1559,9 @@ hipError_t launch_prefill(const Geometry& g, const LayerPtrs& p, const float* x,
     ga.a8 = w.h8; ga.asc = w.hsc; ga.a_plane = (uint64_t)R * I; ga.sc_plane = (uint64_t)R * I / 32;
     ga.oy = w.y; ga.nout = H;
     e = dispatch_mx(false, I, ga, H, T, N, E, true, shared_here, s);
-    if (e == hipSuccess && side != nullptr) e = hipStreamWaitEvent(s, side->join, 0);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_prefill_out, dim3(cdiv(H / 4, kThreads), T), dim3(kThreads), 0, s, T, H, K, g.has_shared, w.pos,
-                       w.y, w.layer.w, w.layer.g, residual, out, y_out);
+    hipLaunchKernelGGL(k_prefill_out, dim3(cdiv(H / 4, kThreads), T), dim3(kThreads), 0, s, T, H, K, E, g.has_shared,
+                       idx, err, w.pos, w.y, w.layer.w, w.layer.g, residual, out, y_out);
     return hipGetLastError();
   }
   ga.a = reinterpret_cast<const _Float16*>(w.xq); ga.as = w.xs;
@@ -1628,11 +1573,10 @@ hipError_t launch_prefill(const Geometry& g, const LayerPtrs& p, const float* x,
   ga.a = reinterpret_cast<const _Float16*>(w.hq); ga.as = w.hs;
   ga.oy = w.y; ga.nout = H;
   e = dispatch_down(g.bits, I, ga, H, T, N, E, true, shared_here, s);
-  if (e == hipSuccess && side != nullptr) e = hipStreamWaitEvent(s, side->join, 0);
   if (e != hipSuccess) return e;
   // combine or scatter
-  hipLaunchKernelGGL(k_prefill_out, dim3(cdiv(H / 4, kThreads), T), dim3(kThreads), 0, s, T, H, K, g.has_shared, w.pos,
-                     w.y, w.layer.w, w.layer.g, residual, out, y_out);
+  hipLaunchKernelGGL(k_prefill_out, dim3(cdiv(H / 4, kThreads), T), dim3(kThreads), 0, s, T, H, K, E, g.has_shared,
+                     idx, err, w.pos, w.y, w.layer.w, w.layer.g, residual, out, y_out);
   return hipGetLastError();
 }
 

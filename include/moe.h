@@ -13,12 +13,8 @@
  *
  * Conventions
  *  - Pointers named *_dev are device (HBM) pointers. The caller allocates and owns every buffer;
- *    the library never allocates or frees device memory. Its only state is side streams: the
- *    prefill path of a layer with a shared expert runs that expert on a side stream,
- *    forked from the caller's stream and joined back within the call. The stream and its two
- *    events are created on the calling host thread's first such call on a device, and live until
- *    the process ends; make that first call outside stream capture. Calls from one thread share
- *    its side stream, so their shared-expert work runs in call order.
+ *    the library never allocates or frees device memory, and every call runs all of its work on
+ *    the caller's stream.
  *  - Calls that take a stream enqueue work on it (a hipStream_t; NULL means the default stream)
  *    and return at once. Results are valid once the stream has reached that point. No call
  *    synchronises the host, so calls can be captured into a HIP graph.
@@ -183,11 +179,19 @@ int moe_router(const moe_layer_t* layer, const float* x_dev, int T, int32_t* idx
  * con FMA"). For each token t and slot k < K, expert idx[t][k] computes
  *   y = W_down (silu(W_gate x) * (W_up x)),
  * and slot K is the shared expert when has_shared is 1.
- *   idx_dev int32 [T][K] (device). Entries outside [0, E) make the call write NaN to that slot's
- *   output and set MOE_EINVAL in the error word, if one is given.
+ *   idx_dev int32 [T][K] (device). An entry outside [0, E) reads no weights (it never addresses
+ *   memory outside the pool) and makes the call write NaN to that slot's output row.
  *   y_dev fp32 [T][K + has_shared][H]. */
 int moe_expert_ffn(const moe_layer_t* layer, const float* x_dev, int T, const int32_t* idx_dev, float* y_dev,
                    void* ws_dev, size_t ws_bytes, void* stream);
+
+/* moe_expert_ffn with a device error word: err_dev (int32, device, 4-byte aligned; may be NULL) is
+ * set to MOE_EINVAL by the kernels when an index of idx_dev lies outside [0, E), and is otherwise
+ * left untouched, so the caller clears it before the call and reads it after a stream sync. The
+ * indices live on the device, so the host cannot check them without a sync; this is how a caller
+ * whose indices come from its own GPU code learns that one was out of range. */
+int moe_expert_ffn_checked(const moe_layer_t* layer, const float* x_dev, int T, const int32_t* idx_dev, float* y_dev,
+                           void* ws_dev, size_t ws_bytes, int32_t* err_dev, void* stream);
 
 /* Combine ("Metal Compute Shaders": MoE combine + residual + gate):
  *   out[t] = residual[t] + sum_k w[t][k] * y[t][k] + g[t] * y[t][K]   (shared term if has_shared)
