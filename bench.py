@@ -132,9 +132,6 @@ def main():
     ap.add_argument("--dequant", default="xsum", choices=["xsum", "literal", "naive"],
                     help="decode GEMV arithmetic: per-chunk x-sum form (default), the pages' per-element "
                          "fma(q, s*x, b*x) form, or the naive (q*s + b)*x form; an A/B ablation")
-    ap.add_argument("--stack-prefetch", action="store_true",
-                    help="stack60: read layer l+1's router and shared expert on a side stream during layer l "
-                         "(MOE_FLAG_PREFETCH_NEXT); an A/B of the cross-layer prefetch")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="first run a plain device copy of this many MiB (a known-size reference for HBM counters)")
     args = ap.parse_args()
@@ -368,10 +365,8 @@ def bench_stack(args, w):
     n = bq.moe_stack_workspace_bytes(layers[0].desc, 1)
     ws = torch.empty(n, dtype=torch.uint8, device=dev)
     descs = [L.desc for L in layers]
-    if args.stack_prefetch:
-        descs[0].flags |= bq.MOE_FLAG_PREFETCH_NEXT
     stream = torch.cuda.Stream(device=dev)
-    # one eager call before capture (it also creates the prefetch side stream when asked for)
+    # one eager call before capture
     with torch.cuda.stream(stream):
         bq.moe_stack_forward(descs, 1e-6, X[0], 1, out[0], idx[0], ws, n, stream=stream)
     torch.cuda.synchronize()
@@ -399,7 +394,7 @@ def bench_stack(args, w):
             {"workload": f"{w.name}: {w.layers} MoE layers (hidden {w.hidden}, {w.n_experts} experts, inter {w.inter}, "
                          f"top-{w.top_k} + shared, {w.bits}-bit, all experts resident), {N} sequential single-token "
                          f"calls in one HIP graph, RMS norm between layers", "tokens_per_step": N,
-             "cross_layer_prefetch": bool(args.stack_prefetch), "parallelism": "single GPU"},
+             "parallelism": "single GPU"},
             {"us_per_token": round(us, 2), "expert_GB/s": round(expert_bytes / (us * 1e-6) / 1e9, 1),
              "all_weights_GB/s": round((expert_bytes + router_bytes) / (us * 1e-6) / 1e9, 1),
              "expert_frac_of_peak": round(expert_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),

@@ -19,7 +19,6 @@ from ._binding import (  # noqa: F401
     MOE_ROUTER_CERTIFIED_MIN_TOKENS,
     MOE_FLAG_DEQUANT_LITERAL,
     MOE_FLAG_DEQUANT_NAIVE,
-    MOE_FLAG_PREFETCH_NEXT,
     SIGNATURES,
     MoeError,
     lib,

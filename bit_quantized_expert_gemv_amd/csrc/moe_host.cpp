@@ -5,7 +5,6 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
-#include <mutex>
 #include <string>
 
 #include "moe.h"
@@ -93,9 +92,9 @@ bool geometry_from(const moe_layer_t* L, Geometry* g, const char** why) {
     return false;
   }
   if (L->has_shared != 0 && L->has_shared != 1) { *why = "has_shared must be 0 or 1"; return false; }
-  const int form = L->flags & ~MOE_FLAG_PREFETCH_NEXT;
+  const int form = L->flags;
   if (form != 0 && form != MOE_FLAG_DEQUANT_LITERAL && form != MOE_FLAG_DEQUANT_NAIVE) {
-    *why = "flags must be 0, MOE_FLAG_DEQUANT_LITERAL or MOE_FLAG_DEQUANT_NAIVE, optionally with MOE_FLAG_PREFETCH_NEXT";
+    *why = "flags must be 0, MOE_FLAG_DEQUANT_LITERAL or MOE_FLAG_DEQUANT_NAIVE";
     return false;
   }
   if (mx && form != 0) { *why = "the dequant-form flags apply to the affine format only"; return false; }
@@ -426,44 +425,6 @@ int moe_layer_forward_timed(const moe_layer_t* layer, const float* x, const floa
   return hip_status(e);
 }
 
-}  // extern "C"
-
-namespace bqmoe {
-namespace {
-// The side stream of the cross-layer prefetch, one per device, created on first use and kept until
-// the process ends, with the event that forks it off the caller's stream.
-constexpr int kMaxDevices = 64;
-struct SideStream {
-  hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-};
-SideStream g_side[kMaxDevices];
-std::mutex g_side_mu;
-
-hipError_t side_stream(SideStream** out) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-  std::lock_guard<std::mutex> lock(g_side_mu);
-  SideStream& ss = g_side[dev];
-  if (ss.s == nullptr) {
-    if ((e = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking)) != hipSuccess) return e;
-    if ((e = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming)) != hipSuccess) return e;
-    if ((e = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming)) != hipSuccess) return e;
-  }
-  *out = &ss;
-  return hipSuccess;
-}
-}  // namespace
-}  // namespace bqmoe
-
-using namespace bqmoe;
-extern "C" {
-
-#ifndef BQ_PREFETCH_BLOCKS
-#define BQ_PREFETCH_BLOCKS 64
-#endif
 int moe_stack_forward(const moe_layer_t* layers, int L, float eps, const float* x, int T, float* out,
                       int32_t* idx_out, void* ws, size_t ws_bytes, void* stream) {
   if (layers == nullptr || L < 1) return fail(MOE_EINVAL, "layers must be non-NULL and L >= 1");
@@ -473,8 +434,9 @@ int moe_stack_forward(const moe_layer_t* layers, int L, float eps, const float* 
   for (int l = 1; l < L; ++l) {
     Geometry gl;
     if ((rc = check_layer(&layers[l], &gl))) return rc;
-    if (gl.H != g.H || gl.I != g.I || gl.E != g.E || gl.K != g.K || gl.bits != g.bits || gl.has_shared != g.has_shared)
-      return fail(MOE_EINVAL, "all layers must share hidden, inter, n_experts, top_k, bits and has_shared");
+    if (gl.H != g.H || gl.I != g.I || gl.E != g.E || gl.K != g.K || gl.bits != g.bits || gl.G != g.G ||
+        gl.form != g.form || gl.has_shared != g.has_shared)
+      return fail(MOE_EINVAL, "all layers must share hidden, inter, n_experts, top_k, bits, group, flags and has_shared");
   }
   if (!(eps >= 0.0f)) return fail(MOE_EINVAL, "eps must be >= 0");
   if (T < 0) return fail(MOE_EINVAL, "T must be >= 0");
@@ -491,23 +453,8 @@ int moe_stack_forward(const moe_layer_t* layers, int L, float eps, const float* 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const float* h = x;  // h_l
   hipError_t e = hipSuccess;
-  // Cross-layer prefetch: at the start of layer l, a side stream forked off the caller's stream reads
-  // layer l+1's router and shared expert; it runs beside layer l's kernels and joins the caller's
-  // stream once, after the last layer.
-  SideStream* side = nullptr;
-  const bool prefetch = (layers[0].flags & MOE_FLAG_PREFETCH_NEXT) != 0 && L > 1;
-  if (prefetch && (e = side_stream(&side)) != hipSuccess) return hip_status(e);
   for (int l = 0; l < L && e == hipSuccess; ++l) {
     const LayerPtrs p = ptrs_of(&layers[l]);
-    if (prefetch && l + 1 < L) {
-      const LayerPtrs pn = ptrs_of(&layers[l + 1]);
-      const Prefetch pf{{reinterpret_cast<const uint8_t*>(pn.router), pn.shared},
-                        {(uint64_t)g.E * g.H * 2, pn.shared != nullptr ? g.blob_bytes : 0}};
-      e = hipEventRecord(side->fork, s);
-      if (e == hipSuccess) e = hipStreamWaitEvent(side->s, side->fork, 0);
-      if (e == hipSuccess) e = launch_prefetch(pf, BQ_PREFETCH_BLOCKS, side->s);
-      if (e != hipSuccess) break;
-    }
     float* h_next = (l == L - 1) ? out : hbuf[l & 1];
     const float* norm_src = (l == 0) ? nullptr : h;
     const float* xin = (l == 0) ? x : W.u;
@@ -516,10 +463,6 @@ int moe_stack_forward(const moe_layer_t* layers, int L, float eps, const float* 
     if (e == hipSuccess) e = launch_gateup(g, p, xin, T, W, nullptr, io, true, nullptr, s);
     if (e == hipSuccess) e = launch_down(g, p, T, W, W.idx, h, h_next, nullptr, s);
     h = h_next;
-  }
-  if (prefetch && e == hipSuccess) {
-    e = hipEventRecord(side->join, side->s);
-    if (e == hipSuccess) e = hipStreamWaitEvent(s, side->join, 0);
   }
   return hip_status(e);
 }

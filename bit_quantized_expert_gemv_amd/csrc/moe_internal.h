@@ -85,15 +85,6 @@ struct KernelEvents {
   hipEvent_t stop = nullptr;
 };
 
-// Memory to read ahead of use (two regions of a multiple of 16 bytes each, 16-byte aligned; either
-// may be empty). launch_prefetch reads it with `blocks` blocks and discards the data, so that the
-// lines sit in the memory-side cache when a later kernel needs them.
-struct Prefetch {
-  const uint8_t* ptr[2];
-  uint64_t bytes[2];
-};
-hipError_t launch_prefetch(const Prefetch& pf, int blocks, hipStream_t s);
-
 // Phase 1: router logits and the shared-gate logit into ws.logits. If norm_src is non-null the layer
 // input is RMSNorm(norm_src) with the given eps (also written to ws.u); otherwise the input is x.
 hipError_t launch_router_phase(const Geometry& g, const LayerPtrs& p, const float* x, const float* norm_src,

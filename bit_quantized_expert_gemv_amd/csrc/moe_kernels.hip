@@ -376,29 +376,6 @@ struct LayerArgs {
   int32_t* err;  // optional error word: set to MOE_EINVAL when a caller's expert index is out of range
 };
 
-// Cross-layer prefetch: the grid reads the two regions (as one concatenated range, split evenly over
-// the blocks, 4 KiB per block pass) so that their lines are filled into the memory-side cache, and
-// discards the data. 8 loads per thread are in flight at a time.
-__global__ __launch_bounds__(kBlock) void k_prefetch(Prefetch pf) {
-  const uint64_t total = pf.bytes[0] + pf.bytes[1];
-  const uint64_t per = ((total + gridDim.x - 1) / gridDim.x + 4095) & ~(uint64_t)4095;
-  const uint64_t lo = (uint64_t)blockIdx.x * per, hi = lo + per < total ? lo + per : total;
-  uint32_t acc = 0;
-  for (uint64_t base = lo; base < hi; base += 8 * 4096) {
-    uint4 v[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint64_t off = base + (uint64_t)i * 4096 + threadIdx.x * 16;
-      if (off + 16 > hi) off = lo;  // past the range: re-read its first line
-      const uint8_t* src = off < pf.bytes[0] ? pf.ptr[0] + off : pf.ptr[1] + (off - pf.bytes[0]);
-      v[i] = *reinterpret_cast<const uint4*>(src);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc ^= v[i].x ^ v[i].w;
-  }
-  asm volatile("" ::"v"(acc));  // keeps the loads
-}
-
 LayerArgs make_args(const Geometry& g, const LayerPtrs& p, const Workspace& ws) {
   LayerArgs a;
   a.H = g.H; a.I = g.I; a.E = g.E; a.K = g.K; a.NE = g.NE; a.has_shared = g.has_shared; a.form = g.form;
@@ -1381,12 +1358,6 @@ hipError_t launch_down(const Geometry& g, const LayerPtrs& p, int T, const Works
   switch (g.I) { BQ_FOR_I(BQ_CASE) }
 #undef BQ_CASE
   return hipErrorInvalidValue;
-}
-
-hipError_t launch_prefetch(const Prefetch& pf, int blocks, hipStream_t s) {
-  if (pf.bytes[0] + pf.bytes[1] == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_prefetch, dim3(blocks), dim3(kBlock), 0, s, pf);
-  return hipGetLastError();
 }
 
 hipError_t launch_topk(const Geometry& g, int T, const Workspace& ws, int32_t* idx, float* w, float* sg,

@@ -84,14 +84,6 @@ extern "C" {
  * differ only by rounding. The prefill GEMMs ignore the flag. */
 #define MOE_FLAG_DEQUANT_LITERAL 1
 #define MOE_FLAG_DEQUANT_NAIVE 2
-/* Cross-layer prefetch in moe_stack_forward (set on layers[0]; other entry points ignore it): the
- * idea of reading the next layer's weights ahead of use, from the page "300b on 32gb MoE-streaming
- * findings + optimisations" (its summary of optimisations), recast for HBM: while layer l runs, a
- * side stream reads layer l+1's router and shared expert, so that they come from MI355X's 256 MB
- * memory-side cache. The first such call on a
- * device creates the side stream and two events, which live until the process ends; make that
- * call outside stream capture. Calls that overlap on one device share the side stream. */
-#define MOE_FLAG_PREFETCH_NEXT 4
 
 /* One MoE layer.
  *   hidden H, inter I: powers of two with 256 <= H <= 8192 and 64 <= I <= 2048. bits 2 or 4 with
@@ -102,8 +94,8 @@ extern "C" {
  *   shared_blob_dev and shared_gate_dev: the shared expert's blob and its gate vector (bf16 [H]).
  *   Required when has_shared is 1, ignored when it is 0.
  *   router_dev: bf16 [E][H] row-major; logit e = row e . x, with no bias.
- *   flags: 0, MOE_FLAG_DEQUANT_LITERAL or MOE_FLAG_DEQUANT_NAIVE (the latter two affine only),
- *   optionally or-ed with MOE_FLAG_PREFETCH_NEXT (other values: MOE_EUNSUPPORTED). */
+ *   flags: 0, MOE_FLAG_DEQUANT_LITERAL or MOE_FLAG_DEQUANT_NAIVE (the latter two affine only;
+ *   other values: MOE_EUNSUPPORTED). */
 typedef struct moe_layer_t {
   int32_t hidden;
   int32_t inter;
@@ -225,7 +217,8 @@ int moe_layer_forward_timed(const moe_layer_t* layer, const float* x_dev, const 
  *   u_l = h_l for l = 0, u_l = h_l / sqrt(mean(h_l^2) + eps) for l >= 1 (unit-weight RMS norm);
  *   h_{l+1} = h_l + MoE_l(u_l), where the router, experts and shared gate of layer l all read u_l.
  * out_dev = h_L, fp32 [T][H]. layers is a host array of L descriptors. All layers must share
- * H, I, E, K, bits, group and has_shared. idx_out_dev int32 [L][T][K] may be NULL. */
+ * H, I, E, K, bits, group, flags and has_shared (MOE_EINVAL otherwise, before any launch).
+ * idx_out_dev int32 [L][T][K] may be NULL. */
 int moe_stack_forward(const moe_layer_t* layers, int L, float eps, const float* x_dev, int T, float* out_dev,
                       int32_t* idx_out_dev, void* ws_dev, size_t ws_bytes, void* stream);
 

@@ -171,16 +171,10 @@ class LayerResult:
     margin: float  # fp64 gap between the K-th and (K+1)-th largest logit (inf when K == E)
 
 
-def layer(x, res, router, gate_vec, get_expert, K: int, group: int, shared_expert=None,
-          force_idx=None) -> LayerResult:
-    """One MoE layer for one token.
-
-    get_expert(e) returns expert e's canonical arrays. force_idx, when given, replaces the
-    top-K choice. Tests use it only at near-ties, where the fp64 margin is below the bound of
-    the GPU's rounding, so that both sides follow the same branch afterwards.
-    """
+def layer(x, res, router, gate_vec, get_expert, K: int, group: int, shared_expert=None) -> LayerResult:
+    """One MoE layer for one token. get_expert(e) returns expert e's canonical arrays."""
     logits = router_logits(router, x)
-    idx = topk(logits, K) if force_idx is None else np.asarray(force_idx, dtype=np.int32)
+    idx = topk(logits, K)
     order = np.sort(logits)[::-1]
     margin = float(order[K - 1] - order[K]) if K < len(order) else float("inf")
     w = route_weights(logits, idx)
@@ -199,32 +193,23 @@ def layer(x, res, router, gate_vec, get_expert, K: int, group: int, shared_exper
 @dataclass
 class StackResult:
     out: np.ndarray  # h_L [H]
-    idx: np.ndarray  # [L][K] choices the oracle followed
-    near_ties: list  # (layer, oracle idx, followed idx, max logit gap) where a near-tie choice was followed
+    idx: np.ndarray  # [L][K] top-K per layer
+    margin: np.ndarray  # [L] fp64 gap between the K-th and (K+1)-th logit per layer
 
 
-def stack(x, layers, K: int, group: int, eps: float, follow=None, tie_bound: float = 0.0) -> StackResult:
+def stack(x, layers, K: int, group: int, eps: float) -> StackResult:
     """A stack of MoE layers for one token (GN+ summary, "Deferred GPU Expert Compute": combine, norm
     and residual feed the next layer). h_0 = x; layer l reads u_l = h_l for l = 0 and
     u_l = rmsnorm(h_l) for l >= 1, and h_{l+1} = h_l + MoE_l(u_l).
 
-    layers[l] = (router, gate_vec, get_expert, shared_expert). When follow[l] (another
-    implementation's top-K at layer l) differs from the oracle's choice, the oracle adopts it only
-    if every rank's logit differs from the oracle's by at most tie_bound (a near-tie under that
-    implementation's rounding). Otherwise it keeps its own choice and the caller sees the
-    mismatch in .idx.
+    layers[l] = (router, gate_vec, get_expert, shared_expert).
     """
     h = np.asarray(x, dtype=np.float64)
-    idx_all, ties = [], []
+    idx_all, margins = [], []
     for l, (router, gate_vec, get_expert, shared) in enumerate(layers):
         u = h if l == 0 else rmsnorm(h, eps)
         r = layer(u, h, router, gate_vec, get_expert, K, group, shared_expert=shared)
-        if follow is not None and list(follow[l]) != list(r.idx):
-            f = np.asarray(follow[l], dtype=np.int32)
-            gap = float(np.max(np.abs(r.logits[f] - r.logits[r.idx])))
-            if len(set(f.tolist())) == K and gap <= tie_bound:
-                ties.append((l, list(r.idx), list(f), gap))
-                r = layer(u, h, router, gate_vec, get_expert, K, group, shared_expert=shared, force_idx=f)
         idx_all.append(r.idx)
+        margins.append(r.margin)
         h = r.out
-    return StackResult(h, np.stack(idx_all), ties)
+    return StackResult(h, np.stack(idx_all), np.asarray(margins))

@@ -3,6 +3,8 @@ host generator (never by the GPU path)."""
 from __future__ import annotations
 
 import functools
+import multiprocessing
+from concurrent.futures import ProcessPoolExecutor
 
 import numpy as np
 
@@ -38,12 +40,63 @@ class Reference:
     def expert(self, e: int):
         return self._experts(e)
 
-    def token(self, x, res=None, force_idx=None) -> oracle.LayerResult:
+    def token(self, x, res=None) -> oracle.LayerResult:
         x = np.asarray(x, dtype=np.float64)
         res = x if res is None else np.asarray(res, dtype=np.float64)
         return oracle.layer(x, res, self.router, self.gate, self.expert, self.w.top_k, self.w.group,
-                            shared_expert=self.shared, force_idx=force_idx)
+                            shared_expert=self.shared)
 
     def expert_out(self, x, e: int):
         ex = self.shared if e == synth.SHARED else self.expert(e)
         return oracle.expert(np.asarray(x, dtype=np.float64), ex, self.w.group)
+
+
+def spread(N: int, n: int) -> list:
+    """n token positions spread evenly over 0..N-1, both ends included."""
+    return sorted({int(round(v)) for v in np.linspace(0, N - 1, n)})
+
+
+def check_topk_all(ref: Reference, xs, idx_gpu, what="token"):
+    """Every token's top-K against oracle.topk of the oracle's fp64 router logits. A mismatch fails
+    and names the fp64 margin (K-th minus (K+1)-th logit) at that decision."""
+    K = ref.w.top_k
+    bad = []
+    for t in range(len(xs)):
+        lg = oracle.router_logits(ref.router, np.asarray(xs[t], dtype=np.float64))
+        want = oracle.topk(lg, K)
+        if list(idx_gpu[t]) != list(want):
+            order = np.sort(lg)[::-1]
+            margin = float(order[K - 1] - order[K]) if K < len(order) else float("inf")
+            bad.append(f"{what} {t}: gpu {list(idx_gpu[t])} oracle {list(want)} fp64 margin {margin:.3e}")
+    assert not bad, f"{len(bad)} top-K mismatches: " + "; ".join(bad[:8])
+
+
+_STACK_REFS = {}
+
+
+def _one_thread():
+    # set before the worker first loads the oracle library, whose OpenMP runtime reads it once
+    import os
+    os.environ["OMP_NUM_THREADS"] = "1"
+
+
+def _stack_token(args):
+    name, n_layers, x = args
+    w = synth.WORKLOADS[name]
+    if name not in _STACK_REFS:
+        _STACK_REFS[name] = [Reference(w, l, cache=1) for l in range(n_layers)]
+    layers = [(r.router, r.gate, r.expert, r.shared) for r in _STACK_REFS[name]]
+    return oracle.stack(x, layers, w.top_k, w.group, STACK_EPS)
+
+
+STACK_EPS = 1e-6
+
+
+def stack_oracle_parallel(name: str, n_layers: int, xs, workers: int = 8):
+    """oracle.stack for several tokens of a named workload, one token per task in single-threaded
+    CPU-only worker processes (spawned, so they never touch the GPU). Returns the pool and the
+    futures, so the caller can run GPU work meanwhile; it shuts the pool down."""
+    ctx = multiprocessing.get_context("spawn")
+    pool = ProcessPoolExecutor(max_workers=min(workers, len(xs)), mp_context=ctx, initializer=_one_thread)
+    futs = [pool.submit(_stack_token, (name, n_layers, np.asarray(x, dtype=np.float64))) for x in xs]
+    return pool, futs

@@ -143,6 +143,7 @@ def _layer(**kw):
     (dict(shared_gate=FAKE + 2), bq.MOE_EINVAL),
     (dict(flags=3), bq.MOE_EUNSUPPORTED),
     (dict(flags=-1), bq.MOE_EUNSUPPORTED),
+    (dict(flags=4), bq.MOE_EUNSUPPORTED),
     (dict(flags=7), bq.MOE_EUNSUPPORTED),
     (dict(flags=8), bq.MOE_EUNSUPPORTED),
     (dict(bits=2, group=32), bq.MOE_EUNSUPPORTED),
@@ -196,6 +197,13 @@ def test_call_validation():
     assert sneed > need
     assert L.moe_stack_forward(arr, 2, 1e-6, FAKE, 1, FAKE + 4096, None, FAKE, sneed - 1, None) == bq.MOE_ENOSPC
     assert L.moe_stack_forward(arr, 0, 1e-6, FAKE, 1, FAKE + 4096, None, FAKE, sneed, None) == bq.MOE_EINVAL
+    # layers that differ in format or dequant form are refused before any launch: an affine layer 0
+    # with an MXFP4 layer 1 would otherwise read layer 1's pool with affine offsets
+    mx = _layer(group=32, bits=4, expert_stride=6_684_672 + 256)
+    for second in (mx, _layer(flags=1), _layer(flags=2)):
+        arr = (bq.moe_layer_t * 2)(layer, second)
+        assert L.moe_stack_forward(arr, 2, 1e-6, FAKE, 1, FAKE + 4096, None, FAKE, 1 << 30, None) == bq.MOE_EINVAL
+        assert "group" in bq.moe_last_error()
 
 
 def test_workspace_monotone():

@@ -13,7 +13,7 @@ import bit_quantized_expert_gemv_amd as bq
 import oracle
 import synth
 from synth.gpu_layers import DeviceLayer
-from tests._ref import Reference, assert_close
+from tests._ref import Reference, assert_close, check_topk_all, spread
 
 pytestmark = pytest.mark.gpu
 
@@ -167,6 +167,53 @@ def test_expert_ffn_invalid_index_is_nan_not_a_fault(tiny):
     assert torch.isfinite(y[0, 0]).all() and torch.isnan(y[0, 1]).all() and torch.isfinite(y[0, 2]).all()
 
 
+@pytest.mark.parametrize("T", [1, 64, 2048])
+def test_expert_ffn_checked_error_word(dec4, T):
+    """moe_expert_ffn_checked: out-of-range indices (past E and negative) set the caller's error
+    word to MOE_EINVAL and give NaN outputs in their slots only; the other slots, and a clean call,
+    match the oracle with the word left at zero. T=1 takes the decode kernels, 64 and 2048 the
+    prefill path."""
+    L, ref = dec4
+    w = L.w
+    _log(f"{w.name}: checked expert FFN, T={T}")
+    x = _x(w, 0, T)
+    xs = x.cpu().numpy().astype(np.float64)
+    rng = np.random.default_rng(T)
+    idx_np = np.stack([rng.choice(w.n_experts, w.top_k, replace=False) for _ in range(T)]).astype(np.int32)
+    bad = {(0, 1): w.n_experts + 5}
+    if T > 1:
+        bad[(T // 2, 0)] = -1
+        bad[(T - 1, 2)] = 1 << 30
+    idx_bad = idx_np.copy()
+    for (t, k), v in bad.items():
+        idx_bad[t, k] = v
+    ws, n = _ws(L.desc, T)
+    NE = w.top_k + 1
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    y = torch.empty(T, NE, w.hidden, dtype=torch.float32, device="cuda")
+    bq.moe_expert_ffn_checked(L.desc, x, T, torch.from_numpy(idx_np).cuda(), y, ws, n, err)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    y_clean = y.cpu().numpy()
+    err.zero_()
+    y.fill_(0.0)
+    bq.moe_expert_ffn_checked(L.desc, x, T, torch.from_numpy(idx_bad).cuda(), y, ws, n, err)
+    torch.cuda.synchronize()
+    assert err.item() == bq.MOE_EINVAL
+    yb = y.cpu().numpy()
+    for (t, k) in bad:
+        assert np.isnan(yb[t, k]).all(), f"slot ({t}, {k}) not NaN"
+    good = np.ones((T, NE), dtype=bool)
+    for (t, k) in bad:
+        good[t, k] = False
+    assert np.isfinite(yb[good]).all()
+    assert np.array_equal(yb[good], y_clean[good]), "valid slots changed when another slot was invalid"
+    for t in sorted({0, T // 2, T - 1}):
+        for k in range(NE):
+            e = synth.SHARED if k == w.top_k else int(idx_np[t, k])
+            assert_close(y_clean[t, k], ref.expert_out(xs[t], e), f"y[{t}][{k}]")
+
+
 # ---- the fused layer -----------------------------------------------------------------------------
 
 @pytest.mark.parametrize("which,t0,T", [("tiny", 0, 1), ("tiny", 1, 24), ("dec4", 0, 1), ("dec4", 500, 4),
@@ -197,7 +244,8 @@ def test_layer_forward_residual_separate(tiny):
 @pytest.mark.parametrize("which", ["dec4", "dec2"])
 def test_decode_sequence_graph(which, request):
     """The benchmark's launch configuration: the tokens as back-to-back T=1 calls captured in one
-    HIP graph. Sampled tokens are checked against the oracle, and two replays must agree bitwise."""
+    HIP graph. Every token's top-K is checked against the oracle's, outputs on 32 spread tokens, and
+    two replays must agree bitwise."""
     L, ref = request.getfixturevalue(which)
     w = L.w
     N = w.tokens
@@ -223,9 +271,9 @@ def test_decode_sequence_graph(which, request):
     assert torch.equal(out, first) and torch.equal(idx, first_idx), "replays differ"
     xs = X.cpu().numpy().astype(np.float64)
     on, ix = out.cpu().numpy(), idx.cpu().numpy()
-    for t in (0, 1, N // 2, N - 2, N - 1):
+    check_topk_all(ref, xs, ix)
+    for t in spread(N, 32):
         r = ref.token(xs[t])
-        assert list(ix[t]) == list(r.idx), f"token {t}"
         assert_close(on[t], r.out, f"out[{t}]")
 
 
@@ -280,6 +328,42 @@ def test_duplicate_router_rows_tie_to_lower_index(gpu_device):
     tied = sorted({best, 2, 5})
     assert list(r.idx) == tied[:2] and list(idx[0]) == tied[:2]
     assert_close(out[0], r.out)
+
+
+@pytest.mark.parametrize("T", [1, 4, 64])
+def test_topk_low_bit_tie_break(gpu_device, T):
+    """Logits equal in their upper 32 bits: row a is row b with one bf16 ulp more at an element
+    where x is 1e-10, so the two fp64 logits differ only far below 2^-20 relative; row c duplicates
+    row b exactly. The order must be a, then the lower of b and c (T=1 and T=4 take the decode
+    routers, T=64 the prefill router)."""
+    w = TINY
+    L = DeviceLayer(w)
+    ref = Reference(w)
+    x = _x(w, 0, 1)[0].cpu().numpy().copy()
+    R = ref.router.copy()
+    lg = oracle.router_logits(R, x.astype(np.float64))
+    b = int(np.argmax(lg))
+    a_row, c_row = [r for r in range(w.n_experts) if r != b][:2]
+    Rb = synth.bf16_to_f32(R[b])
+    j = int(np.flatnonzero(Rb > 0)[0])
+    x[j] = np.float32(1e-10)
+    R[a_row] = R[b]
+    R[a_row, j] = R[b, j] + 1  # one ulp larger in magnitude, and positive
+    R[c_row] = R[b]
+    ref.router = R
+    L.router.copy_(torch.from_numpy(R.view(np.int16)))
+    xd = x.astype(np.float64)
+    lg = oracle.router_logits(R, xd)
+    hi = lambda v: np.float64(v).view(np.uint64) >> np.uint64(32)
+    assert lg[a_row] > lg[b] == lg[c_row] and hi(lg[a_row]) == hi(lg[b]), "the case must tie in the upper 32 bits"
+    want = [a_row, min(b, c_row)]
+    r = ref.token(xd)
+    assert list(r.idx) == want
+    X = torch.from_numpy(np.tile(x, (T, 1))).cuda()
+    out, idx = _forward(L, X)
+    for t in range(T):
+        assert list(idx[t]) == want, f"token {t}: {list(idx[t])} vs {want}"
+        assert_close(out[t], r.out, f"out[{t}]")
 
 
 def test_bitwise_determinism(dec4):

@@ -15,7 +15,7 @@ import bit_quantized_expert_gemv_amd as bq
 import oracle
 import synth
 from synth.gpu_layers import DeviceLayer
-from tests._ref import Reference, assert_close
+from tests._ref import Reference, assert_close, check_topk_all, spread
 
 pytestmark = pytest.mark.gpu
 
@@ -109,15 +109,15 @@ def test_mx_layer_forward(which, t0, T, request):
     bq.moe_layer_forward(L.desc, x, x, T, out, idx, ws, n)
     torch.cuda.synchronize()
     on, ix, xs = out.cpu().numpy(), idx.cpu().numpy(), x.cpu().numpy().astype(np.float64)
-    for t in (range(T) if T <= 24 else (0, 1, T // 2, T - 1)):
+    check_topk_all(ref, xs, ix)
+    for t in (range(T) if T <= 24 else spread(T, 16)):
         r = ref.token(xs[t])
-        assert list(ix[t]) == list(r.idx), f"token {t0 + t}: idx {ix[t]} vs {r.idx} (margin {r.margin:.3e})"
         assert_close(on[t], r.out, f"out[{t0 + t}]")
 
 
 def test_mx_decode_sequence_graph(decmx):
-    """The benchmark's launch configuration: back-to-back T=1 calls in one HIP graph; sampled tokens
-    against the oracle, and two replays agree bitwise."""
+    """The benchmark's launch configuration: back-to-back T=1 calls in one HIP graph. Every token's
+    top-K against the oracle's, outputs on 32 spread tokens, and two replays agree bitwise."""
     L, ref = decmx
     w = L.w
     N = w.tokens
@@ -141,7 +141,7 @@ def test_mx_decode_sequence_graph(decmx):
     assert torch.equal(out, first) and torch.equal(idx, first_idx), "replays differ"
     xs = X.cpu().numpy().astype(np.float64)
     on, ix = out.cpu().numpy(), idx.cpu().numpy()
-    for t in (0, 1, N // 2, N - 1):
+    check_topk_all(ref, xs, ix)
+    for t in spread(N, 32):
         r = ref.token(xs[t])
-        assert list(ix[t]) == list(r.idx), f"token {t}"
         assert_close(on[t], r.out, f"out[{t}]")

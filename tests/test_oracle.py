@@ -471,9 +471,8 @@ def test_stack_two_layers_bruteforce():
     r = oracle.stack(x, layers, w.top_k, w.group, 1e-6)
     assert np.array_equal(r.idx, np.stack([top0, top1]))
     assert np.allclose(r.out, out, rtol=1e-12, atol=1e-12)
-    # a followed choice is adopted only within the tie bound
-    alt = [list(r.idx[0]), list(r.idx[1][::-1])]
-    r2 = oracle.stack(x, layers, w.top_k, w.group, 1e-6, follow=alt, tie_bound=0.0)
-    assert np.array_equal(r2.idx, r.idx) and not r2.near_ties
-    r3 = oracle.stack(x, layers, w.top_k, w.group, 1e-6, follow=alt, tie_bound=1e9)
-    assert list(r3.idx[1]) == alt[1] and len(r3.near_ties) == 1
+    # per-layer margin: the gap between the K-th and (K+1)-th logit of that layer's own input
+    u1_lg = np.sort(_bf(per[1][0]) @ u1)[::-1]
+    x_lg = np.sort(_bf(per[0][0]) @ x)[::-1]
+    K = w.top_k
+    assert np.allclose(r.margin, [x_lg[K - 1] - x_lg[K], u1_lg[K - 1] - u1_lg[K]], rtol=1e-12, atol=1e-15)
