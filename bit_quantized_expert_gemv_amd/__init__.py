@@ -19,6 +19,7 @@ from ._binding import (  # noqa: F401
     MOE_ROUTER_CERTIFIED_MIN_TOKENS,
     MOE_FLAG_DEQUANT_LITERAL,
     MOE_FLAG_DEQUANT_NAIVE,
+    MOE_NOALLOC_SCRATCH_BYTES,
     SIGNATURES,
     MoeError,
     lib,
@@ -31,6 +32,7 @@ from ._binding import (  # noqa: F401
     moe_expert_ffn_checked,
     moe_last_error,
     moe_layer_forward,
+    moe_layer_forward_noalloc,
     moe_layer_forward_timed,
     moe_layer_t,
     moe_pack_expert,

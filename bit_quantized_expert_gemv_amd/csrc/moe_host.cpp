@@ -317,6 +317,20 @@ size_t needed_ws(const Geometry& g, int T) {
   }
   return n;
 }
+
+// Argument checks shared by moe_layer_forward and moe_layer_forward_noalloc (no HIP call). Returns
+// MOE_OK with T == 0 for the empty call.
+int check_layer_call(const moe_layer_t* layer, const float* x, const float* residual, int T, float* out, Geometry* g) {
+  int rc = check_layer(layer, g);
+  if (rc) return rc;
+  if (T < 0) return fail(MOE_EINVAL, "T must be >= 0");
+  if (T == 0) return ok();
+  if ((rc = check_act(x, "x"))) return rc;
+  if ((rc = check_act(out, "out"))) return rc;
+  if (residual == nullptr) return fail(MOE_EINVAL, "residual is NULL");
+  if (x == out) return fail(MOE_EINVAL, "x and out may not alias");
+  return check_prefill_size(*g, T);
+}
 }  // namespace
 
 int moe_router(const moe_layer_t* layer, const float* x, int T, int32_t* idx, float* w, float* shared_g,
@@ -387,14 +401,8 @@ int moe_layer_forward(const moe_layer_t* layer, const float* x, const float* res
 int moe_layer_forward_timed(const moe_layer_t* layer, const float* x, const float* residual, int T, float* out,
                             int32_t* idx_out, void* ws, size_t ws_bytes, void* stream, void* const* events) {
   Geometry g;
-  int rc = check_layer(layer, &g);
-  if (rc) return rc;
-  if (T < 0) return fail(MOE_EINVAL, "T must be >= 0");
-  if (T == 0) return ok();
-  if ((rc = check_act(x, "x"))) return rc;
-  if ((rc = check_act(out, "out"))) return rc;
-  if (residual == nullptr) return fail(MOE_EINVAL, "residual is NULL");
-  if (x == out) return fail(MOE_EINVAL, "x and out may not alias");
+  int rc = check_layer_call(layer, x, residual, T, out, &g);
+  if (rc || T == 0) return rc;
   if (ws == nullptr || !aligned(ws, 256)) return fail(MOE_EINVAL, "workspace must be non-NULL and 256-byte aligned");
   if (ws_bytes < needed_ws(g, T)) return fail(MOE_ENOSPC, "workspace smaller than moe_workspace_bytes()");
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -407,7 +415,6 @@ int moe_layer_forward_timed(const moe_layer_t* layer, const float* x, const floa
     }
     return e;
   };
-  if ((rc = check_prefill_size(g, T))) return rc;
   if (use_prefill(g, T)) {
     // many kernels: events[0] and events[5] are recorded around all of them
     hipError_t e = hipSuccess;
@@ -423,6 +430,20 @@ int moe_layer_forward_timed(const moe_layer_t* layer, const float* x, const floa
   if (e == hipSuccess) e = launch_gateup(g, p, x, T, W, nullptr, idx_out, true, nullptr, s, ev(1));
   if (e == hipSuccess) e = launch_down(g, p, T, W, W.idx, residual, out, nullptr, s, ev(2));
   return hip_status(e);
+}
+
+int moe_layer_forward_noalloc(const moe_layer_t* layer, const float* x, const float* residual, int T, float* out,
+                              int32_t* idx_out, void* stream) {
+  Geometry g;
+  int rc = check_layer_call(layer, x, residual, T, out, &g);
+  if (rc || T == 0) return rc;
+  if (needed_ws(g, T) > (size_t)MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(MOE_ENOSPC, "this layer and T need more workspace than MOE_NOALLOC_SCRATCH_BYTES; call "
+                            "moe_layer_forward with a workspace of moe_workspace_bytes()");
+  void* ws = nullptr;
+  const hipError_t e = noalloc_scratch(&ws);
+  if (e != hipSuccess) return hip_status(e);
+  return moe_layer_forward_timed(layer, x, residual, T, out, idx_out, ws, MOE_NOALLOC_SCRATCH_BYTES, stream, nullptr);
 }
 
 int moe_stack_forward(const moe_layer_t* layers, int L, float eps, const float* x, int T, float* out,

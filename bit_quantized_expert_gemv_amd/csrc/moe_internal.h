@@ -115,6 +115,9 @@ hipError_t launch_topk(const Geometry& g, int T, const Workspace& ws, int32_t* i
                        double* logits_out, int32_t* idx_b, hipStream_t s);
 hipError_t launch_combine(const Geometry& g, int T, const float* residual, const float* y, const float* w,
                           const float* sg, float* out, hipStream_t s);
+// Device address of the no-allocation entry point's scratch array (MOE_NOALLOC_SCRATCH_BYTES) on
+// the current device, looked up on the first call per device and cached.
+hipError_t noalloc_scratch(void** out);
 hipError_t launch_dequant(const Geometry& g, const uint8_t* blob, int matrix, int out_dtype, void* out, hipStream_t s);
 hipError_t launch_pack(int H, int I, int bits, int G, const moe_expert_arrays_t* a, uint8_t* blob, hipStream_t s);
 

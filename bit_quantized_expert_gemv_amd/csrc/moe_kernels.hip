@@ -31,6 +31,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "moe_internal.h"
 
@@ -1426,6 +1427,35 @@ hipError_t launch_pack(int H, int I, int bits, int G, const moe_expert_arrays_t*
                        arr->bias[m], reinterpret_cast<uint32_t*>(blob + 3 * code_bytes + m * ngroups * 4));
   }
   return hipGetLastError();
+}
+
+}  // namespace bqmoe
+
+// Workspace of moe_layer_forward_noalloc: a fixed device array, one copy per GPU, held until the
+// process ends. Host code must not pass `scratch` itself to a kernel (in host code the name is a
+// stand-in, not a device address); noalloc_scratch looks up each device's address once.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace bqmoe {
+
+hipError_t noalloc_scratch(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace bqmoe

@@ -212,6 +212,18 @@ int moe_layer_forward_timed(const moe_layer_t* layer, const float* x_dev, const 
                             float* out_dev, int32_t* idx_out_dev, void* ws_dev, size_t ws_bytes, void* stream,
                             void* const* events);
 
+/* moe_layer_forward for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. It takes no workspace and allocates
+ * nothing. Its workspace is a fixed device array of MOE_NOALLOC_SCRATCH_BYTES inside the library,
+ * one per GPU, held until the process ends; the first call on a device looks up that device's
+ * address. Same kernels and results as moe_layer_forward. A layer and T whose moe_workspace_bytes()
+ * exceeds MOE_NOALLOC_SCRATCH_BYTES return MOE_ENOSPC before any HIP call. Every call on one GPU
+ * shares that GPU's array, so calls that overlap on one GPU (other streams, other threads) race;
+ * calls in order on one stream are safe. Nothing in the array needs clearing between calls. */
+#define MOE_NOALLOC_SCRATCH_BYTES 33554432
+int moe_layer_forward_noalloc(const moe_layer_t* layer, const float* x_dev, const float* residual_dev, int T,
+                              float* out_dev, int32_t* idx_out_dev, void* stream);
+
 /* A stack of L layers, decode only ("Deferred GPU Expert Compute": combine + norm + residual on the
  * GPU hand off to the next layer). With h_0 = x:
  *   u_l = h_l for l = 0, u_l = h_l / sqrt(mean(h_l^2) + eps) for l >= 1 (unit-weight RMS norm);

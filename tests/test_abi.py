@@ -206,6 +206,22 @@ def test_call_validation():
         assert "group" in bq.moe_last_error()
 
 
+def test_noalloc_validation():
+    """The no-allocation entry point checks its arguments and its fixed scratch size before any HIP
+    call, so these run without a GPU."""
+    L = bq.lib()
+    layer = _layer()
+    ref = ctypes.byref(layer)
+    assert L.moe_layer_forward_noalloc(ref, None, None, 0, None, None, None) == bq.MOE_OK
+    assert L.moe_layer_forward_noalloc(ref, FAKE + 4, FAKE, 1, FAKE + 4096, None, None) == bq.MOE_EINVAL
+    assert L.moe_layer_forward_noalloc(ref, FAKE, FAKE, 1, FAKE, None, None) == bq.MOE_EINVAL
+    assert L.moe_layer_forward_noalloc(ref, FAKE, FAKE, -1, FAKE + 4096, None, None) == bq.MOE_EINVAL
+    big = next(T for T in range(64, 4096, 16) if bq.moe_workspace_bytes(layer, T) > bq.MOE_NOALLOC_SCRATCH_BYTES)
+    assert bq.moe_workspace_bytes(layer, big - 16) <= bq.MOE_NOALLOC_SCRATCH_BYTES
+    assert L.moe_layer_forward_noalloc(ref, FAKE, FAKE, big, FAKE + (1 << 32), None, None) == bq.MOE_ENOSPC
+    assert "MOE_NOALLOC_SCRATCH_BYTES" in bq.moe_last_error()
+
+
 def test_workspace_monotone():
     layer = _layer()
     sizes = [bq.moe_workspace_bytes(layer, t) for t in (1, 2, 64, 2048)]
