@@ -144,6 +144,7 @@ PrefillWorkspace carve_prefill_impl(const Geometry& g, int T, void* base, size_t
   const bool mx = g.form == 3;
   w.xq = mx ? nullptr : c.take<uint16_t>(t * g.H);
   w.xs = mx ? nullptr : c.take<float>(t * (g.H / 64));
+  w.xu = mx ? nullptr : c.take<float>(t);
   w.x8 = mx ? c.take<uint8_t>(3 * t * g.H) : nullptr;
   w.xsc = mx ? c.take<uint8_t>(3 * t * (g.H / 32)) : nullptr;
   w.hist = c.take<int32_t>(((N + 255) / 256) * g.E);
@@ -156,6 +157,7 @@ PrefillWorkspace carve_prefill_impl(const Geometry& g, int T, void* base, size_t
   w.perm = c.take<int32_t>(N);
   w.hq = mx ? nullptr : c.take<uint16_t>(R * g.I);
   w.hs = mx ? nullptr : c.take<float>(R * (g.I / 64));
+  w.hu = mx ? nullptr : c.take<float>(R * (g.I / 64));
   w.h32 = mx ? c.take<float>(R * g.I) : nullptr;
   w.h8 = mx ? c.take<uint8_t>(3 * R * g.I) : nullptr;
   w.hsc = mx ? c.take<uint8_t>(3 * R * (g.I / 32)) : nullptr;

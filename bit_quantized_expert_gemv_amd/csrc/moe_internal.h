@@ -49,7 +49,8 @@ struct Workspace {
 struct PrefillWorkspace {
   Workspace layer;  // logits [T][E+1], idx [T][K], w [T][K], g [T]; h and u unused
   uint16_t* xq;     // [T][H] fp16 activations (each 8-block stored in the order 0,2,4,6,1,3,5,7)
-  float* xs;        // [T][H/64] group sums of the fp16 activations
+  float* xs;        // [T][H/64] group sums of the fp16 activations (scaled, like xq)
+  float* xu;        // [T] per-token power of two 2^-e that undoes the scaling of xq and xs
   int32_t* hist;    // [ceil(N/256)][E]
   int32_t* counts;  // [E]
   int32_t* offsets; // [E+1]
@@ -59,7 +60,8 @@ struct PrefillWorkspace {
   int32_t* pos;     // [N] entry -> position
   int32_t* perm;    // [N] position -> entry
   uint16_t* hq;     // [R][I] SwiGLU outputs in fp16 (same 8-block order as xq)
-  float* hs;        // [R][I/64] group sums of the fp16 SwiGLU outputs
+  float* hs;        // [R][I/64] group sums of the fp16 SwiGLU outputs, already scaled back
+  float* hu;        // [R][I/64] per (row, group) power of two 2^-e that undoes the scaling of hq
   float* y;         // [R][H] down outputs
   // MXFP4 layers only (null otherwise): 3-term MXFP8 expansions of the activations and of the
   // SwiGLU outputs (term planes of E4M3 bytes, E8M0 scales per 32), and the fp32 SwiGLU outputs

@@ -25,7 +25,9 @@
 // Per 64-wide group the fp32 MFMA result D = sum q x is finished in the epilogue as
 //   s * D + b * S,   S = sum x over the group (of the fp16 activations the MFMA sees).
 // The activations are rounded to fp16 once (relative 2^-11), which keeps the layer output well
-// inside its error bound.
+// inside its error bound. Before the cast they are scaled by a power of two, so that fp16's range
+// (largest 65504, normal down to 2^-14) never clips them: x per token, the SwiGLU outputs per token
+// and 64-row group. The scale is exact and is undone in the fp32 epilogues.
 //
 // MFMA: v_mfma_f32_32x32x16_f16 with A = activations (32 token rows) and B = codes (32 weight
 // rows). A[i][k] sits in lane i + 32*(k/8), element k%8; B[k][j] in lane j + 32*(k/8), element k%8;
@@ -59,29 +61,67 @@ __device__ __forceinline__ float bf16_val(uint16_t h) { return __uint_as_float((
 __device__ __forceinline__ int perm8(int e) { return (e >> 1) + 4 * (e & 1); }
 
 // ---- 1. activation prep -------------------------------------------------------------------------
-// fp16 copy (8-blocks stored in the order 0,2,4,6,1,3,5,7) and per-64-group sums of the fp16
-// values. Thread i takes 8-block i of the whole [T][H] array: two 16-byte loads, one 16-byte store;
-// the 8 threads of a group add their sums with 3 butterfly steps, in a fixed order.
-__global__ __launch_bounds__(kThreads) void k_prep(int64_t nblk8, const float* __restrict__ x,
-                                                   _Float16* __restrict__ xq, float* __restrict__ xs) {
-  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  const bool live = i < nblk8;  // nblk8 is a multiple of 8, so a group's 8 threads agree
-  const int64_t ib = live ? i : 0;
-  const float4* src = reinterpret_cast<const float4*>(x) + 2 * ib;
-  const float4 a = src[0], b = src[1];
-  const _Float16 h[8] = {(_Float16)a.x, (_Float16)a.y, (_Float16)a.z, (_Float16)a.w,
-                         (_Float16)b.x, (_Float16)b.y, (_Float16)b.z, (_Float16)b.w};
-  if (live) {
-    f16x8_t o;
+// Exponent e of the power of two that brings a largest magnitude m into [2^14, 2^15), inside fp16's
+// range with room to spare (0 for a zero, infinite or NaN m; clamped so that 2^e and 2^-e are
+// normal floats).
+__device__ __forceinline__ int fp16_exponent(float m) {
+  if (!(m > 0.0f) || !(m < INFINITY)) return 0;
+  int k;
+  (void)frexpf(m, &k);  // m in [2^(k-1), 2^k)
+  return min(max(15 - k, -100), 100);
+}
+
+// One block per token: the token's values times 2^e (e from its largest magnitude), as fp16 with
+// each 8-block stored in the order 0,2,4,6,1,3,5,7, the per-64-group sums of those fp16 values,
+// and xu[t] = 2^-e. Thread i takes 8-blocks i, i + 256, ...; the 8 threads of a group add their
+// sums with 3 butterfly steps, in a fixed order.
+constexpr int kPrepPer = 4;  // 8-blocks per thread: hidden <= 8192
+__global__ __launch_bounds__(kThreads) void k_prep(int H, const float* __restrict__ x, _Float16* __restrict__ xq,
+                                                   float* __restrict__ xs, float* __restrict__ xu) {
+  __shared__ float red[kThreads / 64];
+  const int t = blockIdx.x, tid = threadIdx.x, nb = H / 8;
+  const float4* src = reinterpret_cast<const float4*>(x + (size_t)t * H);
+  float4 v[kPrepPer][2];
+  float m = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[perm8(e)] = h[e];
-    reinterpret_cast<f16x8_t*>(xq)[ib] = o;
+  for (int j = 0; j < kPrepPer; ++j) {
+    const int i = tid + j * kThreads;
+    const int ib = i < nb ? i : 0;
+    v[j][0] = src[2 * ib];
+    v[j][1] = src[2 * ib + 1];
+    if (i < nb) {
+      const float4 a = v[j][0], b = v[j][1];
+      m = fmaxf(m, fmaxf(fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))),
+                         fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w)))));
+    }
   }
-  float v = (((float)h[0] + (float)h[1]) + ((float)h[2] + (float)h[3])) +
-            (((float)h[4] + (float)h[5]) + ((float)h[6] + (float)h[7]));
 #pragma unroll
-  for (int m = 1; m < 8; m <<= 1) v += __shfl_xor(v, m, 8);
-  if (live && (i & 7) == 0) xs[i >> 3] = v;
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if ((tid & 63) == 0) red[tid >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const int e = fp16_exponent(m);
+  const float up = ldexpf(1.0f, e);
+  if (tid == 0) xu[t] = ldexpf(1.0f, -e);
+#pragma unroll
+  for (int j = 0; j < kPrepPer; ++j) {
+    const int i = tid + j * kThreads;
+    const bool live = i < nb;  // nb and 256 are multiples of 8, so a group's 8 threads agree
+    const float4 a = v[j][0], b = v[j][1];
+    const _Float16 h[8] = {(_Float16)(a.x * up), (_Float16)(a.y * up), (_Float16)(a.z * up), (_Float16)(a.w * up),
+                           (_Float16)(b.x * up), (_Float16)(b.y * up), (_Float16)(b.z * up), (_Float16)(b.w * up)};
+    if (live) {
+      f16x8_t o;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) o[perm8(q)] = h[q];
+      reinterpret_cast<f16x8_t*>(xq + (size_t)t * H)[i] = o;
+    }
+    float sum = (((float)h[0] + (float)h[1]) + ((float)h[2] + (float)h[3])) +
+                (((float)h[4] + (float)h[5]) + ((float)h[6] + (float)h[7]));
+#pragma unroll
+    for (int msk = 1; msk < 8; msk <<= 1) sum += __shfl_xor(sum, msk, 8);
+    if (live && (i & 7) == 0) xs[(size_t)t * (H / 64) + (i >> 3)] = sum;
+  }
 }
 
 // ---- 2. router GEMM (fp64 MFMA) ---------------------------------------------------------------------
@@ -503,6 +543,7 @@ struct GroupArgs {
   uint64_t off_codes[2], off_sb[2];  // (gate, up) or (down, unused)
   const _Float16* a;                 // activations [rows][KDIM], fp16, 8-blocks permuted
   const float* as;                   // their group sums [rows][KDIM/64]
+  const float* ascale;               // powers of two undoing their scaling: gate/up [T], down [rows][KDIM/64]
   const int32_t* perm;               // routed: position -> entry (t*K + k)
   int K;
   const int32_t* tile_e;
@@ -513,6 +554,7 @@ struct GroupArgs {
   int T;
   _Float16* oh;  // gate/up: SwiGLU outputs [rows][nout] (fp16, 8-blocks permuted), group sums os [rows][nout/64]
   float* os;
+  float* oscale;  // gate/up: [rows][nout/64] powers of two undoing the scaling of oh
   float* oy;  // down: [rows][nout]
   int nout;
   // MXFP4 layers: activations as kMxTerms planes of E4M3 bytes [rows][KDIM] (a_plane bytes apart)
@@ -641,6 +683,9 @@ __global__ __launch_bounds__(kThreads, GATEUP ? BQ_LB_GU : BQ_LB_DOWN) void k_gr
                                                    // [step parity][row][slot ^ swizzle]
   __shared__ float x_lds[GATEUP ? 2 : 1][GATEUP ? 16 : 1][64];  // gate/up: gate results for the up waves
   __shared__ float h_lds[GATEUP ? 2 : 1][kTileM];  // gate/up: per-wave sums of the fp16 SwiGLU outputs
+  __shared__ float hm_lds[GATEUP ? 2 : 1][kTileM]; // gate/up: per-wave largest |SwiGLU output|
+  // powers of two undoing the activations' scaling: gate/up per token row, down per [group][row]
+  __shared__ float u_lds[GATEUP ? kTileM : NG * kTileM];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int c16 = lane & 15, q = lane >> 4;        // MFMA lane: token / row within 16, k slice
@@ -678,6 +723,10 @@ __global__ __launch_bounds__(kThreads, GATEUP ? BQ_LB_GU : BQ_LB_DOWN) void k_gr
   for (int i = tid; i < NG * kTileM; i += kThreads) {
     const int m = i % kTileM, gi = i / kTileM;
     s_lds[i] = g.as[(size_t)arow(m) * NG + gi];
+    if constexpr (!GATEUP) u_lds[i] = g.ascale[(size_t)arow(m) * NG + gi];
+  }
+  if constexpr (GATEUP) {
+    if (tid < kTileM) u_lds[tid] = g.ascale[arow(tid)];
   }
   // this thread's 16-byte activation slot: row tid/8, slot tid%8 of every group
   const int a_row = tid >> 3, a_slot = tid & 7;
@@ -839,13 +888,20 @@ __global__ __launch_bounds__(kThreads, GATEUP ? BQ_LB_GU : BQ_LB_DOWN) void k_gr
       for (int th = 0; th < 2; ++th) {
         if (th < nh) {
           const f16x8_t a0 = a_frag(s, th, G, 0), a1 = a_frag(s, th, G, 1);
+          // down: the group's unscale factors of tokens 16 th + 4 q + e (gate/up undoes its
+          // per-token factor once, in the epilogue)
+          f32x4_t u = {1.0f, 1.0f, 1.0f, 1.0f};
+          if constexpr (!GATEUP) u = *reinterpret_cast<const f32x4_t*>(&u_lds[(k * U + G) * kTileM + 16 * th + 4 * q]);
 #pragma unroll
           for (int rb = 0; rb < 2; ++rb) {
             f32x4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
             d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b[rb][0], d, 0, 0, 0);
             d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b[rb][1], d, 0, 0, 0);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[th][rb][e] = fmaf(sc[rb], d[e], acc[th][rb][e]);
+            for (int e = 0; e < 4; ++e) {
+              if constexpr (GATEUP) acc[th][rb][e] = fmaf(sc[rb], d[e], acc[th][rb][e]);
+              else acc[th][rb][e] = fmaf(sc[rb] * u[e], d[e], acc[th][rb][e]);
+            }
           }
         }
       }
@@ -880,20 +936,54 @@ __global__ __launch_bounds__(kThreads, GATEUP ? BQ_LB_GU : BQ_LB_DOWN) void k_gr
             for (int e = 0; e < 4; ++e) x_lds[wave][8 * th + 4 * rb + e][lane] = acc[th][rb][e];
       }
       __syncthreads();
+      // The up waves finish the SwiGLU in fp32 (undoing the token's activation scaling first), then
+      // cast to fp16 with a power of two per token from the largest |h| over the slab's 64 rows
+      // (both up waves), and keep that factor's inverse for the down projection.
+      const bool active = slab * ROWS_B + wrow < g.nout;  // wave-uniform
+      float hv[2][2][4];
       if (mi == 1) {
-        const bool active = slab * ROWS_B + wrow < g.nout;  // wave-uniform
+#pragma unroll
+        for (int th = 0; th < 2; ++th) {
+          float mx[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float u = u_lds[16 * th + 4 * q + e];
+              const float a = x_lds[wave - 2][8 * th + 4 * rb + e][lane] * u, c = acc[th][rb][e] * u;
+              hv[th][rb][e] = a / (1.0f + expf(-a)) * c;
+              if (active && th < nh) mx[e] = fmaxf(mx[e], fabsf(hv[th][rb][e]));
+            }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+#pragma unroll
+            for (int msk = 8; msk >= 1; msk >>= 1) mx[e] = fmaxf(mx[e], __shfl_xor(mx[e], msk, 16));
+          }
+          if (c16 == 0) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) hm_lds[wave - 2][16 * th + 4 * q + e] = mx[e];
+          }
+        }
+      }
+      __syncthreads();
+      if (mi == 1) {
 #pragma unroll
         for (int th = 0; th < 2; ++th) {
           float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
           if (th < nh) {
+            float up[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int m = 16 * th + 4 * q + e;
+              up[e] = ldexpf(1.0f, fp16_exponent(fmaxf(hm_lds[0][m], hm_lds[1][m])));
+            }
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb) {
               const int row = slab * ROWS_B + wrow + 16 * rb + c16;
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
                 const int m = 16 * th + 4 * q + e;
-                const float a = x_lds[wave - 2][8 * th + 4 * rb + e][lane], c = acc[th][rb][e];
-                const _Float16 h = (_Float16)(a / (1.0f + expf(-a)) * c);
+                const _Float16 h = (_Float16)(hv[th][rb][e] * up[e]);
                 if (active && m < count) g.oh[(size_t)orow(m) * g.nout + (row & ~7) + perm8(row & 7)] = h;
                 part[e] += active ? (float)h : 0.0f;
               }
@@ -914,8 +1004,12 @@ __global__ __launch_bounds__(kThreads, GATEUP ? BQ_LB_GU : BQ_LB_DOWN) void k_gr
       }
       __syncthreads();
       const int col0 = slab * ROWS_B;
-      if (tid < kTileM && tid < count && col0 < g.nout)
-        g.os[(size_t)orow(tid) * (g.nout / 64) + col0 / 64] = h_lds[0][tid] + h_lds[1][tid];
+      if (tid < kTileM && tid < count && col0 < g.nout) {
+        const float down = ldexpf(1.0f, -fp16_exponent(fmaxf(hm_lds[0][tid], hm_lds[1][tid])));
+        const size_t o = (size_t)orow(tid) * (g.nout / 64) + col0 / 64;
+        g.os[o] = (h_lds[0][tid] + h_lds[1][tid]) * down;
+        g.oscale[o] = down;
+      }
     } else {
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
@@ -1527,9 +1621,7 @@ hipError_t launch_prefill(const Geometry& g, const LayerPtrs& p, const float* x,
     hipError_t e = launch_prep_mx(T, 0, T, H, x, w.x8, w.xsc, s);
     if (e != hipSuccess) return e;
   } else {
-    const int64_t nblk8 = (int64_t)T * H / 8;
-    hipLaunchKernelGGL(k_prep, dim3((unsigned)cdiv(nblk8, kThreads)), dim3(kThreads), 0, s, nblk8, x,
-                       reinterpret_cast<_Float16*>(w.xq), w.xs);
+    hipLaunchKernelGGL(k_prep, dim3(T), dim3(kThreads), 0, s, H, x, reinterpret_cast<_Float16*>(w.xq), w.xs, w.xu);
   }
   const bool shared_here = g.has_shared != 0;
   const int32_t* idx = idx_in;
@@ -1564,13 +1656,13 @@ hipError_t launch_prefill(const Geometry& g, const LayerPtrs& p, const float* x,
                        idx, err, w.pos, w.y, w.layer.w, w.layer.g, residual, out, y_out);
     return hipGetLastError();
   }
-  ga.a = reinterpret_cast<const _Float16*>(w.xq); ga.as = w.xs;
-  ga.oh = reinterpret_cast<_Float16*>(w.hq); ga.os = w.hs; ga.nout = I;
+  ga.a = reinterpret_cast<const _Float16*>(w.xq); ga.as = w.xs; ga.ascale = w.xu;
+  ga.oh = reinterpret_cast<_Float16*>(w.hq); ga.os = w.hs; ga.oscale = w.hu; ga.nout = I;
   hipError_t e = dispatch_gateup(g.bits, H, ga, I, T, N, E, true, shared_here, s);
   if (e != hipSuccess) return e;
   // down
   ga.off_codes[0] = g.off_codes[2]; ga.off_sb[0] = g.off_sb[2];
-  ga.a = reinterpret_cast<const _Float16*>(w.hq); ga.as = w.hs;
+  ga.a = reinterpret_cast<const _Float16*>(w.hq); ga.as = w.hs; ga.ascale = w.hu;
   ga.oy = w.y; ga.nout = H;
   e = dispatch_down(g.bits, I, ga, H, T, N, E, true, shared_here, s);
   if (e != hipSuccess) return e;

@@ -15,7 +15,7 @@ import bit_quantized_expert_gemv_amd as bq
 import oracle
 import synth
 from synth.gpu_layers import DeviceLayer
-from tests._ref import Reference, assert_close
+from tests._ref import Reference, assert_close, check_topk_all, spread
 
 pytestmark = pytest.mark.gpu
 
@@ -65,6 +65,37 @@ def test_prefill_tiny_all_tokens(tiny, T):
         assert_close(out[t], r.out, f"out[{t}]")
     counts = np.bincount(idx.reshape(-1), minlength=TINY.n_experts)
     assert counts.sum() == T * TINY.top_k
+
+
+# token t -> factor applied to its synthetic x: far above fp16's largest value (65504), large
+# enough that the SwiGLU outputs pass it while x does not, and far below fp16's normal range
+_RANGE_SCALES = {0: 1e6, 1: 3e3, 2: 1e-6, 5: 2.5e4, 9: 1e-3}
+
+
+@pytest.mark.parametrize("which,T", [("tiny", 64), ("pre4", 100), ("pre4", bq.MOE_ROUTER_CERTIFIED_MIN_TOKENS + 88)])
+def test_prefill_fp16_range(which, T, request):
+    """Prefill casts activations and SwiGLU outputs to fp16 for the MFMAs. Tokens whose x, or whose
+    SwiGLU outputs, lie far outside fp16's range (or deep in its subnormals) must still meet the
+    oracle's bar: every token's top-K, and outputs of the scaled tokens and 16 spread ones."""
+    L, ref = request.getfixturevalue(which)
+    w = L.w
+    _log(f"{w.name}: fp16 range, T={T}")
+    xs = synth.tokens_x(w, 3, T).copy()
+    for t, f in _RANGE_SCALES.items():
+        xs[t] *= np.float32(f)
+    x = torch.from_numpy(xs).cuda()
+    out, idx = _forward(L, x)
+    x64 = xs.astype(np.float64)
+    check_topk_all(ref, x64, idx)
+    big_h = 0.0
+    for t in sorted(set(_RANGE_SCALES) | set(spread(T, 16))):
+        r = ref.token(x64[t])
+        assert np.all(np.isfinite(r.out))
+        if t == 1:
+            ex = ref.expert(int(r.idx[0]))
+            big_h = float(np.max(np.abs(oracle.expert(x64[t], ex, w.group, want_h=True)[1])))
+        assert_close(out[t], r.out, f"out[{t}] (x scaled by {_RANGE_SCALES.get(t, 1.0):g})")
+    assert np.max(np.abs(xs[1])) < 65504 < big_h, "token 1 must keep x inside fp16 and push h past it"
 
 
 def test_prefill_tiny_residual_and_determinism(tiny):
