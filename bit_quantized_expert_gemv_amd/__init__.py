@@ -38,6 +38,7 @@ from ._binding import (  # noqa: F401
     moe_pack_expert,
     moe_pack_expert_device,
     moe_router,
+    moe_router_approx_logits,
     moe_stack_forward,
     moe_stack_workspace_bytes,
     moe_strerror,

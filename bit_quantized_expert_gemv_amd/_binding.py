@@ -46,6 +46,8 @@ SIGNATURES = {
     "moe_expert_ffn": (ctypes.c_int, [ctypes.POINTER(moe_layer_t), c_vp, ctypes.c_int, c_vp, c_vp, c_vp, c_size, c_vp]),
     "moe_expert_ffn_checked": (ctypes.c_int, [ctypes.POINTER(moe_layer_t), c_vp, ctypes.c_int, c_vp, c_vp, c_vp, c_size,
                                               c_vp, c_vp]),
+    "moe_router_approx_logits": (ctypes.c_int, [ctypes.POINTER(moe_layer_t), c_vp, ctypes.c_int, c_vp,
+                                                ctypes.POINTER(ctypes.c_double), c_vp]),
     "moe_combine": (ctypes.c_int, [ctypes.POINTER(moe_layer_t), c_vp, c_vp, c_vp, c_vp, ctypes.c_int, c_vp, c_vp]),
     "moe_layer_forward": (ctypes.c_int, [ctypes.POINTER(moe_layer_t), c_vp, c_vp, ctypes.c_int, c_vp, c_vp, c_vp,
                                          c_size, c_vp]),
@@ -169,6 +171,13 @@ def moe_expert_ffn(layer, x, T, idx, y, ws, ws_bytes, stream=None) -> None:
 def moe_expert_ffn_checked(layer, x, T, idx, y, ws, ws_bytes, err, stream=None) -> None:
     _check(lib().moe_expert_ffn_checked(_ref(layer), ptr(x), T, ptr(idx), ptr(y), ptr(ws), ws_bytes, ptr(err),
                                         stream_handle(stream)), "moe_expert_ffn_checked")
+
+
+def moe_router_approx_logits(layer, x, T, logits, stream=None) -> float:
+    kc = ctypes.c_double(0.0)
+    _check(lib().moe_router_approx_logits(_ref(layer), ptr(x), T, ptr(logits), ctypes.byref(kc), stream_handle(stream)),
+           "moe_router_approx_logits")
+    return kc.value
 
 
 def moe_combine(layer, residual, y, w, shared_g, T, out, stream=None) -> None:

@@ -352,6 +352,21 @@ int moe_router(const moe_layer_t* layer, const float* x, int T, int32_t* idx, fl
   return hip_status(e);
 }
 
+int moe_router_approx_logits(const moe_layer_t* layer, const float* x, int T, double* logits, double* kc,
+                             void* stream) {
+  Geometry g;
+  int rc = check_layer(layer, &g);
+  if (rc) return rc;
+  if (T < 0) return fail(MOE_EINVAL, "T must be >= 0");
+  if (T == 0) return ok();
+  if ((rc = check_act(x, "x"))) return rc;
+  if (logits == nullptr || !aligned(logits, 8)) return fail(MOE_EINVAL, "logits must be non-NULL and 8-byte aligned");
+  double k = 0.0;
+  const hipError_t e = launch_router_approx(g, ptrs_of(layer), x, T, logits, &k, static_cast<hipStream_t>(stream));
+  if (e == hipSuccess && kc != nullptr) *kc = k;
+  return hip_status(e);
+}
+
 int moe_expert_ffn(const moe_layer_t* layer, const float* x, int T, const int32_t* idx, float* y, void* ws,
                    size_t ws_bytes, void* stream) {
   return moe_expert_ffn_checked(layer, x, T, idx, y, ws, ws_bytes, nullptr, stream);

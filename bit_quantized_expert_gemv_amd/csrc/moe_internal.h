@@ -106,6 +106,11 @@ hipError_t launch_down(const Geometry& g, const LayerPtrs& p, int T, const Works
 // ws.rnorm, recomputes in fp64 the rows the bound cannot rule out, and writes idx, w and sg.
 hipError_t launch_topk_certified(const Geometry& g, const LayerPtrs& p, const float* x, int T, const Workspace& ws,
                                  double kc, int32_t* idx, float* w, float* sg, int32_t* idx_b, hipStream_t s);
+// The certified router's first stage: approximate logits (bf16 MFMAs, x split into two bf16 terms)
+// into logits [T][E+1] (column E untouched), and in *kc the factor of their error bound
+// |approx - exact| <= kc |r_e| |x_t| + (|r_e| + 1) 2^-100.
+hipError_t launch_router_approx(const Geometry& g, const LayerPtrs& p, const float* x, int T, double* logits,
+                                double* kc, hipStream_t s);
 // Routing of T tokens into idx/w/sg (and the fp64 logits into logits_out, a copy of idx into idx_b,
 // each when non-null): the certified bf16-MFMA path for many tokens without logits_out, otherwise
 // fp64 logits then the top-K.

@@ -1568,13 +1568,8 @@ hipError_t launch_router_tokens(const Geometry& g, const LayerPtrs& p, const flo
   return launch_router_phase(g, p, x, nullptr, 0.0f, T, ws, s);
 }
 
-hipError_t launch_router_select(const Geometry& g, const LayerPtrs& p, const float* x, int T, const Workspace& ws,
-                                int32_t* idx, float* w, float* sg, double* logits_out, int32_t* idx_b,
-                                hipStream_t s) {
-  if (logits_out != nullptr || T < kRouterCertifiedMinTokens) {
-    hipError_t e = launch_router_tokens(g, p, x, T, ws, s);
-    return e == hipSuccess ? launch_topk(g, T, ws, idx, w, sg, logits_out, idx_b, s) : e;
-  }
+hipError_t launch_router_approx(const Geometry& g, const LayerPtrs& p, const float* x, int T, double* logits,
+                                double* kc_out, hipStream_t s) {
   int rt = BQ_ROUTER_APPROX_RT;
   if (rt == 0) {  // the smallest tile whose grid fits one block per CU (256), else the largest
     rt = 8;
@@ -1586,13 +1581,11 @@ hipError_t launch_router_select(const Geometry& g, const LayerPtrs& p, const flo
   }
   const dim3 ag(cdiv(g.E, 16 * rt), cdiv(T, kAT)), ab(64 * kASplit);
   if (rt == 8)
-    hipLaunchKernelGGL(k_router_approx<8>, ag, ab, 0, s, T, g.H, g.E, x, p.router, ws.logits);
+    hipLaunchKernelGGL(k_router_approx<8>, ag, ab, 0, s, T, g.H, g.E, x, p.router, logits);
   else if (rt == 4)
-    hipLaunchKernelGGL(k_router_approx<4>, ag, ab, 0, s, T, g.H, g.E, x, p.router, ws.logits);
+    hipLaunchKernelGGL(k_router_approx<4>, ag, ab, 0, s, T, g.H, g.E, x, p.router, logits);
   else
-    hipLaunchKernelGGL(k_router_approx<2>, ag, ab, 0, s, T, g.H, g.E, x, p.router, ws.logits);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_router_approx<2>, ag, ab, 0, s, T, g.H, g.E, x, p.router, logits);
   // Error bound of the approximate logits, relative to |r_e| |x_t|:
   //  - splitting x into two bf16 values leaves |d| <= 2^-16 |x|, and |hi| + |lo| <= 1.01 |x|;
   //  - one MFMA adds 32 exact products to its accumulator with an error of at most 34 * 2^-23 times
@@ -1602,10 +1595,24 @@ hipError_t launch_router_select(const Geometry& g, const LayerPtrs& p, const flo
   //    34 * 2^-23 * n * (1 + 34 * 2^-23 * n) times its sum of |r| (|hi| + |lo|);
   //  - the sum of |r_j| |x_j| is at most |r| |x| (Cauchy-Schwarz), and the fp64 sums around
   //    this (the waves' partial sums, the norms, the exact recomputation) are far below it.
-  // The factor 1.25 is a safety margin on all of it.
+  // The factor 1.25 is a safety margin on all of it; the errors measured on the 2048-token
+  // workloads stay far inside the bound (a test asserts below a quarter of it).
   const double n = 2.0 * g.H / (32.0 * kASplit);
   const double u = std::ldexp(1.0, -23);
-  const double kc = 1.25 * (std::ldexp(1.0, -16) * 1.01 + 34.0 * u * n * (1.0 + 34.0 * u * n) * 1.01);
+  *kc_out = 1.25 * (std::ldexp(1.0, -16) * 1.01 + 34.0 * u * n * (1.0 + 34.0 * u * n) * 1.01);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_select(const Geometry& g, const LayerPtrs& p, const float* x, int T, const Workspace& ws,
+                                int32_t* idx, float* w, float* sg, double* logits_out, int32_t* idx_b,
+                                hipStream_t s) {
+  if (logits_out != nullptr || T < kRouterCertifiedMinTokens) {
+    hipError_t e = launch_router_tokens(g, p, x, T, ws, s);
+    return e == hipSuccess ? launch_topk(g, T, ws, idx, w, sg, logits_out, idx_b, s) : e;
+  }
+  double kc = 0.0;
+  hipError_t e = launch_router_approx(g, p, x, T, ws.logits, &kc, s);
+  if (e != hipSuccess) return e;
   return launch_topk_certified(g, p, x, T, ws, kc, idx, w, sg, idx_b, s);
 }
 

@@ -185,6 +185,18 @@ int moe_expert_ffn(const moe_layer_t* layer, const float* x_dev, int T, const in
 int moe_expert_ffn_checked(const moe_layer_t* layer, const float* x_dev, int T, const int32_t* idx_dev, float* y_dev,
                            void* ws_dev, size_t ws_bytes, int32_t* err_dev, void* stream);
 
+/* Test export: the first stage of the certified router that moe_router (without a logits buffer)
+ * and the prefill use from MOE_ROUTER_CERTIFIED_MIN_TOKENS tokens. The HN thread "Flash-MoE:
+ * Running a 397B Parameter Model on a Laptop": the router's result decides which experts are read,
+ * so the approximation only narrows the rows that are then recomputed exactly.
+ * logits_dev fp64 [T][E+1]: column e < E receives router row e . x_t on bf16 MFMAs with each x
+ * split into two bf16 terms; column E is not written. *kc_host (may be NULL) receives the factor
+ * of the error bound the certified top-K relies on:
+ *   |approx - exact| <= kc * |r_e| * |x_t| + (|r_e| + 1) * 2^-100,
+ * |r_e| and |x_t| the Euclidean norms of router row e and token t. */
+int moe_router_approx_logits(const moe_layer_t* layer, const float* x_dev, int T, double* logits_dev, double* kc_host,
+                             void* stream);
+
 /* Combine ("Metal Compute Shaders": MoE combine + residual + gate):
  *   out[t] = residual[t] + sum_k w[t][k] * y[t][k] + g[t] * y[t][K]   (shared term if has_shared)
  * y_dev fp32 [T][K + has_shared][H]; w_dev fp32 [T][K]; shared_g_dev fp32 [T] (NULL iff !has_shared). */

@@ -169,3 +169,31 @@ def test_certified_router_bitwise_repeatable(layers):
     b = _route(L, x, with_logits=False)
     for u, v in zip(a[:3], b[:3]):
         assert np.array_equal(u, v)
+
+
+@pytest.mark.parametrize("name", ["prefill4", "prefillmx"])
+def test_certified_bound_margin(gpu_device, name):
+    """The certified top-K trusts |approx - exact| <= kc |r_e| |x_t| + (|r_e| + 1) 2^-100. Over
+    every token and every row of the 2048-token workloads, the measured error must stay below a
+    quarter of that bound (exact = the oracle's fp64 logits)."""
+    w = synth.WORKLOADS[name]
+    L = DeviceLayer(w)
+    T, E = w.tokens, w.n_experts
+    xs = synth.tokens_x(w, 0, T)
+    x = torch.from_numpy(xs).cuda()
+    lg = torch.full((T, E + 1), float("nan"), dtype=torch.float64, device="cuda")
+    kc = bq.moe_router_approx_logits(L.desc, x, T, lg)
+    torch.cuda.synchronize()
+    approx = lg.cpu().numpy()[:, :E]
+    R = synth.router_weights(w, 0)
+    x64 = xs.astype(np.float64)
+    exact = np.stack([oracle.router_logits(R, x64[t]) for t in range(T)])
+    rn = np.linalg.norm(synth.bf16_to_f32(R).astype(np.float64), axis=1)
+    xn = np.linalg.norm(x64, axis=1)
+    bound = kc * xn[:, None] * rn[None, :] + (rn[None, :] + 1.0) * 2.0 ** -100
+    ratio = np.abs(approx - exact) / bound
+    t, e = np.unravel_index(int(np.argmax(ratio)), ratio.shape)
+    _log(f"{name}: kc {kc:.3e}; max |approx - exact| / bound = {ratio[t, e]:.4f} at token {t} row {e}; "
+         f"mean {ratio.mean():.2e}; 99.99th percentile {np.quantile(ratio, 0.9999):.4f}")
+    assert np.all(np.isfinite(approx))
+    assert ratio.max() < 0.25
