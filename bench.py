@@ -96,28 +96,50 @@ def stream_read_gbs(torch, gib=4, reps=5):
 
 
 def cpu_baseline(w, budget_s):
-    """The oracle as it stands, on the host cores, over the first tokens until ~budget_s of oracle time."""
+    """The oracle as it stands, on the host cores: tokens taken in a stride order that spreads over
+    all of the workload's tokens, until ~budget_s of oracle time with every OpenMP thread, then the
+    same tokens again with one thread until ~budget_s / 2."""
+    import ctypes
+
     import numpy as np
 
     import oracle
     import synth
 
+    gomp = ctypes.CDLL("libgomp.so.1")  # the OpenMP runtime the oracle library is built on
     router = synth.router_weights(w)
     gate = synth.shared_gate_weights(w)
     shared = synth.expert_arrays(w, 0, synth.SHARED)
-    spent, n = 0.0, 0
-    while spent < budget_s and n < w.tokens:
-        x = synth.tokens_x(w, n, 1)[0].astype(np.float64)
-        idx = oracle.topk(oracle.router_logits(router, x), w.top_k)  # untimed: which experts to generate
-        arrays = {int(e): synth.expert_arrays(w, 0, int(e)) for e in idx}
-        t0 = time.perf_counter()
-        oracle.layer(x, x, router, gate, arrays.__getitem__, w.top_k, w.group, shared_expert=shared)
-        spent += time.perf_counter() - t0
-        n += 1
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count()
+    stride = next(p for p in range(w.tokens // 3, w.tokens) if np.gcd(p, w.tokens) == 1)
+    order = [(i * stride) % w.tokens for i in range(w.tokens)]
+
+    def run(budget):
+        spent, n = 0.0, 0
+        while spent < budget and n < w.tokens:
+            t = order[n]
+            x = synth.tokens_x(w, t, 1)[0].astype(np.float64)
+            idx = oracle.topk(oracle.router_logits(router, x), w.top_k)  # untimed: which experts to generate
+            arrays = {int(e): synth.expert_arrays(w, 0, int(e)) for e in idx}
+            t0 = time.perf_counter()
+            oracle.layer(x, x, router, gate, arrays.__getitem__, w.top_k, w.group, shared_expert=shared)
+            spent += time.perf_counter() - t0
+            n += 1
+        return n, spent
+
+    threads = int(gomp.omp_get_max_threads())
+    n, spent = run(budget_s)
+    gomp.omp_set_num_threads(1)
+    try:
+        n1, spent1 = run(budget_s / 2)
+    finally:
+        gomp.omp_set_num_threads(threads)
+    lo, hi = min(order[:n]), max(order[:n])
     return {"value": n / spent, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {n} of the {w.tokens} decode4 tokens, one at a time (router, top-K, 4 experts "
-                      f"dense-dequantised in fp64, combine); expert generation untimed; {spent:.1f} s of oracle time"}
+            "one_core": {"value": n1 / spent1, "unit": "tokens/s", "cores": 1, "tokens": n1},
+            "sample": f"{n} of the {w.tokens} {w.name} tokens (stride {stride} through all of them, so spread over "
+                      f"{lo}..{hi}), one at a time: router, top-K, {w.top_k} routed + shared experts dense-dequantised "
+                      f"in fp64, combine; expert generation untimed; {spent:.1f} s of oracle time on {threads} "
+                      f"threads, then the first {n1} of them on one thread ({spent1:.1f} s)"}
 
 
 def main():

@@ -1,10 +1,11 @@
 // Decode-path kernels of the quantised MoE layer for MI355X (gfx950, wave64).
 //
 // One token's layer runs as three stream-ordered kernels; nothing synchronises the host.
-//   1. router phase: the router logits and the shared-gate logit (fp64 accumulation), plus the
-//      shared expert's gate/up/SwiGLU, which does not depend on the routing;
-//   2. gate/up: each block picks the top-K itself from the logits, then runs gate/up/SwiGLU
-//      for the K routed experts;
+//   1. router phase: the router logits and the shared-gate logit (fp64 accumulation);
+//   2. gate/up: one block per CU and 16-row slice of every expert slot. A routed slot's block
+//      first picks the top-K itself from the logits (one wave, fp64 keys), then runs
+//      gate/up/SwiGLU for its expert; the shared expert is one more slot, which starts its weight
+//      loads at once. One block writes the routing (indices, weights, shared gate);
 //   3. down: the down projections of all K+1 experts, combined with the routing weights, the
 //      shared gate and the residual. Each output row sums all experts, so the result is a
 //      deterministic gather with no atomics.
@@ -1242,14 +1243,17 @@ unsigned blocks_for(int64_t n, int bs) { return (unsigned)((n + bs - 1) / bs); }
 #define BQ_FOR_H(X) X(256) X(512) X(1024) X(2048) X(4096) X(8192)
 #define BQ_FOR_I(X) X(64) X(128) X(256) X(512) X(1024) X(2048)
 
-// Row steps per down wave (the bytes each wave has in flight), tuned on MI355X for the 4096/1024 shape.
+// Row steps per down wave: enough for 16 output rows per block (so hidden 4096 gives 256 blocks,
+// one per CU), at most BQ_P3 (the bytes each wave has in flight, tuned on MI355X for the 4096/1024
+// 4-bit shape). A 2-bit row of 1024 is 16 lanes wide, so its waves take 4 steps of 4 rows.
 #ifndef BQ_P3
 #define BQ_P3 8
 #endif
 #ifndef BQ_ROUTER_STEPS
 #define BQ_ROUTER_STEPS 1
 #endif
-constexpr int kP3 = BQ_P3;  // down
+template <int RPW>
+constexpr int down_steps() { return 16 / RPW < 1 ? 1 : (16 / RPW > BQ_P3 ? BQ_P3 : 16 / RPW); }
 // Tokens per block of the multi-token router (k_router_group).
 #ifndef BQ_ROUTER_GROUP
 #define BQ_ROUTER_GROUP 4
@@ -1311,9 +1315,10 @@ template <int BITS, int I>
 hipError_t down_impl(const LayerArgs& a, int T, const int32_t* idx, const float* residual, float* out, float* y,
                      hipStream_t s, const KernelEvents& ev) {
   using C = RowCfg<BITS, I>;
-  constexpr int RB = C::RPW * kP3;
+  constexpr int P = down_steps<C::RPW>();
+  constexpr int RB = C::RPW * P;
   const int nb = (a.H + RB - 1) / RB;
-#define BQ_DN(F) launch_timed(k_down<BITS, I, kP3, F>, dim3(nb, T), dim3(kBlock), s, ev, a, idx, residual, out, y)
+#define BQ_DN(F) launch_timed(k_down<BITS, I, P, F>, dim3(nb, T), dim3(kBlock), s, ev, a, idx, residual, out, y)
   if constexpr (BITS == 4) {
     if (a.form == 3) return BQ_DN(3);
   }

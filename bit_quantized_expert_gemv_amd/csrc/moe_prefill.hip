@@ -29,12 +29,11 @@
 // (largest 65504, normal down to 2^-14) never clips them: x per token, the SwiGLU outputs per token
 // and 64-row group. The scale is exact and is undone in the fp32 epilogues.
 //
-// MFMA: v_mfma_f32_32x32x16_f16 with A = activations (32 token rows) and B = codes (32 weight
-// rows). A[i][k] sits in lane i + 32*(k/8), element k%8; B[k][j] in lane j + 32*(k/8), element k%8;
-// D[i][j] in lane j + 32*((i/4)%2), element (i/8)*4 + i%4 (checked on the device). The sum over k is
-// order-free, so a lane's 16-byte code load (32 codes of one row, half a 4-bit group) supplies
-// MFMAs m = 0..3 with codes 8m..8m+7. Lanes 32..63 hold the other half of the same group, so every
-// MFMA stays inside one scale group, and the activation operand is read in the same k order.
+// MFMA: v_mfma_f32_16x16x32_f16 with A = activations (16 tokens x 32 k) and B = codes (32 k x 16
+// weight rows); lane l holds k slice l/16 of token or row l%16 (layout checked on the device). Every
+// MFMA stays inside one scale group: lane swaps regroup each lane's 16-byte code load so that the
+// 32 k of one MFMA share a scale, and the activation operand is read in the same k order (details
+// at k_grouped).
 #include <hip/hip_runtime.h>
 #include <type_traits>
 
