@@ -1245,15 +1245,17 @@ unsigned blocks_for(int64_t n, int bs) { return (unsigned)((n + bs - 1) / bs); }
 
 // Row steps per down wave: enough for 16 output rows per block (so hidden 4096 gives 256 blocks,
 // one per CU), at most BQ_P3 (the bytes each wave has in flight, tuned on MI355X for the 4096/1024
-// 4-bit shape). A 2-bit row of 1024 is 16 lanes wide, so its waves take 4 steps of 4 rows.
+// 4-bit shape). A 2-bit row of 1024 is 16 lanes wide, so its waves take 4 steps of 4 rows. With more
+// expert slots than waves (top-6 + shared), each wave takes two slots in turn, and blocks of 8 rows
+// (two per CU) measured 5% faster per token.
 #ifndef BQ_P3
 #define BQ_P3 8
 #endif
 #ifndef BQ_ROUTER_STEPS
 #define BQ_ROUTER_STEPS 1
 #endif
-template <int RPW>
-constexpr int down_steps() { return 16 / RPW < 1 ? 1 : (16 / RPW > BQ_P3 ? BQ_P3 : 16 / RPW); }
+template <int RPW, int ROWS>
+constexpr int down_steps() { return ROWS / RPW < 1 ? 1 : (ROWS / RPW > BQ_P3 ? BQ_P3 : ROWS / RPW); }
 // Tokens per block of the multi-token router (k_router_group).
 #ifndef BQ_ROUTER_GROUP
 #define BQ_ROUTER_GROUP 4
@@ -1315,14 +1317,16 @@ template <int BITS, int I>
 hipError_t down_impl(const LayerArgs& a, int T, const int32_t* idx, const float* residual, float* out, float* y,
                      hipStream_t s, const KernelEvents& ev) {
   using C = RowCfg<BITS, I>;
-  constexpr int P = down_steps<C::RPW>();
-  constexpr int RB = C::RPW * P;
+  constexpr int P16 = down_steps<C::RPW, 16>(), P8 = down_steps<C::RPW, 8>();
+  const bool two_rounds = a.NE > kWaves;
+  const int RB = C::RPW * (two_rounds ? P8 : P16);
   const int nb = (a.H + RB - 1) / RB;
-#define BQ_DN(F) launch_timed(k_down<BITS, I, P, F>, dim3(nb, T), dim3(kBlock), s, ev, a, idx, residual, out, y)
+#define BQ_DN(P, F) launch_timed(k_down<BITS, I, P, F>, dim3(nb, T), dim3(kBlock), s, ev, a, idx, residual, out, y)
   if constexpr (BITS == 4) {
-    if (a.form == 3) return BQ_DN(3);
+    if (a.form == 3) return two_rounds ? BQ_DN(P8, 3) : BQ_DN(P16, 3);
   }
-  return a.form == 1 ? BQ_DN(1) : a.form == 2 ? BQ_DN(2) : BQ_DN(0);
+  if (two_rounds) return a.form == 1 ? BQ_DN(P8, 1) : a.form == 2 ? BQ_DN(P8, 2) : BQ_DN(P8, 0);
+  return a.form == 1 ? BQ_DN(P16, 1) : a.form == 2 ? BQ_DN(P16, 2) : BQ_DN(P16, 0);
 #undef BQ_DN
 }
 
