@@ -658,6 +658,13 @@ __device__ __forceinline__ int kblock(int q, int h) {
 // (weights) and an LDS ring (activations); the activations of step s+1, loaded a step earlier,
 // are parked in the ring and one barrier closes the step. Every load has two steps to land
 // before it is waited for.
+#ifndef BQ_CODE_STAGES
+#define BQ_CODE_STAGES 4
+#endif
+// Code register stages of the k_grouped pipeline: 4 keep three steps of weight loads in flight per
+// wave (12 KB), at 250 VGPRs for the 4-bit gate/up, still two waves per SIMD; against 3 stages the
+// prefill4 grouped GEMMs measured 1099 -> 1040 us per step.
+constexpr int kStages = BQ_CODE_STAGES;
 template <int BITS, int KDIM, int UMAX, bool GATEUP, bool SHARED>
 __global__ __launch_bounds__(kThreads, GATEUP ? BQ_LB_GU : BQ_LB_DOWN) void k_grouped(GroupArgs g, int sgroups) {
   constexpr int NG = KDIM / 64;
@@ -1032,25 +1039,26 @@ __global__ __launch_bounds__(kThreads, GATEUP ? BQ_LB_GU : BQ_LB_DOWN) void k_gr
         for (int e = 0; e < 4; ++e) acc[th][rb][e] = 0.0f;
   };
 
-  // Three code stages (step s computes stage s % 3 while the next two are in flight), two
-  // activation register sets (step s loads set s % 2 with the activations of step s + 2 and parks
-  // the other set, which holds step s + 1), and the (scale, bias) words of a step pair: wp is
-  // loaded two steps ahead and split at the pair's first step into wx. The steps run in an
-  // unrolled period of 6 so that every register set has a fixed name. Past the end a step re-reads
-  // the last one, so every path issues the same loads.
-  Codes c0, c1, c2;
+  // kStages code stages (step s computes stage s % kStages while the next kStages - 1 are in flight),
+  // two activation register sets (step s loads set s % 2 with the activations of step s + 2 and
+  // parks the other set, which holds step s + 1), and the (scale, bias) words of a step pair: wp is
+  // loaded two steps ahead and split at the pair's first step into wx. The steps run in an unrolled
+  // period of lcm(kStages, 2) so that every register set has a fixed name. Past the end a step
+  // re-reads the last one, so every path issues the same loads.
+  constexpr int kAhead = kStages - 1;
+  Codes cst[kStages];
   Act a0, a1;
   GWords wp;
   GWordsX wx;
   auto body = [&](auto ci, auto ai, int s) __attribute__((always_inline)) {
     constexpr int CI = decltype(ci)::value, AI = decltype(ai)::value;
-    Codes& cur = CI == 0 ? c0 : (CI == 1 ? c1 : c2);
-    Codes& ahead = CI == 0 ? c2 : (CI == 1 ? c0 : c1);  // stage (s + 2) % 3
+    Codes& cur = cst[CI];
+    Codes& ahead = cst[(CI + kAhead) % kStages];  // stage (s + kAhead) % kStages
     Act& aload = AI == 0 ? a0 : a1;
     Act& apark = AI == 0 ? a1 : a0;
     if constexpr (AI == 0) split_words(wp, wx);
     if constexpr (!RESIDENT) load_act(aload, min(s + 2, ntot - 1));
-    load_codes(ahead, min(s + 2, ntot - 1));
+    load_codes(ahead, min(s + kAhead, ntot - 1));
     if constexpr (AI == 0) load_words(wp, s / 2 + 1);
     if (s < ntot) {  // uniform per block
       compute(cur, wx.w[AI], s);
@@ -1061,26 +1069,39 @@ __global__ __launch_bounds__(kThreads, GATEUP ? BQ_LB_GU : BQ_LB_DOWN) void k_gr
       __syncthreads();
     }
   };
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
   if constexpr (!RESIDENT) {
     load_act(a0, 0);
     load_act(a1, min(1, ntot - 1));
   }
-  load_codes(c0, 0);
+  load_codes(cst[0], 0);
   load_words(wp, 0);
-  load_codes(c1, min(1, ntot - 1));
+#pragma unroll
+  for (int i = 1; i < kAhead; ++i) load_codes(cst[i], min(i, ntot - 1));
   if constexpr (!RESIDENT) park_act(a0, 0);
   __syncthreads();
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  static_assert(kStages == 3 || kStages == 4, "3 or 4 code stages");
+  if constexpr (kStages == 3) {
 #pragma unroll 1
-  for (int s = 0; s < ntot; s += 6) {
-    body(I0{}, I0{}, s);
-    body(I1{}, I1{}, s + 1);
-    body(I2{}, I0{}, s + 2);
-    body(I0{}, I1{}, s + 3);
-    body(I1{}, I0{}, s + 4);
-    body(I2{}, I1{}, s + 5);
+    for (int s = 0; s < ntot; s += 6) {
+      body(I0{}, I0{}, s);
+      body(I1{}, I1{}, s + 1);
+      body(I2{}, I0{}, s + 2);
+      body(I0{}, I1{}, s + 3);
+      body(I1{}, I0{}, s + 4);
+      body(I2{}, I1{}, s + 5);
+    }
+  } else {
+#pragma unroll 1
+    for (int s = 0; s < ntot; s += 4) {
+      body(I0{}, I0{}, s);
+      body(I1{}, I1{}, s + 1);
+      body(I2{}, I0{}, s + 2);
+      body(I3{}, I1{}, s + 3);
+    }
   }
 }
 
