@@ -664,9 +664,11 @@ __device__ __forceinline__ int kblock(int q, int h) {
 // Code register stages of the k_grouped pipeline: 4 keep three steps of weight loads in flight per
 // wave (12 KB), at 250 VGPRs for the 4-bit gate/up, still two waves per SIMD; against 3 stages the
 // prefill4 grouped GEMMs measured 1099 -> 1040 us per step.
-constexpr int kStages = BQ_CODE_STAGES;
+constexpr int kStagesMax = BQ_CODE_STAGES;
 template <int BITS, int KDIM, int UMAX, bool GATEUP, bool SHARED>
 __global__ __launch_bounds__(kThreads, GATEUP ? BQ_LB_GU : BQ_LB_DOWN) void k_grouped(GroupArgs g, int sgroups) {
+  // short gate/up rows (hidden 256, 512) keep three stages: their fourth spilled registers
+  constexpr int kStages = GATEUP && KDIM <= 512 ? 3 : kStagesMax;
   constexpr int NG = KDIM / 64;
   constexpr int U = NG >= UMAX ? UMAX : NG;  // groups per pipeline step
   static_assert(U <= 4, "a step holds at most four groups");
@@ -913,6 +915,7 @@ __global__ __launch_bounds__(kThreads, GATEUP ? BQ_LB_GU : BQ_LB_DOWN) void k_gr
       }
 #if BQ_GROUP_SCHED_BARRIER
       // one group at a time: keeps the scheduler from widening every group of the step up front
+      // (without it the down GEMMs measured 295 -> 384 us at prefill4; gate/up the same within noise)
       __builtin_amdgcn_sched_barrier(0);
 #endif
     }
