@@ -112,7 +112,8 @@ def test_prefill_tiny_residual_and_determinism(tiny):
 
 def test_prefill4_full(pre4):
     """2048 tokens through the 4-bit layer: every token's top-K against the oracle's fp64 routing,
-    sampled outputs against the oracle, and prefill rows against the decode path's rows."""
+    outputs of 64 spread tokens (and the tile edges) against the oracle, and prefill rows against
+    the decode path's rows."""
     L, ref = pre4
     T = PRE4.tokens
     x = torch.from_numpy(synth.tokens_x(PRE4, 0, T)).cuda()
@@ -120,15 +121,14 @@ def test_prefill4_full(pre4):
     out, idx = _forward(L, x)
     xs = x.cpu().numpy().astype(np.float64)
     _log("prefill4: oracle routing for every token")
-    for t in range(T):
-        lg = oracle.router_logits(ref.router, xs[t])
-        assert list(idx[t]) == list(oracle.topk(lg, PRE4.top_k)), f"token {t}"
+    check_topk_all(ref, xs, idx)
     counts = np.bincount(idx.reshape(-1), minlength=PRE4.n_experts)
     _log(f"prefill4: tokens per expert min {counts.min()} mean {counts.mean():.1f} max {counts.max()}, "
          f"untouched {(counts == 0).sum()}")
     assert counts.sum() == T * PRE4.top_k
     sample = [0, 1, 17, 500, 1023, 1024, 2046, 2047]
-    for t in sample:
+    _log("prefill4: oracle outputs of 64 spread tokens")
+    for t in sorted(set(sample) | set(spread(T, 64))):
         r = ref.token(xs[t])
         assert_close(out[t], r.out, f"prefill out[{t}]")
     # the same tokens through the decode path (T=1 calls)
