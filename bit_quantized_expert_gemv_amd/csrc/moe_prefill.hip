@@ -695,7 +695,10 @@ __global__ __launch_bounds__(kThreads, GATEUP ? BQ_LB_GU : BQ_LB_DOWN) void k_gr
   // powers of two undoing the activations' scaling: gate/up per token row, down per [group][row]
   __shared__ float u_lds[GATEUP ? kTileM : NG * kTileM];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // the wave index through readfirstlane: the compiler then knows it is uniform, so the buffer
+  // descriptors built from it (a matrix per wave in gate/up) stay in scalar registers; derived from
+  // threadIdx alone it counts as divergent, and every buffer load became a waterfall loop
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int c16 = lane & 15, q = lane >> 4;        // MFMA lane: token / row within 16, k slice
   const int mi = GATEUP ? (wave >> 1) : 0;         // matrix of this wave (gate 0, up 1)
   const int wrow = (GATEUP ? (wave & 1) : wave) * 32;  // first row of this wave in a slab
@@ -1207,7 +1210,10 @@ __global__ __launch_bounds__(kThreads, GATEUP ? BQ_LB_GU : BQ_LB_DOWN) void k_gr
   __shared__ uint32_t sc_lds[kMxTerms][kTileM][NB / 4 + 1];
   __shared__ float x_lds[GATEUP ? 2 : 1][16][64];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // the wave index through readfirstlane: the compiler then knows it is uniform, so the buffer
+  // descriptors built from it (a matrix per wave in gate/up) stay in scalar registers; derived from
+  // threadIdx alone it counts as divergent, and every buffer load became a waterfall loop
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int c16 = lane & 15, q = lane >> 4;
   const int mi = GATEUP ? (wave >> 1) : 0;
   const int wrow = (GATEUP ? (wave & 1) : wave) * 32;
