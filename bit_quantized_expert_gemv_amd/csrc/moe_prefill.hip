@@ -56,6 +56,13 @@ constexpr int kThreads = 256;
 
 __device__ __forceinline__ float bf16_val(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
+// silu(a) * c = a / (1 + e^-a) * c, with e^-a as the hardware 2^x of -a log2(e) and the hardware
+// reciprocal (about 1 ulp each, far inside the layer's tolerance). Limits: a -> -inf gives 2^x = inf,
+// a reciprocal of 0 and a product of -0; a -> +inf gives a.
+__device__ __forceinline__ float silu_mul_fast(float a, float c) {
+  return a * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(a * -1.44269504088896341f)) * c;
+}
+
 // Stored position of element e (0..7) of an 8-block: the order 0,2,4,6,1,3,5,7.
 __device__ __forceinline__ int perm8(int e) { return (e >> 1) + 4 * (e & 1); }
 
@@ -963,7 +970,7 @@ __global__ __launch_bounds__(kThreads, GATEUP ? BQ_LB_GU : BQ_LB_DOWN) void k_gr
             for (int e = 0; e < 4; ++e) {
               const float u = u_lds[16 * th + 4 * q + e];
               const float a = x_lds[wave - 2][8 * th + 4 * rb + e][lane] * u, c = acc[th][rb][e] * u;
-              hv[th][rb][e] = a / (1.0f + expf(-a)) * c;
+              hv[th][rb][e] = silu_mul_fast(a, c);
               if (active && th < nh) mx[e] = fmaxf(mx[e], fabsf(hv[th][rb][e]));
             }
 #pragma unroll
@@ -1360,7 +1367,7 @@ __global__ __launch_bounds__(kThreads, GATEUP ? BQ_LB_GU : BQ_LB_DOWN) void k_gr
               for (int e = 0; e < 4; ++e) {
                 const int m = 16 * th + 4 * q + e;
                 const float a = x_lds[wave - 2][8 * th + 4 * rb + e][lane], c = acc[th][rb][e];
-                if (m < count) g.oh32[(size_t)orow(m) * g.nout + row] = a / (1.0f + expf(-a)) * c;
+                if (m < count) g.oh32[(size_t)orow(m) * g.nout + row] = silu_mul_fast(a, c);
               }
             }
           }
