@@ -23,7 +23,8 @@
  *    reason (thread-local).
  *  - Dtypes: activations, residuals and outputs are fp32. Router and shared-gate weights are bf16
  *    (uint16 bit patterns). Expert weights live in packed blobs (format below).
- *  - Thread safety: concurrent calls on distinct streams are safe.
+ *  - Thread safety: concurrent calls on distinct streams are safe, except calls of
+ *    moe_layer_forward_noalloc on one GPU, which share that GPU's scratch array.
  *
  * Packed expert blob (one expert = gate I x H, up I x H, down H x I; bits b in {2, 4}; group G):
  *   [gate codes][up codes][down codes][gate sb][up sb][down sb]
@@ -44,8 +45,10 @@
  *   - scales: one E8M0 byte per (row, block of 32 columns), row-major [rows][cols/32]; 255 is NaN.
  *   - W[r][c] = e2m1(q[r][c]) * 2^(e[r][c/32] - 127); there is no bias.
  *   - Size: 3*I*H/2 + 3*I*H/32 bytes, 6,684,672 B for H = 4096, I = 1024.
- * A layer in this format runs the per-token kernels at every T, with exact fp32 products of the
- * dequantised weights and the fp32 activations.
+ * In decode, a layer in this format computes exact fp32 products of the dequantised weights and
+ * the fp32 activations. Its prefill (from MOE_PREFILL_MIN_TOKENS tokens, with inter >= 128) runs on
+ * the scaled MX MFMA, with the activations expanded into three MXFP8 terms (E4M3 values with an
+ * E8M0 scale per 32); below inter 128 the per-token kernels run at every T.
  */
 #ifndef BQ_MOE_H
 #define BQ_MOE_H
