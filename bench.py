@@ -106,7 +106,10 @@ def cpu_baseline(w, budget_s):
     import oracle
     import synth
 
-    gomp = ctypes.CDLL("libgomp.so.1")  # the OpenMP runtime the oracle library is built on
+    try:
+        gomp = ctypes.CDLL("libgomp.so.1")  # the OpenMP runtime the oracle library is built on
+    except OSError:
+        gomp = None
     router = synth.router_weights(w)
     gate = synth.shared_gate_weights(w)
     shared = synth.expert_arrays(w, 0, synth.SHARED)
@@ -126,16 +129,18 @@ def cpu_baseline(w, budget_s):
             n += 1
         return n, spent
 
-    threads = int(gomp.omp_get_max_threads())
+    threads = int(gomp.omp_get_max_threads()) if gomp else (os.cpu_count() or 1)
     n, spent = run(budget_s)
-    gomp.omp_set_num_threads(1)
-    try:
-        n1, spent1 = run(budget_s / 2)
-    finally:
-        gomp.omp_set_num_threads(threads)
+    n1, spent1 = 0, 0.0
+    if gomp:
+        gomp.omp_set_num_threads(1)
+        try:
+            n1, spent1 = run(budget_s / 2)
+        finally:
+            gomp.omp_set_num_threads(threads)
     lo, hi = min(order[:n]), max(order[:n])
     return {"value": n / spent, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "one_core": {"value": n1 / spent1, "unit": "tokens/s", "cores": 1, "tokens": n1},
+            "one_core": {"value": n1 / spent1, "unit": "tokens/s", "cores": 1, "tokens": n1} if n1 else None,
             "sample": f"{n} of the {w.tokens} {w.name} tokens (stride {stride} through all of them, so spread over "
                       f"{lo}..{hi}), one at a time: router, top-K, {w.top_k} routed + shared experts dense-dequantised "
                       f"in fp64, combine; expert generation untimed; {spent:.1f} s of oracle time on {threads} "
