@@ -62,7 +62,7 @@ extern "C" {
 
 #define MOE_OK 0
 #define MOE_EINVAL (-1)       /* null or misaligned pointer, bad sizes, expert index out of range */
-#define MOE_EUNSUPPORTED (-2) /* a shape or format this build does not implement (see moe_layer_t) */
+#define MOE_EUNSUPPORTED (-2) /* a shape or format the library does not implement (see moe_layer_t) */
 #define MOE_ENOSPC (-3)       /* workspace smaller than moe_workspace_bytes() */
 #define MOE_EHIP (-4)         /* a HIP call or kernel launch failed */
 
