@@ -279,6 +279,33 @@ def test_decode_sequence_graph(which, request):
 
 # ---- edge cases ------------------------------------------------------------------------------------
 
+def test_empty_calls_touch_nothing(tiny):
+    """T = 0 through every compute entry point: MOE_OK, nothing enqueued, every output untouched."""
+    L, _ = tiny
+    w = L.w
+    x = _x(w, 0, 2)
+    ws, n = _ws(L.desc, 2)
+    out = torch.full_like(x, 7.0)
+    idx = torch.full((2, w.top_k), -7, dtype=torch.int32, device="cuda")
+    wt = torch.full((2, w.top_k), 7.0, device="cuda")
+    g = torch.full((2,), 7.0, device="cuda")
+    y = torch.full((2, w.top_k + 1, w.hidden), 7.0, device="cuda")
+    err = torch.full((1,), 7, dtype=torch.int32, device="cuda")
+    sn = bq.moe_stack_workspace_bytes(L.desc, 2)
+    sws = torch.empty(sn, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    bq.moe_layer_forward(L.desc, x, x, 0, out, idx, ws, n)
+    bq.moe_layer_forward_noalloc(L.desc, x, x, 0, out, idx)
+    bq.moe_router(L.desc, x, 0, idx, wt, g, None, ws, n)
+    bq.moe_expert_ffn(L.desc, x, 0, idx, y, ws, n)
+    bq.moe_expert_ffn_checked(L.desc, x, 0, idx, y, ws, n, err)
+    bq.moe_combine(L.desc, x, y, wt, g, 0, out)
+    bq.moe_stack_forward([L.desc, L.desc], 1e-6, x, 0, out, None, sws, sn)
+    torch.cuda.synchronize()
+    assert (out == 7.0).all() and (idx == -7).all() and (wt == 7.0).all() and (g == 7.0).all()
+    assert (y == 7.0).all() and err.item() == 7
+
+
 def test_zero_input_gives_residual(tiny):
     L, _ = tiny
     w = L.w
