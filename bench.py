@@ -159,6 +159,9 @@ def main():
     ap.add_argument("--dequant", default="xsum", choices=["xsum", "literal", "naive"],
                     help="decode GEMV arithmetic: per-chunk x-sum form (default), the pages' per-element "
                          "fma(q, s*x, b*x) form, or the naive (q*s + b)*x form; an A/B ablation")
+    ap.add_argument("--tokens-per-call", type=int, default=1,
+                    help="decode workloads: run the step's tokens as calls of this many tokens each (small-batch "
+                         "decode below the prefill threshold, or the grouped path from it), one graph per step")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="first run a plain device copy of this many MiB (a known-size reference for HBM counters)")
     args = ap.parse_args()
@@ -188,6 +191,8 @@ def main():
         return bench_prefill(args, w)
     if w.layers > 1:
         return bench_stack(args, w)
+    if args.tokens_per_call > 1:
+        return bench_batched(args, w, args.tokens_per_call)
     N = w.tokens
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -323,6 +328,53 @@ def _common(args, w, value, unit, ms_per_step, config, extra):
     }
     result.update(extra)
     print(json.dumps(result), flush=True)
+
+
+def bench_batched(args, w, T):
+    """One step = the workload's tokens as consecutive moe_layer_forward calls of T tokens (the last
+    call takes the remainder), captured in one HIP graph; each call reads its own tokens."""
+    import torch
+
+    import bit_quantized_expert_gemv_amd as bq
+    import synth
+    from synth.gpu_layers import DeviceLayer
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    L = DeviceLayer(w, device=dev)
+    N = w.tokens
+    X = torch.from_numpy(synth.tokens_x(w, 0, N)).to(dev)
+    out = torch.empty_like(X)
+    nws = bq.moe_workspace_bytes(L.desc, T)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.Stream(device=dev)
+    calls = [(c, min(T, N - c)) for c in range(0, N, T)]
+    with torch.cuda.stream(stream):
+        bq.moe_layer_forward(L.desc, X[:T], X[:T], T, out[:T], None, ws, nws, stream=stream)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for c, n in calls:
+            bq.moe_layer_forward(L.desc, X[c:c + n], X[c:c + n], n, out[c:c + n], None, ws, nws, stream=stream)
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(args.steps):
+            g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    secs = e0.elapsed_time(e1) / 1000.0
+    path = "grouped (prefill) path" if T >= bq.MOE_PREFILL_MIN_TOKENS else "per-token (decode) path"
+    _common(args, w, args.steps * N / secs, "tokens/s", secs * 1000.0 / args.steps,
+            {"workload": f"{w.name} tokens as {len(calls)} calls of {T} tokens in one HIP graph ({path}; hidden "
+                         f"{w.hidden}, {w.n_experts} experts, inter {w.inter}, top-{w.top_k} + shared, {w.bits}-bit)",
+             "tokens_per_step": N, "tokens_per_call": T, "parallelism": "single GPU"},
+            {"us_per_call": round(secs * 1e6 / (args.steps * len(calls)), 2),
+             "us_per_token": round(secs * 1e6 / (args.steps * N), 3)})
 
 
 def bench_prefill(args, w):
