@@ -14,7 +14,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbqmoe.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ENOSPC, MOE_EHIP = 0, -1, -2, -3, -4
-MOE_MAX_TOP_K, MOE_MAX_EXPERTS, MOE_PREFILL_MIN_TOKENS = 8, 1024, 64
+MOE_MAX_TOP_K, MOE_MAX_EXPERTS, MOE_PREFILL_MIN_TOKENS = 8, 1024, 48
 MOE_ROUTER_BATCH_MIN_TOKENS, MOE_ROUTER_CERTIFIED_MIN_TOKENS = 96, 512
 MOE_FLAG_DEQUANT_LITERAL, MOE_FLAG_DEQUANT_NAIVE = 1, 2
 MOE_NOALLOC_SCRATCH_BYTES = 33554432

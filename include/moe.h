@@ -69,8 +69,9 @@ extern "C" {
 #define MOE_MAX_TOP_K 8
 #define MOE_MAX_EXPERTS 1024
 /* Token counts at or above this run the prefill path in moe_layer_forward (grouped by expert). Below
- * it, per-token streaming is faster on MI355X for a 512-expert, top-3 layer (measured crossover). */
-#define MOE_PREFILL_MIN_TOKENS 64
+ * it, per-token streaming is faster on MI355X (measured crossover: between 48 and 56 tokens for a
+ * 512-expert, top-3, 4-bit layer; below 48 for the 2-bit and the top-6 MXFP4 layers). */
+#define MOE_PREFILL_MIN_TOKENS 48
 /* Token counts at or above this route all tokens in one fp64 router GEMM instead of per-token
  * router rows. */
 #define MOE_ROUTER_BATCH_MIN_TOKENS 96

@@ -1,5 +1,5 @@
 """GPU parity of MXFP4 expert layers (E2M1 codes, one E8M0 scale per 32, top-6 routing) against the
-fp64 oracle, through the C ABI on an MI355X. From 64 tokens the layer runs the grouped path on the
+fp64 oracle, through the C ABI on an MI355X. From 48 tokens the layer runs the grouped path on the
 scaled MX MFMA, with the activations as 3-term MXFP8 expansions.
 
 Bar as for the affine layers: bit-exact top-K indices and dequantised weights; outputs within

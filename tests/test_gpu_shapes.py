@@ -79,6 +79,7 @@ def _forward(L, x):
     ("max2", 1, (0,)), ("max2", 64, (0, 63)),
     ("mid2", 3, (0, 1, 2)), ("mid2", 100, (0, 50, 99)),
     ("mid4", 2, (0, 1)), ("mid4", 64, (0, 33, 63)),
+    ("mid4", bq.MOE_PREFILL_MIN_TOKENS - 1, (0, 46)), ("mid4", bq.MOE_PREFILL_MIN_TOKENS, (0, 47)),  # both sides of the threshold
     ("mx64", 1, (0,)), ("mx64", 60, (0, 30, 59)),  # MXFP4 below inter 128 decodes at every T
 ])
 def test_edge_shape_layer_forward(layers, name, T, check):
