@@ -888,10 +888,10 @@ __global__ __launch_bounds__(64 * NW) void k_gateup(LayerArgs a, const float* __
 }
 
 // Kernel 3: down projections of all expert slots for a block of output rows; combine or store.
-// 8 waves: wave w handles slots w%4, w%4+4, ... over half the block's rows (w/4 picks the half),
-// and stages its slot's SwiGLU vector through its own LDS region. Against 4 waves over all rows,
-// each wave's compute after its data lands halves: decode4 15.60 -> 15.49, decode2 14.80 -> 14.66,
-// decodemx 20.87 -> 20.65 us/token.
+// 8 waves: wave w handles slots w%4, w%4+4, ... over half the block's rows (w/4 picks the half).
+// Against 4 waves over all rows, each wave's compute after its data lands halves: decode4 15.60 ->
+// 15.49, decode2 14.80 -> 14.66, decodemx 20.87 -> 20.65 us/token. The SwiGLU vectors are loaded
+// once per block rather than once per wave: decode4 15.75 -> 15.61, decodemx 20.50 -> 20.20.
 template <int BITS, int I, int P0, int FORM>
 __global__ __launch_bounds__(2 * kBlock) void k_down(LayerArgs a, const int32_t* __restrict__ idx,
                                                  const float* __restrict__ residual, float* __restrict__ out,
@@ -902,42 +902,72 @@ __global__ __launch_bounds__(2 * kBlock) void k_down(LayerArgs a, const int32_t*
   __shared__ float4 hs[2 * kWaves][I / 4];
   __shared__ float part[2 * kWaves][RB];
   const int t = blockIdx.y;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int sw = wave % kWaves, half = wave / kWaves;
   const int lir = lane % C::LPR, rig = lane / C::LPR;
   const int row0 = blockIdx.x * RB + half * P * C::RPW;
   const bool combine = out != nullptr;
   bool first = true;
-  for (int k = (P0 < 2 && half == 1) ? a.NE : sw; k < a.NE; k += kWaves) {
+  // Slots go in passes of kWaves: in pass q, wave w takes slot q*kWaves + w%4. The pass's SwiGLU
+  // vectors are loaded once by the whole block with coalesced 16-byte loads and parked in LDS
+  // (double-buffered over passes), instead of once per wave: the two halves of the block need
+  // the same vectors, and a CU's time tracks the cache lines it requests.
+  constexpr int N4 = I / 4;                                               // float4 per vector
+  constexpr int HPER = (kWaves * N4 + 2 * kBlock - 1) / (2 * kBlock);     // float4 per thread per pass
+  const bool active = !(P0 < 2 && half == 1);  // with one row step per block, the second half idles
+  const int npass = (a.NE + kWaves - 1) / kWaves;
+  for (int q = 0; q < npass; ++q) {
+    const int k = q * kWaves + sw;
+    const int nk = min(a.NE - q * kWaves, kWaves);  // slots in this pass
+    const float4* hsrc = reinterpret_cast<const float4*>(a.ws.h + ((size_t)t * a.NE + q * kWaves) * I);
+    float4 hv0, hv1, hv2, hv3;  // HPER <= 4 (hidden rows of at most 2048 floats)
+    static_assert(HPER <= 4, "SwiGLU vectors of at most 2048 floats");
+    // past the pass's vectors: its last float4 again, stored again
+    hv0 = hsrc[min((int)threadIdx.x, nk * N4 - 1)];
+    if constexpr (HPER > 1) hv1 = hsrc[min((int)threadIdx.x + 2 * kBlock, nk * N4 - 1)];
+    if constexpr (HPER > 2) hv2 = hsrc[min((int)threadIdx.x + 4 * kBlock, nk * N4 - 1)];
+    if constexpr (HPER > 3) hv3 = hsrc[min((int)threadIdx.x + 6 * kBlock, nk * N4 - 1)];
+    // Every wave issues its weight loads on every path (an idle wave repeats the rows of the pass's
+    // last slot, a bad index reads expert 0's), so the wait before parking the vectors counts only
+    // the vector loads issued before them.
+    const bool work = active && k < a.NE;
+    const int kk = min(k, a.NE - 1);
     const uint8_t* blob = a.shared;
     bool valid = true;
     float coef = 1.0f;
-    if (k < a.K) {
-      const int e = idx[(size_t)t * a.K + k];
+    if (kk < a.K) {
+      const int e = idx[(size_t)t * a.K + kk];
       valid = (e >= 0 && e < a.E);
       blob = a.experts + (size_t)(valid ? e : 0) * a.stride;
-      if (combine) coef = a.ws.w[(size_t)t * a.K + k];
+      if (combine) coef = a.ws.w[(size_t)t * a.K + kk];
     } else if (combine) {
       coef = a.ws.g[t];
     }
-    Stage<I, 64> st;
-    st.load(a.ws.h + ((size_t)t * a.NE + k) * I, lane);
-    float yv[P];
-    if (valid) {
+    uint4 cw[P][C::CPL];
+    uint32_t sb[P][C::CPL];
+    {
       const uint8_t* dc = blob + a.off_codes[2];
       const uint8_t* ds = blob + a.off_sb[2];
-      uint4 cw[P][C::CPL];
-      uint32_t sb[P][C::CPL];
 #pragma unroll
       for (int p = 0; p < P; ++p)
         load_row<C, FORM == 3>(dc, ds, min(row0 + p * C::RPW + rig, a.H - 1), lir, cw[p], sb[p]);
-      __builtin_amdgcn_sched_barrier(0);
-      st.template store<C>(hs[wave], lane, 1.0f);
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    auto park = [&](int j, const float4& hv) __attribute__((always_inline)) {
+      const int i = min((int)threadIdx.x + j * 2 * kBlock, nk * N4 - 1);
+      const int v = i / N4, f = i % N4;
+      hs[(q & 1) * kWaves + v][xslot<C>(f / (C::CH / 4), f % (C::CH / 4))] = hv;
+    };
+    park(0, hv0);
+    if constexpr (HPER > 1) park(1, hv1);
+    if constexpr (HPER > 2) park(2, hv2);
+    if constexpr (HPER > 3) park(3, hv3);
+    __syncthreads();
+    if (!work) continue;
+    float yv[P];
+    if (valid) {
       float xr[C::XPL], S[C::CPL];
-      read_act<C>(hs[wave], lir, xr, S);
+      read_act<C>(hs[(q & 1) * kWaves + sw], lir, xr, S);
 #pragma unroll
       for (int p = 0; p < P; ++p) yv[p] = seg_sum<C::LPR>(row_partial<BITS, C, FORM>(cw[p], sb[p], xr, S));
     } else {
@@ -959,7 +989,6 @@ __global__ __launch_bounds__(2 * kBlock) void k_down(LayerArgs a, const int32_t*
       }
     }
     first = false;
-    __builtin_amdgcn_wave_barrier();  // the next slot reuses this wave's LDS region
   }
   if (!combine) return;
   __syncthreads();
