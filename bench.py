@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 KERNEL_NAMES = ["router (fp64)", "gate/up + SwiGLU (routed + shared)", "down + combine"]
+PAIR_NAME = "router + top-K + gate/up + SwiGLU (one launch)"
 
 
 def _hip():
@@ -162,6 +163,8 @@ def main():
     ap.add_argument("--tokens-per-call", type=int, default=1,
                     help="decode workloads: run the step's tokens as calls of this many tokens each (small-batch "
                          "decode below the prefill threshold, or the grouped path from it), one graph per step")
+    ap.add_argument("--chain", action="store_true",
+                    help="single-token decode as the three-kernel chain even where the two-launch plan applies (A/B)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="first run a plain device copy of this many MiB (a known-size reference for HBM counters)")
     args = ap.parse_args()
@@ -199,12 +202,17 @@ def main():
     print(f"[bench] building {w.name} layer", file=sys.stderr, flush=True)
     L = DeviceLayer(w, device=dev)
     flags = {"xsum": 0, "literal": bq.MOE_FLAG_DEQUANT_LITERAL, "naive": bq.MOE_FLAG_DEQUANT_NAIVE}[args.dequant]
+    if args.chain:
+        flags |= bq.MOE_FLAG_DECODE_CHAIN
     L.desc.flags = flags
+    plan = bq.moe_layer_plan(L.desc, 1)
+    plan_name = {bq.MOE_PLAN_PAIR: "two launches", bq.MOE_PLAN_CHAIN: "three-kernel chain"}[plan]
+    print(f"[bench] plan: {plan_name}", file=sys.stderr, flush=True)
     X = torch.from_numpy(synth.tokens_x(w, 0, N)).to(dev)
     out = torch.empty_like(X)
     idx = torch.empty(N, w.top_k, dtype=torch.int32, device=dev)
     nws = bq.moe_workspace_bytes(L.desc, 1)
-    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+    ws = torch.zeros(nws, dtype=torch.uint8, device=dev)
     stream = torch.cuda.Stream(device=dev)
     torch.cuda.synchronize()
 
@@ -240,6 +248,11 @@ def main():
     # ---- per-kernel durations, live, with HIP events around each launch (eager, same stream)
     hip = _hip()
     per_kernel_bytes, expert_bytes, router_bytes = algorithmic_bytes(w, bq)
+    names, pairs = KERNEL_NAMES, [0, 1, 2]  # per kernel: the index p of its event pair (2p, 2p + 1)
+    if plan == bq.MOE_PLAN_PAIR:  # router rows and gate/up in the first launch, down in the second
+        names, pairs = [PAIR_NAME, KERNEL_NAMES[2]], [0, 2]
+        per_kernel_bytes = [per_kernel_bytes[0] + per_kernel_bytes[1], per_kernel_bytes[2]]
+    nk = len(names)
     events = []
     for _ in range(6 * N):
         e = ctypes.c_void_p()
@@ -250,23 +263,24 @@ def main():
             bq.moe_layer_forward_timed(L.desc, X[t], X[t], 1, out[t], idx[t], ws, nws, events[6 * t: 6 * t + 6],
                                        stream=stream)
     torch.cuda.synchronize()
-    dur = np.zeros((N, 3))
+    dur = np.zeros((N, nk))
     f = ctypes.c_float()
     for t in range(N):
-        for k in range(3):
-            assert hip.hipEventElapsedTime(ctypes.byref(f), events[6 * t + 2 * k], events[6 * t + 2 * k + 1]) == 0
+        for k in range(nk):
+            pk = pairs[k]
+            assert hip.hipEventElapsedTime(ctypes.byref(f), events[6 * t + 2 * pk], events[6 * t + 2 * pk + 1]) == 0
             dur[t, k] = f.value * 1e-3
     for e in events:
         hip.hipEventDestroy(e)
     avg = dur[10:].mean(axis=0)  # skip the first tokens (cold instruction caches)
     dom = int(np.argmax(per_kernel_bytes))
     achieved = per_kernel_bytes[dom] / avg[dom] / 1e9
-    kernels = {KERNEL_NAMES[k]: {"avg_us": round(avg[k] * 1e6, 3), "bytes": per_kernel_bytes[k],
-                                 "GB/s": round(per_kernel_bytes[k] / avg[k] / 1e9, 1)} for k in range(3)}
+    kernels = {names[k]: {"avg_us": round(avg[k] * 1e6, 3), "bytes": per_kernel_bytes[k],
+                          "GB/s": round(per_kernel_bytes[k] / avg[k] / 1e9, 1)} for k in range(nk)}
     print(f"[bench] kernels: {json.dumps(kernels)}", file=sys.stderr, flush=True)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(KERNEL_NAMES[dom], w.name),
-                "kernel": KERNEL_NAMES[dom], "algorithmic_bytes_per_launch": per_kernel_bytes[dom],
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(names[dom], w.name),
+                "kernel": names[dom], "algorithmic_bytes_per_launch": per_kernel_bytes[dom],
                 "avg_launch_us": round(avg[dom] * 1e6, 3),
                 "timing": f"start/stop HIP events recorded by each dispatch itself (hipExtLaunchKernel) on the "
                           f"kernel's stream, averaged over {N - 10} single-token launches",
@@ -305,7 +319,9 @@ def main():
                                f"top-{w.top_k} + shared, {w.bits}-bit group-{w.group} experts; a step is {N} "
                                f"sequential single-token calls in one HIP graph",
                    "tokens_per_step": N, "hidden": w.hidden, "n_experts": w.n_experts, "inter": w.inter,
-                   "top_k": w.top_k, "bits": w.bits, "group": w.group, "dequant_form": args.dequant if w.fmt == "affine" else "mxfp4: e2m1(q) * 2^(e - 127)",
+                   "top_k": w.top_k, "bits": w.bits, "group": w.group,
+                   "decode_plan": plan_name,
+                   "dequant_form": args.dequant if w.fmt == "affine" else "mxfp4: e2m1(q) * 2^(e - 127)",
                    "parallelism": "single GPU"},
         "us_per_token": round(us_tok, 3),
         "expert_GB/s": round(expert_bytes / (us_tok * 1e-6) / 1e9, 1),
@@ -346,7 +362,7 @@ def bench_batched(args, w, T):
     X = torch.from_numpy(synth.tokens_x(w, 0, N)).to(dev)
     out = torch.empty_like(X)
     nws = bq.moe_workspace_bytes(L.desc, T)
-    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+    ws = torch.zeros(nws, dtype=torch.uint8, device=dev)
     stream = torch.cuda.Stream(device=dev)
     calls = [(c, min(T, N - c)) for c in range(0, N, T)]
     with torch.cuda.stream(stream):
@@ -393,7 +409,7 @@ def bench_prefill(args, w):
     out = torch.empty_like(X)
     idx = torch.empty(T, w.top_k, dtype=torch.int32, device=dev)
     n = bq.moe_workspace_bytes(L.desc, T)
-    ws = torch.empty(n, dtype=torch.uint8, device=dev)
+    ws = torch.zeros(n, dtype=torch.uint8, device=dev)
     stream = torch.cuda.Stream(device=dev)
     with torch.cuda.stream(stream):
         for _ in range(args.warmup):
@@ -442,7 +458,7 @@ def bench_stack(args, w):
     out = torch.empty_like(X)
     idx = torch.empty(N, w.layers, w.top_k, dtype=torch.int32, device=dev)
     n = bq.moe_stack_workspace_bytes(layers[0].desc, 1)
-    ws = torch.empty(n, dtype=torch.uint8, device=dev)
+    ws = torch.zeros(n, dtype=torch.uint8, device=dev)
     descs = [L.desc for L in layers]
     stream = torch.cuda.Stream(device=dev)
     # one eager call before capture

@@ -13,10 +13,13 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbqmoe.so")
 
-MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ENOSPC, MOE_EHIP = 0, -1, -2, -3, -4
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ENOSPC, MOE_EHIP, MOE_ETIMEOUT = 0, -1, -2, -3, -4, -5
 MOE_MAX_TOP_K, MOE_MAX_EXPERTS, MOE_PREFILL_MIN_TOKENS = 8, 1024, 48
 MOE_ROUTER_BATCH_MIN_TOKENS, MOE_ROUTER_CERTIFIED_MIN_TOKENS = 96, 512
 MOE_FLAG_DEQUANT_LITERAL, MOE_FLAG_DEQUANT_NAIVE = 1, 2
+MOE_FLAG_DECODE_CHAIN = 4
+MOE_WS_SYNC_BYTES = 32768
+MOE_PLAN_PAIR, MOE_PLAN_CHAIN, MOE_PLAN_PREFILL = 1, 2, 3
 MOE_NOALLOC_SCRATCH_BYTES = 33554432
 
 c_i32, c_u64, c_size, c_vp, c_f32 = ctypes.c_int32, ctypes.c_uint64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
@@ -51,6 +54,7 @@ SIGNATURES = {
     "moe_combine": (ctypes.c_int, [ctypes.POINTER(moe_layer_t), c_vp, c_vp, c_vp, c_vp, ctypes.c_int, c_vp, c_vp]),
     "moe_layer_forward": (ctypes.c_int, [ctypes.POINTER(moe_layer_t), c_vp, c_vp, ctypes.c_int, c_vp, c_vp, c_vp,
                                          c_size, c_vp]),
+    "moe_layer_plan": (ctypes.c_int, [ctypes.POINTER(moe_layer_t), ctypes.c_int]),
     "moe_layer_forward_timed": (ctypes.c_int, [ctypes.POINTER(moe_layer_t), c_vp, c_vp, ctypes.c_int, c_vp, c_vp, c_vp,
                                                c_size, c_vp, ctypes.POINTER(c_vp)]),
     "moe_layer_forward_noalloc": (ctypes.c_int, [ctypes.POINTER(moe_layer_t), c_vp, c_vp, ctypes.c_int, c_vp, c_vp,
@@ -188,6 +192,14 @@ def moe_combine(layer, residual, y, w, shared_g, T, out, stream=None) -> None:
 def moe_layer_forward(layer, x, residual, T, out, idx_out, ws, ws_bytes, stream=None) -> None:
     _check(lib().moe_layer_forward(_ref(layer), ptr(x), ptr(residual), T, ptr(out), ptr(idx_out), ptr(ws), ws_bytes,
                                    stream_handle(stream)), "moe_layer_forward")
+
+
+def moe_layer_plan(layer, T: int) -> int:
+    """MOE_PLAN_PAIR, MOE_PLAN_CHAIN or MOE_PLAN_PREFILL for T tokens of this layer on the current device."""
+    code = lib().moe_layer_plan(_ref(layer), T)
+    if code < 0:
+        raise MoeError(code, "moe_layer_plan")
+    return code
 
 
 def moe_layer_forward_noalloc(layer, x, residual, T, out, idx_out, stream=None) -> None:

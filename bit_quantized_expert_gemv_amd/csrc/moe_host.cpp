@@ -92,11 +92,12 @@ bool geometry_from(const moe_layer_t* L, Geometry* g, const char** why) {
     return false;
   }
   if (L->has_shared != 0 && L->has_shared != 1) { *why = "has_shared must be 0 or 1"; return false; }
-  const int form = L->flags;
+  const int form = L->flags & ~MOE_FLAG_DECODE_CHAIN;
   if (form != 0 && form != MOE_FLAG_DEQUANT_LITERAL && form != MOE_FLAG_DEQUANT_NAIVE) {
-    *why = "flags must be 0, MOE_FLAG_DEQUANT_LITERAL or MOE_FLAG_DEQUANT_NAIVE";
+    *why = "flags must be 0, MOE_FLAG_DEQUANT_LITERAL or MOE_FLAG_DEQUANT_NAIVE, optionally with MOE_FLAG_DECODE_CHAIN";
     return false;
   }
+  g->chain = (L->flags & MOE_FLAG_DECODE_CHAIN) != 0;
   if (mx && form != 0) { *why = "the dequant-form flags apply to the affine format only"; return false; }
   g->form = mx ? 3 : form == MOE_FLAG_DEQUANT_LITERAL ? 1 : form == MOE_FLAG_DEQUANT_NAIVE ? 2 : 0;
   g->H = L->hidden; g->I = L->inter; g->E = L->n_experts; g->K = L->top_k;
@@ -114,7 +115,7 @@ bool geometry_from(const moe_layer_t* L, Geometry* g, const char** why) {
 
 size_t workspace_layer_bytes(const Geometry& g, int T) {
   const size_t t = (size_t)T;
-  return align256(t * (g.E + 1) * 8) + align256(t * g.K * 4) + align256(t * g.K * 4) + align256(t * 4) +
+  return MOE_WS_SYNC_BYTES + align256(t * (g.E + 1) * 8) + align256(t * g.K * 4) + align256(t * g.K * 4) + align256(t * 4) +
          align256(t * g.NE * g.I * 4) + align256(t * g.H * 4) + align256((size_t)g.E * 8);
 }
 
@@ -132,6 +133,7 @@ struct Carver {
 
 PrefillWorkspace carve_prefill_impl(const Geometry& g, int T, void* base, size_t* total) {
   Carver c{static_cast<uint8_t*>(base)};
+  c.take<uint8_t>(MOE_WS_SYNC_BYTES);  // the sync region, which only the single-launch decode uses
   const size_t t = (size_t)T, N = t * g.K, R = N + t * g.has_shared;
   PrefillWorkspace w;
   w.layer.logits = c.take<double>(t * (g.E + 1));
@@ -180,7 +182,7 @@ PrefillWorkspace carve_prefill(const Geometry& g, int T, void* base) {
 
 Workspace carve_workspace(const Geometry& g, int T, void* base) {
   const size_t t = (size_t)T;
-  uint8_t* p = static_cast<uint8_t*>(base);
+  uint8_t* p = static_cast<uint8_t*>(base) + MOE_WS_SYNC_BYTES;  // after the sync region
   Workspace ws;
   ws.logits = reinterpret_cast<double*>(p); p += align256(t * (g.E + 1) * 8);
   ws.idx = reinterpret_cast<int32_t*>(p); p += align256(t * g.K * 4);
@@ -443,10 +445,24 @@ int moe_layer_forward_timed(const moe_layer_t* layer, const float* x, const floa
     return hip_status(e);
   }
   const Workspace W = carve_workspace(g, T, ws);
+  if (T == 1 && pair_supported(g))
+    return hip_status(launch_pair(g, p, x, residual, out, idx_out, W, static_cast<uint8_t*>(ws), nullptr, s, ev(0),
+                                  ev(2)));
   hipError_t e = launch_router_phase(g, p, x, nullptr, 0.0f, T, W, s, ev(0));
   if (e == hipSuccess) e = launch_gateup(g, p, x, T, W, nullptr, idx_out, true, nullptr, s, ev(1));
   if (e == hipSuccess) e = launch_down(g, p, T, W, W.idx, residual, out, nullptr, s, ev(2));
   return hip_status(e);
+}
+
+int moe_layer_plan(const moe_layer_t* layer, int T) {
+  if (layer == nullptr) return fail(MOE_EINVAL, "layer is NULL");
+  Geometry g;
+  const char* why = nullptr;
+  if (!geometry_from(layer, &g, &why)) return fail(MOE_EUNSUPPORTED, why);
+  if (T < 1) return fail(MOE_EINVAL, "T must be >= 1");
+  ok();
+  if (use_prefill(g, T)) return MOE_PLAN_PREFILL;
+  return T == 1 && pair_supported(g) ? MOE_PLAN_PAIR : MOE_PLAN_CHAIN;
 }
 
 int moe_layer_forward_noalloc(const moe_layer_t* layer, const float* x, const float* residual, int T, float* out,
@@ -512,6 +528,7 @@ const char* moe_strerror(int code) {
     case MOE_EUNSUPPORTED: return "unsupported shape or format";
     case MOE_ENOSPC: return "workspace too small";
     case MOE_EHIP: return "HIP error";
+    case MOE_ETIMEOUT: return "the decode's first kernel gave up waiting for its blocks";
     default: return "unknown error";
   }
 }

@@ -21,6 +21,7 @@ struct Geometry {
   int H, I, E, K, NE;  // NE = K + has_shared: expert slots per token
   int bits, G, has_shared;
   int form;               // decode GEMV arithmetic: 0 per-chunk x-sums, 1 fma(q, s*x, b*x), 2 (q*s + b)*x
+  int chain;              // MOE_FLAG_DECODE_CHAIN: single tokens as the three-kernel chain
   uint64_t off_codes[3];  // byte offsets of gate / up / down codes inside a blob
   uint64_t off_sb[3];     // byte offsets of gate / up / down (scale, bias) words
   uint64_t blob_bytes;
@@ -117,6 +118,14 @@ hipError_t launch_router_approx(const Geometry& g, const LayerPtrs& p, const flo
 hipError_t launch_router_select(const Geometry& g, const LayerPtrs& p, const float* x, int T, const Workspace& ws,
                                 int32_t* idx, float* w, float* sg, double* logits_out, int32_t* idx_b,
                                 hipStream_t s);
+// The two-launch decode of one token: whether this layer and the current device take it, and the
+// launches (router, top-K and gate/up + SwiGLU in one kernel, then the down + combine kernel). sync
+// is the workspace's zero-initialised sync region of MOE_WS_SYNC_BYTES; err (optional, device)
+// receives MOE_ETIMEOUT if the first kernel gives up waiting for its blocks.
+bool pair_supported(const Geometry& g);
+hipError_t launch_pair(const Geometry& g, const LayerPtrs& p, const float* x, const float* residual, float* out,
+                       int32_t* idx_out, const Workspace& ws, uint8_t* sync, int32_t* err, hipStream_t s,
+                       const KernelEvents& ev_front = {}, const KernelEvents& ev_down = {});
 // Top-K + weights from ws.logits (router-only path); idx_b, if non-null, receives a copy of idx.
 hipError_t launch_topk(const Geometry& g, int T, const Workspace& ws, int32_t* idx, float* w, float* sg,
                        double* logits_out, int32_t* idx_b, hipStream_t s);

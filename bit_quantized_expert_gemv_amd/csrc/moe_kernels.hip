@@ -1012,6 +1012,244 @@ __global__ __launch_bounds__(2 * kBlock) void k_down(LayerArgs a, const int32_t*
   }
 }
 
+// ---- one token in two launches ---------------------------------------------------------------------
+// Kernel 1 and kernel 2 above as one launch, k_front, followed by k_down. The launch has kFrontBlocks
+// blocks, all resident at once (the host checks the occupancy before it takes this path). Block b
+// computes router rows b and b + 256 and, after the top-K, SwiGLU outputs [4b, 4b + 4) of every
+// expert slot, so it streams a 1/256 share of the router and of every selected gate/up matrix. The
+// logits cross blocks inside the launch: each is stored as two 64-bit words, (tag, upper half) and
+// (tag, lower half), with write-through (agent-scope) stores, and one wave per block polls the words
+// themselves with agent-scope loads until every one carries this call's tag. There is no separate
+// flag, fence or second round trip on that path. The tag is the call's sequence number + 1; the
+// sequence word lives in the workspace's sync region and block 0 advances it at the end of the
+// call, when every block has read it. The region starts zeroed, so a stale word never carries the
+// current tag. The shared expert's rows need no routing and are requested at the start.
+// The wait is bounded: a block that gives up writes NaN into its SwiGLU outputs (so the down kernel
+// writes NaN rows) and marks the region, and every later call on it does the same until the region
+// is zeroed again.
+// Measured alternatives (decode4, same box): the down rows in the same launch, with the SwiGLU
+// outputs handed over through per-block ready tags, 16.3-17.1 us/token against 14.1-14.4 here and
+// 15.4 for the three-kernel chain (256 blocks polling the same tags and reading the same 16 KB from
+// memory cost ~4 us, and the down compute then sits on the critical path); the top-K split over all
+// 8 waves with a merge, 15.1 (2048 pollers contend, and the merge adds a barrier).
+constexpr int kFrontBlocks = 256;
+constexpr int kFrontWaves = 8;
+constexpr size_t kSyncSeq = 0;       // uint32: calls completed on this workspace
+constexpr size_t kSyncPoison = 128;  // uint32: nonzero once a call gave up
+constexpr size_t kSyncLogits = 2048; // uint64[2 (E + 1)]: tagged halves of the fp64 logits
+static_assert(kSyncLogits + 16 * (2 * kFrontBlocks + 1) <= MOE_WS_SYNC_BYTES, "sync region too small");
+#ifndef BQ_SPIN_TICKS
+#define BQ_SPIN_TICKS 2000000  // 20 ms of the 100 MHz real-time counter
+#endif
+
+__device__ __forceinline__ uint64_t ld_agent(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Repeats poll() (true once its condition holds) with a short sleep between tries, until it holds
+// or about BQ_SPIN_TICKS of the 100 MHz real-time counter have passed. The counter is a scalar
+// memory read, so it is read only every 64 tries.
+template <class F>
+__device__ __forceinline__ bool spin_poll(F poll) {
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  for (uint32_t it = 1;; ++it) {
+    if (poll()) return true;
+    if ((it & 63) == 0 && __builtin_amdgcn_s_memrealtime() - t0 > (uint64_t)BQ_SPIN_TICKS) return false;
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+__device__ __forceinline__ void store_logit(uint64_t* tl, int r, uint32_t tag, double v) {
+  const uint64_t bits = (uint64_t)__double_as_longlong(v);
+  store_through(&tl[2 * r], (uint64_t)(((uint64_t)tag << 32) | (bits >> 32)));
+  store_through(&tl[2 * r + 1], (uint64_t)(((uint64_t)tag << 32) | (bits & 0xFFFFFFFFull)));
+}
+
+#ifdef BQ_TIMELINE  // measurement builds: per-block real-time stamps in the sync region's tail
+#define BQ_TLT(k, th)                                                                                        \
+  do {                                                                                                       \
+    if (tid == (th)) reinterpret_cast<uint64_t*>(sync + 12288)[b * 10 + (k)] = __builtin_amdgcn_s_memrealtime(); \
+  } while (0)
+#else
+#define BQ_TLT(k, th) \
+  do {                \
+  } while (0)
+#endif
+#define BQ_TL(k) BQ_TLT(k, 0)
+
+template <int BITS, int FORM, int K, int SH>
+__global__ __launch_bounds__(64 * kFrontWaves) void k_front(LayerArgs a, const float* __restrict__ x,
+                                                            int32_t* __restrict__ idx_out, uint8_t* __restrict__ sync) {
+  constexpr int H = 4096, I = 1024, NW = kFrontWaves, NT = 64 * NW, NE = K + SH;
+  constexpr bool MX = FORM == 3;
+  using Cg = RowCfg<BITS, H>;  // gate/up rows: one row per wave per step (64 lanes)
+  using R = RouterCfg<H>;
+  constexpr int HB = I / kFrontBlocks;  // SwiGLU outputs per block and slot
+  constexpr int RCH = R::CPL / 4;       // router chunks per lane: a row over 4 waves
+  constexpr int Q = Cg::CH / 4;         // float4 per gate/up chunk
+  static_assert(Cg::LPR == 64 && Cg::RPW == 1 && 2 * HB == NW, "one gate or up row per wave and slot");
+  static_assert(R::LPR == 64 && R::CPL % 4 == 0, "router rows over four waves");
+
+  __shared__ float4 xs[H / 4];
+  __shared__ double rpart[NW];
+  __shared__ double gpart[4];
+  __shared__ float gu[NE][NW];
+  __shared__ int32_t sel[MOE_MAX_TOP_K];
+  __shared__ double val[MOE_MAX_TOP_K];
+  __shared__ int status;
+
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int E = a.E;
+  const int nrows = E + SH;
+  uint32_t* seqp = reinterpret_cast<uint32_t*>(sync + kSyncSeq);
+  uint32_t* poisonp = reinterpret_cast<uint32_t*>(sync + kSyncPoison);
+  uint64_t* tl = reinterpret_cast<uint64_t*>(sync + kSyncLogits);
+  BQ_TL(0);
+
+  // ---- requests that need no routing: the sequence word, x, router rows, the shared expert's rows
+  const uint32_t seq = __hip_atomic_load(seqp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t poison = __hip_atomic_load(poisonp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  Stage<H, NT> st;
+  st.load(x, tid);
+  // router rows: waves 0-3 take row b, waves 4-7 row b + 256, each a quarter (the split of the
+  // three-kernel router, so the logits are the same bit for bit); in block 0, when E = 512, waves
+  // 0-3 also take the shared-gate row
+  const int rrow = wave < 4 ? b : b + kFrontBlocks;
+  const int piece = wave & 3;
+  const bool third = SH && b == 0 && nrows > 2 * kFrontBlocks && wave < 4;
+  uint4 rw[RCH], gw[RCH];
+  {
+    const int rr = min(rrow, nrows - 1);
+    const uint16_t* row = rr < E ? a.router + (size_t)rr * H : a.sgate;
+#pragma unroll
+    for (int j = 0; j < RCH; ++j) rw[j] = *reinterpret_cast<const uint4*>(row + (lane + (j * 4 + piece) * 64) * 8);
+    if (third) {
+#pragma unroll
+      for (int j = 0; j < RCH; ++j) gw[j] = *reinterpret_cast<const uint4*>(a.sgate + (lane + (j * 4 + piece) * 64) * 8);
+    }
+  }
+  // gate/up rows: wave w takes matrix w / HB (gate, up), row HB*b + w % HB, in every slot
+  const int gm = wave / HB;
+  const int grow = b * HB + wave % HB;
+  uint4 cg[NE][Cg::CPL];
+  uint32_t sg[NE][Cg::CPL];
+  if constexpr (SH) load_row<Cg, MX>(a.shared + a.off_codes[gm], a.shared + a.off_sb[gm], grow, lane, cg[K], sg[K]);
+  __builtin_amdgcn_sched_barrier(0);
+  st.template store<Cg>(xs, tid, 1.0f);
+  __syncthreads();
+  BQ_TL(1);
+  const uint32_t tag = seq + 1u;
+  auto give_up = [&]() __attribute__((always_inline)) {  // the whole block: NaN outputs, mark the region
+    if (tid < NE * HB) store_through(&a.ws.h[(size_t)(tid / HB) * I + b * HB + tid % HB], (float)NAN);
+    if (tid == 0) {
+      store_through(poisonp, 1u);
+      if (a.err != nullptr) *a.err = MOE_ETIMEOUT;
+    }
+  };
+  if (poison != 0) {
+    give_up();
+    return;
+  }
+
+  // ---- router dot products in fp64 from the parked activations; the logits go out tagged
+  {
+    auto xchunk = [&](int c, float (&xv)[8]) __attribute__((always_inline)) {
+      const float4 u = xs[xslot<Cg>((2 * c) / Q, (2 * c) % Q)], v = xs[xslot<Cg>((2 * c + 1) / Q, (2 * c + 1) % Q)];
+      xv[0] = u.x; xv[1] = u.y; xv[2] = u.z; xv[3] = u.w; xv[4] = v.x; xv[5] = v.y; xv[6] = v.z; xv[7] = v.w;
+    };
+    auto rowdot = [&](const uint4 (&w)[RCH]) __attribute__((always_inline)) {
+      double acc[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+      for (int j = 0; j < RCH; ++j) {
+        float xv[8];
+        xchunk(lane + (j * 4 + piece) * 64, xv);
+        const uint32_t ww[4] = {w[j].x, w[j].y, w[j].z, w[j].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[q] = fma((double)bf16_lo(ww[q]), (double)xv[2 * q], acc[q]);
+          acc[q] = fma((double)bf16_hi(ww[q]), (double)xv[2 * q + 1], acc[q]);
+        }
+      }
+      return seg_sum<64>((acc[0] + acc[1]) + (acc[2] + acc[3]));
+    };
+    const double t0 = rowdot(rw);
+    if (lane == 63) rpart[wave] = t0;
+    if (third) {
+      const double t1 = rowdot(gw);
+      if (lane == 63) gpart[wave] = t1;
+    }
+  }
+  __syncthreads();
+  if (lane == 0 && (wave == 0 || wave == 4)) {
+    const int r = b + (wave == 4 ? kFrontBlocks : 0);
+    if (r < nrows) store_logit(tl, r, tag, ((rpart[wave] + rpart[wave + 1]) + rpart[wave + 2]) + rpart[wave + 3]);
+  }
+  if (SH && b == 0 && nrows > 2 * kFrontBlocks && tid == 64)
+    store_logit(tl, 2 * kFrontBlocks, tag, ((gpart[0] + gpart[1]) + gpart[2]) + gpart[3]);
+  BQ_TL(2);
+
+  // the shared expert's gate/up rows while the logits travel
+  float xr[Cg::XPL], S[Cg::CPL];
+  read_act<Cg>(xs, lane, xr, S);
+  if constexpr (SH) {
+    const float p = seg_sum<64>(row_partial<BITS, Cg, FORM>(cg[K], sg[K], xr, S));
+    if (lane == 63) gu[K][wave] = p;
+  }
+
+  // ---- wave 0: wait for every logit, then the top-K
+  double gate_logit = 0.0;
+  if (wave == 0) {
+    double v[8];
+    const bool done = spin_poll([&]() __attribute__((always_inline)) {
+      uint32_t bad = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int e = lane + 64 * i;
+        const int ee = min(e, E - 1);
+        const uint64_t w0 = ld_agent(&tl[2 * ee]), w1 = ld_agent(&tl[2 * ee + 1]);
+        bad |= (uint32_t)((w0 >> 32) != tag) | (uint32_t)((w1 >> 32) != tag);
+        v[i] = e < E ? __longlong_as_double((long long)((w0 << 32) | (w1 & 0xFFFFFFFFull))) : -INFINITY;
+      }
+      if constexpr (SH) {
+        const uint64_t w0 = ld_agent(&tl[2 * E]), w1 = ld_agent(&tl[2 * E + 1]);
+        bad |= (uint32_t)((w0 >> 32) != tag) | (uint32_t)((w1 >> 32) != tag);
+        gate_logit = __longlong_as_double((long long)((w0 << 32) | (w1 & 0xFFFFFFFFull)));
+      }
+      return __ballot(bad != 0) == 0;
+    });
+    BQ_TL(3);
+    if (done) wave_topk_fast<8>(v, E, K, lane, 0, true, sel, val);
+    if (lane == 0) status = done ? 0 : 1;
+  }
+  __syncthreads();
+  if (status != 0) {
+    give_up();
+    return;
+  }
+  BQ_TL(4);
+
+  // ---- the routed experts' gate/up rows, SwiGLU
+#pragma unroll
+  for (int s = 0; s < K; ++s) {
+    const uint8_t* blob = a.experts + (size_t)sel[s] * a.stride;
+    load_row<Cg, MX>(blob + a.off_codes[gm], blob + a.off_sb[gm], grow, lane, cg[s], sg[s]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if (b == 0 && wave == 0)  // the routing for the down kernel, after this block's loads
+    write_routing(a, 0, lane, sel, val, gate_logit, a.ws.idx, a.ws.w, idx_out, a.ws.g);
+#pragma unroll
+  for (int s = 0; s < K; ++s) {
+    const float p = seg_sum<64>(row_partial<BITS, Cg, FORM>(cg[s], sg[s], xr, S));
+    if (lane == 63) gu[s][wave] = p;
+  }
+  BQ_TL(5);
+  __syncthreads();
+  if (tid < NE * HB) {  // written through: the down kernel reads them next, mostly on other XCDs
+    const int s = tid / HB, i = tid % HB;
+    store_through(&a.ws.h[(size_t)s * I + b * HB + i], silu_mul(gu[s][i], gu[s][i + HB]));
+  }
+  if (b == 0 && tid == 0) store_through(seqp, tag);  // every block has read the sequence word by now
+}
+
 // Router-only top-K: one wave per token.
 template <int PL>
 __global__ __launch_bounds__(64) void k_topk(LayerArgs a, int32_t* __restrict__ idx, float* __restrict__ w,
@@ -1376,6 +1614,31 @@ hipError_t down_impl(const LayerArgs& a, int T, const int32_t* idx, const float*
 #undef BQ_DN
 }
 
+
+// The two-launch decode's first kernel: 4-bit and 2-bit affine, top-3 + shared, H 4096, I 1024.
+template <int BITS>
+constexpr auto front_kernel() { return k_front<BITS, 0, 3, 1>; }
+
+// Whether every block of k_front (kFrontBlocks blocks of 512 threads) can be resident at once on
+// the current device: the occupancy per CU times the CU count, looked up once per device.
+template <int BITS>
+bool front_resident() {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static signed char known[kMaxDevices] = {};  // 0 unknown, 1 yes, -1 no
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return false;
+  std::lock_guard<std::mutex> lock(mu);
+  if (known[dev] == 0) {
+    int cus = 0, per_cu = 0;
+    const bool ok = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+                    hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, front_kernel<BITS>(), 64 * kFrontWaves, 0) ==
+                        hipSuccess &&
+                    (long)cus * per_cu >= kFrontBlocks;
+    known[dev] = ok ? 1 : -1;
+  }
+  return known[dev] > 0;
+}
 }  // namespace
 
 hipError_t launch_router_phase(const Geometry& g, const LayerPtrs& p, const float* x, const float* norm_src,
@@ -1414,6 +1677,25 @@ hipError_t launch_down(const Geometry& g, const LayerPtrs& p, int T, const Works
   switch (g.I) { BQ_FOR_I(BQ_CASE) }
 #undef BQ_CASE
   return hipErrorInvalidValue;
+}
+
+bool pair_supported(const Geometry& g) {
+  if (g.H != 4096 || g.I != 1024 || g.E > 2 * kFrontBlocks || g.K != 3 || !g.has_shared || g.form != 0 ||
+      g.chain || g.G != 64)
+    return false;
+  return g.bits == 4 ? front_resident<4>() : g.bits == 2 ? front_resident<2>() : false;
+}
+
+hipError_t launch_pair(const Geometry& g, const LayerPtrs& p, const float* x, const float* residual, float* out,
+                       int32_t* idx_out, const Workspace& ws, uint8_t* sync, int32_t* err, hipStream_t s,
+                       const KernelEvents& ev_front, const KernelEvents& ev_down) {
+  LayerArgs a = make_args(g, p, ws);
+  a.err = err;
+  const dim3 grid(kFrontBlocks), block(64 * kFrontWaves);
+  const hipError_t e = g.bits == 4 ? launch_timed(front_kernel<4>(), grid, block, s, ev_front, a, x, idx_out, sync)
+                                   : launch_timed(front_kernel<2>(), grid, block, s, ev_front, a, x, idx_out, sync);
+  if (e != hipSuccess) return e;
+  return launch_down(g, p, 1, ws, ws.idx, residual, out, nullptr, s, ev_down);
 }
 
 hipError_t launch_topk(const Geometry& g, int T, const Workspace& ws, int32_t* idx, float* w, float* sg,

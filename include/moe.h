@@ -65,6 +65,7 @@ extern "C" {
 #define MOE_EUNSUPPORTED (-2) /* a shape or format the library does not implement (see moe_layer_t) */
 #define MOE_ENOSPC (-3)       /* workspace smaller than moe_workspace_bytes() */
 #define MOE_EHIP (-4)         /* a HIP call or kernel launch failed */
+#define MOE_ETIMEOUT (-5)     /* written to a device error word: the decode's first kernel gave up waiting */
 
 #define MOE_MAX_TOP_K 8
 #define MOE_MAX_EXPERTS 1024
@@ -88,6 +89,19 @@ extern "C" {
  * differ only by rounding. The prefill GEMMs ignore the flag. */
 #define MOE_FLAG_DEQUANT_LITERAL 1
 #define MOE_FLAG_DEQUANT_NAIVE 2
+/* Single-token calls of moe_layer_forward run as two launches when the layer and the device allow it
+ * (MOE_PLAN_PAIR, see moe_layer_plan); this flag makes them run as the three-kernel chain (router;
+ * top-K + gate/up + SwiGLU; down + combine) instead. Both give the same results bit for bit. */
+#define MOE_FLAG_DECODE_CHAIN 4
+
+/* Workspace sync region. The first MOE_WS_SYNC_BYTES bytes of every workspace hold the cross-block
+ * state of the two-launch decode (a call counter and the router logits tagged with it). They must
+ * be zero before the first call that uses the workspace (allocate it zeroed, or zero that prefix
+ * once); calls keep them valid afterwards, and nothing else in the library writes there. A call
+ * whose first kernel cannot have all of its blocks resident within about 20 ms writes NaN to its
+ * output and marks the region; every later such call on that workspace then writes NaN until the
+ * region is zeroed again. */
+#define MOE_WS_SYNC_BYTES 32768
 
 /* One MoE layer.
  *   hidden H, inter I: powers of two with 256 <= H <= 8192 and 64 <= I <= 2048. bits 2 or 4 with
@@ -98,8 +112,8 @@ extern "C" {
  *   shared_blob_dev and shared_gate_dev: the shared expert's blob and its gate vector (bf16 [H]).
  *   Required when has_shared is 1, ignored when it is 0.
  *   router_dev: bf16 [E][H] row-major; logit e = row e . x, with no bias.
- *   flags: 0, MOE_FLAG_DEQUANT_LITERAL or MOE_FLAG_DEQUANT_NAIVE (the latter two affine only;
- *   other values: MOE_EUNSUPPORTED). */
+ *   flags: 0, MOE_FLAG_DEQUANT_LITERAL or MOE_FLAG_DEQUANT_NAIVE (the latter two affine only),
+ *   optionally or'ed with MOE_FLAG_DECODE_CHAIN; other values: MOE_EUNSUPPORTED. */
 typedef struct moe_layer_t {
   int32_t hidden;
   int32_t inter;
@@ -213,12 +227,27 @@ int moe_combine(const moe_layer_t* layer, const float* residual_dev, const float
  * T < MOE_PREFILL_MIN_TOKENS runs the decode path, in which each token streams its experts'
  * weights with GEMV kernels. Larger T runs the prefill path, which groups tokens by expert
  * ("Deferred GPU Expert Compute" is the one-stream, no-host-sync submission model both follow).
- * idx_out_dev int32 [T][K] may be NULL. x_dev and out_dev may not alias; residual_dev may alias x_dev. */
+ * A single token (T = 1) runs as two launches where moe_layer_plan says so, else as three kernels.
+ * idx_out_dev int32 [T][K] may be NULL. x_dev and out_dev may not alias; residual_dev may alias x_dev.
+ * The workspace's first MOE_WS_SYNC_BYTES bytes must be zero before its first use (see there). */
 int moe_layer_forward(const moe_layer_t* layer, const float* x_dev, const float* residual_dev, int T, float* out_dev,
                       int32_t* idx_out_dev, void* ws_dev, size_t ws_bytes, void* stream);
 
+/* How moe_layer_forward runs T tokens of this layer on the current device: MOE_PLAN_PAIR (router,
+ * top-K and gate/up + SwiGLU in one launch, then the down + combine kernel), MOE_PLAN_CHAIN (three
+ * kernels per call), MOE_PLAN_PREFILL (tokens grouped by expert), or a negative error code. PAIR
+ * takes T = 1 on layers with H = 4096, I = 1024, E <= 512, top_k 3 with a shared expert, the
+ * per-chunk dequant form, without MOE_FLAG_DECODE_CHAIN, on a device where all 256 blocks of 512
+ * threads of its first kernel can be resident at once. The answer is fixed for a layer and device. */
+#define MOE_PLAN_PAIR 1
+#define MOE_PLAN_CHAIN 2
+#define MOE_PLAN_PREFILL 3
+int moe_layer_plan(const moe_layer_t* layer, int T);
+
 /* Instrumented moe_layer_forward, for timing kernels in place: the same kernels on `stream`. In
- * the decode path kernel p (0 router, 1 gate/up + SwiGLU of the routed and shared experts,
+ * the PAIR plan the first launch takes events[0] and events[1], the down kernel events[4] and
+ * events[5]. In the three-kernel decode
+ * kernel p (0 router, 1 gate/up + SwiGLU of the routed and shared experts,
  * 2 down + combine) is launched with events[2p] and events[2p+1] as its start and stop events
  * (hipExtLaunchKernel). They then carry the dispatch's own begin and end timestamps, with no
  * extra packets in between. In the prefill path, events[0] and events[5] are recorded

@@ -143,7 +143,7 @@ def _layer(**kw):
     (dict(shared_gate=FAKE + 2), bq.MOE_EINVAL),
     (dict(flags=3), bq.MOE_EUNSUPPORTED),
     (dict(flags=-1), bq.MOE_EUNSUPPORTED),
-    (dict(flags=4), bq.MOE_EUNSUPPORTED),
+    (dict(flags=12), bq.MOE_EUNSUPPORTED),
     (dict(flags=7), bq.MOE_EUNSUPPORTED),
     (dict(flags=8), bq.MOE_EUNSUPPORTED),
     (dict(bits=2, group=32), bq.MOE_EUNSUPPORTED),

@@ -48,7 +48,7 @@ def dec2(gpu_device):
 
 def _ws(desc, T):
     n = bq.moe_workspace_bytes(desc, T)
-    return torch.empty(n, dtype=torch.uint8, device="cuda"), n
+    return torch.zeros(n, dtype=torch.uint8, device="cuda"), n
 
 
 def _x(w, t0, n):
@@ -292,7 +292,7 @@ def test_empty_calls_touch_nothing(tiny):
     y = torch.full((2, w.top_k + 1, w.hidden), 7.0, device="cuda")
     err = torch.full((1,), 7, dtype=torch.int32, device="cuda")
     sn = bq.moe_stack_workspace_bytes(L.desc, 2)
-    sws = torch.empty(sn, dtype=torch.uint8, device="cuda")
+    sws = torch.zeros(sn, dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
     bq.moe_layer_forward(L.desc, x, x, 0, out, idx, ws, n)
     bq.moe_layer_forward_noalloc(L.desc, x, x, 0, out, idx)
@@ -436,7 +436,7 @@ def test_router_token_groups_bitwise(which, T, request):
     w = L.w
     x = _x(w, 60, T)
     n = bq.moe_workspace_bytes(L.desc, T)
-    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
     idx = torch.empty(T, w.top_k, dtype=torch.int32, device="cuda")
     wt = torch.empty(T, w.top_k, dtype=torch.float32, device="cuda")
     lg = torch.empty(T, w.n_experts, dtype=torch.float64, device="cuda")
@@ -445,7 +445,7 @@ def test_router_token_groups_bitwise(which, T, request):
     i1 = torch.empty(1, w.top_k, dtype=torch.int32, device="cuda")
     w1 = torch.empty(1, w.top_k, dtype=torch.float32, device="cuda")
     n1 = bq.moe_workspace_bytes(L.desc, 1)
-    ws1 = torch.empty(n1, dtype=torch.uint8, device="cuda")
+    ws1 = torch.zeros(n1, dtype=torch.uint8, device="cuda")
     for t in range(T):
         bq.moe_router(L.desc, x[t:t + 1].contiguous(), 1, i1, w1, None, one, ws1, n1)
         torch.cuda.synchronize()

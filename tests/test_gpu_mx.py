@@ -42,7 +42,7 @@ def decmx(gpu_device):
 
 def _ws(desc, T):
     n = bq.moe_workspace_bytes(desc, T)
-    return torch.empty(n, dtype=torch.uint8, device="cuda"), n
+    return torch.zeros(n, dtype=torch.uint8, device="cuda"), n
 
 
 def _x(w, t0, n):

@@ -50,7 +50,7 @@ def _x(w, t0, n):
 def _forward(L, x):
     T = x.shape[0]
     n = bq.moe_workspace_bytes(L.desc, T)
-    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
     out = torch.empty_like(x)
     idx = torch.empty(T, L.w.top_k, dtype=torch.int32, device="cuda")
     bq.moe_layer_forward(L.desc, x, x, T, out, idx, ws, n)
@@ -93,7 +93,7 @@ def test_router_without_shared_gate(ns4):
     T = 5
     x = _x(w, 40, T)
     n = bq.moe_workspace_bytes(L.desc, T)
-    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
     idx = torch.empty(T, w.top_k, dtype=torch.int32, device="cuda")
     wt = torch.empty(T, w.top_k, dtype=torch.float32, device="cuda")
     lg = torch.empty(T, w.n_experts, dtype=torch.float64, device="cuda")
@@ -121,7 +121,7 @@ def test_expert_ffn_and_combine_without_shared(ns4, T):
     idx = torch.from_numpy(idx_np).cuda()
     y = torch.empty(T, w.top_k, w.hidden, dtype=torch.float32, device="cuda")
     n = bq.moe_workspace_bytes(L.desc, T)
-    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
     bq.moe_expert_ffn(L.desc, x, T, idx, y, ws, n)
     wts = torch.from_numpy(rng.dirichlet(np.ones(w.top_k), size=T).astype(np.float32)).cuda()
     out = torch.empty(T, w.hidden, dtype=torch.float32, device="cuda")

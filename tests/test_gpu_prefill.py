@@ -42,7 +42,7 @@ def pre4(gpu_device):
 def _forward(L, x, res=None):
     T = x.shape[0]
     n = bq.moe_workspace_bytes(L.desc, T)
-    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
     out = torch.empty_like(x)
     idx = torch.empty(T, L.w.top_k, dtype=torch.int32, device="cuda")
     bq.moe_layer_forward(L.desc, x, x if res is None else res, T, out, idx, ws, n)
@@ -133,7 +133,7 @@ def test_prefill4_full(pre4):
         assert_close(out[t], r.out, f"prefill out[{t}]")
     # the same tokens through the decode path (T=1 calls)
     n = bq.moe_workspace_bytes(L.desc, 1)
-    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
     for t in sample:
         o1 = torch.empty(1, PRE4.hidden, device="cuda")
         bq.moe_layer_forward(L.desc, x[t:t + 1], x[t:t + 1], 1, o1, None, ws, n)
@@ -146,7 +146,7 @@ def test_prefill_expert_ffn_and_router(pre4):
     T = 96
     x = torch.from_numpy(synth.tokens_x(PRE4, 3000, T)).cuda()
     n = bq.moe_workspace_bytes(L.desc, T)
-    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
     idx = torch.empty(T, PRE4.top_k, dtype=torch.int32, device="cuda")
     wt = torch.empty(T, PRE4.top_k, device="cuda")
     g = torch.empty(T, device="cuda")
@@ -214,7 +214,7 @@ def test_prefill_graph_replays_match_eager(which, T, request):
     x = torch.from_numpy(synth.tokens_x(w, 4000, T)).cuda()
     eager, eager_idx = _forward(L, x)
     n = bq.moe_workspace_bytes(L.desc, T)
-    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
     out = torch.empty_like(x)
     idx = torch.empty(T, w.top_k, dtype=torch.int32, device="cuda")
     s = torch.cuda.Stream()

@@ -66,7 +66,7 @@ def _route(L, x, with_logits):
     w = L.w
     T = x.shape[0]
     n = bq.moe_workspace_bytes(L.desc, T)
-    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
     idx = torch.empty(T, w.top_k, dtype=torch.int32, device="cuda")
     wt = torch.empty(T, w.top_k, dtype=torch.float32, device="cuda")
     g = torch.empty(T, dtype=torch.float32, device="cuda") if w.has_shared else None

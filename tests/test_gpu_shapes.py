@@ -62,7 +62,7 @@ def layers(gpu_device):
 def _forward(L, x):
     T = x.shape[0]
     n = bq.moe_workspace_bytes(L.desc, T)
-    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
     out = torch.empty_like(x)
     idx = torch.empty(T, L.w.top_k, dtype=torch.int32, device="cuda")
     bq.moe_layer_forward(L.desc, x, x, T, out, idx, ws, n)

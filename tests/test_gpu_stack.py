@@ -42,7 +42,7 @@ def _check_stack_token(t, ix_t, out_t, r, what):
 def _run_stack(layers, x, T):
     w = layers[0].w
     n = bq.moe_stack_workspace_bytes(layers[0].desc, T)
-    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
     out = torch.empty_like(x)
     idx = torch.empty(len(layers), T, w.top_k, dtype=torch.int32, device="cuda")
     bq.moe_stack_forward([L.desc for L in layers], EPS, x, T, out, idx, ws, n)
@@ -69,7 +69,7 @@ def test_stack_single_layer_equals_layer_forward(gpu_device):
     x = torch.from_numpy(synth.tokens_x(w, 0, 3)).cuda()
     out_s, idx_s = _run_stack([L], x, 3)
     n = bq.moe_workspace_bytes(L.desc, 3)
-    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
     out = torch.empty_like(x)
     idx = torch.empty(3, w.top_k, dtype=torch.int32, device="cuda")
     bq.moe_layer_forward(L.desc, x, x, 3, out, idx, ws, n)
@@ -88,7 +88,7 @@ def test_stack_graph_replays_match_oracle(gpu_device):
     want = [oracle.stack(xs[t], _oracle_layers(refs), w.top_k, w.group, EPS) for t in range(w.tokens)]
     out0, idx0 = _run_stack(layers, x, w.tokens)
     n = bq.moe_stack_workspace_bytes(layers[0].desc, w.tokens)
-    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
     out = torch.empty_like(x)
     idx = torch.empty(len(layers), w.tokens, w.top_k, dtype=torch.int32, device="cuda")
     s = torch.cuda.Stream()
@@ -133,7 +133,7 @@ def test_stack60_sequence(gpu_device):
         out = torch.empty_like(X)
         idx = torch.empty(N, w.layers, w.top_k, dtype=torch.int32, device="cuda")
         n = bq.moe_stack_workspace_bytes(layers[0].desc, 1)
-        ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+        ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
         descs = [L.desc for L in layers]
         s = torch.cuda.Stream()
         torch.cuda.synchronize()
