@@ -460,6 +460,12 @@ def bench_stack(args, w):
     n = bq.moe_stack_workspace_bytes(layers[0].desc, 1)
     ws = torch.zeros(n, dtype=torch.uint8, device=dev)
     descs = [L.desc for L in layers]
+    if args.chain:
+        for d in descs:
+            d.flags |= bq.MOE_FLAG_DECODE_CHAIN
+    plan_name = {bq.MOE_PLAN_PAIR: "two launches per layer", bq.MOE_PLAN_CHAIN: "three-kernel chain per layer"}[
+        bq.moe_layer_plan(descs[0], 1)]
+    print(f"[bench] plan: {plan_name}", file=sys.stderr, flush=True)
     stream = torch.cuda.Stream(device=dev)
     # one eager call before capture
     with torch.cuda.stream(stream):
@@ -489,7 +495,7 @@ def bench_stack(args, w):
             {"workload": f"{w.name}: {w.layers} MoE layers (hidden {w.hidden}, {w.n_experts} experts, inter {w.inter}, "
                          f"top-{w.top_k} + shared, {w.bits}-bit, all experts resident), {N} sequential single-token "
                          f"calls in one HIP graph, RMS norm between layers", "tokens_per_step": N,
-             "parallelism": "single GPU"},
+             "decode_plan": plan_name, "parallelism": "single GPU"},
             {"us_per_token": round(us, 2), "expert_GB/s": round(expert_bytes / (us * 1e-6) / 1e9, 1),
              "all_weights_GB/s": round((expert_bytes + router_bytes) / (us * 1e-6) / 1e9, 1),
              "expert_frac_of_peak": round(expert_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),

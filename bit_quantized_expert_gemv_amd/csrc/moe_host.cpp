@@ -446,8 +446,8 @@ int moe_layer_forward_timed(const moe_layer_t* layer, const float* x, const floa
   }
   const Workspace W = carve_workspace(g, T, ws);
   if (T == 1 && pair_supported(g))
-    return hip_status(launch_pair(g, p, x, residual, out, idx_out, W, static_cast<uint8_t*>(ws), nullptr, s, ev(0),
-                                  ev(2)));
+    return hip_status(launch_pair(g, p, x, nullptr, 0.0f, residual, out, idx_out, W, static_cast<uint8_t*>(ws),
+                                  nullptr, s, ev(0), ev(2)));
   hipError_t e = launch_router_phase(g, p, x, nullptr, 0.0f, T, W, s, ev(0));
   if (e == hipSuccess) e = launch_gateup(g, p, x, T, W, nullptr, idx_out, true, nullptr, s, ev(1));
   if (e == hipSuccess) e = launch_down(g, p, T, W, W.idx, residual, out, nullptr, s, ev(2));
@@ -513,9 +513,13 @@ int moe_stack_forward(const moe_layer_t* layers, int L, float eps, const float* 
     const float* norm_src = (l == 0) ? nullptr : h;
     const float* xin = (l == 0) ? x : W.u;
     int32_t* io = idx_out ? idx_out + (size_t)l * T * g.K : nullptr;
-    e = launch_router_phase(g, p, x, norm_src, eps, T, W, s);
-    if (e == hipSuccess) e = launch_gateup(g, p, xin, T, W, nullptr, io, true, nullptr, s);
-    if (e == hipSuccess) e = launch_down(g, p, T, W, W.idx, h, h_next, nullptr, s);
+    if (T == 1 && pair_supported(g)) {
+      e = launch_pair(g, p, x, norm_src, eps, h, h_next, io, W, static_cast<uint8_t*>(ws), nullptr, s);
+    } else {
+      e = launch_router_phase(g, p, x, norm_src, eps, T, W, s);
+      if (e == hipSuccess) e = launch_gateup(g, p, xin, T, W, nullptr, io, true, nullptr, s);
+      if (e == hipSuccess) e = launch_down(g, p, T, W, W.idx, h, h_next, nullptr, s);
+    }
     h = h_next;
   }
   return hip_status(e);

@@ -122,10 +122,13 @@ hipError_t launch_router_select(const Geometry& g, const LayerPtrs& p, const flo
 // launches (router, top-K and gate/up + SwiGLU in one kernel, then the down + combine kernel). sync
 // is the workspace's zero-initialised sync region of MOE_WS_SYNC_BYTES; err (optional, device)
 // receives MOE_ETIMEOUT if the first kernel gives up waiting for its blocks.
+// With norm_src non-null (the stack's layers after the first) the layer input is RMSNorm(norm_src)
+// with eps, computed as kernel 1 does; otherwise it is x.
 bool pair_supported(const Geometry& g);
-hipError_t launch_pair(const Geometry& g, const LayerPtrs& p, const float* x, const float* residual, float* out,
-                       int32_t* idx_out, const Workspace& ws, uint8_t* sync, int32_t* err, hipStream_t s,
-                       const KernelEvents& ev_front = {}, const KernelEvents& ev_down = {});
+hipError_t launch_pair(const Geometry& g, const LayerPtrs& p, const float* x, const float* norm_src, float eps,
+                       const float* residual, float* out, int32_t* idx_out, const Workspace& ws, uint8_t* sync,
+                       int32_t* err, hipStream_t s, const KernelEvents& ev_front = {},
+                       const KernelEvents& ev_down = {});
 // Top-K + weights from ws.logits (router-only path); idx_b, if non-null, receives a copy of idx.
 hipError_t launch_topk(const Geometry& g, int T, const Workspace& ws, int32_t* idx, float* w, float* sg,
                        double* logits_out, int32_t* idx_b, hipStream_t s);

@@ -301,15 +301,27 @@ struct Stage {
 };
 
 // This lane's activations (from LDS) and their per-chunk sums.
-template <class C>
+// An fp32 product that is always rounded: the compiler may not fuse it into a later addition.
+__device__ __forceinline__ float mul_rounded(float a, float b) {
+#pragma clang fp contract(off)
+  return a * b;
+}
+
+// With SCALED, each value is multiplied by `scale` as it is read (the same rounded fp32 products as
+// a scaled Stage::store).
+template <class C, bool SCALED = false>
 __device__ __forceinline__ void read_act(const float4* __restrict__ xs, int lir, float (&xr)[C::XPL],
-                                         float (&S)[C::CPL]) {
+                                         float (&S)[C::CPL], float scale = 1.0f) {
 #pragma unroll
   for (int j = 0; j < C::CPL; ++j) {
     const int chunk = lir + j * C::LPR;
 #pragma unroll
     for (int q = 0; q < C::CH / 4; ++q) {
-      const float4 t = xs[xslot<C>(chunk, q)];
+      float4 t = xs[xslot<C>(chunk, q)];
+      if constexpr (SCALED) {  // rounded products, never contracted into the sums below
+        t.x = mul_rounded(t.x, scale); t.y = mul_rounded(t.y, scale);
+        t.z = mul_rounded(t.z, scale); t.w = mul_rounded(t.w, scale);
+      }
       xr[j * C::CH + 4 * q + 0] = t.x;
       xr[j * C::CH + 4 * q + 1] = t.y;
       xr[j * C::CH + 4 * q + 2] = t.z;
@@ -1075,9 +1087,13 @@ __device__ __forceinline__ void store_logit(uint64_t* tl, int r, uint32_t tag, d
 #endif
 #define BQ_TL(k) BQ_TLT(k, 0)
 
+// norm: the stack's layers after the first route u = x / sqrt(mean(x^2) + eps) (unit-weight RMS
+// norm), computed as in kernel 1: the logits are the fp64 dot products with x times the fp64 scale,
+// and the experts read x times the scale rounded to fp32.
 template <int BITS, int FORM, int K, int SH>
-__global__ __launch_bounds__(64 * kFrontWaves) void k_front(LayerArgs a, const float* __restrict__ x,
-                                                            int32_t* __restrict__ idx_out, uint8_t* __restrict__ sync) {
+__global__ __launch_bounds__(64 * kFrontWaves) void k_front(LayerArgs a, const float* __restrict__ x, int norm,
+                                                            float eps, int32_t* __restrict__ idx_out,
+                                                            uint8_t* __restrict__ sync) {
   constexpr int H = 4096, I = 1024, NW = kFrontWaves, NT = 64 * NW, NE = K + SH;
   constexpr bool MX = FORM == 3;
   using Cg = RowCfg<BITS, H>;  // gate/up rows: one row per wave per step (64 lanes)
@@ -1091,6 +1107,7 @@ __global__ __launch_bounds__(64 * kFrontWaves) void k_front(LayerArgs a, const f
   __shared__ float4 xs[H / 4];
   __shared__ double rpart[NW];
   __shared__ double gpart[4];
+  __shared__ double psq[4];
   __shared__ float gu[NE][NW];
   __shared__ int32_t sel[MOE_MAX_TOP_K];
   __shared__ double val[MOE_MAX_TOP_K];
@@ -1171,6 +1188,18 @@ __global__ __launch_bounds__(64 * kFrontWaves) void k_front(LayerArgs a, const f
       }
       return seg_sum<64>((acc[0] + acc[1]) + (acc[2] + acc[3]));
     };
+    if (norm && wave < 4) {  // waves 0-3 hold the whole vector between them, in kernel 1's order
+      double ss = 0.0;
+#pragma unroll
+      for (int j = 0; j < RCH; ++j) {
+        float xv[8];
+        xchunk(lane + (j * 4 + piece) * 64, xv);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) ss = fma((double)xv[q], (double)xv[q], ss);
+      }
+      ss = seg_sum<64>(ss);
+      if (lane == 63) psq[wave] = ss;
+    }
     const double t0 = rowdot(rw);
     if (lane == 63) rpart[wave] = t0;
     if (third) {
@@ -1179,17 +1208,22 @@ __global__ __launch_bounds__(64 * kFrontWaves) void k_front(LayerArgs a, const f
     }
   }
   __syncthreads();
+  const double scale = norm ? rms_inv(((psq[0] + psq[1]) + psq[2]) + psq[3], H, eps) : 1.0;
   if (lane == 0 && (wave == 0 || wave == 4)) {
     const int r = b + (wave == 4 ? kFrontBlocks : 0);
-    if (r < nrows) store_logit(tl, r, tag, ((rpart[wave] + rpart[wave + 1]) + rpart[wave + 2]) + rpart[wave + 3]);
+    const double v = ((rpart[wave] + rpart[wave + 1]) + rpart[wave + 2]) + rpart[wave + 3];
+    if (r < nrows) store_logit(tl, r, tag, norm ? v * scale : v);
   }
-  if (SH && b == 0 && nrows > 2 * kFrontBlocks && tid == 64)
-    store_logit(tl, 2 * kFrontBlocks, tag, ((gpart[0] + gpart[1]) + gpart[2]) + gpart[3]);
+  if (SH && b == 0 && nrows > 2 * kFrontBlocks && tid == 64) {
+    const double v = ((gpart[0] + gpart[1]) + gpart[2]) + gpart[3];
+    store_logit(tl, 2 * kFrontBlocks, tag, norm ? v * scale : v);
+  }
   BQ_TL(2);
 
   // the shared expert's gate/up rows while the logits travel
   float xr[Cg::XPL], S[Cg::CPL];
-  read_act<Cg>(xs, lane, xr, S);
+  if (norm) read_act<Cg, true>(xs, lane, xr, S, (float)scale);
+  else read_act<Cg>(xs, lane, xr, S);
   if constexpr (SH) {
     const float p = seg_sum<64>(row_partial<BITS, Cg, FORM>(cg[K], sg[K], xr, S));
     if (lane == 63) gu[K][wave] = p;
@@ -1615,13 +1649,14 @@ hipError_t down_impl(const LayerArgs& a, int T, const int32_t* idx, const float*
 }
 
 
-// The two-launch decode's first kernel: 4-bit and 2-bit affine, top-3 + shared, H 4096, I 1024.
-template <int BITS>
-constexpr auto front_kernel() { return k_front<BITS, 0, 3, 1>; }
+// The two-launch decode's first kernel: 4-bit and 2-bit affine top-3 and MXFP4 top-6 layers, with a
+// shared expert, H 4096, I 1024.
+template <int BITS, int FORM, int K>
+constexpr auto front_kernel() { return k_front<BITS, FORM, K, 1>; }
 
 // Whether every block of k_front (kFrontBlocks blocks of 512 threads) can be resident at once on
 // the current device: the occupancy per CU times the CU count, looked up once per device.
-template <int BITS>
+template <int BITS, int FORM, int K>
 bool front_resident() {
   constexpr int kMaxDevices = 64;
   static std::mutex mu;
@@ -1632,7 +1667,7 @@ bool front_resident() {
   if (known[dev] == 0) {
     int cus = 0, per_cu = 0;
     const bool ok = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-                    hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, front_kernel<BITS>(), 64 * kFrontWaves, 0) ==
+                    hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, front_kernel<BITS, FORM, K>(), 64 * kFrontWaves, 0) ==
                         hipSuccess &&
                     (long)cus * per_cu >= kFrontBlocks;
     known[dev] = ok ? 1 : -1;
@@ -1680,20 +1715,28 @@ hipError_t launch_down(const Geometry& g, const LayerPtrs& p, int T, const Works
 }
 
 bool pair_supported(const Geometry& g) {
-  if (g.H != 4096 || g.I != 1024 || g.E > 2 * kFrontBlocks || g.K != 3 || !g.has_shared || g.form != 0 ||
-      g.chain || g.G != 64)
-    return false;
-  return g.bits == 4 ? front_resident<4>() : g.bits == 2 ? front_resident<2>() : false;
+  if (g.H != 4096 || g.I != 1024 || g.E > 2 * kFrontBlocks || !g.has_shared || g.chain) return false;
+  if (g.form == 0 && g.K == 3 && g.G == 64)
+    return g.bits == 4 ? front_resident<4, 0, 3>() : g.bits == 2 ? front_resident<2, 0, 3>() : false;
+  if (g.form == 3 && g.K == 6) return front_resident<4, 3, 6>();
+  return false;
 }
 
-hipError_t launch_pair(const Geometry& g, const LayerPtrs& p, const float* x, const float* residual, float* out,
-                       int32_t* idx_out, const Workspace& ws, uint8_t* sync, int32_t* err, hipStream_t s,
-                       const KernelEvents& ev_front, const KernelEvents& ev_down) {
+hipError_t launch_pair(const Geometry& g, const LayerPtrs& p, const float* x, const float* norm_src, float eps,
+                       const float* residual, float* out, int32_t* idx_out, const Workspace& ws, uint8_t* sync,
+                       int32_t* err, hipStream_t s, const KernelEvents& ev_front, const KernelEvents& ev_down) {
   LayerArgs a = make_args(g, p, ws);
   a.err = err;
   const dim3 grid(kFrontBlocks), block(64 * kFrontWaves);
-  const hipError_t e = g.bits == 4 ? launch_timed(front_kernel<4>(), grid, block, s, ev_front, a, x, idx_out, sync)
-                                   : launch_timed(front_kernel<2>(), grid, block, s, ev_front, a, x, idx_out, sync);
+  const float* in = norm_src != nullptr ? norm_src : x;
+  const int norm = norm_src != nullptr;
+  hipError_t e;
+  if (g.form == 3)
+    e = launch_timed(front_kernel<4, 3, 6>(), grid, block, s, ev_front, a, in, norm, eps, idx_out, sync);
+  else if (g.bits == 4)
+    e = launch_timed(front_kernel<4, 0, 3>(), grid, block, s, ev_front, a, in, norm, eps, idx_out, sync);
+  else
+    e = launch_timed(front_kernel<2, 0, 3>(), grid, block, s, ev_front, a, in, norm, eps, idx_out, sync);
   if (e != hipSuccess) return e;
   return launch_down(g, p, 1, ws, ws.idx, residual, out, nullptr, s, ev_down);
 }

@@ -236,9 +236,11 @@ int moe_layer_forward(const moe_layer_t* layer, const float* x_dev, const float*
 /* How moe_layer_forward runs T tokens of this layer on the current device: MOE_PLAN_PAIR (router,
  * top-K and gate/up + SwiGLU in one launch, then the down + combine kernel), MOE_PLAN_CHAIN (three
  * kernels per call), MOE_PLAN_PREFILL (tokens grouped by expert), or a negative error code. PAIR
- * takes T = 1 on layers with H = 4096, I = 1024, E <= 512, top_k 3 with a shared expert, the
- * per-chunk dequant form, without MOE_FLAG_DECODE_CHAIN, on a device where all 256 blocks of 512
- * threads of its first kernel can be resident at once. The answer is fixed for a layer and device. */
+ * takes T = 1 on layers with H = 4096, I = 1024, E <= 512 and a shared expert, either affine
+ * (2- or 4-bit) at top_k 3 with the per-chunk dequant form or MXFP4 at top_k 6, without
+ * MOE_FLAG_DECODE_CHAIN, on a device where all 256 blocks of 512 threads of its first kernel can be
+ * resident at once. moe_stack_forward runs each layer of a single-token call the same way. The
+ * answer is fixed for a layer and device. */
 #define MOE_PLAN_PAIR 1
 #define MOE_PLAN_CHAIN 2
 #define MOE_PLAN_PREFILL 3

@@ -140,3 +140,61 @@ def test_marked_sync_region_writes_nan_until_zeroed(dec4):
     ws[:bq.MOE_WS_SYNC_BYTES].zero_()
     got, got_idx = _run_tokens(L.desc, X, ws, n)
     assert torch.equal(got.view(torch.int32), want.view(torch.int32)) and torch.equal(got_idx, want_idx)
+
+
+def test_pair_mxfp4_equals_chain_and_oracle(gpu_device):
+    """The MXFP4 top-6 layer (decodemx): 64 spread tokens through both plans, equal bit for bit; 6 of
+    them against the oracle."""
+    w = synth.WORKLOADS["decodemx"]
+    _log("build decodemx layer (512 experts, MXFP4)")
+    L = DeviceLayer(w)
+    ref = Reference(w)
+    assert bq.moe_layer_plan(L.desc, 1) == bq.MOE_PLAN_PAIR
+    toks = spread(w.tokens, 64)
+    X = torch.from_numpy(np.stack([synth.tokens_x(w, t, 1)[0] for t in toks])).cuda()
+    n = bq.moe_workspace_bytes(L.desc, 1)
+    out_a, idx_a = _run_tokens(L.desc, X, torch.zeros(n, dtype=torch.uint8, device="cuda"), n)
+    out_b, idx_b = _run_tokens(_chain(L.desc), X, torch.zeros(n, dtype=torch.uint8, device="cuda"), n)
+    assert torch.equal(idx_a, idx_b)
+    assert torch.equal(out_a.view(torch.int32), out_b.view(torch.int32)), "outputs differ in some bit"
+    xs = X.cpu().numpy().astype(np.float64)
+    on, ix = out_a.cpu().numpy(), idx_a.cpu().numpy()
+    for i in spread(len(toks), 6):
+        r = ref.token(xs[i])
+        assert list(ix[i]) == list(r.idx), f"token {toks[i]}"
+        assert_close(on[i], r.out, f"out[{toks[i]}]")
+
+
+def test_pair_stack_equals_chain_and_oracle(gpu_device):
+    """Three layers at the 60-layer stack's shapes (RMS norm before layers 1 and 2): 6 single-token
+    stack calls through both plans, equal bit for bit in every layer's indices and the output; 2 of
+    them against the oracle's stack."""
+    import oracle
+    from tests._ref import STACK_EPS
+
+    w = synth.WORKLOADS["stack60"]
+    nl = 3
+    _log(f"build {nl} layers at stack60 shapes")
+    layers = [DeviceLayer(w, l) for l in range(nl)]
+    descs = [L.desc for L in layers]
+    chains = [_chain(d) for d in descs]
+    X = torch.from_numpy(synth.tokens_x(w, 0, 6)).cuda()
+    n = bq.moe_stack_workspace_bytes(descs[0], 1)
+    res = []
+    for ds in (descs, chains):
+        ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+        out = torch.empty_like(X)
+        idx = torch.empty(6, nl, 1, w.top_k, dtype=torch.int32, device="cuda")
+        for t in range(6):
+            bq.moe_stack_forward(ds, STACK_EPS, X[t], 1, out[t], idx[t], ws, n)
+        torch.cuda.synchronize()
+        res.append((out, idx))
+    assert torch.equal(res[0][1], res[1][1])
+    assert torch.equal(res[0][0].view(torch.int32), res[1][0].view(torch.int32)), "outputs differ in some bit"
+    refs = [Reference(w, l) for l in range(nl)]
+    xs = X.cpu().numpy().astype(np.float64)
+    for t in (0, 5):
+        r = oracle.stack(xs[t], [(q.router, q.gate, q.expert, q.shared) for q in refs], w.top_k, w.group, STACK_EPS)
+        for l in range(nl):
+            assert list(res[0][1][t, l, 0].cpu().numpy()) == list(r.idx[l]), f"token {t} layer {l}"
+        assert_close(res[0][0][t].cpu().numpy(), r.out, f"stack out[{t}]")
