@@ -504,62 +504,78 @@ __device__ __forceinline__ void keymax_step(uint64_t& k, int& i) {
   const uint64_t ok = ((uint64_t)ohi << 32) | olo;
   if (ok > k || (ok == k && oi < i)) { k = ok; i = oi; }
 }
+// The keys of wave_topk_fast's rounds.
 template <int PL>
-__device__ __forceinline__ int wave_topk_fast(const double (&v)[PL], int E, int K, int lane, int want, bool record,
-                                              int32_t* __restrict__ sel, double* __restrict__ val) {
-  uint64_t key[PL];
+__device__ __forceinline__ void topk_keys(const double (&v)[PL], int E, int lane, uint64_t (&key)[PL]) {
 #pragma unroll
   for (int i = 0; i < PL; ++i) {
     const uint64_t b = (uint64_t)__double_as_longlong(v[i]);
     const uint64_t k = (b >> 63) ? ~b : (b | (1ull << 63));
     key[i] = (lane + 64 * i < E && !__builtin_isnan(v[i])) ? k : 0ull;
   }
+}
+// One round: the winner among the remaining keys (retired from key[] on return), recorded as
+// position r in sel/val (LDS, by lane 0) when `record` is set.
+template <int PL>
+__device__ __forceinline__ int topk_round(uint64_t (&key)[PL], const double (&v)[PL], int E, int lane, int r,
+                                          bool record, int32_t* __restrict__ sel, double* __restrict__ val) {
+  uint32_t m = (uint32_t)(key[0] >> 32);
+#pragma unroll
+  for (int i = 1; i < PL; ++i) m = max(m, (uint32_t)(key[i] >> 32));
+  const uint32_t M = (uint32_t)__builtin_amdgcn_readlane((int)wave_max_u32(m), 63);
+  uint32_t cm = 0;  // this lane's values whose upper half is M
+#pragma unroll
+  for (int i = 0; i < PL; ++i) cm |= ((uint32_t)(key[i] >> 32) == M ? 1u : 0u) << i;
+  const uint64_t lanes = __ballot(cm != 0);
+  const int wl0 = __builtin_ctzll(lanes);
+  const uint32_t cm0 = (uint32_t)__builtin_amdgcn_readlane((int)cm, wl0);
+  int win;
+  if ((lanes & (lanes - 1)) == 0 && (cm0 & (cm0 - 1)) == 0) {
+    win = wl0 + 64 * __builtin_ctz(cm0);  // a unique upper half decides the round
+  } else {  // tied upper halves: the full (key, index) argmax over the tied keys
+    uint64_t bk = 0;
+    int bi = 0x7FFFFFFF;
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+      const bool c = ((cm >> i) & 1u) && (bi == 0x7FFFFFFF || key[i] > bk);  // strict: the lower index keeps a tie
+      bk = c ? key[i] : bk;
+      bi = c ? lane + 64 * i : bi;
+    }
+    keymax_step<kDppQuadXor1, 0xF>(bk, bi);
+    keymax_step<kDppQuadXor2, 0xF>(bk, bi);
+    keymax_step<kDppHalfMirror, 0xF>(bk, bi);
+    keymax_step<kDppRowMirror, 0xF>(bk, bi);
+    keymax_step<kDppBcast15, 0xA>(bk, bi);
+    keymax_step<kDppBcast31, 0xC>(bk, bi);
+    win = __builtin_amdgcn_readlane(bi, 63);
+  }
+  win = min(max(win, 0), E - 1);
+  if (record) {  // the winner's fp64 value: each slot read from its lane, then a uniform select
+    const int src = win % 64, q = win / 64;  // (a select among v[] itself compiles to a scratch copy)
+    double wv = wave_read_f64(v[0], src);
+#pragma unroll
+    for (int i = 1; i < PL; ++i) {
+      const double t = wave_read_f64(v[i], src);
+      wv = q == i ? t : wv;
+    }
+    if (lane == 0) {
+      sel[r] = win;
+      val[r] = wv;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < PL; ++i) key[i] = (lane + 64 * i == win) ? 0ull : key[i];
+  return win;
+}
+template <int PL>
+__device__ __forceinline__ int wave_topk_fast(const double (&v)[PL], int E, int K, int lane, int want, bool record,
+                                              int32_t* __restrict__ sel, double* __restrict__ val) {
+  uint64_t key[PL];
+  topk_keys<PL>(v, E, lane, key);
   int chosen = 0;
   for (int r = 0; r < K; ++r) {
-    uint32_t m = (uint32_t)(key[0] >> 32);
-#pragma unroll
-    for (int i = 1; i < PL; ++i) m = max(m, (uint32_t)(key[i] >> 32));
-    const uint32_t M = (uint32_t)__builtin_amdgcn_readlane((int)wave_max_u32(m), 63);
-    uint32_t cm = 0;  // this lane's values whose upper half is M
-#pragma unroll
-    for (int i = 0; i < PL; ++i) cm |= ((uint32_t)(key[i] >> 32) == M ? 1u : 0u) << i;
-    const uint64_t lanes = __ballot(cm != 0);
-    const int wl0 = __builtin_ctzll(lanes);
-    const uint32_t cm0 = (uint32_t)__builtin_amdgcn_readlane((int)cm, wl0);
-    int win;
-    if ((lanes & (lanes - 1)) == 0 && (cm0 & (cm0 - 1)) == 0) {
-      win = wl0 + 64 * __builtin_ctz(cm0);  // a unique upper half decides the round
-    } else {  // tied upper halves: the full (key, index) argmax over the tied keys
-      uint64_t bk = 0;
-      int bi = 0x7FFFFFFF;
-#pragma unroll
-      for (int i = 0; i < PL; ++i) {
-        const bool c = ((cm >> i) & 1u) && (bi == 0x7FFFFFFF || key[i] > bk);  // strict: the lower index keeps a tie
-        bk = c ? key[i] : bk;
-        bi = c ? lane + 64 * i : bi;
-      }
-      keymax_step<kDppQuadXor1, 0xF>(bk, bi);
-      keymax_step<kDppQuadXor2, 0xF>(bk, bi);
-      keymax_step<kDppHalfMirror, 0xF>(bk, bi);
-      keymax_step<kDppRowMirror, 0xF>(bk, bi);
-      keymax_step<kDppBcast15, 0xA>(bk, bi);
-      keymax_step<kDppBcast31, 0xC>(bk, bi);
-      win = __builtin_amdgcn_readlane(bi, 63);
-    }
-    win = min(max(win, 0), E - 1);
+    const int win = topk_round<PL>(key, v, E, lane, r, record, sel, val);
     if (r == want) chosen = win;
-    if (record) {  // the winner's fp64 value, from its lane
-      double wv = v[0];
-#pragma unroll
-      for (int i = 1; i < PL; ++i) wv = (win / 64 == i) ? v[i] : wv;
-      wv = wave_read_f64(wv, win % 64);
-      if (lane == 0) {
-        sel[r] = win;
-        val[r] = wv;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < PL; ++i) key[i] = (lane + 64 * i == win) ? 0ull : key[i];
   }
   return chosen;
 }
@@ -1111,12 +1127,13 @@ __global__ __launch_bounds__(64 * kFrontWaves) void k_front(LayerArgs a, const f
   __shared__ float gu[NE][NW];
   __shared__ int32_t sel[MOE_MAX_TOP_K];
   __shared__ double val[MOE_MAX_TOP_K];
-  __shared__ int status;
+  __shared__ int ready, bail;
 
   const int b = blockIdx.x, tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int E = a.E;
   const int nrows = E + SH;
+  if (tid == 0) ready = bail = 0;  // read only after the first barrier below
   uint32_t* seqp = reinterpret_cast<uint32_t*>(sync + kSyncSeq);
   uint32_t* poisonp = reinterpret_cast<uint32_t*>(sync + kSyncPoison);
   uint64_t* tl = reinterpret_cast<uint64_t*>(sync + kSyncLogits);
@@ -1229,8 +1246,14 @@ __global__ __launch_bounds__(64 * kFrontWaves) void k_front(LayerArgs a, const f
     if (lane == 63) gu[K][wave] = p;
   }
 
-  // ---- wave 0: wait for every logit, then the top-K
+  // ---- wave 0: wait for every logit, then the top-K. Each round's expert is published in LDS at
+  // once (`ready` counts them, -1 if the wait gave up), and every wave requests that expert's rows
+  // while the later rounds run.
   double gate_logit = 0.0;
+  auto load_slot = [&](int s, int e) __attribute__((always_inline)) {
+    const uint8_t* blob = a.experts + (size_t)e * a.stride;
+    load_row<Cg, MX>(blob + a.off_codes[gm], blob + a.off_sb[gm], grow, lane, cg[s], sg[s]);
+  };
   if (wave == 0) {
     double v[8];
     const bool done = spin_poll([&]() __attribute__((always_inline)) {
@@ -1251,22 +1274,42 @@ __global__ __launch_bounds__(64 * kFrontWaves) void k_front(LayerArgs a, const f
       return __ballot(bad != 0) == 0;
     });
     BQ_TL(3);
-    if (done) wave_topk_fast<8>(v, E, K, lane, 0, true, sel, val);
-    if (lane == 0) status = done ? 0 : 1;
+    if (done) {
+      uint64_t key[8];
+      topk_keys<8>(v, E, lane, key);
+#pragma unroll
+      for (int r = 0; r < K; ++r) {
+        const int e = topk_round<8>(key, v, E, lane, r, true, sel, val);
+        if (lane == 0) __hip_atomic_store(&ready, r + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        load_slot(r, e);
+      }
+    } else if (lane == 0) {
+      __hip_atomic_store(&ready, -1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < K; ++r) {
+      int n = 0;  // wave 0 always publishes K experts or -1; the bound is a backstop
+      for (uint32_t it = 0; it < (1u << 24); ++it) {
+        n = __hip_atomic_load(&ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (n > r || n < 0) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
+      if (n <= r) {  // the wait gave up (or, as a backstop, this wave did)
+        if (n >= 0 && lane == 0) bail = 1;
+        break;
+      }
+      load_slot(r, sel[r]);
+    }
   }
   __syncthreads();
-  if (status != 0) {
+  if (ready != K || bail != 0) {
     give_up();
     return;
   }
   BQ_TL(4);
 
   // ---- the routed experts' gate/up rows, SwiGLU
-#pragma unroll
-  for (int s = 0; s < K; ++s) {
-    const uint8_t* blob = a.experts + (size_t)sel[s] * a.stride;
-    load_row<Cg, MX>(blob + a.off_codes[gm], blob + a.off_sb[gm], grow, lane, cg[s], sg[s]);
-  }
   __builtin_amdgcn_sched_barrier(0);
   if (b == 0 && wave == 0)  // the routing for the down kernel, after this block's loads
     write_routing(a, 0, lane, sel, val, gate_logit, a.ws.idx, a.ws.w, idx_out, a.ws.g);
