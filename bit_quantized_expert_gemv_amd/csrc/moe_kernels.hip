@@ -10,8 +10,7 @@
 //      loads at once. One block writes the routing (indices, weights, shared gate);
 //   3. down (k_down): the down projections of all K+1 experts, combined with the routing weights,
 //      the shared gate and the residual. Each output row sums all experts, so the result is a
-//      deterministic gather with no atomics. (Measured and not kept: the residual row and the
-//      expert index requested ahead of the SwiGLU vectors, 13.98 -> 14.50 us/token at decode4.)
+//      deterministic gather with no atomics.
 // GN+ summary "Flash-MoE - Ejecutar un modelo de 397 mil millones de parámetros en una laptop",
 // "Tecnologías clave": "Metal Compute Shaders" lists these operations; "Deferred GPU Expert
 // Compute" submits them without a host round trip; combine + norm + residual stay on the GPU.
@@ -949,6 +948,8 @@ __global__ __launch_bounds__(2 * kBlock) void k_down(LayerArgs a, const int32_t*
   const int row0 = blockIdx.x * RB + half * P * C::RPW;
   const bool combine = out != nullptr;
   bool first = true;
+  static_assert(RB <= 2 * kBlock, "one combined row per thread");
+  float res = 0.0f;
   // Slots go in passes of kWaves: in pass q, wave w takes slot q*kWaves + w%4. The pass's SwiGLU
   // vectors are loaded once by the whole block with coalesced 16-byte loads and parked in LDS
   // (double-buffered over passes), instead of once per wave: the two halves of the block need
@@ -993,6 +994,11 @@ __global__ __launch_bounds__(2 * kBlock) void k_down(LayerArgs a, const int32_t*
       for (int p = 0; p < P; ++p)
         load_row<C, FORM == 3>(dc, ds, min(row0 + p * C::RPW + rig, a.H - 1), lir, cw[p], sb[p]);
     }
+    // the residual row, behind this wave's weight loads: read at the end, it cost the combine a
+    // memory round trip (decode4 13.96 -> 13.93, decodemx 19.09 -> 18.97 us/token); requested
+    // first, together with the expert index, it delayed the weight loads (13.98 -> 14.50)
+    if (q == 0 && combine && (int)threadIdx.x < RB && blockIdx.x * RB + threadIdx.x < a.H)
+      res = residual[(size_t)t * a.H + blockIdx.x * RB + threadIdx.x];
     __builtin_amdgcn_sched_barrier(0);
     auto park = [&](int j, const float4& hv) __attribute__((always_inline)) {
       const int i = min((int)threadIdx.x + j * 2 * kBlock, nk * N4 - 1);
@@ -1037,7 +1043,7 @@ __global__ __launch_bounds__(2 * kBlock) void k_down(LayerArgs a, const int32_t*
     const int r = blockIdx.x * RB + i;
     if (r >= a.H) continue;
     const int hw = (i / (P * C::RPW)) * kWaves;
-    float acc = residual[(size_t)t * a.H + r];
+    float acc = res;
     for (int w = 0; w < kWaves && w < a.NE; ++w) acc += part[hw + w][i];
     store_through(&out[(size_t)t * a.H + r], acc);
   }
