@@ -231,7 +231,7 @@ def test_workspace_monotone():
 
 
 def test_strerror():
-    for c in (0, -1, -2, -3, -4):
+    for c in (0, -1, -2, -3, -4, -5):
         assert bq.moe_strerror(c) != "unknown error"
     assert bq.moe_strerror(-99) == "unknown error"
 
@@ -245,3 +245,34 @@ def test_binding_constants_match_header():
     for name, value in found.items():
         assert hasattr(bq, name), name
         assert getattr(bq, name) == int(value), name
+
+
+def test_layer_plan_validation():
+    """moe_layer_plan: argument errors before any HIP call; the prefill from MOE_PREFILL_MIN_TOKENS
+    tokens; the chain for several decode tokens and whenever MOE_FLAG_DECODE_CHAIN is set."""
+    L = bq.lib()
+    assert L.moe_layer_plan(None, 1) == bq.MOE_EINVAL
+    assert L.moe_layer_plan(ctypes.byref(_layer(bits=3)), 1) == bq.MOE_EUNSUPPORTED
+    assert L.moe_layer_plan(ctypes.byref(_layer()), 0) == bq.MOE_EINVAL
+    assert L.moe_layer_plan(ctypes.byref(_layer()), -3) == bq.MOE_EINVAL
+    assert bq.moe_layer_plan(_layer(), bq.MOE_PREFILL_MIN_TOKENS) == bq.MOE_PLAN_PREFILL
+    assert bq.moe_layer_plan(_layer(), 2) == bq.MOE_PLAN_CHAIN
+    assert bq.moe_layer_plan(_layer(flags=bq.MOE_FLAG_DECODE_CHAIN), 1) == bq.MOE_PLAN_CHAIN
+    # shapes the first kernel does not take stay on the chain, on any device
+    for kw in (dict(hidden=2048), dict(inter=512, expert_stride=bq.moe_blob_bytes(4096, 512, 4)),
+               dict(top_k=2), dict(shared_blob=None, shared_gate=None), dict(flags=bq.MOE_FLAG_DEQUANT_NAIVE)):
+        kw2 = dict(kw)
+        if kw2.pop("shared_blob", 1) is None:
+            lay = bq.make_layer(4096, 1024, 512, 3, 4, FAKE, 7_077_888, FAKE)
+        else:
+            lay = _layer(**kw)
+        assert bq.moe_layer_plan(lay, 1) == bq.MOE_PLAN_CHAIN, kw
+
+
+def test_workspace_holds_the_sync_region():
+    """Every workspace starts with the MOE_WS_SYNC_BYTES sync region, before the per-token buffers."""
+    lay = _layer()
+    n1, n2 = bq.moe_workspace_bytes(lay, 1), bq.moe_workspace_bytes(lay, 2)
+    per_token = n2 - n1
+    assert n1 - per_token >= bq.MOE_WS_SYNC_BYTES
+    assert bq.moe_stack_workspace_bytes(lay, 1) > n1
