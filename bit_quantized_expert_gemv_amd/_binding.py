@@ -41,6 +41,7 @@ SIGNATURES = {
     "moe_blob_bytes": (c_size, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]),
     "moe_workspace_bytes": (c_size, [ctypes.POINTER(moe_layer_t), ctypes.c_int]),
     "moe_stack_workspace_bytes": (c_size, [ctypes.POINTER(moe_layer_t), ctypes.c_int]),
+    "moe_workspace_init": (ctypes.c_int, [c_vp, c_size, c_vp]),
     "moe_pack_expert": (ctypes.c_int, [ctypes.c_int] * 4 + [ctypes.POINTER(moe_expert_arrays_t), c_vp]),
     "moe_pack_expert_device": (ctypes.c_int, [ctypes.c_int] * 4 + [ctypes.POINTER(moe_expert_arrays_t), c_vp, c_vp]),
     "moe_dequant": (ctypes.c_int, [ctypes.POINTER(moe_layer_t), ctypes.c_int, ctypes.c_int, ctypes.c_int, c_vp, c_vp]),
@@ -138,6 +139,10 @@ def moe_workspace_bytes(layer, T: int) -> int:
 
 def moe_stack_workspace_bytes(layer, T: int) -> int:
     return lib().moe_stack_workspace_bytes(_ref(layer), T)
+
+
+def moe_workspace_init(ws, ws_bytes: int, stream=None) -> None:
+    _check(lib().moe_workspace_init(ptr(ws), ws_bytes, stream_handle(stream)), "moe_workspace_init")
 
 
 def _arrays(q, scale, bias) -> moe_expert_arrays_t:

@@ -220,6 +220,12 @@ size_t moe_workspace_bytes(const moe_layer_t* layer, int T) {
   return n;
 }
 
+int moe_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+  if (ws == nullptr || !aligned(ws, 256)) return fail(MOE_EINVAL, "workspace must be non-NULL and 256-byte aligned");
+  if (ws_bytes < (size_t)MOE_WS_SYNC_BYTES) return fail(MOE_ENOSPC, "workspace smaller than MOE_WS_SYNC_BYTES");
+  return hip_status(launch_zero(ws, MOE_WS_SYNC_BYTES, static_cast<hipStream_t>(stream)));
+}
+
 size_t moe_stack_workspace_bytes(const moe_layer_t* layer, int T) {
   const size_t base = moe_workspace_bytes(layer, T);
   if (base == 0) return 0;

@@ -137,6 +137,8 @@ hipError_t launch_combine(const Geometry& g, int T, const float* residual, const
 // Device address of the no-allocation entry point's scratch array (MOE_NOALLOC_SCRATCH_BYTES) on
 // the current device, looked up on the first call per device and cached.
 hipError_t noalloc_scratch(void** out);
+// Zeroes n bytes (a multiple of 16, 16-byte aligned) at p with a fill kernel.
+hipError_t launch_zero(void* p, size_t n, hipStream_t s);
 hipError_t launch_dequant(const Geometry& g, const uint8_t* blob, int matrix, int out_dtype, void* out, hipStream_t s);
 hipError_t launch_pack(int H, int I, int bits, int G, const moe_expert_arrays_t* a, uint8_t* blob, hipStream_t s);
 

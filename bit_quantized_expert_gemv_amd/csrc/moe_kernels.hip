@@ -1584,6 +1584,11 @@ __global__ void k_dequant_mx(int rows, int cols, const uint8_t* __restrict__ cod
   }
 }
 
+__global__ void k_zero16(int64_t n, uint4* __restrict__ p) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
 __global__ void k_pack_e8m0(int64_t n, const uint16_t* __restrict__ s, uint8_t* __restrict__ out) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) out[i] = (uint8_t)s[i];
@@ -1841,6 +1846,12 @@ hipError_t launch_dequant(const Geometry& g, const uint8_t* blob, int matrix, in
   hipLaunchKernelGGL(k_dequant, dim3(blocks_for(n, 256)), dim3(256), 0, s, rows, cols, g.bits,
                      blob + g.off_codes[matrix], reinterpret_cast<const uint32_t*>(blob + g.off_sb[matrix]), out_dtype,
                      out);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero(void* p, size_t n, hipStream_t s) {
+  const int64_t n4 = (int64_t)(n / 16);
+  hipLaunchKernelGGL(k_zero16, dim3(blocks_for(n4, 256)), dim3(256), 0, s, n4, static_cast<uint4*>(p));
   return hipGetLastError();
 }
 

@@ -96,8 +96,8 @@ extern "C" {
 
 /* Workspace sync region. The first MOE_WS_SYNC_BYTES bytes of every workspace hold the cross-block
  * state of the two-launch decode (a call counter and the router logits tagged with it). They must
- * be zero before the first call that uses the workspace (allocate it zeroed, or zero that prefix
- * once); calls keep them valid afterwards, and nothing else in the library writes there. A call
+ * be zero before the first call that uses the workspace (allocate it zeroed, or call
+ * moe_workspace_init once); calls keep them valid afterwards, and nothing else in the library writes there. A call
  * whose first kernel cannot have all of its blocks resident within about 20 ms writes NaN to its
  * output and marks the region; every later such call on that workspace then writes NaN until the
  * region is zeroed again. */
@@ -149,6 +149,12 @@ size_t moe_blob_bytes(int hidden, int inter, int bits, int group);
  * invalid layer. */
 size_t moe_workspace_bytes(const moe_layer_t* layer, int T);
 size_t moe_stack_workspace_bytes(const moe_layer_t* layer, int T);
+
+/* Zeroes a workspace's sync region (its first MOE_WS_SYNC_BYTES bytes) on `stream` with a fill
+ * kernel (no memset node, so it may be captured in a graph): once before the first call on a
+ * workspace that was not allocated zeroed, or to clear a region that a call marked.
+ * ws_dev 256-byte aligned, ws_bytes >= MOE_WS_SYNC_BYTES (MOE_EINVAL, MOE_ENOSPC otherwise). */
+int moe_workspace_init(void* ws_dev, size_t ws_bytes, void* stream);
 
 /* ---- packing -------------------------------------------------------------------------------------- */
 

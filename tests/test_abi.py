@@ -276,3 +276,12 @@ def test_workspace_holds_the_sync_region():
     per_token = n2 - n1
     assert n1 - per_token >= bq.MOE_WS_SYNC_BYTES
     assert bq.moe_stack_workspace_bytes(lay, 1) > n1
+
+
+def test_workspace_init_validation():
+    """moe_workspace_init refuses a NULL or misaligned workspace and one smaller than the sync
+    region, before any HIP call."""
+    L = bq.lib()
+    assert L.moe_workspace_init(None, 1 << 20, None) == bq.MOE_EINVAL
+    assert L.moe_workspace_init(FAKE + 16, 1 << 20, None) == bq.MOE_EINVAL
+    assert L.moe_workspace_init(FAKE, bq.MOE_WS_SYNC_BYTES - 256, None) == bq.MOE_ENOSPC

@@ -198,3 +198,19 @@ def test_pair_stack_equals_chain_and_oracle(gpu_device):
         for l in range(nl):
             assert list(res[0][1][t, l, 0].cpu().numpy()) == list(r.idx[l]), f"token {t} layer {l}"
         assert_close(res[0][0][t].cpu().numpy(), r.out, f"stack out[{t}]")
+
+
+def test_workspace_init_clears_a_garbage_region(dec4):
+    """A workspace filled with garbage, cleared by moe_workspace_init: the same results as a
+    workspace allocated zeroed."""
+    L, _ = dec4
+    w = L.w
+    X = torch.from_numpy(synth.tokens_x(w, 3, 4)).cuda()
+    n = bq.moe_workspace_bytes(L.desc, 1)
+    want, want_idx = _run_tokens(L.desc, X, torch.zeros(n, dtype=torch.uint8, device="cuda"), n)
+    ws = torch.full((n,), 0xA7, dtype=torch.uint8, device="cuda")
+    bq.moe_workspace_init(ws, n)
+    got, got_idx = _run_tokens(L.desc, X, ws, n)
+    assert torch.equal(got_idx, want_idx)
+    assert torch.equal(got.view(torch.int32), want.view(torch.int32))
+    assert int(ws[:bq.MOE_WS_SYNC_BYTES].count_nonzero().item()) > 0  # the calls use the region again
