@@ -933,9 +933,9 @@ __global__ __launch_bounds__(64 * NW) void k_gateup(LayerArgs a, const float* __
 // 15.49, decode2 14.80 -> 14.66, decodemx 20.87 -> 20.65 us/token. The SwiGLU vectors are loaded
 // once per block rather than once per wave: decode4 15.75 -> 15.61, decodemx 20.50 -> 20.20.
 template <int BITS, int I, int P0, int FORM>
-__global__ __launch_bounds__(2 * kBlock) void k_down(LayerArgs a, const int32_t* __restrict__ idx,
-                                                 const float* __restrict__ residual, float* __restrict__ out,
-                                                 float* __restrict__ y) {
+__global__ __launch_bounds__(2 * kBlock) void k_down(const float* __restrict__ h, const int32_t* __restrict__ idx,
+                                                 int ne, int K, LayerArgs a, const float* __restrict__ residual,
+                                                 float* __restrict__ out, float* __restrict__ y) {
   using C = RowCfg<BITS, I>;
   constexpr int RB = C::RPW * P0;
   constexpr int P = P0 >= 2 ? P0 / 2 : 1;
@@ -944,47 +944,53 @@ __global__ __launch_bounds__(2 * kBlock) void k_down(LayerArgs a, const int32_t*
   const int t = blockIdx.y;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int sw = wave % kWaves, half = wave / kWaves;
-  const int lir = lane % C::LPR, rig = lane / C::LPR;
-  const int row0 = blockIdx.x * RB + half * P * C::RPW;
-  const bool combine = out != nullptr;
-  bool first = true;
-  static_assert(RB <= 2 * kBlock, "one combined row per thread");
-  float res = 0.0f;
   // Slots go in passes of kWaves: in pass q, wave w takes slot q*kWaves + w%4. The pass's SwiGLU
   // vectors are loaded once by the whole block with coalesced 16-byte loads and parked in LDS
   // (double-buffered over passes), instead of once per wave: the two halves of the block need
   // the same vectors, and a CU's time tracks the cache lines it requests.
   constexpr int N4 = I / 4;                                               // float4 per vector
   constexpr int HPER = (kWaves * N4 + 2 * kBlock - 1) / (2 * kBlock);     // float4 per thread per pass
-  const bool active = !(P0 < 2 && half == 1);  // with one row step per block, the second half idles
-  const int npass = (a.NE + kWaves - 1) / kWaves;
-  for (int q = 0; q < npass; ++q) {
-    const int k = q * kWaves + sw;
-    const int nk = min(a.NE - q * kWaves, kWaves);  // slots in this pass
-    const float4* hsrc = reinterpret_cast<const float4*>(a.ws.h + ((size_t)t * a.NE + q * kWaves) * I);
-    float4 hv0, hv1, hv2, hv3;  // HPER <= 4 (hidden rows of at most 2048 floats)
-    static_assert(HPER <= 4, "SwiGLU vectors of at most 2048 floats");
-    // past the pass's vectors: its last float4 again, stored again
+  float4 hv0, hv1, hv2, hv3;  // HPER <= 4 (hidden rows of at most 2048 floats)
+  static_assert(HPER <= 4, "SwiGLU vectors of at most 2048 floats");
+  // A pass's SwiGLU vectors (past them: the last float4 again, stored again) and this wave's
+  // expert index. They need only the leading arguments, which arrive preloaded in SGPRs, so pass
+  // 0's requests leave first, before any kernel-argument fetch returns.
+  auto request = [&](int q) __attribute__((always_inline)) {
+    const int nk = min(ne - q * kWaves, kWaves);
+    const float4* hsrc = reinterpret_cast<const float4*>(h + ((size_t)t * ne + q * kWaves) * I);
     hv0 = hsrc[min((int)threadIdx.x, nk * N4 - 1)];
     if constexpr (HPER > 1) hv1 = hsrc[min((int)threadIdx.x + 2 * kBlock, nk * N4 - 1)];
     if constexpr (HPER > 2) hv2 = hsrc[min((int)threadIdx.x + 4 * kBlock, nk * N4 - 1)];
     if constexpr (HPER > 3) hv3 = hsrc[min((int)threadIdx.x + 6 * kBlock, nk * N4 - 1)];
+    return idx[(size_t)t * K + min(q * kWaves + sw, K - 1)];  // the shared slot reads one it ignores
+  };
+  int e = request(0);
+  __builtin_amdgcn_sched_barrier(0);
+  const int lir = lane % C::LPR, rig = lane / C::LPR;
+  const int row0 = blockIdx.x * RB + half * P * C::RPW;
+  const bool combine = out != nullptr;
+  bool first = true;
+  static_assert(RB <= 2 * kBlock, "one combined row per thread");
+  float res = 0.0f;
+  const bool active = !(P0 < 2 && half == 1);  // with one row step per block, the second half idles
+  const int npass = (ne + kWaves - 1) / kWaves;
+  int q = 0;
+  do {  // at least one pass (ne >= 1), so pass 0's requests stay ahead of any branch
+    const int k = q * kWaves + sw;
+    const int nk = min(ne - q * kWaves, kWaves);  // slots in this pass
+    if (q > 0) e = request(q);
     // Every wave issues its weight loads on every path (an idle wave repeats the rows of the pass's
     // last slot, a bad index reads expert 0's), so the wait before parking the vectors counts only
     // the vector loads issued before them.
-    const bool work = active && k < a.NE;
-    const int kk = min(k, a.NE - 1);
-    const uint8_t* blob = a.shared;
-    bool valid = true;
-    float coef = 1.0f;
-    if (kk < a.K) {
-      const int e = idx[(size_t)t * a.K + kk];
-      valid = (e >= 0 && e < a.E);
-      blob = a.experts + (size_t)(valid ? e : 0) * a.stride;
-      if (combine) coef = a.ws.w[(size_t)t * a.K + kk];
-    } else if (combine) {
-      coef = a.ws.g[t];
-    }
+    const bool work = active && k < ne;
+    const int kk = min(k, ne - 1);
+    // selects, not branches: a branch lets the compiler sink the index read behind other waits
+    const bool routed = kk < K;
+    const bool valid = !routed || (e >= 0 && e < a.E);
+    const uint8_t* blob = routed ? a.experts + (size_t)(valid ? e : 0) * a.stride : a.shared;
+    // the combine coefficient's address now, so its pointers arrive with the index; the value is
+    // read after the barrier below, which then waits for no scalar load
+    const float* cp = routed ? a.ws.w + (size_t)t * K + kk : a.ws.g + t;
     uint4 cw[P][C::CPL];
     uint32_t sb[P][C::CPL];
     {
@@ -1011,6 +1017,7 @@ __global__ __launch_bounds__(2 * kBlock) void k_down(LayerArgs a, const int32_t*
     if constexpr (HPER > 3) park(3, hv3);
     __syncthreads();
     if (!work) continue;
+    const float coef = combine ? *cp : 1.0f;
     float yv[P];
     if (valid) {
       float xr[C::XPL], S[C::CPL];
@@ -1031,12 +1038,12 @@ __global__ __launch_bounds__(2 * kBlock) void k_down(LayerArgs a, const int32_t*
           const int i = half * P * C::RPW + p * C::RPW + rig;
           part[wave][i] = first ? v : part[wave][i] + v;
         } else {
-          y[((size_t)t * a.NE + k) * a.H + r] = yv[p];
+          y[((size_t)t * ne + k) * a.H + r] = yv[p];
         }
       }
     }
     first = false;
-  }
+  } while (++q < npass);
   if (!combine) return;
   __syncthreads();
   for (int i = threadIdx.x; i < RB; i += 2 * kBlock) {
@@ -1044,7 +1051,7 @@ __global__ __launch_bounds__(2 * kBlock) void k_down(LayerArgs a, const int32_t*
     if (r >= a.H) continue;
     const int hw = (i / (P * C::RPW)) * kWaves;
     float acc = res;
-    for (int w = 0; w < kWaves && w < a.NE; ++w) acc += part[hw + w][i];
+    for (int w = 0; w < kWaves && w < ne; ++w) acc += part[hw + w][i];
     store_through(&out[(size_t)t * a.H + r], acc);
   }
 }
@@ -1116,9 +1123,10 @@ __device__ __forceinline__ void store_logit(uint64_t* tl, int r, uint32_t tag, d
 // norm), computed as in kernel 1: the logits are the fp64 dot products with x times the fp64 scale,
 // and the experts read x times the scale rounded to fp32.
 template <int BITS, int FORM, int K, int SH>
-__global__ __launch_bounds__(64 * kFrontWaves) void k_front(LayerArgs a, const float* __restrict__ x, int norm,
-                                                            float eps, int32_t* __restrict__ idx_out,
-                                                            uint8_t* __restrict__ sync) {
+__global__ __launch_bounds__(64 * kFrontWaves) void k_front(const float* __restrict__ x, uint8_t* __restrict__ sync,
+                                                            const uint16_t* __restrict__ router,
+                                                            const uint16_t* __restrict__ sgate, int E, LayerArgs a,
+                                                            int norm, float eps, int32_t* __restrict__ idx_out) {
   constexpr int H = 4096, I = 1024, NW = kFrontWaves, NT = 64 * NW, NE = K + SH;
   constexpr bool MX = FORM == 3;
   using Cg = RowCfg<BITS, H>;  // gate/up rows: one row per wave per step (64 lanes)
@@ -1140,7 +1148,6 @@ __global__ __launch_bounds__(64 * kFrontWaves) void k_front(LayerArgs a, const f
 
   const int b = blockIdx.x, tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int E = a.E;
   const int nrows = E + SH;
   if (tid == 0) ready = bail = 0;  // read only after the first barrier below
   uint32_t* seqp = reinterpret_cast<uint32_t*>(sync + kSyncSeq);
@@ -1162,12 +1169,12 @@ __global__ __launch_bounds__(64 * kFrontWaves) void k_front(LayerArgs a, const f
   uint4 rw[RCH], gw[RCH];
   {
     const int rr = min(rrow, nrows - 1);
-    const uint16_t* row = rr < E ? a.router + (size_t)rr * H : a.sgate;
+    const uint16_t* row = rr < E ? router + (size_t)rr * H : sgate;
 #pragma unroll
     for (int j = 0; j < RCH; ++j) rw[j] = *reinterpret_cast<const uint4*>(row + (lane + (j * 4 + piece) * 64) * 8);
     if (third) {
 #pragma unroll
-      for (int j = 0; j < RCH; ++j) gw[j] = *reinterpret_cast<const uint4*>(a.sgate + (lane + (j * 4 + piece) * 64) * 8);
+      for (int j = 0; j < RCH; ++j) gw[j] = *reinterpret_cast<const uint4*>(sgate + (lane + (j * 4 + piece) * 64) * 8);
     }
   }
   // gate/up rows: wave w takes matrix w / HB (gate, up), row HB*b + w % HB, in every slot
@@ -1696,7 +1703,7 @@ hipError_t down_impl(const LayerArgs& a, int T, const int32_t* idx, const float*
   const bool two_rounds = a.NE > kWaves;
   const int RB = C::RPW * (two_rounds ? P8 : P16);
   const int nb = (a.H + RB - 1) / RB;
-#define BQ_DN(P, F) launch_timed(k_down<BITS, I, P, F>, dim3(nb, T), dim3(2 * kBlock), s, ev, a, idx, residual, out, y)
+#define BQ_DN(P, F) launch_timed(k_down<BITS, I, P, F>, dim3(nb, T), dim3(2 * kBlock), s, ev, (const float*)a.ws.h, idx, a.NE, a.K, a, residual, out, y)
   if constexpr (BITS == 4) {
     if (a.form == 3) return two_rounds ? BQ_DN(P8, 3) : BQ_DN(P16, 3);
   }
@@ -1789,11 +1796,14 @@ hipError_t launch_pair(const Geometry& g, const LayerPtrs& p, const float* x, co
   const int norm = norm_src != nullptr;
   hipError_t e;
   if (g.form == 3)
-    e = launch_timed(front_kernel<4, 3, 6>(), grid, block, s, ev_front, a, in, norm, eps, idx_out, sync);
+    e = launch_timed(front_kernel<4, 3, 6>(), grid, block, s, ev_front, in, sync, p.router, p.sgate, g.E, a, norm,
+                     eps, idx_out);
   else if (g.bits == 4)
-    e = launch_timed(front_kernel<4, 0, 3>(), grid, block, s, ev_front, a, in, norm, eps, idx_out, sync);
+    e = launch_timed(front_kernel<4, 0, 3>(), grid, block, s, ev_front, in, sync, p.router, p.sgate, g.E, a, norm,
+                     eps, idx_out);
   else
-    e = launch_timed(front_kernel<2, 0, 3>(), grid, block, s, ev_front, a, in, norm, eps, idx_out, sync);
+    e = launch_timed(front_kernel<2, 0, 3>(), grid, block, s, ev_front, in, sync, p.router, p.sgate, g.E, a, norm,
+                     eps, idx_out);
   if (e != hipSuccess) return e;
   return launch_down(g, p, 1, ws, ws.idx, residual, out, nullptr, s, ev_down);
 }
