@@ -516,8 +516,21 @@ __device__ __forceinline__ void topk_keys(const double (&v)[PL], int E, int lane
     key[i] = (lane + 64 * i < E && !__builtin_isnan(v[i])) ? k : 0ull;
   }
 }
+// The fp64 value at expert index `win` (wave-uniform): each slot read from its lane, then a uniform
+// select (a select among v[] itself compiles to a scratch copy).
+template <int PL>
+__device__ __forceinline__ double wave_value_at(const double (&v)[PL], int win) {
+  const int src = win % 64, q = win / 64;
+  double wv = wave_read_f64(v[0], src);
+#pragma unroll
+  for (int i = 1; i < PL; ++i) {
+    const double t = wave_read_f64(v[i], src);
+    wv = q == i ? t : wv;
+  }
+  return wv;
+}
 // One round: the winner among the remaining keys (retired from key[] on return), recorded as
-// position r in sel/val (LDS, by lane 0) when `record` is set.
+// position r in sel (and its value in val, unless val is null) by lane 0 when `record` is set.
 template <int PL>
 __device__ __forceinline__ int topk_round(uint64_t (&key)[PL], const double (&v)[PL], int E, int lane, int r,
                                           bool record, int32_t* __restrict__ sel, double* __restrict__ val) {
@@ -552,14 +565,10 @@ __device__ __forceinline__ int topk_round(uint64_t (&key)[PL], const double (&v)
     win = __builtin_amdgcn_readlane(bi, 63);
   }
   win = min(max(win, 0), E - 1);
-  if (record) {  // the winner's fp64 value: each slot read from its lane, then a uniform select
-    const int src = win % 64, q = win / 64;  // (a select among v[] itself compiles to a scratch copy)
-    double wv = wave_read_f64(v[0], src);
-#pragma unroll
-    for (int i = 1; i < PL; ++i) {
-      const double t = wave_read_f64(v[i], src);
-      wv = q == i ? t : wv;
-    }
+  if (record && val == nullptr) {
+    if (lane == 0) sel[r] = win;
+  } else if (record) {
+    const double wv = wave_value_at<PL>(v, win);
     if (lane == 0) {
       sel[r] = win;
       val[r] = wv;
@@ -1293,11 +1302,19 @@ __global__ __launch_bounds__(64 * kFrontWaves) void k_front(const float* __restr
     if (done) {
       uint64_t key[8];
       topk_keys<8>(v, E, lane, key);
+      int es[K];
 #pragma unroll
-      for (int r = 0; r < K; ++r) {
-        const int e = topk_round<8>(key, v, E, lane, r, true, sel, val);
+      for (int r = 0; r < K; ++r) {  // the values only in the block that writes the routing, afterwards
+        es[r] = topk_round<8>(key, v, E, lane, r, true, sel, nullptr);
         if (lane == 0) __hip_atomic_store(&ready, r + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-        load_slot(r, e);
+        load_slot(r, es[r]);
+      }
+      if (b == 0) {
+#pragma unroll
+        for (int r = 0; r < K; ++r) {
+          const double wv = wave_value_at<8>(v, es[r]);
+          if (lane == 0) val[r] = wv;
+        }
       }
     } else if (lane == 0) {
       __hip_atomic_store(&ready, -1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
