@@ -941,6 +941,9 @@ __global__ __launch_bounds__(64 * NW) void k_gateup(LayerArgs a, const float* __
 // Against 4 waves over all rows, each wave's compute after its data lands halves: decode4 15.60 ->
 // 15.49, decode2 14.80 -> 14.66, decodemx 20.87 -> 20.65 us/token. The SwiGLU vectors are loaded
 // once per block rather than once per wave: decode4 15.75 -> 15.61, decodemx 20.50 -> 20.20.
+// The SwiGLU vectors and the expert index are requested first, from the leading arguments, which
+// arrive preloaded in SGPRs; the combine coefficient is read after the parking barrier, so that the
+// barrier waits for no scalar load.
 template <int BITS, int I, int P0, int FORM>
 __global__ __launch_bounds__(2 * kBlock) void k_down(const float* __restrict__ h, const int32_t* __restrict__ idx,
                                                  int ne, int K, LayerArgs a, const float* __restrict__ residual,
@@ -1130,7 +1133,9 @@ __device__ __forceinline__ void store_logit(uint64_t* tl, int r, uint32_t tag, d
 
 // norm: the stack's layers after the first route u = x / sqrt(mean(x^2) + eps) (unit-weight RMS
 // norm), computed as in kernel 1: the logits are the fp64 dot products with x times the fp64 scale,
-// and the experts read x times the scale rounded to fp32.
+// and the experts read x times the scale rounded to fp32. The arguments of the first requests (x,
+// the sync region, the router and shared-gate rows, E) lead the list, so they arrive preloaded in
+// SGPRs and those requests leave before any kernel-argument fetch returns.
 template <int BITS, int FORM, int K, int SH>
 __global__ __launch_bounds__(64 * kFrontWaves) void k_front(const float* __restrict__ x, uint8_t* __restrict__ sync,
                                                             const uint16_t* __restrict__ router,
