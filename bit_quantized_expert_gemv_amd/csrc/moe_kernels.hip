@@ -943,7 +943,7 @@ __global__ __launch_bounds__(64 * NW) void k_gateup(LayerArgs a, const float* __
 // once per block rather than once per wave: decode4 15.75 -> 15.61, decodemx 20.50 -> 20.20.
 // The SwiGLU vectors and the expert index are requested first, from the leading arguments, which
 // arrive preloaded in SGPRs; the combine coefficient is read after the parking barrier, so that the
-// barrier waits for no scalar load.
+// barrier does not wait for that load.
 template <int BITS, int I, int P0, int FORM>
 __global__ __launch_bounds__(2 * kBlock) void k_down(const float* __restrict__ h, const int32_t* __restrict__ idx,
                                                  int ne, int K, LayerArgs a, const float* __restrict__ residual,
@@ -1000,8 +1000,8 @@ __global__ __launch_bounds__(2 * kBlock) void k_down(const float* __restrict__ h
     const bool routed = kk < K;
     const bool valid = !routed || (e >= 0 && e < a.E);
     const uint8_t* blob = routed ? a.experts + (size_t)(valid ? e : 0) * a.stride : a.shared;
-    // the combine coefficient's address now, so its pointers arrive with the index; the value is
-    // read after the barrier below, which then waits for no scalar load
+    // the combine coefficient's address; the value is read after the barrier below, so that the
+    // barrier does not wait for it
     const float* cp = routed ? a.ws.w + (size_t)t * K + kk : a.ws.g + t;
     uint4 cw[P][C::CPL];
     uint32_t sb[P][C::CPL];
