@@ -272,7 +272,9 @@ int moe_layer_forward_timed(const moe_layer_t* layer, const float* x_dev, const 
  * address. Same kernels and results as moe_layer_forward. A layer and T whose moe_workspace_bytes()
  * exceeds MOE_NOALLOC_SCRATCH_BYTES return MOE_ENOSPC before any HIP call. Every call on one GPU
  * shares that GPU's array, so calls that overlap on one GPU (other streams, other threads) race;
- * calls in order on one stream are safe. Nothing in the array needs clearing between calls. */
+ * calls in order on one stream are safe. Nothing in the array needs clearing between calls. A
+ * decode call whose bounded wait gave up (MOE_ETIMEOUT) marks the array, and later calls on that
+ * GPU write NaN outputs until the process ends: the caller has no handle to clear it. */
 #define MOE_NOALLOC_SCRATCH_BYTES 33554432
 int moe_layer_forward_noalloc(const moe_layer_t* layer, const float* x_dev, const float* residual_dev, int T,
                               float* out_dev, int32_t* idx_out_dev, void* stream);
