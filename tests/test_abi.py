@@ -285,3 +285,16 @@ def test_workspace_init_validation():
     assert L.moe_workspace_init(None, 1 << 20, None) == bq.MOE_EINVAL
     assert L.moe_workspace_init(FAKE + 16, 1 << 20, None) == bq.MOE_EINVAL
     assert L.moe_workspace_init(FAKE, bq.MOE_WS_SYNC_BYTES - 256, None) == bq.MOE_ENOSPC
+
+
+def test_build_flags():
+    """Every HIP source is built for gfx950 without packed-fp32 instructions, and with the leading
+    kernel arguments preloaded into SGPRs (the decode kernels' first requests depend on it)."""
+    import bit_quantized_expert_gemv_amd._build as B
+    f = B.HIP_FLAGS
+    assert "--offload-arch=gfx950" in f
+    i = f.index("-packed-fp32-ops")
+    assert f[i - 3:i] == ["-Xclang", "-target-feature", "-Xclang"]
+    assert any(x.startswith("-amdgpu-kernarg-preload-count=") for x in f)
+    j = next(k for k, x in enumerate(f) if x.startswith("-amdgpu-kernarg-preload-count="))
+    assert f[j - 1] == "-mllvm"
