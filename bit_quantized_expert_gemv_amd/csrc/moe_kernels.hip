@@ -743,9 +743,13 @@ __global__ __launch_bounds__(kBlock) void k_router_phase(LayerArgs a, const floa
 // Kernel 1 for several tokens without the stack's norm: each block reads its router row once for a
 // group of TG tokens, and every lane accumulates one fp64 dot product per token. A token's logits
 // are summed in the same order as in k_router_phase, so they are bitwise the same; only the row
-// traffic drops, from T reads of the router to T / TG.
+// traffic drops, from T reads of the router to T / TG. The arguments of the first requests lead the
+// list, so they arrive preloaded in SGPRs.
 template <int H, int TG>
-__global__ __launch_bounds__(kBlock) void k_router_group(LayerArgs a, const float* __restrict__ x, int T) {
+__global__ __launch_bounds__(kBlock) void k_router_group(const float* __restrict__ x,
+                                                        const uint16_t* __restrict__ router,
+                                                        const uint16_t* __restrict__ sgate, int E, int nrows, int T,
+                                                        LayerArgs a) {
   using R = RouterCfg<H>;
   constexpr int SPLIT = (R::CPL % BQ_ROUTER_SPLIT == 0) ? BQ_ROUTER_SPLIT : 1;  // waves per row
   constexpr int CPW = R::CPL / SPLIT;                                            // chunks per lane
@@ -753,13 +757,12 @@ __global__ __launch_bounds__(kBlock) void k_router_group(LayerArgs a, const floa
   const int t0 = blockIdx.y * TG;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int lir = lane % R::LPR, rig = lane / R::LPR;
-  const int nrows = a.E + a.has_shared;
   const int piece = wave % SPLIT;
   const int r = (blockIdx.x * (kWaves / SPLIT) + wave / SPLIT) * R::RPW + rig;  // one row step per block
   uint4 w[CPW];
   {
     const int rr = min(r, nrows - 1);
-    const uint16_t* row = (rr < a.E) ? a.router + (size_t)rr * H : a.sgate;
+    const uint16_t* row = (rr < E) ? router + (size_t)rr * H : sgate;
 #pragma unroll
     for (int j = 0; j < CPW; ++j) w[j] = *reinterpret_cast<const uint4*>(row + (lir + (j * SPLIT + piece) * R::LPR) * 8);
   }
@@ -795,7 +798,7 @@ __global__ __launch_bounds__(kBlock) void k_router_group(LayerArgs a, const floa
     if (lir == R::LPR - 1 && r < nrows) {
 #pragma unroll
       for (int g = 0; g < TG; ++g)
-        if (t0 + g < T) store_through(&a.ws.logits[(size_t)(t0 + g) * (a.E + 1) + r], tot[g]);
+        if (t0 + g < T) store_through(&a.ws.logits[(size_t)(t0 + g) * (E + 1) + r], tot[g]);
     }
   } else {
     if (lane == 63) {
@@ -809,7 +812,7 @@ __global__ __launch_bounds__(kBlock) void k_router_group(LayerArgs a, const floa
         if (t0 + g >= T) continue;
         double v = part[g][wave];
         for (int q = 1; q < SPLIT; ++q) v += part[g][wave + q];
-        store_through(&a.ws.logits[(size_t)(t0 + g) * (a.E + 1) + r], v);
+        store_through(&a.ws.logits[(size_t)(t0 + g) * (E + 1) + r], v);
       }
     }
   }
@@ -821,16 +824,17 @@ __global__ __launch_bounds__(kBlock) void k_router_group(LayerArgs a, const floa
 // number of cache lines in flight, so its time tracks the lines it touches, and the activations were
 // most of them when four 4-wave blocks shared a CU. Wave 0 of a routed block picks the expert with
 // the two-phase top-K and shares it through LDS; the shared slot's blocks, which need no routing,
-// stream their weights meanwhile. h goes straight from the row lanes to memory.
+// stream their weights meanwhile. h goes straight from the row lanes to memory. The arguments of
+// the first requests (logits, x, the caller's indices, E, K) lead the list, so they arrive
+// preloaded in SGPRs.
 constexpr int kSlice = 16;  // rows of gate and up per block
 template <int BITS, int H, int FORM, int PL, int NW>
-__global__ __launch_bounds__(64 * NW) void k_gateup(LayerArgs a, const float* __restrict__ x,
-                                                    const int32_t* __restrict__ idx_in, int32_t* __restrict__ idx_out) {
+__global__ __launch_bounds__(64 * NW) void k_gateup(const double* __restrict__ logits, const float* __restrict__ x,
+                                                    const int32_t* __restrict__ idx_in, int E, int K, LayerArgs a,
+                                                    int32_t* __restrict__ idx_out) {
   using C = RowCfg<BITS, H>;
   constexpr int NT = 64 * NW;
   constexpr bool MX = FORM == 3;
-  const int I = a.I;
-  const int NSL = I / kSlice;                            // slices per expert
   constexpr int STEPS = kSlice / C::RPW;                 // row steps of a slice (gate and up rows)
   constexpr int PW = (STEPS + NW - 1) / NW;              // row steps per wave
   constexpr int PP0 = 8 / C::CPL > 0 ? 8 / C::CPL : 1;   // steps in registers at once
@@ -844,14 +848,16 @@ __global__ __launch_bounds__(64 * NW) void k_gateup(LayerArgs a, const float* __
   const int t = blockIdx.z;
   // Routed slots in reverse when K > 4 (slot s needs top-K rounds 0..s, so the ones with the most
   // rounds start first); the shared expert's slot K stays last.
-  const bool reversed = a.K > 4;
-  const int slot = reversed && (int)blockIdx.y < a.K ? a.K - 1 - (int)blockIdx.y : (int)blockIdx.y;
-  const int bx = blockIdx.x;
-  const int slice = (NSL & 7) == 0 ? (bx & 7) * (NSL >> 3) + (bx >> 3) : bx;
+  const bool reversed = K > 4;
+  const int slot = reversed && (int)blockIdx.y < K ? K - 1 - (int)blockIdx.y : (int)blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int lir = lane % C::LPR, rig = lane / C::LPR;
-  float* hout = a.ws.h + ((size_t)t * a.NE + slot) * I + (size_t)slice * kSlice;  // this block's rows of h
-  const uint8_t* blob = a.shared;
+  // the rest of the arguments only after the first requests (below) have left
+  auto rows_of_h = [&]() __attribute__((always_inline)) {  // this block's rows of h
+    const int NSL = a.I / kSlice, bx = blockIdx.x;  // slices per expert
+    const int slice = (NSL & 7) == 0 ? (bx & 7) * (NSL >> 3) + (bx >> 3) : bx;
+    return a.ws.h + ((size_t)t * a.NE + slot) * a.I + (size_t)slice * kSlice;
+  };
+  int e = 0;
   Stage<H, NT> st;
   __shared__ int32_t chosen;
   // Wave 0 of a routed block picks the expert (the other waves would only repeat its work on the
@@ -860,21 +866,21 @@ __global__ __launch_bounds__(64 * NW) void k_gateup(LayerArgs a, const float* __
   // the gate logit's load would hold back the block's weight loads).
   bool writer = false;
   double gate_logit = 0.0;
-  const bool routed = slot < a.K;
+  const bool routed = slot < K;
   if (routed) {
     if (idx_in != nullptr) {
-      if (threadIdx.x == 0) chosen = idx_in[(size_t)t * a.K + slot];
+      if (threadIdx.x == 0) chosen = idx_in[(size_t)t * K + slot];
       st.load(x + (size_t)t * H, threadIdx.x);
     } else if (wave == 0) {
-      const double* lg = a.ws.logits + (size_t)t * (a.E + 1);
+      const double* lg = logits + (size_t)t * (E + 1);
       // the logits are requested first, so waiting for them never waits for the activations
       double v[PL];
-      load_topk_values<PL>(lg, a.E, lane, v);
-      gate_logit = lg[a.E];  // the shared-gate logit (row E), for the routing write at the end
+      load_topk_values<PL>(lg, E, lane, v);
+      gate_logit = lg[E];  // the shared-gate logit (row E), for the routing write at the end
       st.load(x + (size_t)t * H, threadIdx.x);
       writer = blockIdx.x == 0 && blockIdx.y == 0;  // in the first routed slot dispatched
       // slot s needs rounds 0..s only; the writer takes all K to record the routing
-      const int e = wave_topk_fast<PL>(v, a.E, writer ? a.K : slot + 1, lane, slot, writer, sel, val);
+      const int e = wave_topk_fast<PL>(v, E, writer ? K : slot + 1, lane, slot, writer, sel, val);
       if (lane == 0) chosen = e;
     } else {
       st.load(x + (size_t)t * H, threadIdx.x);
@@ -883,16 +889,22 @@ __global__ __launch_bounds__(64 * NW) void k_gateup(LayerArgs a, const float* __
     // as soon as its data lands, instead of waiting at a barrier behind throttled load issue
     st.template store<C>(xs, threadIdx.x, 1.0f);
     __syncthreads();
-    const int e = chosen;
-    if (e < 0 || e >= a.E) {  // a caller's index outside the pool: the slot's h is NaN, nothing is read
-      if ((int)threadIdx.x < kSlice) hout[threadIdx.x] = NAN;
+    e = chosen;
+    if (e < 0 || e >= E) {  // a caller's index outside the pool: the slot's h is NaN, nothing is read
+      if ((int)threadIdx.x < kSlice) rows_of_h()[threadIdx.x] = NAN;
       if (a.err != nullptr && threadIdx.x == 0) *a.err = MOE_EINVAL;
       return;  // the whole block takes this branch (slot is per block)
     }
-    blob = a.experts + (size_t)e * a.stride;
   } else {
     st.load(x + (size_t)t * H, threadIdx.x);
   }
+  const int I = a.I;
+  const int NSL = I / kSlice;  // slices per expert
+  const int bx = blockIdx.x;
+  const int slice = (NSL & 7) == 0 ? (bx & 7) * (NSL >> 3) + (bx >> 3) : bx;
+  const int lir = lane % C::LPR, rig = lane / C::LPR;
+  float* hout = rows_of_h();
+  const uint8_t* blob = routed ? a.experts + (size_t)e * a.stride : a.shared;
 
   // 1. weight loads: gate/up rows of the first pass
   const uint8_t* gc = blob + a.off_codes[0];
@@ -1691,7 +1703,8 @@ hipError_t router_phase_impl(const LayerArgs& a, const float* x, const float* no
   const int nrb = (nrows + rows_per_block - 1) / rows_per_block;
   if (norm_src == nullptr && T >= BQ_ROUTER_GROUP_MIN_TOKENS && router_steps == 1) {  // one read per token group
     return launch_timed(k_router_group<H, kRouterGroup>, dim3(nrb, (T + kRouterGroup - 1) / kRouterGroup),
-                        dim3(kBlock), s, ev, a, x, T);
+                        dim3(kBlock), s, ev, x, (const uint16_t*)a.router, (const uint16_t*)a.sgate, a.E,
+                        a.E + a.has_shared, T, a);
   }
   return launch_timed(k_router_phase<H>, dim3(nrb, T), dim3(kBlock), s, ev, a, x, norm_src, eps, router_steps);
 }
@@ -1708,7 +1721,9 @@ hipError_t gateup_impl(const LayerArgs& a, const float* x, int T, const int32_t*
   constexpr int NW = (H >= 64 * BQ_GATEUP_WAVES && H <= 4096) ? BQ_GATEUP_WAVES : 4;
   const int slots = a.K + ((with_shared && a.has_shared) ? 1 : 0);
   const dim3 grid(a.I / kSlice, slots, T), block(64 * NW);
-#define BQ_GU(PL, F) launch_timed(k_gateup<BITS, H, F, PL, NW>, grid, block, s, ev, a, x, idx_in, idx_out)
+#define BQ_GU(PL, F) \
+  launch_timed(k_gateup<BITS, H, F, PL, NW>, grid, block, s, ev, (const double*)a.ws.logits, x, idx_in, a.E, a.K, a, \
+               idx_out)
   if constexpr (BITS == 4) {
     if (a.form == 3) return a.E <= 512 ? BQ_GU(8, 3) : BQ_GU(16, 3);
   }
