@@ -627,13 +627,17 @@ __device__ __forceinline__ double readlane_f64(double v, int lane) {
 // ---------------------------------------------------------------------------------------------
 // Kernel 1: router logits and the shared-gate logit (row E), accumulated in fp64. In a stack the
 // input is RMS-normalised first, and the blocks together store the normalised vector for kernel 2.
+// The arguments of the first requests (the input, the router and shared-gate rows, E, the row
+// count, the row steps) lead the list, so they arrive preloaded in SGPRs.
 #ifndef BQ_ROUTER_SPLIT
 #define BQ_ROUTER_SPLIT 4
 #endif
 template <int H>
-__global__ __launch_bounds__(kBlock) void k_router_phase(LayerArgs a, const float* __restrict__ x,
-                                                         const float* __restrict__ norm_src, float eps,
-                                                         int router_steps) {
+__global__ __launch_bounds__(kBlock) void k_router_phase(const float* __restrict__ src0,
+                                                         const uint16_t* __restrict__ router,
+                                                         const uint16_t* __restrict__ sgate, int E, int nrows,
+                                                         int router_steps, LayerArgs a, const float* __restrict__ x,
+                                                         const float* __restrict__ norm_src, float eps) {
   using R = RouterCfg<H>;
   constexpr int SPLIT = (R::CPL % BQ_ROUTER_SPLIT == 0) ? BQ_ROUTER_SPLIT : 1;  // waves per row
   constexpr int CPW = R::CPL / SPLIT;                                            // chunks per lane
@@ -642,7 +646,6 @@ __global__ __launch_bounds__(kBlock) void k_router_phase(LayerArgs a, const floa
   const int t = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int lir = lane % R::LPR, rig = lane / R::LPR;
-  const int nrows = a.E + a.has_shared;
   const int piece = wave % SPLIT;
   auto row_of = [&](int s) {
     const int base = ((blockIdx.x * (kWaves / SPLIT) + wave / SPLIT) * router_steps + s) * R::RPW;
@@ -650,14 +653,14 @@ __global__ __launch_bounds__(kBlock) void k_router_phase(LayerArgs a, const floa
   };
   auto load_w = [&](int s, uint4 (&w)[CPW]) {
     const int rr = min(row_of(s), nrows - 1);
-    const uint16_t* row = (rr < a.E) ? a.router + (size_t)rr * H : a.sgate;
+    const uint16_t* row = (rr < E) ? router + (size_t)rr * H : sgate;
 #pragma unroll
     for (int j = 0; j < CPW; ++j) w[j] = *reinterpret_cast<const uint4*>(row + (lir + (j * SPLIT + piece) * R::LPR) * 8);
   };
   // The norm's scale is a scalar, so a row's dot product with the raw input is taken first and
   // scaled at the end: sum_j R[e][j] (s h_j) = s sum_j R[e][j] h_j, with every product exact in fp64.
   const bool norm = norm_src != nullptr;
-  const float* src = (norm ? norm_src : x) + (size_t)t * H;
+  const float* src = src0 + (size_t)t * H;  // norm_src when norm, else x
   uint4 w[CPW];
   float4 xr[CPW][2];
   load_w(0, w);
@@ -704,7 +707,7 @@ __global__ __launch_bounds__(kBlock) void k_router_phase(LayerArgs a, const floa
     }
     const double tot = seg_sum<R::LPR>((acc[0] + acc[1]) + (acc[2] + acc[3]));
     if constexpr (SPLIT == 1) {
-      if (lir == R::LPR - 1 && r < nrows) store_through(&a.ws.logits[(size_t)t * (a.E + 1) + r], norm ? tot * scale : tot);
+      if (lir == R::LPR - 1 && r < nrows) store_through(&a.ws.logits[(size_t)t * (E + 1) + r], norm ? tot * scale : tot);
     } else {
       if (lane == 63) part[wave] = tot;
       __syncthreads();
@@ -716,7 +719,7 @@ __global__ __launch_bounds__(kBlock) void k_router_phase(LayerArgs a, const floa
       if (piece == 0 && lane == 63 && r < nrows) {
         double v = part[wave];
         for (int q = 1; q < SPLIT; ++q) v += part[wave + q];
-        store_through(&a.ws.logits[(size_t)t * (a.E + 1) + r], norm ? v * scale : v);
+        store_through(&a.ws.logits[(size_t)t * (E + 1) + r], norm ? v * scale : v);
       }
       __syncthreads();
     }
@@ -1706,7 +1709,9 @@ hipError_t router_phase_impl(const LayerArgs& a, const float* x, const float* no
                         dim3(kBlock), s, ev, x, (const uint16_t*)a.router, (const uint16_t*)a.sgate, a.E,
                         a.E + a.has_shared, T, a);
   }
-  return launch_timed(k_router_phase<H>, dim3(nrb, T), dim3(kBlock), s, ev, a, x, norm_src, eps, router_steps);
+  return launch_timed(k_router_phase<H>, dim3(nrb, T), dim3(kBlock), s, ev, norm_src != nullptr ? norm_src : x,
+                      (const uint16_t*)a.router, (const uint16_t*)a.sgate, a.E, a.E + a.has_shared, router_steps, a,
+                      x, norm_src, eps);
 }
 
 // Waves per gate/up block: 8 (two per SIMD, so one computes while the other waits), except where a
