@@ -13,9 +13,9 @@ OBJ = os.path.join(HERE, "_build")
 # -packed-fp32-ops: keep the compiler from forming packed fp32 instructions.
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-             # leading scalar kernel arguments (up to six) preloaded into SGPRs at wave launch, so
+             # leading scalar kernel arguments (up to eight) preloaded into SGPRs at wave launch, so
              # the decode kernels' first loads wait for no kernel-argument fetch
-             "-mllvm", "-amdgpu-kernarg-preload-count=6",
+             "-mllvm", "-amdgpu-kernarg-preload-count=8",
              "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 SOURCES = ["moe_host.cpp", "moe_kernels.hip", "moe_prefill.hip"]
 

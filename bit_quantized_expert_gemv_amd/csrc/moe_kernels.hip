@@ -961,8 +961,9 @@ __global__ __launch_bounds__(64 * NW) void k_gateup(const double* __restrict__ l
 // barrier does not wait for that load.
 template <int BITS, int I, int P0, int FORM>
 __global__ __launch_bounds__(2 * kBlock) void k_down(const float* __restrict__ h, const int32_t* __restrict__ idx,
-                                                 int ne, int K, LayerArgs a, const float* __restrict__ residual,
-                                                 float* __restrict__ out, float* __restrict__ y) {
+                                                 int ne, int K, int H, const uint8_t* __restrict__ sdc,
+                                                 const uint8_t* __restrict__ sds, const float* __restrict__ residual,
+                                                 LayerArgs a, float* __restrict__ out, float* __restrict__ y) {
   using C = RowCfg<BITS, I>;
   constexpr int RB = C::RPW * P0;
   constexpr int P = P0 >= 2 ? P0 / 2 : 1;
@@ -995,7 +996,7 @@ __global__ __launch_bounds__(2 * kBlock) void k_down(const float* __restrict__ h
   __builtin_amdgcn_sched_barrier(0);
   const int lir = lane % C::LPR, rig = lane / C::LPR;
   const int row0 = blockIdx.x * RB + half * P * C::RPW;
-  const bool combine = out != nullptr;
+  const bool combine = residual != nullptr;  // the host passes a residual exactly when out is set
   bool first = true;
   static_assert(RB <= 2 * kBlock, "one combined row per thread");
   float res = 0.0f;
@@ -1011,28 +1012,31 @@ __global__ __launch_bounds__(2 * kBlock) void k_down(const float* __restrict__ h
     // the vector loads issued before them.
     const bool work = active && k < ne;
     const int kk = min(k, ne - 1);
-    // selects, not branches: a branch lets the compiler sink the index read behind other waits
+    // the shared slot's down rows come from preloaded arguments, so its waves request them at once;
+    // a routed slot's wait for its index and the layout arguments together
     const bool routed = kk < K;
-    const bool valid = !routed || (e >= 0 && e < a.E);
-    const uint8_t* blob = routed ? a.experts + (size_t)(valid ? e : 0) * a.stride : a.shared;
-    // the combine coefficient's address; the value is read after the barrier below, so that the
-    // barrier does not wait for it
-    const float* cp = routed ? a.ws.w + (size_t)t * K + kk : a.ws.g + t;
+    bool valid = true;
+    const uint8_t* dc = sdc;
+    const uint8_t* ds = sds;
+    if (routed) {
+      valid = e >= 0 && e < a.E;
+      const uint8_t* blob = a.experts + (size_t)(valid ? e : 0) * a.stride;
+      dc = blob + a.off_codes[2];
+      ds = blob + a.off_sb[2];
+    }
     uint4 cw[P][C::CPL];
     uint32_t sb[P][C::CPL];
-    {
-      const uint8_t* dc = blob + a.off_codes[2];
-      const uint8_t* ds = blob + a.off_sb[2];
 #pragma unroll
-      for (int p = 0; p < P; ++p)
-        load_row<C, FORM == 3>(dc, ds, min(row0 + p * C::RPW + rig, a.H - 1), lir, cw[p], sb[p]);
-    }
+    for (int p = 0; p < P; ++p) load_row<C, FORM == 3>(dc, ds, min(row0 + p * C::RPW + rig, H - 1), lir, cw[p], sb[p]);
+    __builtin_amdgcn_sched_barrier(0);
     // the residual row, behind this wave's weight loads: read at the end, it cost the combine a
     // memory round trip (decode4 13.96 -> 13.93, decodemx 19.09 -> 18.97 us/token); requested
     // first, together with the expert index, it delayed the weight loads (13.98 -> 14.50)
-    if (q == 0 && combine && (int)threadIdx.x < RB && blockIdx.x * RB + threadIdx.x < a.H)
-      res = residual[(size_t)t * a.H + blockIdx.x * RB + threadIdx.x];
-    __builtin_amdgcn_sched_barrier(0);
+    if (q == 0 && combine && (int)threadIdx.x < RB && blockIdx.x * RB + threadIdx.x < H)
+      res = residual[(size_t)t * H + blockIdx.x * RB + threadIdx.x];
+    // the combine coefficient's address; the value is read after the barrier below, so that the
+    // barrier does not wait for it
+    const float* cp = routed ? a.ws.w + (size_t)t * K + kk : a.ws.g + t;
     auto park = [&](int j, const float4& hv) __attribute__((always_inline)) {
       const int i = min((int)threadIdx.x + j * 2 * kBlock, nk * N4 - 1);
       const int v = i / N4, f = i % N4;
@@ -1059,13 +1063,13 @@ __global__ __launch_bounds__(2 * kBlock) void k_down(const float* __restrict__ h
 #pragma unroll
       for (int p = 0; p < P; ++p) {
         const int r = row0 + p * C::RPW + rig;
-        if (r >= a.H) continue;
+        if (r >= H) continue;
         if (combine) {
           const float v = coef * yv[p];
           const int i = half * P * C::RPW + p * C::RPW + rig;
           part[wave][i] = first ? v : part[wave][i] + v;
         } else {
-          y[((size_t)t * ne + k) * a.H + r] = yv[p];
+          y[((size_t)t * ne + k) * H + r] = yv[p];
         }
       }
     }
@@ -1075,11 +1079,11 @@ __global__ __launch_bounds__(2 * kBlock) void k_down(const float* __restrict__ h
   __syncthreads();
   for (int i = threadIdx.x; i < RB; i += 2 * kBlock) {
     const int r = blockIdx.x * RB + i;
-    if (r >= a.H) continue;
+    if (r >= H) continue;
     const int hw = (i / (P * C::RPW)) * kWaves;
     float acc = res;
     for (int w = 0; w < kWaves && w < ne; ++w) acc += part[hw + w][i];
-    store_through(&out[(size_t)t * a.H + r], acc);
+    store_through(&out[(size_t)t * H + r], acc);
   }
 }
 
@@ -1745,7 +1749,9 @@ hipError_t down_impl(const LayerArgs& a, int T, const int32_t* idx, const float*
   const bool two_rounds = a.NE > kWaves;
   const int RB = C::RPW * (two_rounds ? P8 : P16);
   const int nb = (a.H + RB - 1) / RB;
-#define BQ_DN(P, F) launch_timed(k_down<BITS, I, P, F>, dim3(nb, T), dim3(2 * kBlock), s, ev, (const float*)a.ws.h, idx, a.NE, a.K, a, residual, out, y)
+#define BQ_DN(P, F) launch_timed(k_down<BITS, I, P, F>, dim3(nb, T), dim3(2 * kBlock), s, ev, (const float*)a.ws.h, idx, a.NE, a.K, a.H, \
+                                        (const uint8_t*)a.shared + a.off_codes[2], (const uint8_t*)a.shared + a.off_sb[2], \
+                                        residual, a, out, y)
   if constexpr (BITS == 4) {
     if (a.form == 3) return two_rounds ? BQ_DN(P8, 3) : BQ_DN(P16, 3);
   }
@@ -1810,6 +1816,7 @@ hipError_t launch_gateup(const Geometry& g, const LayerPtrs& p, const float* x, 
 
 hipError_t launch_down(const Geometry& g, const LayerPtrs& p, int T, const Workspace& ws, const int32_t* idx,
                        const float* residual, float* out, float* y, hipStream_t s, const KernelEvents& ev) {
+  if ((residual == nullptr) != (out == nullptr)) return hipErrorInvalidValue;  // k_down combines iff residual
   const LayerArgs a = make_args(g, p, ws);
 #define BQ_CASE(IV)                                                                        \
   case IV:                                                                                 \
